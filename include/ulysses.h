@@ -1,0 +1,171 @@
+/*
+ * ulysses.h -- C ABI of one GPU's share of a Ulysses sequence-parallel attention layer
+ * on MI355X (gfx950).
+ *
+ * What the share computes (pages: "Ulysses Sequence Parallelism: Training with
+ * Million-Token Contexts", section "how Ulysses works", steps 1-5; tilnote.io
+ * commentary, sections on what Ulysses changes and on activation memory):
+ *   1. the local half of the first all-to-all: P sequence shards [s_l, H, d] (every
+ *      head, a contiguous token chunk each) become one head shard [s, H/P, d]
+ *      (every position, this rank's heads)                         -> ulysses_pack
+ *   2. dense causal (optionally packed-document) attention over the whole sequence
+ *      for the head shard, forward and backward                    -> attn_fwd, attn_bwd
+ *   3. the local half of the second all-to-all: the head shard goes back to the
+ *      sequence shards                                             -> ulysses_unpack
+ *   4. the UPipe schedule: 1-3 run a few heads at a time so that the attention
+ *      intermediates stay small                                    -> attn_fwd_chunked
+ * The P ranks are P separate device buffers on one GPU; no collective runs here.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers; arrays of pointers (the P shards) are HOST
+ *     arrays read during the call only. Layouts are row-major with d fastest:
+ *     a sequence shard is [s_l, H, d], a head shard [s, H_l, d], LSE [H_l, s] fp32.
+ *   - Rank p holds tokens [p*s_l, (p+1)*s_l); rank r owns q heads [r*Hq/P, (r+1)*Hq/P)
+ *     and kv heads [r*Hkv/P, (r+1)*Hkv/P). q head h reads kv head h / (Hq/Hkv).
+ *   - dtype: ULY_BF16 (the tuned path; fp32 accumulation inside) or ULY_F32.
+ *     d must be 64 or 128 (ULY_F32: 64 only).
+ *   - Every call enqueues work on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream), returns without synchronising and allocates nothing. The caller
+ *     owns every buffer. Inputs and outputs must not overlap.
+ *   - All arguments are checked on the host before any launch; on error nothing is
+ *     enqueued and the status says why. Device-array contents (cu_seqlens) are a
+ *     precondition and are not checked.
+ *   - Base pointers must be 16-byte aligned.
+ *   - Status codes are the uly_status values below; uly_status_string() names them.
+ */
+#ifndef ULYSSES_H
+#define ULYSSES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ULY_BF16 = 0, ULY_F32 = 1 } uly_dtype;
+
+typedef enum {
+  ULY_OK = 0,
+  ULY_ERR_NULL = 1,        /* a required pointer is NULL */
+  ULY_ERR_SHAPE = 2,       /* sizes inconsistent: P, rank, H % P, Hq % Hkv, s, ... */
+  ULY_ERR_UNSUPPORTED = 3, /* dtype / head_dim combination not built */
+  ULY_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned */
+  ULY_ERR_WORKSPACE = 5,   /* workspace smaller than required */
+  ULY_ERR_HIP = 6          /* a HIP launch or runtime call failed */
+} uly_status;
+
+#define ULY_MAX_RANKS 64
+
+/* Name of a status code (static string). */
+const char* uly_status_string(int status);
+
+/* ABI version, bumped on any signature change. */
+int uly_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * ulysses_pack -- local half of the first all-to-all (sequence shards -> head shard).
+ * Pages: "how Ulysses works" steps 1 and 3 (each GPU ends up holding every sequence
+ * position for a subset of heads); tilnote.io, section on what Ulysses changes.
+ *   shards : host array of P device pointers, shard p is [s_l, H, d] of `dtype`
+ *   P      : number of ranks, 1..ULY_MAX_RANKS;  rank in [0, P)
+ *   H      : global head count, divisible by P (the commentary's divisibility rule)
+ *   out    : device [P*s_l, H/P, d]; out[p*s_l + t, j, :] = shard_p[t, rank*H/P + j, :]
+ * Bits are copied unchanged (bit-exact).
+ * ------------------------------------------------------------------------- */
+int ulysses_pack(const void* const* shards, int P, int rank, int64_t s_l, int H, int d,
+                 int dtype, void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ulysses_unpack -- local half of the second all-to-all (head shard -> sequence shards);
+ * also the backward of ulysses_pack. Pages: "how Ulysses works" step 5.
+ *   in     : device [P*s_l, H/P, d]
+ *   shards : host array of P device pointers [s_l, H, d]; for every p, t, j:
+ *            shard_p[t, rank*H/P + j, :] = in[p*s_l + t, j, :]. Other heads untouched.
+ * ------------------------------------------------------------------------- */
+int ulysses_unpack(const void* in, int P, int rank, int64_t s_l, int H, int d, int dtype,
+                   void* const* shards, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * attn_fwd -- attention forward of one head shard. Pages: "how Ulysses works" step 4
+ * (local FlashAttention/SDPA on the assigned heads over every position); the
+ * long-sequence section (FlashAttention: exact attention in O(n) memory); TRL
+ * SFTTrainer section (packed documents).
+ *   q [s, Hq, d], k, v [s, Hkv, d] : device, `dtype`; Hq = local q heads, Hq % Hkv == 0
+ *   o [s, Hq, d]                   : device, `dtype`, written
+ *   lse [Hq, s]                    : device fp32, written; natural-log log-sum-exp of
+ *                                    each row's visible scaled scores
+ *   scale  : multiplies q.k (1/sqrt(d) for the standard layer)
+ *   causal : 1 -> key j visible to row i iff j <= i; 0 -> all keys
+ *   cu_seqlens : NULL, or device int32 [n_docs + 1], 0 = cu[0] < ... < cu[n_docs] = s;
+ *                keys are then further restricted to the row's own document
+ * Every row must see at least one key (true whenever causal or cu_seqlens is used).
+ * ------------------------------------------------------------------------- */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
+             const int32_t* cu_seqlens, int n_docs, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * attn_bwd -- attention backward of one head shard: dq, dk, dv from dout, given the
+ * forward's o and lse. Runs attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq.
+ * The gradient of a kv head sums the G = Hq/Hkv q heads that read it.
+ *   q, k, v, o, lse, dout : as produced/consumed by attn_fwd (dout shaped like o)
+ *   dq [s, Hq, d], dk, dv [s, Hkv, d] : device `dtype`, written (fully overwritten)
+ *   workspace : device scratch of at least attn_bwd_workspace_bytes(s, Hq) bytes.
+ *               If workspace == NULL the call only stores that size into
+ *               *workspace_bytes and returns ULY_OK. Otherwise *workspace_bytes (if
+ *               workspace_bytes != NULL) is the capacity and is checked.
+ * Deterministic: no atomics, every output element is written by one thread.
+ * ------------------------------------------------------------------------- */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv,
+             int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
+             const int32_t* cu_seqlens, int n_docs,
+             void* workspace, size_t* workspace_bytes, void* stream);
+
+size_t attn_bwd_workspace_bytes(int64_t s, int Hq);
+
+/* The three phases of attn_bwd, exported so that each can be timed on its own.
+ * delta [Hq, s] fp32: delta[h, i] = sum_x dout[i, h, x] * o[i, h, x].            */
+int attn_bwd_preprocess(const void* o, const void* dout, float* delta,
+                        int64_t s, int Hq, int d, int dtype, void* stream);
+/* dk, dv for every key: per kv head, loops over the rows of its G q heads.        */
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                  const void* dout, const float* delta, void* dk, void* dv,
+                  int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
+                  const int32_t* cu_seqlens, int n_docs, void* stream);
+/* dq for every row: loops over the visible keys.                                   */
+int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                const void* dout, const float* delta, void* dq,
+                int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
+                const int32_t* cu_seqlens, int n_docs, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * attn_fwd_chunked -- the UPipe headwise-chunked forward of rank `rank` (tilnote.io
+ * commentary, section on activation memory: process a few heads at a time to cut the
+ * memory of attention intermediates). For each chunk of `heads_per_chunk` local q
+ * heads (the last chunk may be smaller): pack those q heads and the kv heads they read
+ * (kv heads are re-packed only when the range changes), run the forward, unpack the
+ * chunk's output into the o shards. Same results as ulysses_pack + attn_fwd +
+ * ulysses_unpack, with smaller intermediates.
+ *   q_shards / o_shards : host arrays of P device pointers [s_l, Hq, d] (global Hq)
+ *   k_shards / v_shards : host arrays of P device pointers [s_l, Hkv, d]
+ *   lse : device fp32 [Hq/P, s], written for this rank's heads
+ *   workspace : at least attn_fwd_chunked_workspace_bytes(...) bytes; NULL -> size query
+ *               into *workspace_bytes as for attn_bwd. This is the peak intermediate
+ *               memory of the schedule.
+ * ------------------------------------------------------------------------- */
+int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards,
+                     const void* const* v_shards, void* const* o_shards, float* lse,
+                     int P, int rank, int64_t s_l, int Hq, int Hkv, int d, int dtype,
+                     float scale, int causal, const int32_t* cu_seqlens, int n_docs,
+                     int heads_per_chunk, void* workspace, size_t* workspace_bytes,
+                     void* stream);
+
+size_t attn_fwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int d,
+                                        int dtype, int heads_per_chunk);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ULYSSES_H */

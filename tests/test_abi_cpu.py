@@ -1,0 +1,140 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the header
+declares, and rejects bad arguments on the host before touching the device.
+
+Only calls that fail validation (or only report sizes) run here; nothing is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ulysses_sequence_parallelism_rank_amd as U
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ulysses.h")
+
+FAKE = 0x10000   # 16-byte aligned stand-in for a device pointer; never dereferenced
+MIS = 0x10008    # misaligned stand-in
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\**\s+\**([a-z_][a-z0-9_]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_parses():
+    names = declared_functions()
+    for want in ("ulysses_pack", "ulysses_unpack", "attn_fwd", "attn_bwd", "attn_fwd_chunked"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(U.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(U.SIGNATURES)
+
+
+def test_status_strings_and_version():
+    L = U.lib()
+    assert L.uly_abi_version() == 1
+    for code, name in U.STATUS.items():
+        assert L.uly_status_string(code).decode() == name
+
+
+def _ptr_array(vals):
+    arr = (ctypes.c_void_p * len(vals))(*vals)
+    return ctypes.cast(arr, U._vpp), arr
+
+
+@pytest.mark.parametrize("P,rank,s_l,H,d,dt,want", [
+    (0, 0, 4, 4, 64, 0, 2), (65, 0, 4, 65, 64, 0, 2), (2, 2, 4, 4, 64, 0, 2), (2, -1, 4, 4, 64, 0, 2),
+    (2, 0, 0, 4, 64, 0, 2), (3, 0, 4, 4, 64, 0, 2), (2, 0, 4, 4, 64, 7, 3), (2, 0, 4, 2, 4, 0, 4),
+])
+def test_pack_rejects(P, rank, s_l, H, d, dt, want):
+    L = U.lib()
+    pp, keep = _ptr_array([FAKE] * max(P, 1))
+    assert L.ulysses_pack(pp, P, rank, s_l, H, d, dt, FAKE, None) == want
+    assert L.ulysses_unpack(FAKE, P, rank, s_l, H, d, dt, pp, None) == want
+
+
+def test_pack_null_and_alignment():
+    L = U.lib()
+    pp, keep = _ptr_array([FAKE, None])
+    assert L.ulysses_pack(pp, 2, 0, 4, 4, 64, 0, FAKE, None) == 1
+    assert L.ulysses_pack(None, 2, 0, 4, 4, 64, 0, FAKE, None) == 1
+    pp, keep = _ptr_array([FAKE, MIS])
+    assert L.ulysses_pack(pp, 2, 0, 4, 4, 64, 0, FAKE, None) == 4
+    pp, keep = _ptr_array([FAKE, FAKE])
+    assert L.ulysses_pack(pp, 2, 0, 4, 4, 64, 0, MIS, None) == 4
+
+
+def _fwd(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, s=16, Hq=4, Hkv=2, d=128, dt=0, scale=0.1,
+                causal=1, cu=None, nd=0)
+    args.update(kw)
+    a = args
+    return U.lib().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["s"], a["Hq"], a["Hkv"], a["d"],
+                            a["dt"], a["scale"], a["causal"], a["cu"], a["nd"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
+    (dict(Hq=3, Hkv=2), 2), (dict(s=0), 2), (dict(Hkv=0), 2), (dict(cu=FAKE, nd=0), 2),
+    (dict(d=96), 3), (dict(dt=1, d=128), 3), (dict(dt=5), 3),
+    (dict(k=MIS), 4), (dict(o=MIS), 4),
+])
+def test_attn_fwd_rejects(kw, want):
+    assert _fwd(**kw) == want
+
+
+def test_bwd_workspace_query_and_checks():
+    L = U.lib()
+    need = ctypes.c_size_t(0)
+    z = [FAKE] * 9
+    st = L.attn_bwd(*z, 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None, ctypes.byref(need), None)
+    assert st == 0 and need.value == L.attn_bwd_workspace_bytes(1000, 8) and need.value >= 1000 * 8 * 4
+    small = ctypes.c_size_t(need.value - 1)
+    assert L.attn_bwd(*z, 1000, 8, 2, 128, 0, 0.1, 1, None, 0, FAKE, ctypes.byref(small), None) == 5
+    assert L.attn_bwd(*z, 1000, 8, 3, 128, 0, 0.1, 1, None, 0, None, ctypes.byref(need), None) == 2
+    assert L.attn_bwd(*z, 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None, None, None) == 1
+    assert L.attn_bwd_preprocess(FAKE, None, FAKE, 10, 2, 128, 0, None) == 1
+    assert L.attn_bwd_dkdv(*[FAKE] * 8, 10, 4, 3, 128, 0, 0.1, 1, None, 0, None) == 2
+    assert L.attn_bwd_dq(*[FAKE] * 7, 10, 4, 2, 100, 0, 0.1, 1, None, 0, None) == 3
+
+
+def test_chunked_workspace_matches_upipe_accounting():
+    L = U.lib()
+    MiB = 2 ** 20
+    # 262144 tokens, 64 q / 8 kv heads, P = 8, d = 128, bf16
+    assert L.attn_fwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 1) == 256 * MiB
+    assert L.attn_fwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 2) == 384 * MiB
+    assert L.attn_fwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 8) == 1152 * MiB
+    assert L.attn_fwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 0) == 0
+
+
+def test_chunked_rejects():
+    L = U.lib()
+    pp, keep = _ptr_array([FAKE] * 2)
+    need = ctypes.c_size_t(0)
+    args = lambda **kw: dict(dict(P=2, rank=0, s_l=8, Hq=8, Hkv=4, d=64, dt=0, u=1), **kw)
+
+    def call(ws=None, cap=None, **kw):
+        a = args(**kw)
+        return L.attn_fwd_chunked(pp, pp, pp, pp, FAKE, a["P"], a["rank"], a["s_l"], a["Hq"], a["Hkv"], a["d"],
+                                  a["dt"], 0.1, 1, None, 0, a["u"], ws, cap, None)
+    assert call(cap=ctypes.byref(need)) == 0 and need.value > 0
+    assert call(cap=ctypes.byref(need), u=0) == 2
+    assert call(cap=ctypes.byref(need), Hkv=3) == 2
+    assert call(cap=ctypes.byref(need), Hq=6, Hkv=3) == 2    # Hkv % P
+    assert call(cap=ctypes.byref(need), rank=2) == 2
+    small = ctypes.c_size_t(need.value - 256)
+    assert call(ws=FAKE, cap=ctypes.byref(small)) == 5
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        U.attn_fwd(x, x, x)

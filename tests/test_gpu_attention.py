@@ -1,0 +1,99 @@
+"""GPU parity of the attention forward and backward against the fp64 oracle.
+
+Small and medium cases compare every element; edge cases cover one token, ragged tails
+that are not a multiple of any tile, noncausal attention, packed documents of length 1,
+and both head dims. Tolerances are stated in tests/helpers.py."""
+import numpy as np
+import pytest
+import torch
+
+import ulysses_sequence_parallelism_rank_amd as U
+import workloads as W
+from oracle import attention as OA
+from tests.helpers import LSE_ABS, compare, dev_to_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(s, Hq, Hkv, d, dtype, seed, amp=1.0):
+    rng = np.random.default_rng(seed)
+    mk = lambda H, a: rng.standard_normal((s, H, d), dtype=np.float32) * np.float32(a)
+    host = {"q": mk(Hq, amp), "k": mk(Hkv, amp), "v": mk(Hkv, amp), "do": mk(Hq, 1.0)}
+    bits = {n: (W.to_bf16_bits(x) if dtype == "bf16" else x.view(np.uint32)) for n, x in host.items()}
+    f64 = {n: W.bits_to_f64(b, dtype) for n, b in bits.items()}
+    dev = {n: to_dev(b, dtype) for n, b in bits.items()}
+    return f64, dev
+
+
+CASES = [
+    # s, Hq, Hkv, d, dtype, causal, cu
+    (1, 2, 1, 128, "bf16", True, None),
+    (31, 4, 4, 64, "bf16", True, None),
+    (257, 8, 2, 128, "bf16", True, None),
+    (600, 4, 1, 128, "bf16", True, None),
+    (600, 4, 2, 64, "bf16", False, None),
+    (777, 2, 1, 128, "bf16", True, [0, 1, 2, 100, 101, 390, 777]),
+    (520, 4, 2, 128, "bf16", False, [0, 300, 301, 520]),
+    (1024, 8, 2, 128, "bf16", True, None),
+    (300, 4, 2, 64, "f32", True, None),
+    (200, 2, 1, 64, "f32", True, [0, 1, 57, 200]),
+    (130, 2, 2, 64, "f32", False, None),
+]
+
+
+@pytest.mark.parametrize("s,Hq,Hkv,d,dtype,causal,cu", CASES)
+def test_fwd_bwd_matches_oracle(s, Hq, Hkv, d, dtype, causal, cu):
+    print(f"case s={s} Hq={Hq} Hkv={Hkv} d={d} {dtype} causal={causal} cu={cu is not None}", flush=True)
+    f, g = _inputs(s, Hq, Hkv, d, dtype, seed=s + Hq)
+    scale = 1.0 / np.sqrt(d)
+    cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    o, lse = U.attn_fwd(g["q"], g["k"], g["v"], scale, causal, cu_dev)
+    dq, dk, dv = U.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale, causal, cu_dev)
+    torch.cuda.synchronize()
+    wo, wl = OA.forward(f["q"], f["k"], f["v"], scale, causal, cu)
+    wq, wk, wv = OA.backward(f["q"], f["k"], f["v"], f["do"], scale, causal, cu)
+    compare("O", dev_to_f64(o), wo, bf16=(dtype == "bf16"))
+    compare("LSE", lse.cpu().numpy(), wl, max_abs=LSE_ABS, rel_fro=1e-4)
+    compare("dQ", dev_to_f64(dq), wq, bf16=(dtype == "bf16"))
+    compare("dK", dev_to_f64(dk), wk, bf16=(dtype == "bf16"))
+    compare("dV", dev_to_f64(dv), wv, bf16=(dtype == "bf16"))
+
+
+def test_deterministic():
+    f, g = _inputs(700, 8, 2, 128, "bf16", seed=3)
+    outs = []
+    for _ in range(2):
+        o, lse = U.attn_fwd(g["q"], g["k"], g["v"])
+        dq, dk, dv = U.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"])
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (o, lse, dq, dk, dv)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.float32 else a, b.view(torch.uint8)
+                           if b.dtype != torch.float32 else b)
+
+
+def test_phases_compose_to_attn_bwd():
+    f, g = _inputs(333, 4, 2, 128, "bf16", seed=4)
+    o, lse = U.attn_fwd(g["q"], g["k"], g["v"])
+    dq, dk, dv = U.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"])
+    delta = U.attn_bwd_preprocess(o, g["do"])
+    dk2, dv2 = U.attn_bwd_dkdv(g["q"], g["k"], g["v"], lse, g["do"], delta)
+    dq2 = U.attn_bwd_dq(g["q"], g["k"], g["v"], lse, g["do"], delta)
+    torch.cuda.synchronize()
+    want_delta = (dev_to_f64(o) * dev_to_f64(g["do"])).sum(-1).T
+    np.testing.assert_allclose(delta.cpu().numpy(), want_delta, rtol=1e-5, atol=1e-5)
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_q_zero_gives_prefix_means():
+    s, d = 500, 128
+    f, g = _inputs(s, 2, 1, d, "bf16", seed=5)
+    q0 = torch.zeros_like(g["q"])
+    o, lse = U.attn_fwd(q0, g["k"], g["v"])
+    torch.cuda.synchronize()
+    v = f["v"][:, 0]
+    want = np.cumsum(v, axis=0) / np.arange(1, s + 1)[:, None]
+    for h in range(2):
+        compare(f"O head {h}", dev_to_f64(o)[:, h], want, bf16=True)
+    np.testing.assert_allclose(lse.cpu().numpy(), np.log(np.arange(1, s + 1))[None, :].repeat(2, 0), atol=1e-4)

@@ -1,0 +1,230 @@
+"""Python binding of libulysses: one GPU's share of a Ulysses attention layer on MI355X.
+
+Argument marshalling only. Every step runs in the HIP kernels of libulysses.so (built
+in-tree by `_build.py`); torch supplies device memory and the current stream. If the
+library is missing, every call raises: there is no fallback path.
+
+The names follow the C ABI in include/ulysses.h:
+  ulysses_pack, ulysses_unpack        -- local halves of the two all-to-alls
+  attn_fwd, attn_bwd                  -- attention of one head shard
+  attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq -- the phases of attn_bwd
+  attn_fwd_chunked                    -- the UPipe headwise-chunked forward
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libulysses.so")
+
+ULY_BF16, ULY_F32 = 0, 1
+STATUS = {0: "ULY_OK", 1: "ULY_ERR_NULL", 2: "ULY_ERR_SHAPE", 3: "ULY_ERR_UNSUPPORTED",
+          4: "ULY_ERR_ALIGN", 5: "ULY_ERR_WORKSPACE", 6: "ULY_ERR_HIP"}
+MAX_RANKS = 64
+
+_lib = None
+
+_vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_vpp = ctypes.POINTER(ctypes.c_void_p)
+_szp = ctypes.POINTER(ctypes.c_size_t)
+
+SIGNATURES = {
+    "uly_status_string": (ctypes.c_char_p, [_i32]),
+    "uly_abi_version": (_i32, []),
+    "ulysses_pack": (_i32, [_vpp, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp]),
+    "ulysses_unpack": (_i32, [_vp, _i32, _i32, _i64, _i32, _i32, _i32, _vpp, _vp]),
+    "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp]),
+    "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
+                        _vp, _i32, _vp, _szp, _vp]),
+    "attn_bwd_workspace_bytes": (_sz, [_i64, _i32]),
+    "attn_bwd_preprocess": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
+    "attn_bwd_dkdv": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
+                             _vp, _i32, _vp]),
+    "attn_bwd_dq": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
+                           _vp, _i32, _vp]),
+    "attn_fwd_chunked": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
+                                _i32, _vp, _i32, _i32, _vp, _szp, _vp]),
+    "attn_fwd_chunked_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
+}
+
+
+class UlyssesError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+def lib():
+    """Load libulysses.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libulysses.so not built at {LIB_PATH}; run "
+                               "`python -m ulysses_sequence_parallelism_rank_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _call(name, *args):
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise UlyssesError(name, st)
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return ULY_BF16
+    if t.dtype == torch.float32:
+        return ULY_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t):
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _ptrs(ts):
+    arr = (ctypes.c_void_p * len(ts))(*[_dev(t) for t in ts])
+    return ctypes.cast(arr, _vpp), arr
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _cu(cu_seqlens):
+    if cu_seqlens is None:
+        return None, 0
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    return _dev(cu_seqlens), cu_seqlens.numel() - 1
+
+
+def ulysses_pack(shards, rank, out=None):
+    """P sequence shards [s_l, H, d] -> this rank's head shard [P*s_l, H/P, d]."""
+    P = len(shards)
+    s_l, H, d = shards[0].shape
+    if out is None:
+        out = torch.empty((P * s_l, H // P, d), dtype=shards[0].dtype, device=shards[0].device)
+    pp, _keep = _ptrs(shards)
+    _call("ulysses_pack", pp, P, rank, s_l, H, d, _dtype(shards[0]), _dev(out), _stream())
+    return out
+
+
+def ulysses_unpack(y, rank, shards):
+    """Head shard [P*s_l, H/P, d] -> head slice `rank` of the P shards [s_l, H, d] (in place)."""
+    P = len(shards)
+    s_l, H, d = shards[0].shape
+    pp, _keep = _ptrs(shards)
+    _call("ulysses_unpack", _dev(y), P, rank, s_l, H, d, _dtype(y), pp, _stream())
+    return shards
+
+
+def _default_scale(d, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def attn_fwd(q, k, v, scale=None, causal=True, cu_seqlens=None, out=None, lse=None):
+    """q [s, Hq, d], k, v [s, Hkv, d] -> (o [s, Hq, d], lse [Hq, s] fp32)."""
+    s, Hq, d = q.shape
+    Hkv = k.shape[1]
+    o = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((Hq, s), dtype=torch.float32, device=q.device)
+    cu, nd = _cu(cu_seqlens)
+    _call("attn_fwd", _dev(q), _dev(k), _dev(v), _dev(o), _dev(lse), s, Hq, Hkv, d, _dtype(q),
+          _default_scale(d, scale), int(causal), cu, nd, _stream())
+    return o, lse
+
+
+def attn_bwd_workspace_bytes(s, Hq):
+    return int(lib().attn_bwd_workspace_bytes(s, Hq))
+
+
+def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=True, cu_seqlens=None, workspace=None,
+             dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv) of the attention forward, given its o and lse and dout."""
+    s, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_bytes(s, Hq)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    cu, nd = _cu(cu_seqlens)
+    _call("attn_bwd", _dev(q), _dev(k), _dev(v), _dev(o), _dev(lse), _dev(dout), _dev(dq), _dev(dk), _dev(dv),
+          s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, _dev(workspace),
+          ctypes.byref(cap), _stream())
+    return dq, dk, dv
+
+
+def attn_bwd_preprocess(o, dout, delta=None):
+    s, Hq, d = o.shape
+    if delta is None:
+        delta = torch.empty((Hq, s), dtype=torch.float32, device=o.device)
+    _call("attn_bwd_preprocess", _dev(o), _dev(dout), _dev(delta), s, Hq, d, _dtype(o), _stream())
+    return delta
+
+
+def attn_bwd_dkdv(q, k, v, lse, dout, delta, scale=None, causal=True, cu_seqlens=None, dk=None, dv=None):
+    s, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    cu, nd = _cu(cu_seqlens)
+    _call("attn_bwd_dkdv", _dev(q), _dev(k), _dev(v), _dev(lse), _dev(dout), _dev(delta), _dev(dk), _dev(dv),
+          s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, _stream())
+    return dk, dv
+
+
+def attn_bwd_dq(q, k, v, lse, dout, delta, scale=None, causal=True, cu_seqlens=None, dq=None):
+    s, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dq = torch.empty_like(q) if dq is None else dq
+    cu, nd = _cu(cu_seqlens)
+    _call("attn_bwd_dq", _dev(q), _dev(k), _dev(v), _dev(lse), _dev(dout), _dev(delta), _dev(dq),
+          s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, _stream())
+    return dq
+
+
+def attn_fwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, dtype, heads_per_chunk):
+    dt = dtype if isinstance(dtype, int) else _dtype(torch.empty(0, dtype=dtype))
+    return int(lib().attn_fwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, dt, heads_per_chunk))
+
+
+def attn_fwd_chunked(q_shards, k_shards, v_shards, o_shards, rank, heads_per_chunk, scale=None,
+                     causal=True, cu_seqlens=None, workspace=None, lse=None):
+    """UPipe forward of rank `rank`: writes this rank's heads of o_shards; returns lse [Hq/P, s]."""
+    P = len(q_shards)
+    s_l, Hq, d = q_shards[0].shape
+    Hkv = k_shards[0].shape[1]
+    s = P * s_l
+    if lse is None:
+        lse = torch.empty((Hq // P, s), dtype=torch.float32, device=q_shards[0].device)
+    need = attn_fwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, _dtype(q_shards[0]), heads_per_chunk)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_shards[0].device)
+    cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    qp, k1 = _ptrs(q_shards)
+    kp, k2 = _ptrs(k_shards)
+    vp, k3 = _ptrs(v_shards)
+    op, k4 = _ptrs(o_shards)
+    cu, nd = _cu(cu_seqlens)
+    _call("attn_fwd_chunked", qp, kp, vp, op, _dev(lse), P, rank, s_l, Hq, Hkv, d, _dtype(q_shards[0]),
+          _default_scale(d, scale), int(causal), cu, nd, heads_per_chunk, _dev(workspace), ctypes.byref(cap),
+          _stream())
+    return lse

@@ -1,0 +1,351 @@
+// C ABI of libulysses: argument checks, dispatch to the gfx950 kernels, and the
+// headwise-chunked (UPipe) schedule. Every check runs on the host before anything is
+// enqueued; see include/ulysses.h for the contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "uly_internal.h"
+#include "ulysses.h"
+
+using namespace uly;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int esize(int dtype) { return dtype == ULY_BF16 ? 2 : 4; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline int hip_status(hipError_t e) { return e == hipSuccess ? ULY_OK : ULY_ERR_HIP; }
+inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+int check_dtype_dim(int dtype, int d) {
+  if (dtype == ULY_BF16) return (d == 64 || d == 128) ? ULY_OK : ULY_ERR_UNSUPPORTED;
+  if (dtype == ULY_F32) return d == 64 ? ULY_OK : ULY_ERR_UNSUPPORTED;
+  return ULY_ERR_UNSUPPORTED;
+}
+
+// P, rank, s_l, H checks shared by the permutes and the chunked forward.
+int check_ranks(int P, int rank, int64_t s_l, int H) {
+  if (P < 1 || P > ULY_MAX_RANKS || rank < 0 || rank >= P) return ULY_ERR_SHAPE;
+  if (s_l < 1 || H < 1 || H % P != 0) return ULY_ERR_SHAPE;
+  return ULY_OK;
+}
+
+// The permute kernels index 16-byte chunks with 32-bit integers.
+bool chunks_fit(int P, int64_t s_l, int64_t run_bytes, int64_t row_bytes) {
+  const uint64_t total = (uint64_t)P * (uint64_t)s_l * (uint64_t)(run_bytes / 16);
+  const uint64_t shard = (uint64_t)s_l * (uint64_t)(row_bytes / 16);
+  return total < (1ull << 32) && shard < (1ull << 32);
+}
+
+int check_attn(const void* q, const void* k, const void* v, int64_t s, int Hq, int Hkv, int d,
+               int dtype, const int32_t* cu, int n_docs) {
+  if (!q || !k || !v) return ULY_ERR_NULL;
+  int st = check_dtype_dim(dtype, d);
+  if (st != ULY_OK) return st;
+  if (s < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ULY_ERR_SHAPE;
+  if (s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;  // cu_seqlens are int32
+  if (cu != nullptr && n_docs < 1) return ULY_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ULY_ERR_ALIGN;
+  return ULY_OK;
+}
+
+AttnArgs make_args(int64_t s, int Hq, int Hkv, int d, float scale, int causal, const int32_t* cu,
+                   int n_docs) {
+  AttnArgs a{};
+  a.s = s;
+  a.q_row = (int64_t)Hq * d;
+  a.kv_row = (int64_t)Hkv * d;
+  a.lse_row = s;
+  a.n_heads = Hq;
+  a.n_kv = Hkv;
+  a.G = Hq / Hkv;
+  a.q_off = 0;
+  a.kv_off = 0;
+  a.scale = scale;
+  a.causal = causal ? 1 : 0;
+  a.cu = cu;
+  a.n_docs = cu ? n_docs : 0;
+  return a;
+}
+
+int fwd_dispatch(const AttnArgs& a, int d, int dtype, hipStream_t st) {
+  const hipError_t e = dtype == ULY_BF16 ? launch_attn_fwd_bf16(a, d, st) : launch_attn_fwd_f32(a, d, st);
+  return hip_status(e);
+}
+
+ShardPtrs shard_ptrs(const void* const* p, int P) {
+  ShardPtrs sp{};
+  for (int i = 0; i < P; ++i) sp.p[i] = p[i];
+  return sp;
+}
+
+// q heads [c0, c1) of the rank's Hq_l local heads read kv heads [c0/G, (c1-1)/G] (local).
+int max_kv_span(int Hq_l, int G, int u) {
+  int span = 0;
+  for (int c0 = 0; c0 < Hq_l; c0 += u) {
+    const int c1 = std::min(c0 + u, Hq_l);
+    span = std::max(span, (c1 - 1) / G - c0 / G + 1);
+  }
+  return span;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* uly_status_string(int status) {
+  switch (status) {
+    case ULY_OK: return "ULY_OK";
+    case ULY_ERR_NULL: return "ULY_ERR_NULL";
+    case ULY_ERR_SHAPE: return "ULY_ERR_SHAPE";
+    case ULY_ERR_UNSUPPORTED: return "ULY_ERR_UNSUPPORTED";
+    case ULY_ERR_ALIGN: return "ULY_ERR_ALIGN";
+    case ULY_ERR_WORKSPACE: return "ULY_ERR_WORKSPACE";
+    case ULY_ERR_HIP: return "ULY_ERR_HIP";
+    default: return "ULY_ERR_UNKNOWN";
+  }
+}
+
+int uly_abi_version(void) { return kAbiVersion; }
+
+int ulysses_pack(const void* const* shards, int P, int rank, int64_t s_l, int H, int d, int dtype,
+                 void* out, void* stream) {
+  if (!shards || !out) return ULY_ERR_NULL;
+  int st = check_ranks(P, rank, s_l, H);
+  if (st != ULY_OK) return st;
+  if (dtype != ULY_BF16 && dtype != ULY_F32) return ULY_ERR_UNSUPPORTED;
+  if (d < 1) return ULY_ERR_SHAPE;
+  const int64_t Hl = H / P, e = esize(dtype);
+  const int64_t run = Hl * d * e, row = (int64_t)H * d * e;
+  if (run % 16 != 0) return ULY_ERR_ALIGN;
+  for (int p = 0; p < P; ++p) {
+    if (!shards[p]) return ULY_ERR_NULL;
+    if (!aligned16(shards[p])) return ULY_ERR_ALIGN;
+  }
+  if (!aligned16(out)) return ULY_ERR_ALIGN;
+  if (!chunks_fit(P, s_l, run, row)) return ULY_ERR_SHAPE;
+  return hip_status(launch_pack(shard_ptrs(shards, P), out, P, s_l, row, rank * run, run, as_stream(stream)));
+}
+
+int ulysses_unpack(const void* in, int P, int rank, int64_t s_l, int H, int d, int dtype,
+                   void* const* shards, void* stream) {
+  if (!shards || !in) return ULY_ERR_NULL;
+  int st = check_ranks(P, rank, s_l, H);
+  if (st != ULY_OK) return st;
+  if (dtype != ULY_BF16 && dtype != ULY_F32) return ULY_ERR_UNSUPPORTED;
+  if (d < 1) return ULY_ERR_SHAPE;
+  const int64_t Hl = H / P, e = esize(dtype);
+  const int64_t run = Hl * d * e, row = (int64_t)H * d * e;
+  if (run % 16 != 0) return ULY_ERR_ALIGN;
+  for (int p = 0; p < P; ++p) {
+    if (!shards[p]) return ULY_ERR_NULL;
+    if (!aligned16(shards[p])) return ULY_ERR_ALIGN;
+  }
+  if (!aligned16(in)) return ULY_ERR_ALIGN;
+  if (!chunks_fit(P, s_l, run, row)) return ULY_ERR_SHAPE;
+  return hip_status(launch_unpack(in, shard_ptrs(const_cast<const void* const*>(shards), P), P, s_l, row,
+                                  rank * run, run, as_stream(stream)));
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t s, int Hq,
+             int Hkv, int d, int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,
+             void* stream) {
+  int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, cu_seqlens, n_docs);
+  if (st != ULY_OK) return st;
+  if (!o || !lse) return ULY_ERR_NULL;
+  if (!aligned16(o) || !aligned16(lse)) return ULY_ERR_ALIGN;
+  AttnArgs a = make_args(s, Hq, Hkv, d, scale, causal, cu_seqlens, n_docs);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = o;
+  a.lse_out = lse;
+  return fwd_dispatch(a, d, dtype, as_stream(stream));
+}
+
+size_t attn_bwd_workspace_bytes(int64_t s, int Hq) {
+  if (s < 1 || Hq < 1) return 0;
+  return round256((size_t)s * (size_t)Hq * sizeof(float));
+}
+
+int attn_bwd_preprocess(const void* o, const void* dout, float* delta, int64_t s, int Hq, int d, int dtype,
+                        void* stream) {
+  if (!o || !dout || !delta) return ULY_ERR_NULL;
+  int st = check_dtype_dim(dtype, d);
+  if (st != ULY_OK) return st;
+  if (s < 1 || Hq < 1 || s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return ULY_ERR_ALIGN;
+  AttnArgs a = make_args(s, Hq, Hq, d, 1.f, 1, nullptr, 0);
+  a.o = o;
+  a.dout = dout;
+  a.lse_out = delta;
+  return hip_status(launch_bwd_preprocess(a, d, dtype, as_stream(stream)));
+}
+
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                  const float* delta, void* dk, void* dv, int64_t s, int Hq, int Hkv, int d, int dtype,
+                  float scale, int causal, const int32_t* cu_seqlens, int n_docs, void* stream) {
+  int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, cu_seqlens, n_docs);
+  if (st != ULY_OK) return st;
+  if (!lse || !dout || !delta || !dk || !dv) return ULY_ERR_NULL;
+  if (!aligned16(lse) || !aligned16(dout) || !aligned16(delta) || !aligned16(dk) || !aligned16(dv))
+    return ULY_ERR_ALIGN;
+  AttnArgs a = make_args(s, Hq, Hkv, d, scale, causal, cu_seqlens, n_docs);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse_in = lse;
+  a.delta = delta;
+  a.out_k = dk;
+  a.out_v = dv;
+  const hipError_t e = dtype == ULY_BF16 ? launch_attn_dkdv_bf16(a, d, as_stream(stream))
+                                         : launch_attn_dkdv_f32(a, d, as_stream(stream));
+  return hip_status(e);
+}
+
+int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                const float* delta, void* dq, int64_t s, int Hq, int Hkv, int d, int dtype, float scale,
+                int causal, const int32_t* cu_seqlens, int n_docs, void* stream) {
+  int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, cu_seqlens, n_docs);
+  if (st != ULY_OK) return st;
+  if (!lse || !dout || !delta || !dq) return ULY_ERR_NULL;
+  if (!aligned16(lse) || !aligned16(dout) || !aligned16(delta) || !aligned16(dq)) return ULY_ERR_ALIGN;
+  AttnArgs a = make_args(s, Hq, Hkv, d, scale, causal, cu_seqlens, n_docs);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse_in = lse;
+  a.delta = delta;
+  a.out = dq;
+  const hipError_t e = dtype == ULY_BF16 ? launch_attn_dq_bf16(a, d, as_stream(stream))
+                                         : launch_attn_dq_f32(a, d, as_stream(stream));
+  return hip_status(e);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
+             const int32_t* cu_seqlens, int n_docs, void* workspace, size_t* workspace_bytes, void* stream) {
+  int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, cu_seqlens, n_docs);
+  if (st != ULY_OK) return st;
+  const size_t need = attn_bwd_workspace_bytes(s, Hq);
+  if (workspace == nullptr) {
+    if (!workspace_bytes) return ULY_ERR_NULL;
+    *workspace_bytes = need;
+    return ULY_OK;
+  }
+  if (workspace_bytes && *workspace_bytes < need) return ULY_ERR_WORKSPACE;
+  if (!o || !lse || !dout || !dq || !dk || !dv) return ULY_ERR_NULL;
+  if (!aligned16(o) || !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || !aligned16(workspace))
+    return ULY_ERR_ALIGN;
+  float* delta = static_cast<float*>(workspace);
+  st = attn_bwd_preprocess(o, dout, delta, s, Hq, d, dtype, stream);
+  if (st != ULY_OK) return st;
+  st = attn_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens, n_docs,
+                     stream);
+  if (st != ULY_OK) return st;
+  return attn_bwd_dq(q, k, v, lse, dout, delta, dq, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens, n_docs,
+                     stream);
+}
+
+// ---- UPipe headwise-chunked forward ------------------------------------------------
+
+size_t attn_fwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int d, int dtype,
+                                        int heads_per_chunk) {
+  if (P < 1 || s_l < 1 || Hq < 1 || Hkv < 1 || d < 1 || heads_per_chunk < 1) return 0;
+  if (Hq % P != 0 || Hkv % P != 0 || Hq % Hkv != 0) return 0;
+  const int Hq_l = Hq / P, G = Hq / Hkv;
+  const int u = std::min(heads_per_chunk, Hq_l);
+  const size_t s = (size_t)P * (size_t)s_l, e = (size_t)esize(dtype);
+  const size_t qo = round256(s * (size_t)u * (size_t)d * e);
+  const size_t kv = round256(s * (size_t)max_kv_span(Hq_l, G, u) * (size_t)d * e);
+  return 2 * qo + 2 * kv;
+}
+
+int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards, const void* const* v_shards,
+                     void* const* o_shards, float* lse, int P, int rank, int64_t s_l, int Hq, int Hkv, int d,
+                     int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,
+                     int heads_per_chunk, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!q_shards || !k_shards || !v_shards || !o_shards) return ULY_ERR_NULL;
+  int st = check_ranks(P, rank, s_l, Hq);
+  if (st != ULY_OK) return st;
+  if (Hkv < 1 || Hkv % P != 0 || Hq % Hkv != 0) return ULY_ERR_SHAPE;
+  st = check_dtype_dim(dtype, d);
+  if (st != ULY_OK) return st;
+  if (heads_per_chunk < 1) return ULY_ERR_SHAPE;
+  const int64_t s = (int64_t)P * s_l;
+  if (s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
+  if (cu_seqlens != nullptr && n_docs < 1) return ULY_ERR_SHAPE;
+  const size_t need = attn_fwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, dtype, heads_per_chunk);
+  if (workspace == nullptr) {
+    if (!workspace_bytes) return ULY_ERR_NULL;
+    *workspace_bytes = need;
+    return ULY_OK;
+  }
+  if (workspace_bytes && *workspace_bytes < need) return ULY_ERR_WORKSPACE;
+  if (!lse) return ULY_ERR_NULL;
+  if (!aligned16(lse) || !aligned16(workspace)) return ULY_ERR_ALIGN;
+  for (int p = 0; p < P; ++p) {
+    if (!q_shards[p] || !k_shards[p] || !v_shards[p] || !o_shards[p]) return ULY_ERR_NULL;
+    if (!aligned16(q_shards[p]) || !aligned16(k_shards[p]) || !aligned16(v_shards[p]) || !aligned16(o_shards[p]))
+      return ULY_ERR_ALIGN;
+  }
+  const int Hq_l = Hq / P, Hkv_l = Hkv / P, G = Hq / Hkv;
+  const int u = std::min(heads_per_chunk, Hq_l);
+  const int64_t e = esize(dtype);
+  const int64_t qrow = (int64_t)Hq * d * e, kvrow = (int64_t)Hkv * d * e, hb = (int64_t)d * e;
+  if (!chunks_fit(P, s_l, qrow, qrow) || !chunks_fit(P, s_l, kvrow, kvrow)) return ULY_ERR_SHAPE;
+
+  const int span = max_kv_span(Hq_l, G, u);
+  char* ws = static_cast<char*>(workspace);
+  const size_t qo = round256((size_t)s * u * d * e);
+  void* qc = ws;
+  void* oc = ws + qo;
+  void* kc = ws + 2 * qo;
+  void* vc = ws + 2 * qo + round256((size_t)s * span * d * e);
+  const ShardPtrs qs = shard_ptrs(q_shards, P), ks = shard_ptrs(k_shards, P), vs = shard_ptrs(v_shards, P);
+  const ShardPtrs os = shard_ptrs(const_cast<const void* const*>(o_shards), P);
+  hipStream_t strm = as_stream(stream);
+
+  int kv_lo = -1, kv_hi = -1;  // local kv heads currently packed in kc / vc
+  for (int c0 = 0; c0 < Hq_l; c0 += u) {
+    const int c1 = std::min(c0 + u, Hq_l), nq = c1 - c0;
+    const int g0 = c0 / G, g1 = (c1 - 1) / G + 1;
+    hipError_t err;
+    if (g0 != kv_lo || g1 != kv_hi) {
+      const int64_t off = ((int64_t)rank * Hkv_l + g0) * hb, run = (int64_t)(g1 - g0) * hb;
+      if ((err = launch_pack(ks, kc, P, s_l, kvrow, off, run, strm)) != hipSuccess) return ULY_ERR_HIP;
+      if ((err = launch_pack(vs, vc, P, s_l, kvrow, off, run, strm)) != hipSuccess) return ULY_ERR_HIP;
+      kv_lo = g0;
+      kv_hi = g1;
+    }
+    const int64_t qoff = ((int64_t)rank * Hq_l + c0) * hb, qrun = (int64_t)nq * hb;
+    if ((err = launch_pack(qs, qc, P, s_l, qrow, qoff, qrun, strm)) != hipSuccess) return ULY_ERR_HIP;
+
+    AttnArgs a = make_args(s, nq, 1, d, scale, causal, cu_seqlens, n_docs);
+    a.q_row = (int64_t)nq * d;
+    a.kv_row = (int64_t)(g1 - g0) * d;
+    a.n_heads = nq;
+    a.n_kv = g1 - g0;
+    a.G = G;
+    a.q_off = c0;   // chunk head j is local head c0 + j
+    a.kv_off = g0;  // which reads local kv head (c0 + j) / G, stored at index - g0
+    a.q = qc;
+    a.k = kc;
+    a.v = vc;
+    a.out = oc;
+    a.lse_out = lse + (int64_t)c0 * s;
+    st = fwd_dispatch(a, d, dtype, strm);
+    if (st != ULY_OK) return st;
+    if ((err = launch_unpack(oc, os, P, s_l, qrow, qoff, qrun, strm)) != hipSuccess) return ULY_ERR_HIP;
+  }
+  return ULY_OK;
+}
+
+}  // extern "C"

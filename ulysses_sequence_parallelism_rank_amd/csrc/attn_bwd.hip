@@ -1,0 +1,522 @@
+// Attention backward for one head shard on gfx950: the preprocess (delta = rowsum(dO*O)),
+// a dK/dV kernel and a separate dQ kernel, bf16 in, fp32 accumulation.
+//
+// Pages: "Ulysses Sequence Parallelism: Training with Million-Token Contexts" -- the
+// method trains models (title and opening section), so each rank also runs the backward
+// of its local attention (step 4 of "how Ulysses works"); FlashAttention's O(n) memory
+// (long-sequence section) means P is recomputed from Q, K and the saved LSE rather than
+// stored.
+//
+// Per row i of q head h (kv head g), with P_ij = exp(scale q_i.k_j - LSE_i):
+//   dV_j += sum_i P_ij dO_i                 dP_ij = dO_i . v_j
+//   dS_ij = P_ij (dP_ij - delta_i)          delta_i = dO_i . O_i
+//   dQ_i  = scale sum_j dS_ij k_j           dK_j += scale sum_i dS_ij q_i
+// dK/dV of a kv head sum over its G q heads inside one workgroup, in fp32, so no atomics
+// are needed and the result is deterministic. dQ is a separate pass over key tiles.
+//
+// Both kernels use v_mfma_f32_32x32x16_bf16. Operands whose contraction index is the
+// row-major tile's row (K for dQ, Q and dO for dK/dV) come from the transposing LDS read
+// ds_read_b64_tr_b16, so no tile is ever transposed in memory.
+#include "uly_device.h"
+#include "uly_internal.h"
+
+namespace uly {
+
+namespace {
+
+constexpr int kWaves = 4;
+
+// ---------------------------------------------------------------------------------------
+// delta[h, i] = sum_x dO[i, h, x] * O[i, h, x] (fp32). TPR threads per (row, head), 16 B each.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
+  constexpr int TPR = D * (int)sizeof(T) / 16;
+  constexpr int EPV = 16 / (int)sizeof(T);
+  const int64_t idx = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  const int64_t row = idx / a.n_heads;
+  const int h = (int)(idx % a.n_heads);
+  float acc = 0.f;
+  if (row < a.s) {
+    const int64_t off = row * a.q_row + (int64_t)h * D + part * EPV;
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.o) + off);
+    const u32x4 gv = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dout) + off);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc += bf16_to_f32((uint16_t)(ov[i] & 0xffff)) * bf16_to_f32((uint16_t)(gv[i] & 0xffff));
+        acc += bf16_to_f32((uint16_t)(ov[i] >> 16)) * bf16_to_f32((uint16_t)(gv[i] >> 16));
+      }
+    } else {
+      // bit-cast whole vectors: clang mis-handles __builtin_bit_cast of a vector element
+      const f32x4 of = __builtin_bit_cast(f32x4, ov), gf = __builtin_bit_cast(f32x4, gv);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc += of[i] * gf[i];
+    }
+  }
+#pragma unroll
+  for (int o = TPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (part == 0 && row < a.s) a.lse_out[(int64_t)h * a.lse_row + row] = acc;
+}
+
+// ---------------------------------------------------------------------------------------
+// dQ: one workgroup = BM query rows of one q head; loops over key tiles of BN keys.
+template <int D, int RB, int KB>
+struct DqCfg {
+  static constexpr int BM = kWaves * RB * 32;
+  static constexpr int BN = KB * 32;
+  static constexpr int DT = D / 16, DB = D / 32;
+  static constexpr int STR = D + 8;
+  static constexpr int KVEC = BN * D / 8 / (kWaves * 64);
+};
+
+template <int D, int RB, int KB>
+__global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
+  using C = DqCfg<D, RB, KB>;
+  constexpr int BM = C::BM, BN = C::BN, DT = C::DT, DB = C::DB, STR = C::STR;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * STR];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * STR];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5, gi = lane >> 4, li = lane & 15;
+  const int64_t s = a.s;
+  const int nmb = (int)((s + BM - 1) / BM);
+  const int h = blockIdx.x % a.n_heads;
+  const int mb = nmb - 1 - (int)(blockIdx.x / a.n_heads);
+  const int64_t m0 = (int64_t)mb * BM;
+  const int kvh = (h + a.q_off) / a.G - a.kv_off;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + (int64_t)h * D;
+  const uint16_t* dO = static_cast<const uint16_t*>(a.dout) + (int64_t)h * D;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + (int64_t)kvh * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + (int64_t)kvh * D;
+  const float c = a.scale * kLog2e;
+
+  int64_t row[RB], lo[RB], hi[RB];
+  float lse2[RB], dl[RB];
+  bf16x8 qf[RB][DT], gf[RB][DT];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    row[rb] = m0 + wave * RB * 32 + rb * 32 + l32;
+    lo[rb] = 0;
+    hi[rb] = s;
+    lse2[rb] = 0.f;
+    dl[rb] = 0.f;
+    if (row[rb] < s) {
+      if (a.cu != nullptr) {
+        const int dk = doc_of(a.cu, a.n_docs, row[rb]);
+        lo[rb] = a.cu[dk];
+        hi[rb] = a.cu[dk + 1];
+      }
+      lse2[rb] = a.lse_in[(int64_t)h * a.lse_row + row[rb]] * kLog2e;
+      dl[rb] = a.delta[(int64_t)h * a.lse_row + row[rb]];
+    }
+    if (a.causal) hi[rb] = hi[rb] < row[rb] + 1 ? hi[rb] : row[rb] + 1;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      u32x4 v = {0, 0, 0, 0}, w = {0, 0, 0, 0};
+      if (row[rb] < s) {
+        v = *reinterpret_cast<const u32x4*>(Q + row[rb] * a.q_row + 16 * t + 8 * hf);
+        w = *reinterpret_cast<const u32x4*>(dO + row[rb] * a.q_row + 16 * t + 8 * hf);
+      }
+      qf[rb][t] = __builtin_bit_cast(bf16x8, v);
+      gf[rb][t] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  const int64_t wr0 = m0 + wave * RB * 32;
+  const int64_t wr1 = (wr0 + RB * 32 < s ? wr0 + RB * 32 : s) - 1;
+  const int64_t last_row = (m0 + BM < s ? m0 + BM : s) - 1;
+  int64_t kbeg = 0, kend = s, wkbeg = 0, wkend = s, w_lo_last = 0, w_hi_first = s;
+  if (a.cu != nullptr) {
+    kbeg = a.cu[doc_of(a.cu, a.n_docs, m0)];
+    kend = a.cu[doc_of(a.cu, a.n_docs, last_row) + 1];
+    if (wr0 < s) {
+      wkbeg = a.cu[doc_of(a.cu, a.n_docs, wr0)];
+      w_hi_first = a.cu[doc_of(a.cu, a.n_docs, wr0) + 1];
+      w_lo_last = a.cu[doc_of(a.cu, a.n_docs, wr1)];
+      wkend = a.cu[doc_of(a.cu, a.n_docs, wr1) + 1];
+    }
+  }
+  if (a.causal) {
+    kend = kend < last_row + 1 ? kend : last_row + 1;
+    wkend = wkend < wr1 + 1 ? wkend : wr1 + 1;
+  }
+  kbeg = (kbeg / BN) * BN;
+  const bool wave_has_rows = wr0 < s;
+
+  u32x4 pk[C::KVEC], pv[C::KVEC];
+  auto load_tile = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < C::KVEC; ++i) {
+      const int vi = tid + i * kWaves * 64;
+      const int r = vi / (D / 8), c8 = vi % (D / 8);
+      const int64_t key = k0 + r;
+      pk[i] = u32x4{0, 0, 0, 0};
+      pv[i] = u32x4{0, 0, 0, 0};
+      if (key < s) {
+        pk[i] = *reinterpret_cast<const u32x4*>(K + key * a.kv_row + 8 * c8);
+        pv[i] = *reinterpret_cast<const u32x4*>(V + key * a.kv_row + 8 * c8);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::KVEC; ++i) {
+      const int vi = tid + i * kWaves * 64;
+      const int r = vi / (D / 8), c8 = vi % (D / 8);
+      *reinterpret_cast<u32x4*>(&sK[buf][r * STR + 8 * c8]) = pk[i];
+      *reinterpret_cast<u32x4*>(&sV[buf][r * STR + 8 * c8]) = pv[i];
+    }
+  };
+
+  f32x16 dqacc[RB][DB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dqacc[rb][db] = f32x16{};
+
+  if (kbeg < kend) load_tile(kbeg);
+  int buf = 0;
+  for (int64_t k0 = kbeg; k0 < kend; k0 += BN, buf ^= 1) {
+    store_tile(buf);
+    __syncthreads();
+    if (k0 + BN < kend) load_tile(k0 + BN);
+
+    const bool active = wave_has_rows && k0 < wkend && k0 + BN > wkbeg;
+    if (active) {
+      const bool full = (k0 + BN <= s) && (!a.causal || k0 + BN - 1 <= wr0) &&
+                        (a.cu == nullptr || (k0 >= w_lo_last && k0 + BN <= w_hi_first));
+      f32x16 sacc[KB][RB], pacc[KB][RB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          sacc[kb][rb] = f32x16{};
+          pacc[kb][rb] = f32x16{};
+        }
+      // S^T = K Q^T and dP^T = V dO^T (key x row)
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][(kb * 32 + l32) * STR + 16 * t + 8 * hf]);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[buf][(kb * 32 + l32) * STR + 16 * t + 8 * hf]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            sacc[kb][rb] = mfma32x32x16(kf, qf[rb][t], sacc[kb][rb]);
+            pacc[kb][rb] = mfma32x32x16(vf, gf[rb][t], pacc[kb][rb]);
+          }
+        }
+      // dS^T = P^T o (dP^T - delta)
+      bf16x8 dsf[RB][KB][2];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            float p = fast_exp2(__builtin_fmaf(sacc[kb][rb][j], c, -lse2[rb]));
+            if (!full) {
+              const int64_t key = k0 + kb * 32 + 8 * (j / 4) + 4 * hf + (j % 4);
+              if (key < lo[rb] || key >= hi[rb]) p = 0.f;
+            }
+            sacc[kb][rb][j] = p * (pacc[kb][rb][j] - dl[rb]);
+          }
+          dsf[rb][kb][0] = to_bf16x8(sacc[kb][rb], 0);
+          dsf[rb][kb][1] = to_bf16x8(sacc[kb][rb], 1);
+        }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int kr = kb * 32 + 16 * tt + 4 * hf + (li >> 2);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
+            const i16x4 k0v = lds_read_tr16(&sK[buf][kr * STR + col]);
+            const i16x4 k1v = lds_read_tr16(&sK[buf][(kr + 8) * STR + col]);
+            const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0v, k1v, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) dqacc[rb][db] = mfma32x32x16(kt, dsf[rb][kb][tt], dqacc[rb][db]);
+          }
+        }
+    }
+  }
+
+  uint16_t* dQ = static_cast<uint16_t*>(a.out) + (int64_t)h * D;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if (row[rb] >= s) continue;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        u32x2 w;
+        w[0] = pack_bf16x2(dqacc[rb][db][4 * jj + 0] * a.scale, dqacc[rb][db][4 * jj + 1] * a.scale);
+        w[1] = pack_bf16x2(dqacc[rb][db][4 * jj + 2] * a.scale, dqacc[rb][db][4 * jj + 3] * a.scale);
+        *reinterpret_cast<u32x2*>(dQ + row[rb] * a.q_row + db * 32 + 8 * jj + 4 * hf) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dK/dV: one workgroup = 128 keys (32 per wave) of one kv head; loops over the G q heads
+// and their query tiles of QB*32 rows. Each wave keeps its keys' K and V rows in VGPRs.
+template <int D, int QB>
+struct DkvCfg {
+  static constexpr int BNK = kWaves * 32;
+  static constexpr int BMQ = QB * 32;
+  static constexpr int DT = D / 16, DB = D / 32;
+  static constexpr int STR = D + 8;
+  static constexpr int QVEC = BMQ * D / 8 / (kWaves * 64);
+};
+
+template <int D, int QB>
+__global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
+  using C = DkvCfg<D, QB>;
+  constexpr int BNK = C::BNK, BMQ = C::BMQ, DT = C::DT, DB = C::DB, STR = C::STR;
+  static_assert(C::QVEC >= 1, "query tile too small for the thread count");
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BMQ * STR];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[2][BMQ * STR];
+  __shared__ __attribute__((aligned(16))) float sL[2][BMQ];
+  __shared__ __attribute__((aligned(16))) float sD[2][BMQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5, gi = lane >> 4, li = lane & 15;
+  const int64_t s = a.s;
+  const int kvh = blockIdx.x % a.n_kv;
+  const int64_t n0 = (int64_t)(blockIdx.x / a.n_kv) * BNK;  // earliest keys (most rows) first
+  const int G = a.G;
+  const float c = a.scale * kLog2e;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + (int64_t)kvh * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + (int64_t)kvh * D;
+
+  // this lane's key and the rows that may see it: [rlo, rhi)
+  const int64_t key = n0 + wave * 32 + l32;
+  int64_t rlo = 0, rhi = s;
+  if (a.cu != nullptr && key < s) {
+    const int dk = doc_of(a.cu, a.n_docs, key);
+    rlo = a.cu[dk];
+    rhi = a.cu[dk + 1];
+  }
+  if (a.causal) rlo = key;
+  if (key >= s) rhi = rlo;  // padding key: seen by no row
+  bf16x8 kf[DT], vf[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+    if (key < s) {
+      x = *reinterpret_cast<const u32x4*>(K + key * a.kv_row + 16 * t + 8 * hf);
+      y = *reinterpret_cast<const u32x4*>(V + key * a.kv_row + 16 * t + 8 * hf);
+    }
+    kf[t] = __builtin_bit_cast(bf16x8, x);
+    vf[t] = __builtin_bit_cast(bf16x8, y);
+  }
+
+  // row ranges of the workgroup and of this wave
+  const int64_t last_key = (n0 + BNK < s ? n0 + BNK : s) - 1;
+  const int64_t wk0 = n0 + wave * 32;
+  const int64_t wk1 = (wk0 + 32 < s ? wk0 + 32 : s) - 1;
+  int64_t qbeg = a.causal ? n0 : 0, qend = s;
+  int64_t wqbeg = a.causal ? wk0 : 0, wqend = s, w_hi_first = s, w_lo_last = 0;
+  if (a.cu != nullptr) {
+    qend = a.cu[doc_of(a.cu, a.n_docs, last_key) + 1];
+    if (!a.causal) qbeg = a.cu[doc_of(a.cu, a.n_docs, n0)];
+    if (wk0 < s) {
+      wqend = a.cu[doc_of(a.cu, a.n_docs, wk1) + 1];
+      w_hi_first = a.cu[doc_of(a.cu, a.n_docs, wk0) + 1];
+      w_lo_last = a.cu[doc_of(a.cu, a.n_docs, wk1)];
+      if (!a.causal) wqbeg = a.cu[doc_of(a.cu, a.n_docs, wk0)];
+    }
+  }
+  qbeg = (qbeg / BMQ) * BMQ;
+  const bool wave_has_keys = wk0 < s;
+  const int64_t ntile = qend > qbeg ? (qend - qbeg + BMQ - 1) / BMQ : 0;
+  const int64_t nsteps = ntile * G;
+
+  u32x4 pq[C::QVEC], pg[C::QVEC];
+  float pl = 0.f, pd = 0.f;
+  auto load_tile = [&](int64_t step) {
+    const int hq = kvh * G + (int)(step / ntile);
+    const int64_t q0 = qbeg + (step % ntile) * BMQ;
+    const uint16_t* Qh = static_cast<const uint16_t*>(a.q) + (int64_t)hq * D;
+    const uint16_t* Gh = static_cast<const uint16_t*>(a.dout) + (int64_t)hq * D;
+#pragma unroll
+    for (int i = 0; i < C::QVEC; ++i) {
+      const int vi = tid + i * kWaves * 64;
+      const int r = vi / (D / 8), c8 = vi % (D / 8);
+      const int64_t qr = q0 + r;
+      pq[i] = u32x4{0, 0, 0, 0};
+      pg[i] = u32x4{0, 0, 0, 0};
+      if (qr < s) {
+        pq[i] = *reinterpret_cast<const u32x4*>(Qh + qr * a.q_row + 8 * c8);
+        pg[i] = *reinterpret_cast<const u32x4*>(Gh + qr * a.q_row + 8 * c8);
+      }
+    }
+    if (tid < BMQ) {
+      const int64_t qr = q0 + tid;
+      pl = qr < s ? a.lse_in[(int64_t)hq * a.lse_row + qr] * kLog2e : 0.f;
+      pd = qr < s ? a.delta[(int64_t)hq * a.lse_row + qr] : 0.f;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::QVEC; ++i) {
+      const int vi = tid + i * kWaves * 64;
+      const int r = vi / (D / 8), c8 = vi % (D / 8);
+      *reinterpret_cast<u32x4*>(&sQ[buf][r * STR + 8 * c8]) = pq[i];
+      *reinterpret_cast<u32x4*>(&sG[buf][r * STR + 8 * c8]) = pg[i];
+    }
+    if (tid < BMQ) {
+      sL[buf][tid] = pl;
+      sD[buf][tid] = pd;
+    }
+  };
+
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+
+  if (nsteps > 0) load_tile(0);
+  int buf = 0;
+  for (int64_t step = 0; step < nsteps; ++step, buf ^= 1) {
+    store_tile(buf);
+    __syncthreads();
+    if (step + 1 < nsteps) load_tile(step + 1);
+    const int64_t q0 = qbeg + (step % ntile) * BMQ;
+
+    const bool active = wave_has_keys && q0 < wqend && q0 + BMQ > wqbeg;
+    if (active) {
+      const bool full = (q0 + BMQ <= s) && (!a.causal || q0 >= wk1) &&
+                        (a.cu == nullptr || (q0 + BMQ <= w_hi_first && q0 >= w_lo_last));
+      // S = Q K^T and dP = dO V^T (row x key)
+      f32x16 sacc[QB], pacc[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        sacc[qb] = f32x16{};
+        pacc[qb] = f32x16{};
+      }
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sQ[buf][(qb * 32 + l32) * STR + 16 * t + 8 * hf]);
+          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&sG[buf][(qb * 32 + l32) * STR + 16 * t + 8 * hf]);
+          sacc[qb] = mfma32x32x16(qa, kf[t], sacc[qb]);
+          pacc[qb] = mfma32x32x16(ga, vf[t], pacc[qb]);
+        }
+      // P and dS for rows 32qb + 8(j/4) + 4hf + j%4 of the tile and this lane's key
+      bf16x8 pf[QB][2], dsf[QB][2];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[buf][qb * 32 + 8 * jj + 4 * hf]);
+          const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[buf][qb * 32 + 8 * jj + 4 * hf]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * jj + e;
+            float p = fast_exp2(__builtin_fmaf(sacc[qb][j], c, -L4[e]));
+            if (!full) {
+              const int64_t qr = q0 + qb * 32 + 8 * jj + 4 * hf + e;
+              if (qr < rlo || qr >= rhi) p = 0.f;
+            }
+            sacc[qb][j] = p;
+            pacc[qb][j] = p * (pacc[qb][j] - D4[e]);
+          }
+        }
+        pf[qb][0] = to_bf16x8(sacc[qb], 0);
+        pf[qb][1] = to_bf16x8(sacc[qb], 1);
+        dsf[qb][0] = to_bf16x8(pacc[qb], 0);
+        dsf[qb][1] = to_bf16x8(pacc[qb], 1);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (d x key)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int qr = qb * 32 + 16 * tt + 4 * hf + (li >> 2);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
+            const i16x4 g0 = lds_read_tr16(&sG[buf][qr * STR + col]);
+            const i16x4 g1 = lds_read_tr16(&sG[buf][(qr + 8) * STR + col]);
+            const i16x4 q0v = lds_read_tr16(&sQ[buf][qr * STR + col]);
+            const i16x4 q1v = lds_read_tr16(&sQ[buf][(qr + 8) * STR + col]);
+            const bf16x8 gt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7));
+            const bf16x8 qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0v, q1v, 0, 1, 2, 3, 4, 5, 6, 7));
+            dvacc[db] = mfma32x32x16(gt, pf[qb][tt], dvacc[db]);
+            dkacc[db] = mfma32x32x16(qt, dsf[qb][tt], dkacc[db]);
+          }
+        }
+    }
+  }
+
+  if (key < s) {
+    uint16_t* dK = static_cast<uint16_t*>(a.out_k) + (int64_t)kvh * D;
+    uint16_t* dV = static_cast<uint16_t*>(a.out_v) + (int64_t)kvh * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        u32x2 wk, wv;
+        wk[0] = pack_bf16x2(dkacc[db][4 * jj + 0] * a.scale, dkacc[db][4 * jj + 1] * a.scale);
+        wk[1] = pack_bf16x2(dkacc[db][4 * jj + 2] * a.scale, dkacc[db][4 * jj + 3] * a.scale);
+        wv[0] = pack_bf16x2(dvacc[db][4 * jj + 0], dvacc[db][4 * jj + 1]);
+        wv[1] = pack_bf16x2(dvacc[db][4 * jj + 2], dvacc[db][4 * jj + 3]);
+        *reinterpret_cast<u32x2*>(dK + key * a.kv_row + db * 32 + 8 * jj + 4 * hf) = wk;
+        *reinterpret_cast<u32x2*>(dV + key * a.kv_row + db * 32 + 8 * jj + 4 * hf) = wv;
+      }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_pre_t(const AttnArgs& a, hipStream_t stream) {
+  constexpr int TPR = D * (int)sizeof(T) / 16;
+  const int64_t items = a.s * a.n_heads;
+  const int64_t blocks = (items + (256 / TPR) - 1) / (256 / TPR);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int RB, int KB>
+hipError_t launch_dq_t(const AttnArgs& a, hipStream_t stream) {
+  using C = DqCfg<D, RB, KB>;
+  const int64_t blocks = (a.s + C::BM - 1) / C::BM * a.n_heads;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_dq_kernel<D, RB, KB>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int QB>
+hipError_t launch_dkdv_t(const AttnArgs& a, hipStream_t stream) {
+  using C = DkvCfg<D, QB>;
+  const int64_t blocks = (a.s + C::BNK - 1) / C::BNK * a.n_kv;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_dkdv_kernel<D, QB>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_preprocess(const AttnArgs& a, int d, int dtype, hipStream_t stream) {
+  if (dtype == ULY_BF16) return d == 128 ? launch_pre_t<uint16_t, 128>(a, stream) : launch_pre_t<uint16_t, 64>(a, stream);
+  return d == 128 ? launch_pre_t<float, 128>(a, stream) : launch_pre_t<float, 64>(a, stream);
+}
+
+hipError_t launch_attn_dq_bf16(const AttnArgs& a, int d, hipStream_t stream) {
+  if (d == 128) return launch_dq_t<128, 1, 2>(a, stream);
+  return launch_dq_t<64, 1, 2>(a, stream);
+}
+
+hipError_t launch_attn_dkdv_bf16(const AttnArgs& a, int d, hipStream_t stream) {
+  if (d == 128) return launch_dkdv_t<128, 2>(a, stream);
+  return launch_dkdv_t<64, 2>(a, stream);
+}
+
+}  // namespace uly

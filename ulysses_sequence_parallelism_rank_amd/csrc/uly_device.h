@@ -1,0 +1,74 @@
+// Device-side helpers shared by the gfx950 kernels of the Ulysses attention share.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace uly {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
+// Operand lanes: lane l supplies row (A) / column (B) l%32 and the 8 contraction
+// elements 8*(l/32) .. 8*(l/32)+7. Result lane l holds column l%32, rows
+// 8*(j/4) + 4*(l/32) + j%4 for j = 0..15 (checked on gfx950 by the layout test).
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// 16 fp32 accumulator values j = 8t..8t+7 -> one bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& a, int t) {
+  u32x4 r;
+  r[0] = pack_bf16x2(a[8 * t + 0], a[8 * t + 1]);
+  r[1] = pack_bf16x2(a[8 * t + 2], a[8 * t + 3]);
+  r[2] = pack_bf16x2(a[8 * t + 4], a[8 * t + 5]);
+  r[3] = pack_bf16x2(a[8 * t + 6], a[8 * t + 7]);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes, lane i
+// receives element e (e = 0..3) from the 8 bytes addressed by lane 4*e + i/4 of the
+// group, taking that lane's element i%4. If lane 4*r + c of the group points at row r,
+// columns 4c..4c+3 of a row-major [rows][cols] bf16 tile, lane i receives column i of
+// those 4 rows (checked on gfx950 by the layout test).
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_ptr) {
+  typedef i16x4 __attribute__((address_space(3))) * lds_i16x4_ptr;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(lds_ptr));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// First document boundary > i, searched in cu[0..n]; returns index k with cu[k] <= i < cu[k+1].
+__device__ __forceinline__ int doc_of(const int32_t* cu, int n, int64_t i) {
+  int lo = 0, hi = n;  // invariant: cu[lo] <= i < cu[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (cu[mid] <= i) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace uly

@@ -1,0 +1,57 @@
+// Host-side declarations shared by the translation units of libulysses (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ulysses.h"
+
+namespace uly {
+
+// The P shard base pointers, passed to kernels by value.
+struct ShardPtrs {
+  const void* p[ULY_MAX_RANKS];
+};
+
+// Attention problem description shared by the forward and backward kernels.
+//   q / o / do / dq : [s, q_heads, D], row stride q_row elements
+//   k / v / dk / dv : [s, kv_heads, D], row stride kv_row elements
+// q head h (0 <= h < n_heads of the launch) reads kv head (h + q_off) / G - kv_off.
+// lse / delta rows are [n_heads][s] with row stride lse_row.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse_in;
+  const float* delta;
+  void* out;      // o (forward) or dq
+  void* out_k;    // dk
+  void* out_v;    // dv
+  float* lse_out; // forward LSE / preprocess delta
+  int64_t s;
+  int64_t q_row, kv_row;
+  int64_t lse_row;
+  int n_heads;    // q heads processed by the launch
+  int n_kv;       // kv heads (dkdv launch)
+  int G, q_off, kv_off;
+  float scale;
+  int causal;
+  const int32_t* cu;
+  int n_docs;
+};
+
+hipError_t launch_pack(const ShardPtrs& src, void* out, int P, int64_t s_l, int64_t row_bytes,
+                       int64_t off_bytes, int64_t run_bytes, hipStream_t stream);
+hipError_t launch_unpack(const void* in, const ShardPtrs& dst, int P, int64_t s_l, int64_t row_bytes,
+                         int64_t off_bytes, int64_t run_bytes, hipStream_t stream);
+
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream);
+hipError_t launch_bwd_preprocess(const AttnArgs& a, int d, int dtype, hipStream_t stream);
+hipError_t launch_attn_dkdv_bf16(const AttnArgs& a, int d, hipStream_t stream);
+hipError_t launch_attn_dq_bf16(const AttnArgs& a, int d, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t stream);
+hipError_t launch_attn_dkdv_f32(const AttnArgs& a, int d, hipStream_t stream);
+hipError_t launch_attn_dq_f32(const AttnArgs& a, int d, hipStream_t stream);
+
+}  // namespace uly
