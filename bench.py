@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark one GPU's share of a Ulysses sequence-parallel attention layer on MI355X.
+
+One step = the whole hot path for one rank over one batch of synthetic input:
+  pack Q, K, V (sequence shards -> head shard) -> attention forward -> unpack O
+  -> pack dO -> attention backward (delta, dK/dV, dQ) -> unpack dQ, dK, dV.
+Default workload: the 64K-token Qwen3-4B-shaped SP=4 share (4 shards of 16384 tokens,
+32 q / 8 kv heads -> 8 q / 2 kv heads after the exchange, head dim 128, bf16, causal).
+
+Metric: causal attention TFLOP/s, fwd+bwd counted FLOPs (4 d N fwd + 10 d N bwd per q
+head, N = s^2/2 visible pairs, or sum of l^2/2 over packed documents) divided by the
+time of the whole step (permutes included). Prints ONE JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import ulysses_sequence_parallelism_rank_amd as U  # noqa: E402
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+METRIC = "fwd+bwd causal attention TFLOP/s @64K (8q/2kv heads, d128); % MFMA peak"
+KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "permute.hip", "uly_device.h"]
+
+
+def counted_pairs(cfg, cu):
+    if cu is not None:
+        lens = np.diff(np.asarray(cu, dtype=np.float64))
+        return float((lens * lens).sum() / 2)
+    return float(cfg.s) ** 2 / 2
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "ulysses_sequence_parallelism_rank_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_inputs(cfg, seed=0):
+    glob = {n: W.gen_global(cfg, n, seed) for n in ("q", "k", "v", "do")}
+    shards = {n: [W.torch_from_bits(x, cfg.dtype, "cuda") for x in W.shards_of(g, cfg.P)]
+              for n, g in glob.items()}
+    return glob, shards
+
+
+class Phases:
+    """HIP events around every phase of every timed step, on the stream the library uses."""
+
+    def __init__(self):
+        self.marks = []   # (name, start_event, end_event)
+
+    def run(self, name, fn, record):
+        if not record:
+            return fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = fn()
+        b.record()
+        self.marks.append((name, a, b))
+        return r
+
+    def summary(self, steps):
+        tot = {}
+        for name, a, b in self.marks:
+            tot[name] = tot.get(name, 0.0) + a.elapsed_time(b)
+        return {k: v / steps for k, v in tot.items()}
+
+
+def run_training_share(cfg, steps, warmup, cu_dev):
+    _, sh = make_inputs(cfg)
+    rank = 0
+    s, Hq_l, Hkv_l, d = cfg.s, cfg.Hq_l, cfg.Hkv_l, cfg.d
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dev = "cuda"
+    # intermediates, allocated once
+    q = torch.empty((s, Hq_l, d), dtype=dt, device=dev)
+    k = torch.empty((s, Hkv_l, d), dtype=dt, device=dev)
+    v = torch.empty_like(k)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq_l, s), dtype=torch.float32, device=dev)
+    do = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(U.attn_bwd_workspace_bytes(s, Hq_l), dtype=torch.uint8, device=dev)
+    delta = ws.view(torch.float32)[: Hq_l * s].view(Hq_l, s)
+    o_sh = [torch.empty_like(t) for t in sh["q"]]
+    dq_sh = [torch.empty_like(t) for t in sh["q"]]
+    dk_sh = [torch.empty_like(t) for t in sh["k"]]
+    dv_sh = [torch.empty_like(t) for t in sh["v"]]
+    ph = Phases()
+
+    def step(rec):
+        ph.run("pack_qkv", lambda: (U.ulysses_pack(sh["q"], rank, q), U.ulysses_pack(sh["k"], rank, k),
+                                    U.ulysses_pack(sh["v"], rank, v)), rec)
+        ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse), rec)
+        ph.run("unpack_o", lambda: U.ulysses_unpack(o, rank, o_sh), rec)
+        ph.run("pack_do", lambda: U.ulysses_pack(sh["do"], rank, do), rec)
+        ph.run("bwd_preprocess", lambda: U.attn_bwd_preprocess(o, do, delta), rec)
+        ph.run("bwd_dkdv", lambda: U.attn_bwd_dkdv(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev,
+                                                   dk=dk, dv=dv), rec)
+        ph.run("bwd_dq", lambda: U.attn_bwd_dq(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev, dq=dq), rec)
+        ph.run("unpack_grads", lambda: (U.ulysses_unpack(dq, rank, dq_sh), U.ulysses_unpack(dk, rank, dk_sh),
+                                        U.ulysses_unpack(dv, rank, dv_sh)), rec)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    return wall, ph.summary(steps)
+
+
+def run_upipe(cfg, steps, warmup, u):
+    _, sh = make_inputs(cfg)
+    o_sh = [torch.empty_like(t) for t in sh["q"]]
+    lse = torch.empty((cfg.Hq_l, cfg.s), dtype=torch.float32, device="cuda")
+    need = U.attn_fwd_chunked_workspace_bytes(cfg.P, cfg.s_l, cfg.Hq, cfg.Hkv, cfg.d, torch.bfloat16, u)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ph = Phases()
+    for i in range(warmup + steps):
+        if i == warmup:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        ph.run("attn_fwd_chunked", lambda: U.attn_fwd_chunked(sh["q"], sh["k"], sh["v"], o_sh, 0, u, cfg.scale,
+                                                              cfg.causal, None, ws, lse), i >= warmup)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps, ph.summary(steps), need
+
+
+def cpu_baseline(cfg):
+    """The oracle, untuned, on a bounded sample of the same workload: one q head (and its kv
+    head) over the first `prefix` tokens of the sequence, causal forward + backward."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as OA
+    prefix = min(cfg.s, 32768)
+    f = {n: W.bits_to_f64(W.gen_rows(cfg, n, 0, prefix)[:, :1], cfg.dtype) for n in ("q", "k", "v", "do")}
+    t0 = time.perf_counter()
+    OA.forward(f["q"], f["k"], f["v"], cfg.scale, cfg.causal)
+    OA.backward(f["q"], f["k"], f["v"], f["do"], cfg.scale, cfg.causal)
+    dt = time.perf_counter() - t0
+    flops = 14.0 * cfg.d * prefix * prefix / 2
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"numpy fp64 oracle, causal fwd+bwd of 1 q head (+ its kv head) over the first {prefix} "
+                      f"tokens, d={cfg.d}; {dt:.1f} s; FLOPs counted as in the metric"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen_64k", choices=sorted(W.CONFIGS))
+    ap.add_argument("--heads-per-chunk", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the layer on one GPU; runs on more than one GPU are "
+              "not part of this build (the P ranks are simulated as buffers on one device).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    U.lib()
+    cfg = W.CONFIGS[args.workload]
+    cu = W.cu_seqlens_for(cfg)
+    cu_dev = None if cu is None else torch.from_numpy(cu).to("cuda")
+    pairs = counted_pairs(cfg, cu)
+    d, Hq_l, Hkv_l, e = cfg.d, cfg.Hq_l, cfg.Hkv_l, cfg.esize
+
+    if cfg.backward:
+        wall, ph = run_training_share(cfg, args.steps, args.warmup, cu_dev)
+        flops = 14.0 * d * pairs * Hq_l
+        kern = {
+            "attn_fwd": ("mfma", 4.0 * d * pairs * Hq_l),
+            "bwd_dkdv": ("mfma", 8.0 * d * pairs * Hq_l),
+            "bwd_dq": ("mfma", 2.0 * d * pairs * Hq_l),
+            "pack_qkv": ("hbm", 2.0 * cfg.s * (Hq_l + 2 * Hkv_l) * d * e),
+            "unpack_o": ("hbm", 2.0 * cfg.s * Hq_l * d * e),
+            "pack_do": ("hbm", 2.0 * cfg.s * Hq_l * d * e),
+            "bwd_preprocess": ("hbm", 2.0 * cfg.s * Hq_l * d * e + 4.0 * cfg.s * Hq_l),
+            "unpack_grads": ("hbm", 2.0 * cfg.s * (Hq_l + 2 * Hkv_l) * d * e),
+        }
+    else:
+        wall, ph, ws_bytes = run_upipe(cfg, args.steps, args.warmup, args.heads_per_chunk)
+        flops = 4.0 * d * pairs * Hq_l
+        kern = {"attn_fwd_chunked": ("mfma", flops)}
+
+    step_ms = wall * 1e3
+    dom = max(ph, key=ph.get)
+    bound, work = kern[dom]
+    ms = ph[dom]
+    if bound == "mfma":
+        achieved = work / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = work / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = dom
+    roof["avg_ms"] = round(ms, 4)
+    roof["traffic"] = read_traffic(dom, args.workload)
+
+    attn_ms = sum(ph.get(k, 0.0) for k in ("attn_fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "attn_fwd_chunked"))
+    perm_ms = sum(ph.get(k, 0.0) for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads"))
+    perm_bytes = sum(kern[k][1] for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads") if k in kern)
+    value = flops / wall / 1e12
+    out = {
+        "metric": METRIC if args.workload == "qwen_64k" else f"{METRIC} [workload {args.workload}]",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": {"qwen_64k": "Qwen3-4B-shaped SP=4 rank share at 65536 tokens",
+                         "qwen_8k": "Qwen3-4B-shaped SP=4 rank share at 8192 tokens",
+                         "packed_96k": "packed SFT batch at 98304 tokens (documents ~ geometric, mean 6000)",
+                         "upipe_256k": f"UPipe chunked forward, 32B-shaped SP=8 share at 262144 tokens, "
+                                       f"{args.heads_per_chunk} q heads per chunk",
+                         "tiny_f32": "tiny fp32 case"}[args.workload],
+            "seq_len": cfg.s, "ranks_simulated": cfg.P, "rank": 0, "q_heads": Hq_l, "kv_heads": Hkv_l,
+            "head_dim": d, "causal": cfg.causal, "packed_docs": None if cu is None else int(len(cu) - 1),
+            "global_batch": 1, "parallelism": f"sp{cfg.P} (one rank's share, ranks as buffers)",
+        },
+        "roofline": roof,
+        "mfma_frac_of_step": round(value / PEAK_BF16_TFLOPS, 4),
+        "attention_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2) if attn_ms else None,
+        "permute_gbs": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1) if perm_ms else None,
+        "phase_ms": {k: round(v, 4) for k, v in ph.items()},
+    }
+    if not cfg.backward:
+        out["workspace_bytes"] = ws_bytes
+        out["unchunked_intermediate_bytes"] = int(2 * cfg.s * Hq_l * d * e + 2 * cfg.s * Hkv_l * d * e)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
