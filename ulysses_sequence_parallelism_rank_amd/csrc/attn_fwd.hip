@@ -48,7 +48,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_kernel(AttnArgs a) {
   using C = FwdCfg<D, RB, KB>;
   constexpr int BM = C::BM, BN = C::BN, DT = C::DT, DB = C::DB, KSTR = C::KSTR, VSTR = C::VSTR;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[3][BN * VSTR];
+  static_assert(KB == 1, "the pipelined loop works on 32-key tiles");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -107,7 +108,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_kernel(AttnArgs a) {
   kbeg = (kbeg / BN) * BN;
   const bool wave_has_rows = wr0 < s;
 
-  // ---- K/V tile staging: global -> registers -> LDS
+  // ---- K/V tile staging: global -> registers -> LDS.
+  // K tiles rotate through 2 LDS buffers and V tiles through 3: in iteration j a wave reads
+  // K(j+1) and V(j) while a faster wave may already be storing tile j+1's successor.
   u32x4 pk[C::KVEC], pv[C::KVEC];
   auto load_tile = [&](int64_t k0) {
 #pragma unroll
@@ -123,14 +126,32 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_kernel(AttnArgs a) {
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int kbuf, int vbuf) {
 #pragma unroll
     for (int i = 0; i < C::KVEC; ++i) {
       const int vi = tid + i * kWaves * 64;
       const int r = vi / (D / 8), c8 = vi % (D / 8);
-      *reinterpret_cast<u32x4*>(&sK[buf][r * KSTR + 8 * c8]) = pk[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][r * VSTR + 8 * c8]) = pv[i];
+      *reinterpret_cast<u32x4*>(&sK[kbuf][r * KSTR + 8 * c8]) = pk[i];
+      *reinterpret_cast<u32x4*>(&sV[vbuf][r * VSTR + 8 * c8]) = pv[i];
     }
+  };
+  // S^T of one tile: s_out[rb][j] = q(row[rb]) . k(k0 + 8(j/4) + 4hf + j%4)
+  auto qk = [&](int kbuf, f32x16 (&s_out)[RB]) {
+    bf16x8 kf[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+      kf[t] = *reinterpret_cast<const bf16x8*>(&sK[kbuf][l32 * KSTR + 16 * t + 8 * hf]);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s_out[rb] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s_out[rb] = mfma32x32x16(kf[t], qf[rb][t], s_out[rb]);
+  };
+  // the tile needs no mask for any row of this wave
+  auto tile_full = [&](int64_t k0) {
+    return wave_has_rows && (k0 + BN <= s) && (!a.causal || k0 + BN - 1 <= wr0) && k0 + BN > wkbeg &&
+           k0 < wkend && (a.cu == nullptr || (k0 >= w_lo_last && k0 + BN <= w_hi_first));
   };
 
   f32x16 oacc[RB][DB];
@@ -143,92 +164,98 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_kernel(AttnArgs a) {
     for (int db = 0; db < DB; ++db) oacc[rb][db] = f32x16{};
   }
 
-  if (kbeg < kend) load_tile(kbeg);
-  int buf = 0;
-  for (int64_t k0 = kbeg; k0 < kend; k0 += BN, buf ^= 1) {
-    store_tile(buf);
-    __syncthreads();
-    if (k0 + BN < kend) load_tile(k0 + BN);
+  const int ntiles = kbeg < kend ? (int)((kend - kbeg + BN - 1) / BN) : 0;
+  const int gi = lane >> 4, li = lane & 15;
+  f32x16 sc[RB];  // S^T of the current tile, masked
+  float tmax[RB]; // its row max (log2 units)
+  auto mask_and_max = [&](int64_t k0) {
+    if (!tile_full(k0)) {
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int64_t key = k0 + 8 * (jj / 4) + 4 * hf + (jj % 4);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (key < lo[rb] || key >= hi[rb]) sc[rb][jj] = -INFINITY;
+      }
+    }
+    bool grow = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float mx = sc[rb][0];
+#pragma unroll
+      for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, sc[rb][jj]);
+      tmax[rb] = half_swap_max(mx) * c;
+      grow = grow || (tmax[rb] > m[rb] + kTau);
+    }
+    return __ballot(grow) != 0;
+  };
 
-    const bool active = wave_has_rows && k0 < wkend && k0 + BN > wkbeg;
-    if (active) {
-      const bool full = (k0 + BN <= s) && (!a.causal || k0 + BN - 1 <= wr0) &&
-                        (a.cu == nullptr || (k0 >= w_lo_last && k0 + BN <= w_hi_first));
-      // S^T = K Q^T : sacc[kb][rb][j] = q(row[rb]) . k(k0 + 32kb + 8(j/4) + 4hf + j%4)
-      f32x16 sacc[KB][RB];
+  // Pipeline: in iteration j the VALU turns S(j) into P(j) while the matrix cores compute
+  // S(j+1) from K(j+1); then O^T += V(j)^T P(j).
+  int j = 0;
+  if (ntiles > 0) {
+    load_tile(kbeg);
+    store_tile(0, 0);
+    __syncthreads();
+    if (ntiles > 1) load_tile(kbeg + BN);
+    qk(0, sc);
+    mask_and_max(kbeg);
+  }
+  // Outer loop: the (rare) rescale of O when a row max grew by more than kTau. The inner
+  // loop never writes O outside an MFMA, which keeps the accumulator in AGPRs.
+  while (j < ntiles) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+    for (int rb = 0; rb < RB; ++rb) {
+      // wave-uniform branch: an MFMA must never run under a partial exec mask
+      const bool need = tmax[rb] > m[rb] + kTau;
+      if (__ballot(need) == 0) continue;
+      const float mnew = need ? tmax[rb] : m[rb];
+      const float alpha = need ? fast_exp2(m[rb] - mnew) : 1.f;  // m = -inf on the first visible tile -> 0
+      m[rb] = mnew;
+      l[rb] *= alpha;
+      // Pass the scaled accumulator through an MFMA that adds zero, so that every definition
+      // of oacc is an MFMA result and it stays in AGPRs across the loop.
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sacc[kb][rb] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][(kb * 32 + l32) * KSTR + 16 * t + 8 * hf]);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) sacc[kb][rb] = mfma32x32x16(kf, qf[rb][t], sacc[kb][rb]);
-        }
-      }
-      if (!full) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int64_t key = k0 + kb * 32 + 8 * (j / 4) + 4 * hf + (j % 4);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-              if (key < lo[rb] || key >= hi[rb]) sacc[kb][rb][j] = -INFINITY;
-          }
-      }
-      // online softmax (log2 domain, lazy rescale)
-      bf16x8 pf[RB][KB][2];
+      for (int db = 0; db < DB; ++db) oacc[rb][db] = mfma32x32x16(bf16x8{}, bf16x8{}, oacc[rb][db] * alpha);
+    }
+    for (;;) {
+      const int64_t k0 = kbeg + (int64_t)j * BN;
+      const int vb = j % 3;
+      if (j + 1 < ntiles) store_tile((j + 1) & 1, (j + 1) % 3);
+      __syncthreads();
+      if (j + 2 < ntiles) load_tile(k0 + 2 * BN);
+      // P(j) on the VALU while the matrix cores compute S(j+1); then O^T += V(j)^T P(j)
+      bf16x8 pf[RB][2];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][rb][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float tmax = mx * c;
-        if (__ballot(tmax > m[rb] + kTau) != 0) {
-          const float mnew = fmaxf(m[rb], tmax);
-          const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m[rb] - mnew);
-          m[rb] = mnew;
-          l[rb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
-        }
         const float ms = m[rb] == -INFINITY ? 0.f : m[rb];
+        float ls = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int jj = 0; jj < 16; ++jj) {
+          const float pj = fast_exp2(__builtin_fmaf(sc[rb][jj], c, -ms));
+          sc[rb][jj] = pj;
+          ls += pj;
+        }
+        l[rb] += ls;
+        pf[rb][0] = to_bf16x8(sc[rb], 0);
+        pf[rb][1] = to_bf16x8(sc[rb], 1);
+      }
+      qk((j + 1) & 1, sc);
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float pj = fast_exp2(__builtin_fmaf(sacc[kb][rb][j], c, -ms));
-            sacc[kb][rb][j] = pj;
-            l[rb] += pj;
-          }
-          pf[rb][kb][0] = to_bf16x8(sacc[kb][rb], 0);
-          pf[rb][kb][1] = to_bf16x8(sacc[kb][rb], 1);
+      for (int tt = 0; tt < 2; ++tt) {
+        const int kr = 16 * tt + 4 * hf + (li >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
+          const i16x4 v0 = lds_read_tr16(&sV[vb][kr * VSTR + col]);
+          const i16x4 v1 = lds_read_tr16(&sV[vb][(kr + 8) * VSTR + col]);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32x32x16(vf, pf[rb][tt], oacc[rb][db]);
         }
       }
-      // O^T += V^T P^T
-      const int gi = lane >> 4, li = lane & 15;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int kr = kb * 32 + 16 * tt + 4 * hf + (li >> 2);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
-            const i16x4 v0 = lds_read_tr16(&sV[buf][kr * VSTR + col]);
-            const i16x4 v1 = lds_read_tr16(&sV[buf][(kr + 8) * VSTR + col]);
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32x32x16(vf, pf[rb][kb][tt], oacc[rb][db]);
-          }
-        }
+      if (++j >= ntiles) break;
+      if (mask_and_max(k0 + BN)) break;
     }
   }
 
@@ -236,7 +263,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_kernel(AttnArgs a) {
   uint16_t* O = static_cast<uint16_t*>(a.out) + (int64_t)h * D;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const float lt = l[rb] + __shfl_xor(l[rb], 32);
+    const float lt = half_swap_sum(l[rb]);
     if (row[rb] >= s) continue;
     const float inv = 1.f / lt;
 #pragma unroll

@@ -26,10 +26,35 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32 on gfx950).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair, round to nearest even: one v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// v_permlane32_swap on two copies of x: r[0] holds x of lanes 0..31 in both halves and r[1]
+// x of lanes 32..63 in both halves, so max(r[0], r[1]) / r[0] + r[1] combine lanes l and l^32.
+// (Elements are copied to scalars before any bit cast: clang's __builtin_bit_cast of a vector
+// element reads element 0.)
+__device__ __forceinline__ void half_swap(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float half_swap_max(float x) {
+  float a, b;
+  half_swap(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  float a, b;
+  half_swap(x, a, b);
+  return a + b;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
