@@ -66,16 +66,15 @@ struct DqCfg {
   static constexpr int BM = kWaves * RB * 32;
   static constexpr int BN = KB * 32;
   static constexpr int DT = D / 16, DB = D / 32;
-  static constexpr int STR = D + 8;
   static constexpr int KVEC = BN * D / 8 / (kWaves * 64);
 };
 
 template <int D, int RB, int KB>
 __global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
   using C = DqCfg<D, RB, KB>;
-  constexpr int BM = C::BM, BN = C::BN, DT = C::DT, DB = C::DB, STR = C::STR;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * STR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * STR];
+  constexpr int BM = C::BM, BN = C::BN, DT = C::DT, DB = C::DB;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5, gi = lane >> 4, li = lane & 15;
@@ -164,8 +163,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
     for (int i = 0; i < C::KVEC; ++i) {
       const int vi = tid + i * kWaves * 64;
       const int r = vi / (D / 8), c8 = vi % (D / 8);
-      *reinterpret_cast<u32x4*>(&sK[buf][r * STR + 8 * c8]) = pk[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][r * STR + 8 * c8]) = pv[i];
+      *reinterpret_cast<u32x4*>(&sK[buf][tile_off<D>(r, 8 * c8)]) = pk[i];
+      *reinterpret_cast<u32x4*>(&sV[buf][tile_off<D>(r, 8 * c8)]) = pv[i];
     }
   };
 
@@ -199,8 +198,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
       for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][(kb * 32 + l32) * STR + 16 * t + 8 * hf]);
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[buf][(kb * 32 + l32) * STR + 16 * t + 8 * hf]);
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][tile_off<D>(kb * 32 + l32, 16 * t + 8 * hf)]);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[buf][tile_off<D>(kb * 32 + l32, 16 * t + 8 * hf)]);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
             sacc[kb][rb] = mfma32x32x16(kf, qf[rb][t], sacc[kb][rb]);
@@ -234,8 +233,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
-            const i16x4 k0v = lds_read_tr16(&sK[buf][kr * STR + col]);
-            const i16x4 k1v = lds_read_tr16(&sK[buf][(kr + 8) * STR + col]);
+            const i16x4 k0v = lds_read_tr16(&sK[buf][tile_off<D>(kr, col)]);
+            const i16x4 k1v = lds_read_tr16(&sK[buf][tile_off<D>(kr + 8, col)]);
             const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0v, k1v, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) dqacc[rb][db] = mfma32x32x16(kt, dsf[rb][kb][tt], dqacc[rb][db]);
@@ -268,17 +267,16 @@ struct DkvCfg {
   static constexpr int BNK = kWaves * 32;
   static constexpr int BMQ = QB * 32;
   static constexpr int DT = D / 16, DB = D / 32;
-  static constexpr int STR = D + 8;
   static constexpr int QVEC = BMQ * D / 8 / (kWaves * 64);
 };
 
 template <int D, int QB>
 __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
   using C = DkvCfg<D, QB>;
-  constexpr int BNK = C::BNK, BMQ = C::BMQ, DT = C::DT, DB = C::DB, STR = C::STR;
+  constexpr int BNK = C::BNK, BMQ = C::BMQ, DT = C::DT, DB = C::DB;
   static_assert(C::QVEC >= 1, "query tile too small for the thread count");
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BMQ * STR];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[2][BMQ * STR];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BMQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[2][BMQ * D];
   __shared__ __attribute__((aligned(16))) float sL[2][BMQ];
   __shared__ __attribute__((aligned(16))) float sD[2][BMQ];
 
@@ -365,8 +363,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
     for (int i = 0; i < C::QVEC; ++i) {
       const int vi = tid + i * kWaves * 64;
       const int r = vi / (D / 8), c8 = vi % (D / 8);
-      *reinterpret_cast<u32x4*>(&sQ[buf][r * STR + 8 * c8]) = pq[i];
-      *reinterpret_cast<u32x4*>(&sG[buf][r * STR + 8 * c8]) = pg[i];
+      *reinterpret_cast<u32x4*>(&sQ[buf][tile_off<D>(r, 8 * c8)]) = pq[i];
+      *reinterpret_cast<u32x4*>(&sG[buf][tile_off<D>(r, 8 * c8)]) = pg[i];
     }
     if (tid < BMQ) {
       sL[buf][tid] = pl;
@@ -404,8 +402,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
       for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sQ[buf][(qb * 32 + l32) * STR + 16 * t + 8 * hf]);
-          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&sG[buf][(qb * 32 + l32) * STR + 16 * t + 8 * hf]);
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sQ[buf][tile_off<D>(qb * 32 + l32, 16 * t + 8 * hf)]);
+          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&sG[buf][tile_off<D>(qb * 32 + l32, 16 * t + 8 * hf)]);
           sacc[qb] = mfma32x32x16(qa, kf[t], sacc[qb]);
           pacc[qb] = mfma32x32x16(ga, vf[t], pacc[qb]);
         }
@@ -443,10 +441,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
-            const i16x4 g0 = lds_read_tr16(&sG[buf][qr * STR + col]);
-            const i16x4 g1 = lds_read_tr16(&sG[buf][(qr + 8) * STR + col]);
-            const i16x4 q0v = lds_read_tr16(&sQ[buf][qr * STR + col]);
-            const i16x4 q1v = lds_read_tr16(&sQ[buf][(qr + 8) * STR + col]);
+            const i16x4 g0 = lds_read_tr16(&sG[buf][tile_off<D>(qr, col)]);
+            const i16x4 g1 = lds_read_tr16(&sG[buf][tile_off<D>(qr + 8, col)]);
+            const i16x4 q0v = lds_read_tr16(&sQ[buf][tile_off<D>(qr, col)]);
+            const i16x4 q1v = lds_read_tr16(&sQ[buf][tile_off<D>(qr + 8, col)]);
             const bf16x8 gt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7));
             const bf16x8 qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0v, q1v, 0, 1, 2, 3, 4, 5, 6, 7));
             dvacc[db] = mfma32x32x16(gt, pf[qb][tt], dvacc[db]);

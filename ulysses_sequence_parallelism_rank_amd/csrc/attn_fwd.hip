@@ -32,6 +32,17 @@ namespace {
 constexpr int kWaves = 4;
 constexpr float kTau = 8.0f;
 
+// Tile shape of the d=128 kernel: 32-row blocks per wave and workgroups per CU.
+#ifndef ULY_FWD_RB
+#define ULY_FWD_RB 1
+#endif
+#ifndef ULY_FWD_KB
+#define ULY_FWD_KB 1
+#endif
+#ifndef ULY_FWD_OCC
+#define ULY_FWD_OCC 2
+#endif
+
 template <int D, int RB, int KB>
 struct FwdCfg {
   static constexpr int BM = kWaves * RB * 32;  // query rows per workgroup
@@ -43,13 +54,12 @@ struct FwdCfg {
   static constexpr int KVEC = BN * D / 8 / (kWaves * 64);  // 16-byte vectors per thread per tile
 };
 
-template <int D, int RB, int KB>
-__global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_kernel(AttnArgs a) {
+template <int D, int RB, int KB, int OCC>
+__global__ __launch_bounds__(kWaves * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
   using C = FwdCfg<D, RB, KB>;
   constexpr int BM = C::BM, BN = C::BN, DT = C::DT, DB = C::DB, KSTR = C::KSTR, VSTR = C::VSTR;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[3][BN * VSTR];
-  static_assert(KB == 1, "the pipelined loop works on 32-key tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * VSTR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -108,9 +118,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_kernel(AttnArgs a) {
   kbeg = (kbeg / BN) * BN;
   const bool wave_has_rows = wr0 < s;
 
-  // ---- K/V tile staging: global -> registers -> LDS.
-  // K tiles rotate through 2 LDS buffers and V tiles through 3: in iteration j a wave reads
-  // K(j+1) and V(j) while a faster wave may already be storing tile j+1's successor.
+  // ---- K/V tile staging: global -> registers -> LDS, two LDS buffers each.
+  // In iteration j the waves read K(j+1) (stored before this iteration's barrier) and V(j)
+  // (stored after the previous barrier); V(j+1) is stored only after this barrier, when
+  // every wave is done with V(j-1), whose buffer it reuses.
   u32x4 pk[C::KVEC], pv[C::KVEC];
   auto load_tile = [&](int64_t k0) {
 #pragma unroll
@@ -126,27 +137,37 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_kernel(AttnArgs a) {
       }
     }
   };
-  auto store_tile = [&](int kbuf, int vbuf) {
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < C::KVEC; ++i) {
       const int vi = tid + i * kWaves * 64;
       const int r = vi / (D / 8), c8 = vi % (D / 8);
-      *reinterpret_cast<u32x4*>(&sK[kbuf][r * KSTR + 8 * c8]) = pk[i];
-      *reinterpret_cast<u32x4*>(&sV[vbuf][r * VSTR + 8 * c8]) = pv[i];
+      *reinterpret_cast<u32x4*>(&sK[buf][r * KSTR + 8 * c8]) = pk[i];
     }
   };
-  // S^T of one tile: s_out[rb][j] = q(row[rb]) . k(k0 + 8(j/4) + 4hf + j%4)
-  auto qk = [&](int kbuf, f32x16 (&s_out)[RB]) {
-    bf16x8 kf[DT];
+  auto store_v = [&](int buf) {
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
-      kf[t] = *reinterpret_cast<const bf16x8*>(&sK[kbuf][l32 * KSTR + 16 * t + 8 * hf]);
+    for (int i = 0; i < C::KVEC; ++i) {
+      const int vi = tid + i * kWaves * 64;
+      const int r = vi / (D / 8), c8 = vi % (D / 8);
+      *reinterpret_cast<u32x4*>(&sV[buf][r * VSTR + 8 * c8]) = pv[i];
+    }
+  };
+  // S^T of one tile: s_out[kb][rb][j] = q(row[rb]) . k(k0 + 32kb + 8(j/4) + 4hf + j%4)
+  auto qk = [&](int kbuf, f32x16 (&s_out)[KB][RB]) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) s_out[rb] = f32x16{};
+    for (int kb = 0; kb < KB; ++kb) {
+      bf16x8 kf[DT];
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+      for (int t = 0; t < DT; ++t)
+        kf[t] = *reinterpret_cast<const bf16x8*>(&sK[kbuf][(kb * 32 + l32) * KSTR + 16 * t + 8 * hf]);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) s_out[rb] = mfma32x32x16(kf[t], qf[rb][t], s_out[rb]);
+      for (int rb = 0; rb < RB; ++rb) s_out[kb][rb] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s_out[kb][rb] = mfma32x32x16(kf[t], qf[rb][t], s_out[kb][rb]);
+    }
   };
   // the tile needs no mask for any row of this wave
   auto tile_full = [&](int64_t k0) {
@@ -166,24 +187,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_kernel(AttnArgs a) {
 
   const int ntiles = kbeg < kend ? (int)((kend - kbeg + BN - 1) / BN) : 0;
   const int gi = lane >> 4, li = lane & 15;
-  f32x16 sc[RB];  // S^T of the current tile, masked
-  float tmax[RB]; // its row max (log2 units)
+  f32x16 sc[KB][RB];  // S^T of the current tile, masked
+  float tmax[RB];     // its row max (log2 units)
   auto mask_and_max = [&](int64_t k0) {
     if (!tile_full(k0)) {
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int64_t key = k0 + 8 * (jj / 4) + 4 * hf + (jj % 4);
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          if (key < lo[rb] || key >= hi[rb]) sc[rb][jj] = -INFINITY;
-      }
+        for (int jj = 0; jj < 16; ++jj) {
+          const int64_t key = k0 + 32 * kb + 8 * (jj / 4) + 4 * hf + (jj % 4);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            if (key < lo[rb] || key >= hi[rb]) sc[kb][rb][jj] = -INFINITY;
+        }
     }
     bool grow = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float mx = sc[rb][0];
+      float mx = sc[0][rb][0];
 #pragma unroll
-      for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, sc[rb][jj]);
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, sc[kb][rb][jj]);
       tmax[rb] = half_swap_max(mx) * c;
       grow = grow || (tmax[rb] > m[rb] + kTau);
     }
@@ -195,7 +220,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_kernel(AttnArgs a) {
   int j = 0;
   if (ntiles > 0) {
     load_tile(kbeg);
-    store_tile(0, 0);
+    store_k(0);
+    store_v(0);
     __syncthreads();
     if (ntiles > 1) load_tile(kbeg + BN);
     qk(0, sc);
@@ -220,40 +246,46 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_kernel(AttnArgs a) {
     }
     for (;;) {
       const int64_t k0 = kbeg + (int64_t)j * BN;
-      const int vb = j % 3;
-      if (j + 1 < ntiles) store_tile((j + 1) & 1, (j + 1) % 3);
+      const int vb = j & 1;
+      if (j + 1 < ntiles) store_k((j + 1) & 1);
       __syncthreads();
+      if (j + 1 < ntiles) store_v((j + 1) & 1);
       if (j + 2 < ntiles) load_tile(k0 + 2 * BN);
       // P(j) on the VALU while the matrix cores compute S(j+1); then O^T += V(j)^T P(j)
-      bf16x8 pf[RB][2];
+      bf16x8 pf[RB][KB][2];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const float ms = m[rb] == -INFINITY ? 0.f : m[rb];
         float ls = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const float pj = fast_exp2(__builtin_fmaf(sc[rb][jj], c, -ms));
-          sc[rb][jj] = pj;
-          ls += pj;
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const float pj = fast_exp2(__builtin_fmaf(sc[kb][rb][jj], c, -ms));
+            sc[kb][rb][jj] = pj;
+            ls += pj;
+          }
+          pf[rb][kb][0] = to_bf16x8(sc[kb][rb], 0);
+          pf[rb][kb][1] = to_bf16x8(sc[kb][rb], 1);
         }
         l[rb] += ls;
-        pf[rb][0] = to_bf16x8(sc[rb], 0);
-        pf[rb][1] = to_bf16x8(sc[rb], 1);
       }
       qk((j + 1) & 1, sc);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int kr = 16 * tt + 4 * hf + (li >> 2);
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
-          const i16x4 v0 = lds_read_tr16(&sV[vb][kr * VSTR + col]);
-          const i16x4 v1 = lds_read_tr16(&sV[vb][(kr + 8) * VSTR + col]);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int tt = 0; tt < 2; ++tt) {
+          const int kr = 32 * kb + 16 * tt + 4 * hf + (li >> 2);
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32x32x16(vf, pf[rb][tt], oacc[rb][db]);
+          for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
+            const i16x4 v0 = lds_read_tr16(&sV[vb][kr * VSTR + col]);
+            const i16x4 v1 = lds_read_tr16(&sV[vb][(kr + 8) * VSTR + col]);
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32x32x16(vf, pf[rb][kb][tt], oacc[rb][db]);
+          }
         }
-      }
       if (++j >= ntiles) break;
       if (mask_and_max(k0 + BN)) break;
     }
@@ -279,21 +311,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int RB, int KB>
+template <int D, int RB, int KB, int OCC>
 hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t stream) {
   using C = FwdCfg<D, RB, KB>;
   const int64_t nmb = (a.s + C::BM - 1) / C::BM;
   const int64_t blocks = nmb * a.n_heads;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, RB, KB>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, RB, KB, OCC>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream) {
-  if (d == 128) return launch_fwd_t<128, 2, 1>(a, stream);
-  return launch_fwd_t<64, 2, 1>(a, stream);
+  if (d == 128) return launch_fwd_t<128, ULY_FWD_RB, ULY_FWD_KB, ULY_FWD_OCC>(a, stream);
+  return launch_fwd_t<64, 2, 1, 1>(a, stream);
 }
 
 }  // namespace uly

@@ -81,6 +81,23 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_ptr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(lds_ptr));
 }
 
+// Bank-conflict-free layout for row-major bf16 tiles of D columns in LDS: the 16-byte
+// chunks of row r are XOR-permuted by swz_chunk(r). Both access patterns of the MFMA
+// operands hit 64 distinct banks: 16-byte reads of one column chunk by 16 consecutive rows
+// (ds_read_b128), and the transposing read of 4 consecutive rows x 4 chunks by 32 lanes
+// (ds_read_b64_tr_b16).
+template <int D>
+__device__ __forceinline__ int swz_chunk(int row) {
+  static_assert(D == 64 || D == 128, "head dim");
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+// element offset of (row, col) in a swizzled [rows][D] tile; col is a multiple of 4
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz_chunk<D>(row)) << 3) | (col & 7));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
