@@ -189,6 +189,9 @@ def main():
     ap.add_argument("--workload", default="qwen_64k", choices=sorted(W.CONFIGS))
     ap.add_argument("--heads-per-chunk", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device copy (ulysses_pack with one rank) and exit; "
+                         "its FETCH_SIZE/WRITE_SIZE counters scale the traffic of other kernels")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the layer on one GPU; runs on more than one GPU are "
@@ -198,6 +201,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     U.lib()
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty((n // 256, 1, 128), dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        U.ulysses_pack([src], 0, dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
+        return
     cfg = W.CONFIGS[args.workload]
     cu = W.cu_seqlens_for(cfg)
     cu_dev = None if cu is None else torch.from_numpy(cu).to("cuda")

@@ -277,8 +277,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
   static_assert(C::QVEC >= 1, "query tile too small for the thread count");
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BMQ * D];
   __shared__ __attribute__((aligned(16))) uint16_t sG[2][BMQ * D];
-  __shared__ __attribute__((aligned(16))) float sL[2][BMQ];
-  __shared__ __attribute__((aligned(16))) float sD[2][BMQ];
+  __shared__ __attribute__((aligned(16))) float sL[2][64];
+  __shared__ __attribute__((aligned(16))) float sD[2][64];
+  static_assert(BMQ <= 64, "one wave loads the per-row statistics");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5, gi = lane >> 4, li = lane & 15;
@@ -333,42 +334,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
   const int64_t ntile = qend > qbeg ? (qend - qbeg + BMQ - 1) / BMQ : 0;
   const int64_t nsteps = ntile * G;
 
-  u32x4 pq[C::QVEC], pg[C::QVEC];
-  float pl = 0.f, pd = 0.f;
-  auto load_tile = [&](int64_t step) {
-    const int hq = kvh * G + (int)(step / ntile);
-    const int64_t q0 = qbeg + (step % ntile) * BMQ;
-    const uint16_t* Qh = static_cast<const uint16_t*>(a.q) + (int64_t)hq * D;
-    const uint16_t* Gh = static_cast<const uint16_t*>(a.dout) + (int64_t)hq * D;
-#pragma unroll
-    for (int i = 0; i < C::QVEC; ++i) {
-      const int vi = tid + i * kWaves * 64;
-      const int r = vi / (D / 8), c8 = vi % (D / 8);
-      const int64_t qr = q0 + r;
-      pq[i] = u32x4{0, 0, 0, 0};
-      pg[i] = u32x4{0, 0, 0, 0};
-      if (qr < s) {
-        pq[i] = *reinterpret_cast<const u32x4*>(Qh + qr * a.q_row + 8 * c8);
-        pg[i] = *reinterpret_cast<const u32x4*>(Gh + qr * a.q_row + 8 * c8);
-      }
-    }
-    if (tid < BMQ) {
-      const int64_t qr = q0 + tid;
-      pl = qr < s ? a.lse_in[(int64_t)hq * a.lse_row + qr] * kLog2e : 0.f;
-      pd = qr < s ? a.delta[(int64_t)hq * a.lse_row + qr] : 0.f;
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::QVEC; ++i) {
-      const int vi = tid + i * kWaves * 64;
-      const int r = vi / (D / 8), c8 = vi % (D / 8);
-      *reinterpret_cast<u32x4*>(&sQ[buf][tile_off<D>(r, 8 * c8)]) = pq[i];
-      *reinterpret_cast<u32x4*>(&sG[buf][tile_off<D>(r, 8 * c8)]) = pg[i];
-    }
-    if (tid < BMQ) {
-      sL[buf][tid] = pl;
-      sD[buf][tid] = pd;
+  // Steps walk the query tiles from the last one down, the G heads of a tile back to back:
+  // every causal workgroup ends at the last row, so workgroups running at the same time read
+  // the same Q/dO tiles and share them through L2. Tiles travel to LDS by DMA.
+  auto tile_q0 = [&](int64_t step) { return qbeg + (ntile - 1 - step / G) * BMQ; };
+  auto issue_tile = [&](int64_t step, int b) {
+    const int hq = kvh * G + (int)(step % G);
+    const int64_t q0 = tile_q0(step);
+    dma_tile<D, BMQ, kWaves * 64>(static_cast<const uint16_t*>(a.q) + (int64_t)hq * D, a.q_row, q0, s, sQ[b], tid);
+    dma_tile<D, BMQ, kWaves * 64>(static_cast<const uint16_t*>(a.dout) + (int64_t)hq * D, a.q_row, q0, s, sG[b], tid);
+    if (wave == 0) {
+      // one fp32 per lane: lane i lands at sL[b][i] / sD[b][i]
+      int64_t qr = q0 + (lane < BMQ ? lane : BMQ - 1);
+      qr = qr < s ? qr : s - 1;
+      __builtin_amdgcn_global_load_lds(a.lse_in + (int64_t)hq * a.lse_row + qr, &sL[b][0], 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.delta + (int64_t)hq * a.lse_row + qr, &sD[b][0], 4, 0, 0);
     }
   };
 
@@ -379,13 +359,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
     dvacc[db] = f32x16{};
   }
 
-  if (nsteps > 0) load_tile(0);
+  if (nsteps > 0) issue_tile(0, 0);
   int buf = 0;
   for (int64_t step = 0; step < nsteps; ++step, buf ^= 1) {
-    store_tile(buf);
-    __syncthreads();
-    if (step + 1 < nsteps) load_tile(step + 1);
-    const int64_t q0 = qbeg + (step % ntile) * BMQ;
+    __syncthreads();  // tile `step` has landed and every wave is done with tile step-1
+    if (step + 1 < nsteps) issue_tile(step + 1, buf ^ 1);
+    const int64_t q0 = tile_q0(step);
 
     const bool active = wave_has_keys && q0 < wqend && q0 + BMQ > wqbeg;
     if (active) {
@@ -418,7 +397,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = 4 * jj + e;
-            float p = fast_exp2(__builtin_fmaf(sacc[qb][j], c, -L4[e]));
+            float p = fast_exp2(__builtin_fmaf(sacc[qb][j], c, -L4[e] * kLog2e));
             if (!full) {
               const int64_t qr = q0 + qb * 32 + 8 * jj + 4 * hf + e;
               if (qr < rlo || qr >= rhi) p = 0.f;

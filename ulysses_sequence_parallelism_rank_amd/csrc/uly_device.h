@@ -98,6 +98,31 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * D + ((((col >> 3) ^ swz_chunk<D>(row)) << 3) | (col & 7));
 }
 
+// Copy rows [r0, r0 + ROWS) of a row-major bf16 matrix (row stride `stride` elements, D
+// columns) into a swizzled LDS tile (tile_off layout) with LDS DMA (global_load_lds_dwordx4):
+// no registers hold the data on its way. Each wave instruction fills 64 consecutive 16-byte
+// slots; a lane fetches the logical chunk that the swizzle maps to its slot. Rows at or past
+// `nrows` are read from row nrows - 1 (finite values for rows the caller masks). The data is
+// visible to the workgroup after the next __syncthreads (its fence waits for the DMA).
+template <int D, int ROWS, int NTHREADS>
+__device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t stride, int64_t r0, int64_t nrows,
+                                         uint16_t* lds_tile, int tid) {
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int SLOTS = ROWS * CPR;   // 16-byte slots in the tile
+  static_assert(SLOTS % NTHREADS == 0, "tile must be a whole number of wave instructions");
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int i = 0; i < SLOTS / NTHREADS; ++i) {
+    const int sl0 = (i * (NTHREADS / 64) + wave) * 64;  // first slot of this instruction (wave-uniform)
+    const int sl = sl0 + lane;
+    const int row = sl / CPR, pc = sl % CPR;
+    const int c = pc ^ swz_chunk<D>(row);
+    int64_t gr = r0 + row;
+    gr = gr < nrows ? gr : nrows - 1;
+    __builtin_amdgcn_global_load_lds(src + gr * stride + c * 8, lds_tile + sl0 * 8, 16, 0, 0);
+  }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
