@@ -99,18 +99,19 @@ def forward(q, k, v, scale, causal=True, cu_seqlens=None, rows=None):
 
 
 def rows_attending(keys, s, causal, cu_seqlens):
-    """Every row i that can see at least one key of `keys`."""
+    """Every row i that can see at least one key of `keys` (exactly those rows): per
+    document holding a key, its rows from the smallest such key (causal) or from the
+    document start (noncausal) to the document end."""
     keys = np.asarray(keys)
-    if not causal and cu_seqlens is None:
-        return np.arange(s)
-    lo = int(keys.min()) if causal else 0
-    cand = np.arange(lo, s)
-    if cu_seqlens is not None:
-        cu = np.asarray(cu_seqlens, dtype=np.int64)
-        docs = np.unique(np.searchsorted(cu, keys, side="right") - 1)
-        cand_docs = np.searchsorted(cu, cand, side="right") - 1
-        cand = cand[np.isin(cand_docs, docs)]
-    return cand
+    if cu_seqlens is None:
+        return np.arange(int(keys.min()) if causal else 0, s)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    kdoc = np.searchsorted(cu, keys, side="right") - 1
+    parts = []
+    for doc in np.unique(kdoc):
+        lo = int(keys[kdoc == doc].min()) if causal else int(cu[doc])
+        parts.append(np.arange(lo, int(cu[doc + 1])))
+    return np.concatenate(parts)
 
 
 def backward(q, k, v, do, scale, causal=True, cu_seqlens=None, q_rows=None, kv_cols=None):

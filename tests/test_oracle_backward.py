@@ -114,6 +114,23 @@ def test_subsets_match_full():
     np.testing.assert_allclose(dq2, dq[rows], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(dk2, dk[cols], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(dv2, dv[cols], rtol=1e-12, atol=1e-13)
+    # keys in two documents, noncausal too
+    cols = np.array([3, 390, 1020])
+    for causal in (True, False):
+        dq, dk, dv = attention.backward(q, k, v, do, 0.4, causal, cu)
+        _, dk2, dv2 = attention.backward(q, k, v, do, 0.4, causal, cu, q_rows=np.zeros(0, int), kv_cols=cols)
+        np.testing.assert_allclose(dk2, dk[cols], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(dv2, dv[cols], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("cu", [None, [0, 7, 8, 20, 31]])
+def test_rows_attending_is_exact(causal, cu):
+    """By brute force over the mask: the rows that see at least one of the keys."""
+    s = 31
+    for keys in ([0], [30], [5, 6], [7], [3, 19, 25], [8, 30]):
+        want = [i for i in range(s) if attention.allowed([i], keys, causal, cu).any()]
+        assert list(attention.rows_attending(keys, s, causal, cu)) == want
 
 
 def test_planted_missing_D_term_is_caught(monkeypatch):

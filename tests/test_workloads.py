@@ -48,6 +48,15 @@ def test_documents_cover_the_sequence():
     assert 2000 < lens.mean() < 20000
 
 
+def test_packed_seed0_instance():
+    """The seed-0 packed 96K instance: 11 documents, the last truncated, about a fifth of
+    the dense-causal pair count."""
+    cu = W.cu_seqlens_for(W.CONFIGS["packed_96k"])
+    assert list(cu) == [0, 4080, 10198, 10317, 10331, 13633, 23412, 27454, 31986, 48886, 85230, 98304]
+    lens = np.diff(cu).astype(np.int64)
+    assert int((lens ** 2).sum()) == 1974925326
+
+
 def test_config_shapes():
     c = W.CONFIGS["qwen_64k"]
     assert (c.s, c.Hq_l, c.Hkv_l, c.G, c.d) == (65536, 8, 2, 4, 128)

@@ -21,7 +21,7 @@ Recipe (also stated in the design doc):
     nearest even) or kept as fp32. Any row range can therefore be regenerated
     without drawing the rest of the tensor.
   * rank p holds rows [p*s_l, (p+1)*s_l) of each global tensor (contiguous chunks).
-  * packed documents: lengths from default_rng([seed, 99]).geometric(1/mean) until
+  * packed documents: lengths from their own default_rng(seed).geometric(1/mean) until
     their sum reaches s, the last one truncated to fit; cu_seqlens = running sums.
 """
 from __future__ import annotations
@@ -142,8 +142,9 @@ def head_slice(glob: np.ndarray, P: int, rank: int) -> np.ndarray:
 
 
 def doc_lengths(s: int, mean: float, seed: int = 0) -> list:
-    """Packed document lengths: geometric(1/mean) draws until they cover s, last truncated."""
-    rng = np.random.default_rng([seed, 99])
+    """Packed document lengths: geometric(1/mean) draws (support >= 1) from their own
+    default_rng(seed) stream until they cover s; the last one is truncated to fit."""
+    rng = np.random.default_rng(seed)
     out, tot = [], 0
     while tot < s:
         n = int(rng.geometric(1.0 / mean))
