@@ -122,26 +122,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
     }
   }
 
-  const int64_t wr0 = m0 + wave * RB * 32;
-  const int64_t wr1 = (wr0 + RB * 32 < s ? wr0 + RB * 32 : s) - 1;
+  // key range of the workgroup: keys any of its rows may see
   const int64_t last_row = (m0 + BM < s ? m0 + BM : s) - 1;
-  int64_t kbeg = 0, kend = s, wkbeg = 0, wkend = s, w_lo_last = 0, w_hi_first = s;
+  int64_t kbeg = 0, kend = s;
   if (a.cu != nullptr) {
     kbeg = a.cu[doc_of(a.cu, a.n_docs, m0)];
     kend = a.cu[doc_of(a.cu, a.n_docs, last_row) + 1];
-    if (wr0 < s) {
-      wkbeg = a.cu[doc_of(a.cu, a.n_docs, wr0)];
-      w_hi_first = a.cu[doc_of(a.cu, a.n_docs, wr0) + 1];
-      w_lo_last = a.cu[doc_of(a.cu, a.n_docs, wr1)];
-      wkend = a.cu[doc_of(a.cu, a.n_docs, wr1) + 1];
-    }
   }
-  if (a.causal) {
-    kend = kend < last_row + 1 ? kend : last_row + 1;
-    wkend = wkend < wr1 + 1 ? wkend : wr1 + 1;
-  }
+  if (a.causal) kend = kend < last_row + 1 ? kend : last_row + 1;
   kbeg = (kbeg / BN) * BN;
-  const bool wave_has_rows = wr0 < s;
+  // key k is seen by row rb of this lane iff (uint32)(k - lo[rb]) < width[rb]
+  uint32_t width[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) width[rb] = (uint32_t)(hi[rb] - lo[rb]);
 
   u32x4 pk[C::KVEC], pv[C::KVEC];
   auto load_tile = [&](int64_t k0) {
@@ -181,10 +174,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
     __syncthreads();
     if (k0 + BN < kend) load_tile(k0 + BN);
 
-    const bool active = wave_has_rows && k0 < wkend && k0 + BN > wkbeg;
-    if (active) {
-      const bool full = (k0 + BN <= s) && (!a.causal || k0 + BN - 1 <= wr0) &&
-                        (a.cu == nullptr || (k0 >= w_lo_last && k0 + BN <= w_hi_first));
+    // Every wave runs every tile; keys outside a row's range get P = 0 from an unsigned
+    // compare, so no branch surrounds the MFMAs.
+    {
       f32x16 sacc[KB][RB], pacc[KB][RB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -212,13 +204,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
+          const int32_t krel0 = (int32_t)(k0 - lo[rb]) + kb * 32 + 4 * hf;
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             float p = fast_exp2(__builtin_fmaf(sacc[kb][rb][j], c, -lse2[rb]));
-            if (!full) {
-              const int64_t key = k0 + kb * 32 + 8 * (j / 4) + 4 * hf + (j % 4);
-              if (key < lo[rb] || key >= hi[rb]) p = 0.f;
-            }
+            p = (uint32_t)(krel0 + 8 * (j / 4) + (j % 4)) < width[rb] ? p : 0.f;
             sacc[kb][rb][j] = p * (pacc[kb][rb][j] - dl[rb]);
           }
           dsf[rb][kb][0] = to_bf16x8(sacc[kb][rb], 0);
@@ -301,6 +291,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
   }
   if (a.causal) rlo = key;
   if (key >= s) rhi = rlo;  // padding key: seen by no row
+  const uint32_t width = (uint32_t)(rhi - rlo);  // row r is seen iff (uint32)(r - rlo) < width
   bf16x8 kf[DT], vf[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
@@ -313,34 +304,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
     vf[t] = __builtin_bit_cast(bf16x8, y);
   }
 
-  // row ranges of the workgroup and of this wave
+  // row range of the workgroup: rows that may see any of its keys
   const int64_t last_key = (n0 + BNK < s ? n0 + BNK : s) - 1;
-  const int64_t wk0 = n0 + wave * 32;
-  const int64_t wk1 = (wk0 + 32 < s ? wk0 + 32 : s) - 1;
   int64_t qbeg = a.causal ? n0 : 0, qend = s;
-  int64_t wqbeg = a.causal ? wk0 : 0, wqend = s, w_hi_first = s, w_lo_last = 0;
   if (a.cu != nullptr) {
     qend = a.cu[doc_of(a.cu, a.n_docs, last_key) + 1];
     if (!a.causal) qbeg = a.cu[doc_of(a.cu, a.n_docs, n0)];
-    if (wk0 < s) {
-      wqend = a.cu[doc_of(a.cu, a.n_docs, wk1) + 1];
-      w_hi_first = a.cu[doc_of(a.cu, a.n_docs, wk0) + 1];
-      w_lo_last = a.cu[doc_of(a.cu, a.n_docs, wk1)];
-      if (!a.causal) wqbeg = a.cu[doc_of(a.cu, a.n_docs, wk0)];
-    }
   }
   qbeg = (qbeg / BMQ) * BMQ;
-  const bool wave_has_keys = wk0 < s;
   const int64_t ntile = qend > qbeg ? (qend - qbeg + BMQ - 1) / BMQ : 0;
   const int64_t nsteps = ntile * G;
 
   // Steps walk the query tiles from the last one down, the G heads of a tile back to back:
   // every causal workgroup ends at the last row, so workgroups running at the same time read
   // the same Q/dO tiles and share them through L2. Tiles travel to LDS by DMA.
-  auto tile_q0 = [&](int64_t step) { return qbeg + (ntile - 1 - step / G) * BMQ; };
-  auto issue_tile = [&](int64_t step, int b) {
-    const int hq = kvh * G + (int)(step % G);
-    const int64_t q0 = tile_q0(step);
+  auto issue_tile = [&](int tile, int hi, int b) {
+    const int hq = kvh * G + hi;
+    const int64_t q0 = qbeg + (int64_t)(ntile - 1 - tile) * BMQ;
     dma_tile<D, BMQ, kWaves * 64>(static_cast<const uint16_t*>(a.q) + (int64_t)hq * D, a.q_row, q0, s, sQ[b], tid);
     dma_tile<D, BMQ, kWaves * 64>(static_cast<const uint16_t*>(a.dout) + (int64_t)hq * D, a.q_row, q0, s, sG[b], tid);
     if (wave == 0) {
@@ -359,17 +339,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
     dvacc[db] = f32x16{};
   }
 
-  if (nsteps > 0) issue_tile(0, 0);
+  if (nsteps > 0) issue_tile(0, 0, 0);
   int buf = 0;
-  for (int64_t step = 0; step < nsteps; ++step, buf ^= 1) {
+  int cur_t = 0, cur_h = 0;  // tile and head of this step
+  for (int step = 0; step < (int)nsteps; ++step, buf ^= 1) {
     __syncthreads();  // tile `step` has landed and every wave is done with tile step-1
-    if (step + 1 < nsteps) issue_tile(step + 1, buf ^ 1);
-    const int64_t q0 = tile_q0(step);
+    const int nxt_h = cur_h + 1 == G ? 0 : cur_h + 1;
+    const int nxt_t = cur_h + 1 == G ? cur_t + 1 : cur_t;
+    if (step + 1 < (int)nsteps) issue_tile(nxt_t, nxt_h, buf ^ 1);
+    const int64_t q0 = qbeg + (int64_t)(ntile - 1 - cur_t) * BMQ;
+    cur_t = nxt_t;
+    cur_h = nxt_h;
 
-    const bool active = wave_has_keys && q0 < wqend && q0 + BMQ > wqbeg;
-    if (active) {
-      const bool full = (q0 + BMQ <= s) && (!a.causal || q0 >= wk1) &&
-                        (a.cu == nullptr || (q0 + BMQ <= w_hi_first && q0 >= w_lo_last));
+    // Every wave runs every step: a row outside this lane's [rlo, rhi) gets P = 0 from an
+    // unsigned compare, so the loop has no branch around its MFMAs (a branch there makes the
+    // compiler shuttle the accumulators between AGPRs and VGPRs every step).
+    {
+      const int32_t qrel0 = (int32_t)(q0 - rlo) + 4 * hf;
       // S = Q K^T and dP = dO V^T (row x key)
       f32x16 sacc[QB], pacc[QB];
 #pragma unroll
@@ -398,10 +384,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
           for (int e = 0; e < 4; ++e) {
             const int j = 4 * jj + e;
             float p = fast_exp2(__builtin_fmaf(sacc[qb][j], c, -L4[e] * kLog2e));
-            if (!full) {
-              const int64_t qr = q0 + qb * 32 + 8 * jj + 4 * hf + e;
-              if (qr < rlo || qr >= rhi) p = 0.f;
-            }
+            p = (uint32_t)(qrel0 + qb * 32 + 8 * jj + e) < width ? p : 0.f;
             sacc[qb][j] = p;
             pacc[qb][j] = p * (pacc[qb][j] - D4[e]);
           }
