@@ -17,6 +17,8 @@
 // Both kernels use v_mfma_f32_32x32x16_bf16. Operands whose contraction index is the
 // row-major tile's row (K for dQ, Q and dO for dK/dV) come from the transposing LDS read
 // ds_read_b64_tr_b16, so no tile is ever transposed in memory.
+#include <type_traits>
+
 #include "uly_device.h"
 #include "uly_internal.h"
 
@@ -25,6 +27,18 @@ namespace uly {
 namespace {
 
 constexpr int kWaves = 4;
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+#ifndef ULY_DKV_PF
+#define ULY_DKV_PF 3
+#endif
 
 // ---------------------------------------------------------------------------------------
 // delta[h, i] = sum_x dO[i, h, x] * O[i, h, x] (fp32). TPR threads per (row, head), 16 B each.
@@ -251,7 +265,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------------------
 // dK/dV: one workgroup = 128 keys (32 per wave) of one kv head; loops over the G q heads
-// and their query tiles of QB*32 rows. Each wave keeps its keys' K and V rows in VGPRs.
+// and their query tiles of QB*32 rows. Each wave keeps its keys' K and V rows in VGPRs,
+// which with the dK/dV accumulators leaves room for one wave per SIMD: latency is hidden
+// inside the wave by the schedule described at the step loop.
 template <int D, int QB>
 struct DkvCfg {
   static constexpr int BNK = kWaves * 32;
@@ -270,6 +286,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float sL[2][64];
   __shared__ __attribute__((aligned(16))) float sD[2][64];
   static_assert(BMQ <= 64, "one wave loads the per-row statistics");
+  static_assert(QB == 2, "the step schedule staggers exactly two 32-row halves");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5, gi = lane >> 4, li = lane & 15;
@@ -312,15 +329,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
     if (!a.causal) qbeg = a.cu[doc_of(a.cu, a.n_docs, n0)];
   }
   qbeg = (qbeg / BMQ) * BMQ;
-  const int64_t ntile = qend > qbeg ? (qend - qbeg + BMQ - 1) / BMQ : 0;
-  const int64_t nsteps = ntile * G;
+  const int ntile = qend > qbeg ? (int)((qend - qbeg + BMQ - 1) / BMQ) : 0;
+  const int nsteps = ntile * G;
 
   // Steps walk the query tiles from the last one down, the G heads of a tile back to back:
   // every causal workgroup ends at the last row, so workgroups running at the same time read
   // the same Q/dO tiles and share them through L2. Tiles travel to LDS by DMA.
+  auto tile_row0 = [&](int tile) { return qbeg + (int64_t)(ntile - 1 - tile) * BMQ; };
   auto issue_tile = [&](int tile, int hi, int b) {
     const int hq = kvh * G + hi;
-    const int64_t q0 = qbeg + (int64_t)(ntile - 1 - tile) * BMQ;
+    const int64_t q0 = tile_row0(tile);
     dma_tile<D, BMQ, kWaves * 64>(static_cast<const uint16_t*>(a.q) + (int64_t)hq * D, a.q_row, q0, s, sQ[b], tid);
     dma_tile<D, BMQ, kWaves * 64>(static_cast<const uint16_t*>(a.dout) + (int64_t)hq * D, a.q_row, q0, s, sG[b], tid);
     if (wave == 0) {
@@ -339,81 +357,112 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
     dvacc[db] = f32x16{};
   }
 
+  // Within a step the two 32-row halves of the tile are staggered so that the VALU work of
+  // one half (P, dS) runs while the MFMA pipe works on the other:
+  //   S/dP(h0) | S/dP(h1) + P/dS(h0) | dV/dK(h0) + P/dS(h1) | dV/dK(h1)
+  // Scheduling barriers keep that order and bound register pressure.
+  auto load_sdp = [&](int b, int qb, int t, bf16x8& qa, bf16x8& ga) {
+    qa = *reinterpret_cast<const bf16x8*>(&sQ[b][tile_off<D>(qb * 32 + l32, 16 * t + 8 * hf)]);
+    ga = *reinterpret_cast<const bf16x8*>(&sG[b][tile_off<D>(qb * 32 + l32, 16 * t + 8 * hf)]);
+  };
+  auto load_dkdv = [&](int b, int qb, int i, bf16x8& gt, bf16x8& qt) {
+    const int tt = i / DB, db = i % DB;
+    const int qr = qb * 32 + 16 * tt + 4 * hf + (li >> 2);
+    const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
+    const i16x4 g0 = lds_read_tr16(&sG[b][tile_off<D>(qr, col)]);
+    const i16x4 g1 = lds_read_tr16(&sG[b][tile_off<D>(qr + 8, col)]);
+    const i16x4 q0v = lds_read_tr16(&sQ[b][tile_off<D>(qr, col)]);
+    const i16x4 q1v = lds_read_tr16(&sQ[b][tile_off<D>(qr + 8, col)]);
+    gt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7));
+    qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0v, q1v, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // P and dS of rows 32qb + 8jj + 4hf + e (e < 4) for this lane's key; every wave runs every
+  // step and a row outside [rlo, rhi) gets P = 0 from an unsigned compare, so no branch
+  // surrounds the MFMAs (a branch there makes the compiler shuttle the accumulators
+  // between AGPRs and VGPRs every step).
+  auto soft4 = [&](int b, int32_t qrel0, int qb, int jj, const f32x16& si, const f32x16& pi, f32x4& pv, f32x4& dv) {
+    const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[b][qb * 32 + 8 * jj + 4 * hf]);
+    const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[b][qb * 32 + 8 * jj + 4 * hf]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float p = fast_exp2(__builtin_fmaf(si[4 * jj + e], c, -L4[e] * kLog2e));
+      p = (uint32_t)(qrel0 + qb * 32 + 8 * jj + e) < width ? p : 0.f;
+      pv[e] = p;
+      dv[e] = p * (pi[4 * jj + e] - D4[e]);
+    }
+  };
+  auto pack8 = [](const f32x4& x, const f32x4& y) {
+    u32x4 r;
+    r[0] = pack_bf16x2(x[0], x[1]);
+    r[1] = pack_bf16x2(x[2], x[3]);
+    r[2] = pack_bf16x2(y[0], y[1]);
+    r[3] = pack_bf16x2(y[2], y[3]);
+    return __builtin_bit_cast(bf16x8, r);
+  };
+  constexpr int NC = 2 * DB;  // dV/dK products per half (tt, db)
+
   if (nsteps > 0) issue_tile(0, 0, 0);
   int buf = 0;
   int cur_t = 0, cur_h = 0;  // tile and head of this step
-  for (int step = 0; step < (int)nsteps; ++step, buf ^= 1) {
+  for (int step = 0; step < nsteps; ++step, buf ^= 1) {
     __syncthreads();  // tile `step` has landed and every wave is done with tile step-1
     const int nxt_h = cur_h + 1 == G ? 0 : cur_h + 1;
     const int nxt_t = cur_h + 1 == G ? cur_t + 1 : cur_t;
-    if (step + 1 < (int)nsteps) issue_tile(nxt_t, nxt_h, buf ^ 1);
-    const int64_t q0 = qbeg + (int64_t)(ntile - 1 - cur_t) * BMQ;
+    if (step + 1 < nsteps) issue_tile(nxt_t, nxt_h, buf ^ 1);
+    const int32_t qrel0 = (int32_t)(tile_row0(cur_t) - rlo) + 4 * hf;
     cur_t = nxt_t;
     cur_h = nxt_h;
 
-    // Every wave runs every step: a row outside this lane's [rlo, rhi) gets P = 0 from an
-    // unsigned compare, so the loop has no branch around its MFMAs (a branch there makes the
-    // compiler shuttle the accumulators between AGPRs and VGPRs every step).
-    {
-      const int32_t qrel0 = (int32_t)(q0 - rlo) + 4 * hf;
-      // S = Q K^T and dP = dO V^T (row x key)
-      f32x16 sacc[QB], pacc[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        sacc[qb] = f32x16{};
-        pacc[qb] = f32x16{};
+    f32x16 sacc[2], pacc[2];
+    f32x4 pv[4], dv[4];
+    bf16x8 pf[2][2], dsf[2][2];
+    // The step is a fixed sequence of MFMA groups (two MFMAs each):
+    //   [0, DT)          S/dP of half 0, k-step t
+    //   [DT, 2DT)        S/dP of half 1, k-step t      + P/dS of half 0
+    //   [2DT, 2DT+NC)    dV/dK of half 0, product i    + P/dS of half 1
+    //   [2DT+NC, NGRP)   dV/dK of half 1, product i
+    // Operands are read from LDS ULY_DKV_PF groups ahead into a ring of registers.
+    constexpr int NGRP = 2 * DT + 2 * NC, PF = ULY_DKV_PF, R = PF + 1;
+    auto load_group = [&](int k, bf16x8& x, bf16x8& y) {
+      if (k < 2 * DT) load_sdp(buf, k / DT, k % DT, x, y);
+      else load_dkdv(buf, (k - 2 * DT) / NC, (k - 2 * DT) % NC, x, y);
+    };
+    bf16x8 ox[R], oy[R];
+    static_for<0, PF>([&](auto K) {
+      constexpr int k = decltype(K)::value;
+      load_group(k, ox[k % R], oy[k % R]);
+    });
+    static_for<0, NGRP>([&](auto K) {
+      constexpr int k = decltype(K)::value;
+      if constexpr (k + PF < NGRP) load_group(k + PF, ox[(k + PF) % R], oy[(k + PF) % R]);
+      const bf16x8& x = ox[k % R];
+      const bf16x8& y = oy[k % R];
+      if constexpr (k < 2 * DT) {
+        const int h = k / DT, t = k % DT;
+        sacc[h] = mfma32x32x16(x, kf[t], t == 0 ? f32x16{} : sacc[h]);
+        pacc[h] = mfma32x32x16(y, vf[t], t == 0 ? f32x16{} : pacc[h]);
+      } else {
+        const int h = (k - 2 * DT) / NC, i = (k - 2 * DT) % NC;
+        const int tt = i / DB, db = i % DB;
+        dvacc[db] = mfma32x32x16(x, pf[h][tt], dvacc[db]);
+        dkacc[db] = mfma32x32x16(y, dsf[h][tt], dkacc[db]);
       }
+      // P/dS of half sh spread over the groups of its window
+      const int sh = k < 2 * DT ? 0 : 1;
+      const int w0 = k < 2 * DT ? DT : 2 * DT, wn = k < 2 * DT ? DT : NC;
+      if (k >= w0 && k < w0 + wn) {
+        const int kk = k - w0;
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sQ[buf][tile_off<D>(qb * 32 + l32, 16 * t + 8 * hf)]);
-          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&sG[buf][tile_off<D>(qb * 32 + l32, 16 * t + 8 * hf)]);
-          sacc[qb] = mfma32x32x16(qa, kf[t], sacc[qb]);
-          pacc[qb] = mfma32x32x16(ga, vf[t], pacc[qb]);
-        }
-      // P and dS for rows 32qb + 8(j/4) + 4hf + j%4 of the tile and this lane's key
-      bf16x8 pf[QB][2], dsf[QB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[buf][qb * 32 + 8 * jj + 4 * hf]);
-          const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[buf][qb * 32 + 8 * jj + 4 * hf]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = 4 * jj + e;
-            float p = fast_exp2(__builtin_fmaf(sacc[qb][j], c, -L4[e] * kLog2e));
-            p = (uint32_t)(qrel0 + qb * 32 + 8 * jj + e) < width ? p : 0.f;
-            sacc[qb][j] = p;
-            pacc[qb][j] = p * (pacc[qb][j] - D4[e]);
+        for (int g = kk * 4 / wn; g < (kk + 1) * 4 / wn; ++g) {
+          soft4(buf, qrel0, sh, g, sacc[sh], pacc[sh], pv[g], dv[g]);
+          if (g & 1) {
+            pf[sh][g / 2] = pack8(pv[g - 1], pv[g]);
+            dsf[sh][g / 2] = pack8(dv[g - 1], dv[g]);
           }
         }
-        pf[qb][0] = to_bf16x8(sacc[qb], 0);
-        pf[qb][1] = to_bf16x8(sacc[qb], 1);
-        dsf[qb][0] = to_bf16x8(pacc[qb], 0);
-        dsf[qb][1] = to_bf16x8(pacc[qb], 1);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS (d x key)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int qr = qb * 32 + 16 * tt + 4 * hf + (li >> 2);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
-            const i16x4 g0 = lds_read_tr16(&sG[buf][tile_off<D>(qr, col)]);
-            const i16x4 g1 = lds_read_tr16(&sG[buf][tile_off<D>(qr + 8, col)]);
-            const i16x4 q0v = lds_read_tr16(&sQ[buf][tile_off<D>(qr, col)]);
-            const i16x4 q1v = lds_read_tr16(&sQ[buf][tile_off<D>(qr + 8, col)]);
-            const bf16x8 gt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7));
-            const bf16x8 qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0v, q1v, 0, 1, 2, 3, 4, 5, 6, 7));
-            dvacc[db] = mfma32x32x16(gt, pf[qb][tt], dvacc[db]);
-            dkacc[db] = mfma32x32x16(qt, dsf[qb][tt], dkacc[db]);
-          }
-        }
-    }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   }
 
   if (key < s) {
