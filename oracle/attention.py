@@ -6,8 +6,8 @@ What is computed, and where the pages fix it:
   * After the first all-to-all each GPU runs ordinary dense attention over the whole
     sequence for its heads ("Ulysses Sequence Parallelism: Training with
     Million-Token Contexts", section "how Ulysses works", step 4; tilnote.io
-    commentary, section on what Ulysses changes: "dense attention" on the full
-    sequence for a head piece).
+    commentary, section on what Ulysses changes: each GPU attends densely over the
+    full sequence for its slice of heads).
   * FlashAttention computes the same attention with O(n) memory (same page,
     section on the long-sequence challenge), so the exact softmax result is the
     reference; no tiling or online softmax appears here.

@@ -7,8 +7,8 @@ Source: "Ulysses Sequence Parallelism: Training with Million-Token Contexts"
 holds a local chunk of tokens with every head; the first all-to-all leaves each GPU
 with every sequence position for a subset of heads; the second returns the output
 to the sequence-sharded form. The tilnote.io commentary (section on what Ulysses
-changes) states the same swap: "short sequence piece + all heads" becomes "full
-sequence + head piece".
+changes) describes the same swap: each GPU goes from a short piece of the sequence
+with every head to the whole sequence with a slice of the heads.
 
 Readings taken where the pages are silent:
   * rank p holds tokens [p*s_l, (p+1)*s_l) (contiguous local chunks);
