@@ -16,7 +16,10 @@
 //
 // Both kernels use v_mfma_f32_32x32x16_bf16. Operands whose contraction index is the
 // row-major tile's row (K for dQ, Q and dO for dK/dV) come from the transposing LDS read
-// ds_read_b64_tr_b16, so no tile is ever transposed in memory.
+// ds_read_b64_tr_b16, so no tile is ever transposed in memory. Both stage their streamed
+// tiles by LDS DMA and hide latency inside one wave per SIMD with a fixed, software-
+// pipelined sequence of MFMA groups (operands read a few groups ahead, the VALU work of
+// one half-tile under the MFMAs of the other).
 #include <type_traits>
 
 #include "uly_device.h"
@@ -36,6 +39,9 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<B + 1, E>(f);
   }
 }
+#ifndef ULY_DQ_PF
+#define ULY_DQ_PF 3
+#endif
 #ifndef ULY_DKV_PF
 #define ULY_DKV_PF 3
 #endif
@@ -80,7 +86,6 @@ struct DqCfg {
   static constexpr int BM = kWaves * RB * 32;
   static constexpr int BN = KB * 32;
   static constexpr int DT = D / 16, DB = D / 32;
-  static constexpr int KVEC = BN * D / 8 / (kWaves * 64);
 };
 
 template <int D, int RB, int KB>
@@ -150,114 +155,111 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) width[rb] = (uint32_t)(hi[rb] - lo[rb]);
 
-  u32x4 pk[C::KVEC], pv[C::KVEC];
-  auto load_tile = [&](int64_t k0) {
+  // K/V tiles travel to LDS by DMA (double buffered, XOR-swizzled rows). Within a tile
+  // the two 32-key halves are staggered like the dK/dV kernel's query halves:
+  //   S/dP(h0) | S/dP(h1) + dS(h0) | dQ(h0) + dS(h1) | dQ(h1)
+  // with LDS operands read PF groups ahead and the next tile's DMA issued mid-tile.
+  static_assert(RB == 1 && KB == 2, "the tile schedule staggers exactly two 32-key halves");
+  auto issue_kv = [&](int64_t k0, int b) {
+    dma_tile<D, BN, kWaves * 64>(K, a.kv_row, k0, s, sK[b], tid);
+    dma_tile<D, BN, kWaves * 64>(V, a.kv_row, k0, s, sV[b], tid);
+  };
+  auto load_sdp = [&](int b, int kb, int t, bf16x8& kx, bf16x8& vx) {
+    kx = *reinterpret_cast<const bf16x8*>(&sK[b][tile_off<D>(kb * 32 + l32, 16 * t + 8 * hf)]);
+    vx = *reinterpret_cast<const bf16x8*>(&sV[b][tile_off<D>(kb * 32 + l32, 16 * t + 8 * hf)]);
+  };
+  // K^T operands of dQ^T product i = (tt, db) of half kb; the second register is unused
+  auto load_dq = [&](int b, int kb, int i, bf16x8& kt, bf16x8& unused) {
+    const int tt = i / DB, db = i % DB;
+    const int kr = kb * 32 + 16 * tt + 4 * hf + (li >> 2);
+    const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
+    const i16x4 k0v = lds_read_tr16(&sK[b][tile_off<D>(kr, col)]);
+    const i16x4 k1v = lds_read_tr16(&sK[b][tile_off<D>(kr + 8, col)]);
+    kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0v, k1v, 0, 1, 2, 3, 4, 5, 6, 7));
+    (void)unused;
+  };
+  // dS of keys kb*32 + 8jj + 4hf + e (e < 4) for this lane's row; keys outside the row's
+  // range get P = 0 from an unsigned compare, so no branch surrounds the MFMAs.
+  auto soft4 = [&](int32_t krel0, int kb, int jj, const f32x16& si, const f32x16& pi, f32x4& dv) {
 #pragma unroll
-    for (int i = 0; i < C::KVEC; ++i) {
-      const int vi = tid + i * kWaves * 64;
-      const int r = vi / (D / 8), c8 = vi % (D / 8);
-      const int64_t key = k0 + r;
-      pk[i] = u32x4{0, 0, 0, 0};
-      pv[i] = u32x4{0, 0, 0, 0};
-      if (key < s) {
-        pk[i] = *reinterpret_cast<const u32x4*>(K + key * a.kv_row + 8 * c8);
-        pv[i] = *reinterpret_cast<const u32x4*>(V + key * a.kv_row + 8 * c8);
-      }
+    for (int e = 0; e < 4; ++e) {
+      float p = fast_exp2(__builtin_fmaf(si[4 * jj + e], c, -lse2[0]));
+      p = (uint32_t)(krel0 + kb * 32 + 8 * jj + e) < width[0] ? p : 0.f;
+      dv[e] = p * (pi[4 * jj + e] - dl[0]);
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::KVEC; ++i) {
-      const int vi = tid + i * kWaves * 64;
-      const int r = vi / (D / 8), c8 = vi % (D / 8);
-      *reinterpret_cast<u32x4*>(&sK[buf][tile_off<D>(r, 8 * c8)]) = pk[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][tile_off<D>(r, 8 * c8)]) = pv[i];
-    }
+  auto pack8 = [](const f32x4& x, const f32x4& y) {
+    u32x4 r;
+    r[0] = pack_bf16x2(x[0], x[1]);
+    r[1] = pack_bf16x2(x[2], x[3]);
+    r[2] = pack_bf16x2(y[0], y[1]);
+    r[3] = pack_bf16x2(y[2], y[3]);
+    return __builtin_bit_cast(bf16x8, r);
   };
 
-  f32x16 dqacc[RB][DB];
+  f32x16 dqacc[DB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) dqacc[rb][db] = f32x16{};
+  for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
 
-  if (kbeg < kend) load_tile(kbeg);
+  constexpr int NC = 2 * DB;  // dQ products per half (tt, db)
+  constexpr int NGRP = 2 * DT + 2 * NC, PF = ULY_DQ_PF, R = PF + 1;
+  if (kbeg < kend) issue_kv(kbeg, 0);
   int buf = 0;
   for (int64_t k0 = kbeg; k0 < kend; k0 += BN, buf ^= 1) {
-    store_tile(buf);
-    __syncthreads();
-    if (k0 + BN < kend) load_tile(k0 + BN);
-
-    // Every wave runs every tile; keys outside a row's range get P = 0 from an unsigned
-    // compare, so no branch surrounds the MFMAs.
-    {
-      f32x16 sacc[KB][RB], pacc[KB][RB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          sacc[kb][rb] = f32x16{};
-          pacc[kb][rb] = f32x16{};
-        }
-      // S^T = K Q^T and dP^T = V dO^T (key x row)
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][tile_off<D>(kb * 32 + l32, 16 * t + 8 * hf)]);
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[buf][tile_off<D>(kb * 32 + l32, 16 * t + 8 * hf)]);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            sacc[kb][rb] = mfma32x32x16(kf, qf[rb][t], sacc[kb][rb]);
-            pacc[kb][rb] = mfma32x32x16(vf, gf[rb][t], pacc[kb][rb]);
-          }
-        }
-      // dS^T = P^T o (dP^T - delta)
-      bf16x8 dsf[RB][KB][2];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int32_t krel0 = (int32_t)(k0 - lo[rb]) + kb * 32 + 4 * hf;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            float p = fast_exp2(__builtin_fmaf(sacc[kb][rb][j], c, -lse2[rb]));
-            p = (uint32_t)(krel0 + 8 * (j / 4) + (j % 4)) < width[rb] ? p : 0.f;
-            sacc[kb][rb][j] = p * (pacc[kb][rb][j] - dl[rb]);
-          }
-          dsf[rb][kb][0] = to_bf16x8(sacc[kb][rb], 0);
-          dsf[rb][kb][1] = to_bf16x8(sacc[kb][rb], 1);
-        }
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int kr = kb * 32 + 16 * tt + 4 * hf + (li >> 2);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
-            const i16x4 k0v = lds_read_tr16(&sK[buf][tile_off<D>(kr, col)]);
-            const i16x4 k1v = lds_read_tr16(&sK[buf][tile_off<D>(kr + 8, col)]);
-            const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0v, k1v, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) dqacc[rb][db] = mfma32x32x16(kt, dsf[rb][kb][tt], dqacc[rb][db]);
-          }
-        }
-    }
+    __syncthreads();  // tile k0 has landed and every wave is done with the previous tile
+    const int32_t krel0 = (int32_t)(k0 - lo[0]) + 4 * hf;
+    f32x16 sacc[2], pacc[2];
+    f32x4 dv[4];
+    bf16x8 dsf[2][2];
+    auto load_group = [&](int k, bf16x8& x, bf16x8& y) {
+      if (k < 2 * DT) load_sdp(buf, k / DT, k % DT, x, y);
+      else load_dq(buf, (k - 2 * DT) / NC, (k - 2 * DT) % NC, x, y);
+    };
+    bf16x8 ox[R], oy[R];
+    static_for<0, PF>([&](auto K) {
+      constexpr int k = decltype(K)::value;
+      load_group(k, ox[k % R], oy[k % R]);
+    });
+    static_for<0, NGRP>([&](auto K) {
+      constexpr int k = decltype(K)::value;
+      if constexpr (k == 2 * DT + 2) {
+        if (k0 + BN < kend) issue_kv(k0 + BN, buf ^ 1);
+      }
+      if constexpr (k + PF < NGRP) load_group(k + PF, ox[(k + PF) % R], oy[(k + PF) % R]);
+      if constexpr (k < 2 * DT) {
+        constexpr int hh = k / DT, t = k % DT;
+        sacc[hh] = mfma32x32x16(ox[k % R], qf[0][t], t == 0 ? f32x16{} : sacc[hh]);
+        pacc[hh] = mfma32x32x16(oy[k % R], gf[0][t], t == 0 ? f32x16{} : pacc[hh]);
+      } else {
+        constexpr int hh = (k - 2 * DT) / NC, i = (k - 2 * DT) % NC;
+        constexpr int tt = i / DB, db = i % DB;
+        dqacc[db] = mfma32x32x16(ox[k % R], dsf[hh][tt], dqacc[db]);
+      }
+      // dS of half sh spread over the groups of its window
+      constexpr int sh = k < 2 * DT ? 0 : 1;
+      constexpr int w0 = k < 2 * DT ? DT : 2 * DT, wn = k < 2 * DT ? DT : NC;
+      if constexpr (k >= w0 && k < w0 + wn) {
+        constexpr int kk = k - w0;
+        static_for<kk * 4 / wn, (kk + 1) * 4 / wn>([&](auto Gc) {
+          constexpr int g = decltype(Gc)::value;
+          soft4(krel0, sh, g, sacc[sh], pacc[sh], dv[g]);
+          if constexpr (g & 1) dsf[sh][g / 2] = pack8(dv[g - 1], dv[g]);
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   }
 
+  const int rb = 0;
   uint16_t* dQ = static_cast<uint16_t*>(a.out) + (int64_t)h * D;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    if (row[rb] >= s) continue;
+  if (row[rb] < s) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         u32x2 w;
-        w[0] = pack_bf16x2(dqacc[rb][db][4 * jj + 0] * a.scale, dqacc[rb][db][4 * jj + 1] * a.scale);
-        w[1] = pack_bf16x2(dqacc[rb][db][4 * jj + 2] * a.scale, dqacc[rb][db][4 * jj + 3] * a.scale);
+        w[0] = pack_bf16x2(dqacc[db][4 * jj + 0] * a.scale, dqacc[db][4 * jj + 1] * a.scale);
+        w[1] = pack_bf16x2(dqacc[db][4 * jj + 2] * a.scale, dqacc[db][4 * jj + 3] * a.scale);
         *reinterpret_cast<u32x2*>(dQ + row[rb] * a.q_row + db * 32 + 8 * jj + 4 * hf) = w;
       }
   }
@@ -408,7 +410,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
     __syncthreads();  // tile `step` has landed and every wave is done with tile step-1
     const int nxt_h = cur_h + 1 == G ? 0 : cur_h + 1;
     const int nxt_t = cur_h + 1 == G ? cur_t + 1 : cur_t;
-    if (step + 1 < nsteps) issue_tile(nxt_t, nxt_h, buf ^ 1);
     const int32_t qrel0 = (int32_t)(tile_row0(cur_t) - rlo) + 4 * hf;
     cur_t = nxt_t;
     cur_h = nxt_h;
@@ -434,6 +435,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
     });
     static_for<0, NGRP>([&](auto K) {
       constexpr int k = decltype(K)::value;
+      // The next tile's DMA is issued a few groups into the dV/dK phase: issued at the top of
+      // the step it slowed the S/dP operand reads that follow the barrier (measured).
+      if constexpr (k == 2 * DT + 4) {
+        if (step + 1 < nsteps) issue_tile(nxt_t, nxt_h, buf ^ 1);
+      }
       if constexpr (k + PF < NGRP) load_group(k + PF, ox[(k + PF) % R], oy[(k + PF) % R]);
       const bf16x8& x = ox[k % R];
       const bf16x8& y = oy[k % R];
