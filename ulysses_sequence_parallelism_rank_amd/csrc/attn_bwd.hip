@@ -39,9 +39,6 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<B + 1, E>(f);
   }
 }
-#ifndef ULY_DQ_PF
-#define ULY_DQ_PF 3
-#endif
 #ifndef ULY_DKV_PF
 #define ULY_DKV_PF 3
 #endif
@@ -89,7 +86,7 @@ struct DqCfg {
 };
 
 template <int D, int RB, int KB>
-__global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a) {
   using C = DqCfg<D, RB, KB>;
   constexpr int BM = C::BM, BN = C::BN, DT = C::DT, DB = C::DB;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
@@ -155,11 +152,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) width[rb] = (uint32_t)(hi[rb] - lo[rb]);
 
-  // K/V tiles travel to LDS by DMA (double buffered, XOR-swizzled rows). Within a tile
-  // the two 32-key halves are staggered like the dK/dV kernel's query halves:
-  //   S/dP(h0) | S/dP(h1) + dS(h0) | dQ(h0) + dS(h1) | dQ(h1)
-  // with LDS operands read PF groups ahead and the next tile's DMA issued mid-tile.
-  static_assert(RB == 1 && KB == 2, "the tile schedule staggers exactly two 32-key halves");
+  // K/V tiles travel to LDS by DMA (double buffered, XOR-swizzled rows). Two workgroups share
+  // a CU (at most 256 VGPRs each), so one wave's VALU work (dS) runs while the other wave on
+  // the SIMD issues MFMAs; within a wave the two 32-key halves of a tile run one after the
+  // other: S/dP, dS, dQ.
+  static_assert(RB == 1 && KB == 2, "the tile is two 32-key halves of one 32-row wave tile");
   auto issue_kv = [&](int64_t k0, int b) {
     dma_tile<D, BN, kWaves * 64>(K, a.kv_row, k0, s, sK[b], tid);
     dma_tile<D, BN, kWaves * 64>(V, a.kv_row, k0, s, sV[b], tid);
@@ -202,52 +199,39 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dq_kernel(AttnArgs a) {
   for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
 
   constexpr int NC = 2 * DB;  // dQ products per half (tt, db)
-  constexpr int NGRP = 2 * DT + 2 * NC, PF = ULY_DQ_PF, R = PF + 1;
   if (kbeg < kend) issue_kv(kbeg, 0);
   int buf = 0;
   for (int64_t k0 = kbeg; k0 < kend; k0 += BN, buf ^= 1) {
+    wait_dma();
     __syncthreads();  // tile k0 has landed and every wave is done with the previous tile
     const int32_t krel0 = (int32_t)(k0 - lo[0]) + 4 * hf;
-    f32x16 sacc[2], pacc[2];
-    f32x4 dv[4];
-    bf16x8 dsf[2][2];
-    auto load_group = [&](int k, bf16x8& x, bf16x8& y) {
-      if (k < 2 * DT) load_sdp(buf, k / DT, k % DT, x, y);
-      else load_dq(buf, (k - 2 * DT) / NC, (k - 2 * DT) % NC, x, y);
-    };
-    bf16x8 ox[R], oy[R];
-    static_for<0, PF>([&](auto K) {
-      constexpr int k = decltype(K)::value;
-      load_group(k, ox[k % R], oy[k % R]);
-    });
-    static_for<0, NGRP>([&](auto K) {
-      constexpr int k = decltype(K)::value;
-      if constexpr (k == 2 * DT + 2) {
-        if (k0 + BN < kend) issue_kv(k0 + BN, buf ^ 1);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        bf16x8 kx, vx;
+        load_sdp(buf, hh, t, kx, vx);
+        sacc = mfma32x32x16(kx, qf[0][t], t == 0 ? f32x16{} : sacc);
+        pacc = mfma32x32x16(vx, gf[0][t], t == 0 ? f32x16{} : pacc);
       }
-      if constexpr (k + PF < NGRP) load_group(k + PF, ox[(k + PF) % R], oy[(k + PF) % R]);
-      if constexpr (k < 2 * DT) {
-        constexpr int hh = k / DT, t = k % DT;
-        sacc[hh] = mfma32x32x16(ox[k % R], qf[0][t], t == 0 ? f32x16{} : sacc[hh]);
-        pacc[hh] = mfma32x32x16(oy[k % R], gf[0][t], t == 0 ? f32x16{} : pacc[hh]);
-      } else {
-        constexpr int hh = (k - 2 * DT) / NC, i = (k - 2 * DT) % NC;
-        constexpr int tt = i / DB, db = i % DB;
-        dqacc[db] = mfma32x32x16(ox[k % R], dsf[hh][tt], dqacc[db]);
+      f32x4 dv[4];
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        soft4(krel0, hh, g, sacc, pacc, dv[g]);
+        if (g & 1) dsf[g / 2] = pack8(dv[g - 1], dv[g]);
       }
-      // dS of half sh spread over the groups of its window
-      constexpr int sh = k < 2 * DT ? 0 : 1;
-      constexpr int w0 = k < 2 * DT ? DT : 2 * DT, wn = k < 2 * DT ? DT : NC;
-      if constexpr (k >= w0 && k < w0 + wn) {
-        constexpr int kk = k - w0;
-        static_for<kk * 4 / wn, (kk + 1) * 4 / wn>([&](auto Gc) {
-          constexpr int g = decltype(Gc)::value;
-          soft4(krel0, sh, g, sacc[sh], pacc[sh], dv[g]);
-          if constexpr (g & 1) dsf[sh][g / 2] = pack8(dv[g - 1], dv[g]);
-        });
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        bf16x8 kt, unused;
+        load_dq(buf, hh, i, kt, unused);
+        dqacc[i % DB] = mfma32x32x16(kt, dsf[i / DB], dqacc[i % DB]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    });
+    }
+    // the next tile's DMA after this tile's last LDS read: the wait the compiler places
+    // before LDS reads that follow a DMA then falls on the next barrier
+    if (k0 + BN < kend) issue_kv(k0 + BN, buf ^ 1);
   }
 
   const int rb = 0;
@@ -407,6 +391,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
   int buf = 0;
   int cur_t = 0, cur_h = 0;  // tile and head of this step
   for (int step = 0; step < nsteps; ++step, buf ^= 1) {
+    wait_dma();
     __syncthreads();  // tile `step` has landed and every wave is done with tile step-1
     const int nxt_h = cur_h + 1 == G ? 0 : cur_h + 1;
     const int nxt_t = cur_h + 1 == G ? cur_t + 1 : cur_t;

@@ -123,6 +123,12 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t stride, in
   }
 }
 
+// Wait until this wave's LDS DMA (global_load_lds) has landed: s_waitcnt vmcnt(0), the other
+// counters left alone (gfx9 encoding: expcnt 7 in bits 6:4, lgkmcnt 15 in bits 11:8). A
+// workgroup barrier does not order another wave's DMA writes before this wave's LDS reads, so
+// every wave waits for its own DMA before the barrier that publishes a DMA'd tile.
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
