@@ -17,9 +17,8 @@
 // Both kernels use v_mfma_f32_32x32x16_bf16. Operands whose contraction index is the
 // row-major tile's row (K for dQ, Q and dO for dK/dV) come from the transposing LDS read
 // ds_read_b64_tr_b16, so no tile is ever transposed in memory. Both stage their streamed
-// tiles by LDS DMA and hide latency inside one wave per SIMD with a fixed, software-
-// pipelined sequence of MFMA groups (operands read a few groups ahead, the VALU work of
-// one half-tile under the MFMAs of the other).
+// tiles by LDS DMA and run two waves per SIMD, so one wave's VALU work (exp, dS) overlaps
+// the other's MFMAs.
 #include <type_traits>
 
 #include "uly_device.h"
@@ -30,18 +29,6 @@ namespace uly {
 namespace {
 
 constexpr int kWaves = 4;
-
-// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-#ifndef ULY_DKV_PF
-#define ULY_DKV_PF 3
-#endif
 
 // ---------------------------------------------------------------------------------------
 // delta[h, i] = sum_x dO[i, h, x] * O[i, h, x] (fp32). TPR threads per (row, head), 16 B each.
@@ -250,61 +237,70 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// dK/dV: one workgroup = 128 keys (32 per wave) of one kv head; loops over the G q heads
-// and their query tiles of QB*32 rows. Each wave keeps its keys' K and V rows in VGPRs,
-// which with the dK/dV accumulators leaves room for one wave per SIMD: latency is hidden
-// inside the wave by the schedule described at the step loop.
-template <int D, int QB>
-struct DkvCfg {
-  static constexpr int BNK = kWaves * 32;
-  static constexpr int BMQ = QB * 32;
+// dK/dV with split roles: one workgroup = 128 keys of one kv head and 8 waves, two per SIMD.
+// Waves 0-3 ("P waves", keys 32w..32w+31) compute S = Q K^T, P = exp(S - LSE) (masked) and
+// dV^T += dO^T P; waves 4-7 ("dS waves", the same keys) compute dP = dO V^T, read P from LDS,
+// form dS = P (dP - delta) and dK^T += Q^T dS. Each wave holds one accumulator set (dV or
+// dK) and one of K/V, so two waves fit a SIMD and one's VALU work overlaps the other's MFMAs.
+// Per 64-row query tile: S | dP, barrier, dV | dS + dK. P crosses in fp32 through LDS, in the
+// MFMA accumulator layout of the lane that made it (each dS lane reads its own twin's slot).
+// Query tiles (Q, dO, LSE, delta) arrive by DMA into double buffers that are distinct LDS
+// objects, with steps unrolled by two so buffer choices are compile-time: the compiler then
+// knows the DMA into one buffer does not alias reads of the other.
+template <int D>
+struct DkvSplitCfg {
+  static constexpr int BNK = 128, BMQ = 64, NW = 8;
   static constexpr int DT = D / 16, DB = D / 32;
-  static constexpr int QVEC = BMQ * D / 8 / (kWaves * 64);
 };
 
-template <int D, int QB>
-__global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
-  using C = DkvCfg<D, QB>;
+template <int D>
+__global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
+  using C = DkvSplitCfg<D>;
   constexpr int BNK = C::BNK, BMQ = C::BMQ, DT = C::DT, DB = C::DB;
-  static_assert(C::QVEC >= 1, "query tile too small for the thread count");
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BMQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[2][BMQ * D];
-  __shared__ __attribute__((aligned(16))) float sL[2][64];
-  __shared__ __attribute__((aligned(16))) float sD[2][64];
-  static_assert(BMQ <= 64, "one wave loads the per-row statistics");
-  static_assert(QB == 2, "the step schedule staggers exactly two 32-row halves");
+  // per buffer: one object for the Q and dO tiles, one for the LSE and delta rows (few DMA
+  // target objects keep the compiler's per-object tracking of LDS DMA exact)
+  __shared__ __attribute__((aligned(16))) uint16_t sT0[2 * BMQ * D], sT1[2 * BMQ * D];
+  __shared__ __attribute__((aligned(16))) float sS0[2 * BMQ], sS1[2 * BMQ];
+  // P of key group g, half qb: 64 lanes x 16 floats, 16-byte chunks XOR-swizzled by lane/4
+  __shared__ __attribute__((aligned(16))) float sP[4][2][64 * 16];
+  struct Buf {
+    uint16_t* q;
+    uint16_t* g;
+    float* l;
+    float* d;
+  };
+  auto bufs = [&](auto B) -> Buf {
+    if constexpr (decltype(B)::value == 0) return {sT0, sT0 + BMQ * D, sS0, sS0 + BMQ};
+    else return {sT1, sT1 + BMQ * D, sS1, sS1 + BMQ};
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int role = wave >> 2, kg = wave & 3;  // role 0: P and dV; role 1: dS and dK
   const int l32 = lane & 31, hf = lane >> 5, gi = lane >> 4, li = lane & 15;
   const int64_t s = a.s;
   const int kvh = blockIdx.x % a.n_kv;
   const int64_t n0 = (int64_t)(blockIdx.x / a.n_kv) * BNK;  // earliest keys (most rows) first
   const int G = a.G;
   const float c = a.scale * kLog2e;
-  const uint16_t* K = static_cast<const uint16_t*>(a.k) + (int64_t)kvh * D;
-  const uint16_t* V = static_cast<const uint16_t*>(a.v) + (int64_t)kvh * D;
 
-  // this lane's key and the rows that may see it: [rlo, rhi)
-  const int64_t key = n0 + wave * 32 + l32;
-  int64_t rlo = 0, rhi = s;
+  // this lane's key, the rows that may see it [rlo, rhi), and its K (role 0) or V row
+  const int64_t key = n0 + kg * 32 + l32;
+  int32_t rlo = 0, rhi = (int32_t)s;  // positions fit in int32 (the boundary checks s)
   if (a.cu != nullptr && key < s) {
     const int dk = doc_of(a.cu, a.n_docs, key);
     rlo = a.cu[dk];
     rhi = a.cu[dk + 1];
   }
-  if (a.causal) rlo = key;
+  if (a.causal) rlo = (int32_t)key;
   if (key >= s) rhi = rlo;  // padding key: seen by no row
   const uint32_t width = (uint32_t)(rhi - rlo);  // row r is seen iff (uint32)(r - rlo) < width
-  bf16x8 kf[DT], vf[DT];
+  const uint16_t* KV = static_cast<const uint16_t*>(role == 0 ? a.k : a.v) + (int64_t)kvh * D;
+  bf16x8 kv[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
-    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-    if (key < s) {
-      x = *reinterpret_cast<const u32x4*>(K + key * a.kv_row + 16 * t + 8 * hf);
-      y = *reinterpret_cast<const u32x4*>(V + key * a.kv_row + 16 * t + 8 * hf);
-    }
-    kf[t] = __builtin_bit_cast(bf16x8, x);
-    vf[t] = __builtin_bit_cast(bf16x8, y);
+    u32x4 x = {0, 0, 0, 0};
+    if (key < s) x = *reinterpret_cast<const u32x4*>(KV + key * a.kv_row + 16 * t + 8 * hf);
+    kv[t] = __builtin_bit_cast(bf16x8, x);
   }
 
   // row range of the workgroup: rows that may see any of its keys
@@ -318,158 +314,147 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_dkdv_kernel(AttnArgs a) {
   const int ntile = qend > qbeg ? (int)((qend - qbeg + BMQ - 1) / BMQ) : 0;
   const int nsteps = ntile * G;
 
-  // Steps walk the query tiles from the last one down, the G heads of a tile back to back:
-  // every causal workgroup ends at the last row, so workgroups running at the same time read
-  // the same Q/dO tiles and share them through L2. Tiles travel to LDS by DMA.
+  // Steps walk the query tiles from the last one down, the G heads of a tile back to back.
   auto tile_row0 = [&](int tile) { return qbeg + (int64_t)(ntile - 1 - tile) * BMQ; };
-  auto issue_tile = [&](int tile, int hi, int b) {
+  // Only the dS waves issue DMA: the P waves then never hold outstanding DMA, so nothing
+  // makes them wait for it before their LDS writes of P.
+  auto issue_tile = [&](int tile, int hi, const Buf& b) {
     const int hq = kvh * G + hi;
     const int64_t q0 = tile_row0(tile);
-    dma_tile<D, BMQ, kWaves * 64>(static_cast<const uint16_t*>(a.q) + (int64_t)hq * D, a.q_row, q0, s, sQ[b], tid);
-    dma_tile<D, BMQ, kWaves * 64>(static_cast<const uint16_t*>(a.dout) + (int64_t)hq * D, a.q_row, q0, s, sG[b], tid);
-    if (wave == 0) {
-      // one fp32 per lane: lane i lands at sL[b][i] / sD[b][i]
-      int64_t qr = q0 + (lane < BMQ ? lane : BMQ - 1);
-      qr = qr < s ? qr : s - 1;
-      __builtin_amdgcn_global_load_lds(a.lse_in + (int64_t)hq * a.lse_row + qr, &sL[b][0], 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(a.delta + (int64_t)hq * a.lse_row + qr, &sD[b][0], 4, 0, 0);
-    }
+    const int t2 = tid - 256;
+    dma_tile<D, BMQ, 256>(static_cast<const uint16_t*>(a.q) + (int64_t)hq * D, a.q_row, q0, s, b.q, t2);
+    dma_tile<D, BMQ, 256>(static_cast<const uint16_t*>(a.dout) + (int64_t)hq * D, a.q_row, q0, s, b.g, t2);
+    // one fp32 per lane: lane i lands at b.l[i] (wave 4) or b.d[i] (wave 5)
+    int64_t qr = q0 + (lane < BMQ ? lane : BMQ - 1);
+    qr = qr < s ? qr : s - 1;
+    if (wave == 4) __builtin_amdgcn_global_load_lds(a.lse_in + (int64_t)hq * a.lse_row + qr, b.l, 4, 0, 0);
+    if (wave == 5) __builtin_amdgcn_global_load_lds(a.delta + (int64_t)hq * a.lse_row + qr, b.d, 4, 0, 0);
   };
-
-  f32x16 dkacc[DB], dvacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dkacc[db] = f32x16{};
-    dvacc[db] = f32x16{};
-  }
-
-  // Within a step the two 32-row halves of the tile are staggered so that the VALU work of
-  // one half (P, dS) runs while the MFMA pipe works on the other:
-  //   S/dP(h0) | S/dP(h1) + P/dS(h0) | dV/dK(h0) + P/dS(h1) | dV/dK(h1)
-  // Scheduling barriers keep that order and bound register pressure.
-  auto load_sdp = [&](int b, int qb, int t, bf16x8& qa, bf16x8& ga) {
-    qa = *reinterpret_cast<const bf16x8*>(&sQ[b][tile_off<D>(qb * 32 + l32, 16 * t + 8 * hf)]);
-    ga = *reinterpret_cast<const bf16x8*>(&sG[b][tile_off<D>(qb * 32 + l32, 16 * t + 8 * hf)]);
+  auto p_off = [&](int qb, int chunk) {  // float offset of this lane's 16-byte chunk of P
+    return ((kg * 2 + qb) * 64 + lane) * 16 + ((chunk ^ ((lane >> 2) & 3)) << 2);
   };
-  auto load_dkdv = [&](int b, int qb, int i, bf16x8& gt, bf16x8& qt) {
-    const int tt = i / DB, db = i % DB;
-    const int qr = qb * 32 + 16 * tt + 4 * hf + (li >> 2);
-    const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
-    const i16x4 g0 = lds_read_tr16(&sG[b][tile_off<D>(qr, col)]);
-    const i16x4 g1 = lds_read_tr16(&sG[b][tile_off<D>(qr + 8, col)]);
-    const i16x4 q0v = lds_read_tr16(&sQ[b][tile_off<D>(qr, col)]);
-    const i16x4 q1v = lds_read_tr16(&sQ[b][tile_off<D>(qr + 8, col)]);
-    gt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7));
-    qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0v, q1v, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  // P and dS of rows 32qb + 8jj + 4hf + e (e < 4) for this lane's key; every wave runs every
-  // step and a row outside [rlo, rhi) gets P = 0 from an unsigned compare, so no branch
-  // surrounds the MFMAs (a branch there makes the compiler shuttle the accumulators
-  // between AGPRs and VGPRs every step).
-  auto soft4 = [&](int b, int32_t qrel0, int qb, int jj, const f32x16& si, const f32x16& pi, f32x4& pv, f32x4& dv) {
-    const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[b][qb * 32 + 8 * jj + 4 * hf]);
-    const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[b][qb * 32 + 8 * jj + 4 * hf]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float p = fast_exp2(__builtin_fmaf(si[4 * jj + e], c, -L4[e] * kLog2e));
-      p = (uint32_t)(qrel0 + qb * 32 + 8 * jj + e) < width ? p : 0.f;
-      pv[e] = p;
-      dv[e] = p * (pi[4 * jj + e] - D4[e]);
-    }
-  };
-  auto pack8 = [](const f32x4& x, const f32x4& y) {
+  auto pack8 = [](const f32x16& x, int h) {
     u32x4 r;
-    r[0] = pack_bf16x2(x[0], x[1]);
-    r[1] = pack_bf16x2(x[2], x[3]);
-    r[2] = pack_bf16x2(y[0], y[1]);
-    r[3] = pack_bf16x2(y[2], y[3]);
+    r[0] = pack_bf16x2(x[8 * h + 0], x[8 * h + 1]);
+    r[1] = pack_bf16x2(x[8 * h + 2], x[8 * h + 3]);
+    r[2] = pack_bf16x2(x[8 * h + 4], x[8 * h + 5]);
+    r[3] = pack_bf16x2(x[8 * h + 6], x[8 * h + 7]);
     return __builtin_bit_cast(bf16x8, r);
   };
-  constexpr int NC = 2 * DB;  // dV/dK products per half (tt, db)
+  // transposed operand (dO^T for role 0, Q^T for role 1) of product (qb, tt, db)
+  auto load_tr = [&](const uint16_t* tile, int qb, int tt, int db) {
+    const int qr = qb * 32 + 16 * tt + 4 * hf + (li >> 2);
+    const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
+    const i16x4 x0 = lds_read_tr16(&tile[tile_off<D>(qr, col)]);
+    const i16x4 x1 = lds_read_tr16(&tile[tile_off<D>(qr + 8, col)]);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
-  if (nsteps > 0) issue_tile(0, 0, 0);
-  int buf = 0;
+  f32x16 acc[DB];  // dV^T (role 0) or dK^T (role 1), d x key
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
   int cur_t = 0, cur_h = 0;  // tile and head of this step
-  for (int step = 0; step < nsteps; ++step, buf ^= 1) {
+  auto run_step = [&](auto B, int step) {
+    const Buf buf = bufs(B), nbuf = bufs(std::integral_constant<int, 1 - decltype(B)::value>{});
     wait_dma();
-    __syncthreads();  // tile `step` has landed and every wave is done with tile step-1
+    __syncthreads();  // tile `step` has landed; every wave is done with tile step-1 and with P
     const int nxt_h = cur_h + 1 == G ? 0 : cur_h + 1;
     const int nxt_t = cur_h + 1 == G ? cur_t + 1 : cur_t;
-    const int32_t qrel0 = (int32_t)(tile_row0(cur_t) - rlo) + 4 * hf;
+    if (role == 1 && step + 1 < nsteps) issue_tile(nxt_t, nxt_h, nbuf);
+    const int32_t qrel0 = (int32_t)tile_row0(cur_t) - rlo + 4 * hf;
     cur_t = nxt_t;
     cur_h = nxt_h;
-
-    f32x16 sacc[2], pacc[2];
-    f32x4 pv[4], dv[4];
-    bf16x8 pf[2][2], dsf[2][2];
-    // The step is a fixed sequence of MFMA groups (two MFMAs each):
-    //   [0, DT)          S/dP of half 0, k-step t
-    //   [DT, 2DT)        S/dP of half 1, k-step t      + P/dS of half 0
-    //   [2DT, 2DT+NC)    dV/dK of half 0, product i    + P/dS of half 1
-    //   [2DT+NC, NGRP)   dV/dK of half 1, product i
-    // Operands are read from LDS ULY_DKV_PF groups ahead into a ring of registers.
-    constexpr int NGRP = 2 * DT + 2 * NC, PF = ULY_DKV_PF, R = PF + 1;
-    auto load_group = [&](int k, bf16x8& x, bf16x8& y) {
-      if (k < 2 * DT) load_sdp(buf, k / DT, k % DT, x, y);
-      else load_dkdv(buf, (k - 2 * DT) / NC, (k - 2 * DT) % NC, x, y);
-    };
-    bf16x8 ox[R], oy[R];
-    static_for<0, PF>([&](auto K) {
-      constexpr int k = decltype(K)::value;
-      load_group(k, ox[k % R], oy[k % R]);
-    });
-    static_for<0, NGRP>([&](auto K) {
-      constexpr int k = decltype(K)::value;
-      // The next tile's DMA is issued a few groups into the dV/dK phase: issued at the top of
-      // the step it slowed the S/dP operand reads that follow the barrier (measured).
-      if constexpr (k == 2 * DT + 4) {
-        if (step + 1 < nsteps) issue_tile(nxt_t, nxt_h, buf ^ 1);
-      }
-      if constexpr (k + PF < NGRP) load_group(k + PF, ox[(k + PF) % R], oy[(k + PF) % R]);
-      const bf16x8& x = ox[k % R];
-      const bf16x8& y = oy[k % R];
-      if constexpr (k < 2 * DT) {
-        const int h = k / DT, t = k % DT;
-        sacc[h] = mfma32x32x16(x, kf[t], t == 0 ? f32x16{} : sacc[h]);
-        pacc[h] = mfma32x32x16(y, vf[t], t == 0 ? f32x16{} : pacc[h]);
-      } else {
-        const int h = (k - 2 * DT) / NC, i = (k - 2 * DT) % NC;
-        const int tt = i / DB, db = i % DB;
-        dvacc[db] = mfma32x32x16(x, pf[h][tt], dvacc[db]);
-        dkacc[db] = mfma32x32x16(y, dsf[h][tt], dkacc[db]);
-      }
-      // P/dS of half sh spread over the groups of its window
-      const int sh = k < 2 * DT ? 0 : 1;
-      const int w0 = k < 2 * DT ? DT : 2 * DT, wn = k < 2 * DT ? DT : NC;
-      if (k >= w0 && k < w0 + wn) {
-        const int kk = k - w0;
+    // The two roles run separate code, each naming its LDS objects directly (a runtime choice
+    // between buffers would hide from the compiler which object a read touches).
+    f32x16 x[2];
+    bf16x8 op[2][2];  // P (role 0) or dS (role 1) as bf16 MFMA operands, [qb][tt]
+    auto part_a = [&](auto ROLE) {
+      constexpr int r = decltype(ROLE)::value;
+      // S (role 0) or dP (role 1), row x key: the query-side operand is Q or dO
+      const uint16_t* qs = r == 0 ? buf.q : buf.g;
 #pragma unroll
-        for (int g = kk * 4 / wn; g < (kk + 1) * 4 / wn; ++g) {
-          soft4(buf, qrel0, sh, g, sacc[sh], pacc[sh], pv[g], dv[g]);
-          if (g & 1) {
-            pf[sh][g / 2] = pack8(pv[g - 1], pv[g]);
-            dsf[sh][g / 2] = pack8(dv[g - 1], dv[g]);
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&qs[tile_off<D>(qb * 32 + l32, 16 * t + 8 * hf)]);
+          x[qb] = mfma32x32x16(qa, kv[t], t == 0 ? f32x16{} : x[qb]);
+        }
+      if constexpr (r == 0) {
+        // P = exp2(S c - LSE log2e) on rows 32qb + 8(j/4) + 4hf + j%4, 0 outside [rlo, rhi)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 L4 = *reinterpret_cast<const f32x4*>(&buf.l[qb * 32 + 8 * jj + 4 * hf]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float p = fast_exp2(__builtin_fmaf(x[qb][4 * jj + e], c, -L4[e] * kLog2e));
+              x[qb][4 * jj + e] = (uint32_t)(qrel0 + qb * 32 + 8 * jj + e) < width ? p : 0.f;
+            }
+            *reinterpret_cast<f32x4*>(&sP[0][0][p_off(qb, jj)]) =
+                f32x4{x[qb][4 * jj], x[qb][4 * jj + 1], x[qb][4 * jj + 2], x[qb][4 * jj + 3]};
           }
+          op[qb][0] = pack8(x[qb], 0);
+          op[qb][1] = pack8(x[qb], 1);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-    });
+    };
+    auto part_b = [&](auto ROLE) {
+      constexpr int r = decltype(ROLE)::value;
+      if constexpr (r == 1) {
+        // dS = P (dP - delta)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 D4 = *reinterpret_cast<const f32x4*>(&buf.d[qb * 32 + 8 * jj + 4 * hf]);
+            const f32x4 P4 = *reinterpret_cast<const f32x4*>(&sP[0][0][p_off(qb, jj)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[qb][4 * jj + e] = P4[e] * (x[qb][4 * jj + e] - D4[e]);
+          }
+          op[qb][0] = pack8(x[qb], 0);
+          op[qb][1] = pack8(x[qb], 1);
+        }
+      }
+      // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1)
+      const uint16_t* ts = r == 0 ? buf.g : buf.q;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16(load_tr(ts, qb, tt, db), op[qb][tt], acc[db]);
+    };
+    if (role == 0) part_a(std::integral_constant<int, 0>{});
+    else part_a(std::integral_constant<int, 1>{});
+    __syncthreads();  // P of this tile is in LDS
+    if (role == 0) part_b(std::integral_constant<int, 0>{});
+    else part_b(std::integral_constant<int, 1>{});
+  };
+
+  if (nsteps > 0) {
+    if (role == 1) issue_tile(0, 0, bufs(std::integral_constant<int, 0>{}));
+    for (int step = 0;;) {
+      run_step(std::integral_constant<int, 0>{}, step);
+      if (++step >= nsteps) break;
+      run_step(std::integral_constant<int, 1>{}, step);
+      if (++step >= nsteps) break;
+    }
   }
 
   if (key < s) {
-    uint16_t* dK = static_cast<uint16_t*>(a.out_k) + (int64_t)kvh * D;
-    uint16_t* dV = static_cast<uint16_t*>(a.out_v) + (int64_t)kvh * D;
+    const bool is_k = role == 1;
+    uint16_t* out = static_cast<uint16_t*>(is_k ? a.out_k : a.out_v) + (int64_t)kvh * D;
+    const float f = is_k ? a.scale : 1.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        u32x2 wk, wv;
-        wk[0] = pack_bf16x2(dkacc[db][4 * jj + 0] * a.scale, dkacc[db][4 * jj + 1] * a.scale);
-        wk[1] = pack_bf16x2(dkacc[db][4 * jj + 2] * a.scale, dkacc[db][4 * jj + 3] * a.scale);
-        wv[0] = pack_bf16x2(dvacc[db][4 * jj + 0], dvacc[db][4 * jj + 1]);
-        wv[1] = pack_bf16x2(dvacc[db][4 * jj + 2], dvacc[db][4 * jj + 3]);
-        *reinterpret_cast<u32x2*>(dK + key * a.kv_row + db * 32 + 8 * jj + 4 * hf) = wk;
-        *reinterpret_cast<u32x2*>(dV + key * a.kv_row + db * 32 + 8 * jj + 4 * hf) = wv;
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[db][4 * jj + 0] * f, acc[db][4 * jj + 1] * f);
+        w[1] = pack_bf16x2(acc[db][4 * jj + 2] * f, acc[db][4 * jj + 3] * f);
+        *reinterpret_cast<u32x2*>(out + key * a.kv_row + db * 32 + 8 * jj + 4 * hf) = w;
       }
   }
 }
@@ -493,12 +478,12 @@ hipError_t launch_dq_t(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int QB>
-hipError_t launch_dkdv_t(const AttnArgs& a, hipStream_t stream) {
-  using C = DkvCfg<D, QB>;
+template <int D>
+hipError_t launch_dkdv_split_t(const AttnArgs& a, hipStream_t stream) {
+  using C = DkvSplitCfg<D>;
   const int64_t blocks = (a.s + C::BNK - 1) / C::BNK * a.n_kv;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_dkdv_kernel<D, QB>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((attn_dkdv_split_kernel<D>), dim3((unsigned)blocks), dim3(C::NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -515,8 +500,8 @@ hipError_t launch_attn_dq_bf16(const AttnArgs& a, int d, hipStream_t stream) {
 }
 
 hipError_t launch_attn_dkdv_bf16(const AttnArgs& a, int d, hipStream_t stream) {
-  if (d == 128) return launch_dkdv_t<128, 2>(a, stream);
-  return launch_dkdv_t<64, 2>(a, stream);
+  if (d == 128) return launch_dkdv_split_t<128>(a, stream);
+  return launch_dkdv_split_t<64>(a, stream);
 }
 
 }  // namespace uly
