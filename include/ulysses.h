@@ -165,6 +165,37 @@ int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards,
 size_t attn_fwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int d,
                                         int dtype, int heads_per_chunk);
 
+/* ---------------------------------------------------------------------------
+ * attn_bwd_chunked -- the backward of the UPipe schedule for rank `rank` (same passage
+ * as attn_fwd_chunked: only some heads are resident at a time, which matters most in
+ * training). For each chunk of `heads_per_chunk` local q heads: pack the chunk's Q, O and
+ * dO (and its kv heads' K and V when their range changes), form delta, dK/dV and dQ of the
+ * chunk, and unpack dQ into the dq shards. The dK/dV of a kv head read by several chunks
+ * are summed in fp32 across those chunks and rounded once; the rank's dK and dV are
+ * unpacked into the dk / dv shards after the last chunk. dQ is identical to the
+ * unchunked attn_bwd's; dK/dV differ from it only in the order of the fp32 sums.
+ *   q_shards / o_shards / do_shards / dq_shards : host arrays of P device pointers
+ *                        [s_l, Hq, d] (global Hq); o and lse as written by the forward
+ *   k_shards / v_shards / dk_shards / dv_shards : host arrays of P device pointers
+ *                        [s_l, Hkv, d]
+ *   lse : device fp32 [Hq/P, s] of this rank's heads
+ *   dq / dk / dv shards: only this rank's head slices are written.
+ *   workspace : at least attn_bwd_chunked_workspace_bytes(...) bytes; NULL -> size query
+ *               into *workspace_bytes as for attn_bwd: the chunk buffers (Q, O, dO, dQ
+ *               of u heads, K and V of the kv heads they read, delta) plus fp32 dK/dV
+ *               sums and the rank's dK/dV.
+ * Errors as for attn_fwd_chunked.
+ * ------------------------------------------------------------------------- */
+int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards,
+                     const void* const* v_shards, const void* const* o_shards, const float* lse,
+                     const void* const* do_shards, void* const* dq_shards, void* const* dk_shards,
+                     void* const* dv_shards, int P, int rank, int64_t s_l, int Hq, int Hkv, int d,
+                     int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,
+                     int heads_per_chunk, void* workspace, size_t* workspace_bytes, void* stream);
+
+size_t attn_bwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int d,
+                                        int dtype, int heads_per_chunk);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,4 +1,4 @@
-"""Oracle for the headwise-chunked (UPipe-style) forward.
+"""Oracle for the headwise-chunked (UPipe-style) forward and backward.
 
 Test infrastructure only (see the package docstring).
 
@@ -10,7 +10,9 @@ as the unchunked layer (pack, attention, unpack) restricted to its heads.
 
 Readings (listed in the design doc): chunks cover the rank's q heads in order, u heads
 each, the last one smaller when u does not divide H_q/P; a chunk's kv heads are
-those its q heads read (h // G).
+those its q heads read (h // G). In the backward, the gradient of a kv head read by
+several chunks is the sum of the chunks' contributions (the chain rule over the heads
+that read it, exactly as in the unchunked GQA backward).
 """
 import numpy as np
 
@@ -59,3 +61,37 @@ def workspace_elems(s, Hq_l, G, d, heads_per_chunk):
         c1 = min(c0 + u, Hq_l)
         n_kv = max(n_kv, (c1 - 1) // G - c0 // G + 1)
     return 2 * s * u * d + 2 * s * n_kv * d
+
+
+def backward(q_shards, k_shards, v_shards, do_shards, rank, heads_per_chunk, scale, causal=True,
+             cu_seqlens=None, to_f64=None):
+    """Chunked backward for rank `rank` (the UPipe schedule applied to training).
+
+    Same readings as forward(): chunks of u local q heads in order, each with the kv heads
+    its q heads read. Per chunk, each q head's gradients come from the plain backward of
+    that head with its kv head; the dK/dV of a kv head are summed over the chunks (and
+    heads) that read it. Returns float64 (dq [s, Hq/P, d], dk [s, Hkv/P, d], dv)."""
+    P = len(q_shards)
+    s_l, Hq, d = q_shards[0].shape
+    Hkv = k_shards[0].shape[1]
+    Hq_l, Hkv_l = Hq // P, Hkv // P
+    G = Hq // Hkv
+    s = P * s_l
+    dq = np.zeros((s, Hq_l, d))
+    dk = np.zeros((s, Hkv_l, d))
+    dv = np.zeros((s, Hkv_l, d))
+    for c0 in range(0, Hq_l, heads_per_chunk):
+        c1 = min(c0 + heads_per_chunk, Hq_l)
+        g0, g1 = c0 // G, (c1 - 1) // G + 1
+        qc = to_f64(permute.pack(q_shards, rank, h0=rank * Hq_l + c0, nh=c1 - c0))
+        gc = to_f64(permute.pack(do_shards, rank, h0=rank * Hq_l + c0, nh=c1 - c0))
+        kc = to_f64(permute.pack(k_shards, rank, h0=rank * Hkv_l + g0, nh=g1 - g0))
+        vc = to_f64(permute.pack(v_shards, rank, h0=rank * Hkv_l + g0, nh=g1 - g0))
+        for j in range(c1 - c0):
+            g = (c0 + j) // G - g0
+            q1, k1, v1 = attention.backward(qc[:, j:j + 1], kc[:, g:g + 1], vc[:, g:g + 1], gc[:, j:j + 1],
+                                            scale, causal, cu_seqlens)
+            dq[:, c0 + j] = q1[:, 0]
+            dk[:, g0 + g] += k1[:, 0]
+            dv[:, g0 + g] += v1[:, 0]
+    return dq, dk, dv

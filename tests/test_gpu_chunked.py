@@ -94,29 +94,42 @@ def test_chunked_workspace_matches_query():
     assert o_sh[0][:, :4].float().abs().sum().item() > 0
 
 
-@pytest.mark.timeout(600)
+_UPIPE = {}
+
+
+def _upipe_inputs():
+    """Device shards of q, k, v, dO for the 256K UPipe share (8 ranks x 32768 tokens, 64 q /
+    8 kv heads) and float64 copies of what the oracle reads for rank 0: q and dO of every
+    local head, k and v of local kv head 0. Generated once per module."""
+    if _UPIPE:
+        return _UPIPE
+    cfg = W.CONFIGS["upipe_256k"]
+    rank, P, s_l, Hl = 0, cfg.P, cfg.s_l, cfg.Hq_l
+    print("generating upipe_256k inputs", flush=True)
+    dev = {n: [] for n in ("q", "k", "v", "do")}
+    f = {n: np.zeros((cfg.s, Hl if n in ("q", "do") else 1, cfg.d)) for n in dev}
+    for p in range(P):
+        r0, r1 = p * s_l, (p + 1) * s_l
+        for n in dev:
+            b = W.gen_rows(cfg, n, r0, r1)
+            dev[n].append(to_dev(b, "bf16"))
+            h0 = rank * (Hl if n in ("q", "do") else cfg.Hkv_l)
+            f[n][r0:r1] = W.bits_to_f64(b[:, h0:h0 + f[n].shape[1]], "bf16")
+            del b
+        print(f"  shard {p} on device", flush=True)
+    _UPIPE.update(cfg=cfg, rank=rank, dev=dev, f=f)
+    return _UPIPE
+
+
+@pytest.mark.timeout(900)
 def test_chunked_full_upipe_share():
     """The 256K UPipe share (8 ranks x 32768 tokens, 64 q / 8 kv heads, rank 0) at u = 1
     and u = 2: bitwise equal to the unchunked path, sampled rows of two heads against
     the oracle, and the workspace (peak intermediate bytes) as the analysis predicts."""
-    cfg = W.CONFIGS["upipe_256k"]
-    rank, P, s_l, Hl = 0, cfg.P, cfg.s_l, cfg.Hq_l
+    X = _upipe_inputs()
+    cfg, rank, dev, f = X["cfg"], X["rank"], X["dev"], X["f"]
+    P, s_l, Hl = cfg.P, cfg.s_l, cfg.Hq_l
     heads = (0, Hl - 1)            # local q heads checked against the oracle (both read kv head 0)
-    print("generating upipe_256k inputs", flush=True)
-    dev, f = {n: [] for n in ("q", "k", "v")}, {}
-    qh = np.zeros((cfg.s, len(heads), cfg.d))
-    kh = np.zeros((cfg.s, 1, cfg.d))
-    vh = np.zeros((cfg.s, 1, cfg.d))
-    for p in range(P):
-        r0, r1 = p * s_l, (p + 1) * s_l
-        for n in ("q", "k", "v"):
-            b = W.gen_rows(cfg, n, r0, r1)
-            dev[n].append(to_dev(b, "bf16"))
-            if n == "q":
-                qh[r0:r1] = W.bits_to_f64(b[:, [rank * Hl + h for h in heads]], "bf16")
-            else:
-                (kh if n == "k" else vh)[r0:r1] = W.bits_to_f64(b[:, rank * cfg.Hkv_l:rank * cfg.Hkv_l + 1], "bf16")
-        print(f"  shard {p} on device", flush=True)
     want_o, want_lse = _unchunked(dev["q"], dev["k"], dev["v"], rank, cfg.scale, True, None)
     torch.cuda.synchronize()
     print("unchunked done", flush=True)
@@ -139,9 +152,166 @@ def test_chunked_full_upipe_share():
         print(f"u={u} bitwise equal to unchunked", flush=True)
 
     rows = sample_rows(cfg.s)
-    wo, wl = OA.forward(qh, kh, vh, cfg.scale, True, None, rows=rows)
+    wo, wl = OA.forward(f["q"][:, list(heads)], f["k"], f["v"], cfg.scale, True, None, rows=rows)
     got = torch.stack([torch.stack([t[:, rank * Hl + h] for h in heads], 1) for t in want_o], 0)
     got = got.reshape(cfg.s, len(heads), cfg.d)[torch.as_tensor(rows, device="cuda")]
     compare("upipe O sampled", dev_to_f64(got), wo, bf16=True)
     compare("upipe LSE sampled", want_lse[list(heads)][:, torch.as_tensor(rows, device="cuda")].cpu().numpy(),
             wl, max_abs=LSE_ABS, rel_fro=1e-4)
+
+
+# ---------------------------------------------------------------------------
+# attn_bwd_chunked: dQ must be bitwise equal to the unchunked attn_bwd (each q head's dQ
+# is computed by the same kernel over the same rows); dK/dV of a kv head whose q heads
+# span several chunks are fp32 sums taken in another order, so they are held to the
+# oracle (and bitwise equal to the unchunked result when every chunk holds whole groups).
+
+def _unchunked_bwd(dev, o_sh, lse, rank, scale, causal, cu_dev):
+    q, k, v, o, do = (U.ulysses_pack(x, rank) for x in (dev["q"], dev["k"], dev["v"], o_sh, dev["do"]))
+    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, do, scale, causal, cu_dev)
+    out = {}
+    for n, y, like in (("dq", dq, dev["q"]), ("dk", dk, dev["k"]), ("dv", dv, dev["v"])):
+        out[n] = _sentinel_like(like)
+        U.ulysses_unpack(y, rank, out[n])
+    return out
+
+
+def _rank_cat(sh, rank, P):
+    x = torch.cat(sh, 0)
+    Hl = x.shape[1] // P
+    return x[:, rank * Hl:(rank + 1) * Hl]
+
+
+def _groups_whole(Hq_l, G, u):
+    u = min(u, Hq_l)
+    return all(min(c0 + u, Hq_l) % G == 0 and c0 % G == 0 for c0 in range(0, Hq_l, u)) if u >= G else False
+
+
+SMALL_BWD = [
+    # P, s_l, Hq, Hkv, d, dtype, u, rank, cu
+    (4, 300, 24, 8, 128, "bf16", 1, 0, None),      # G = 3: every kv head in three chunks
+    (4, 300, 24, 8, 128, "bf16", 2, 3, None),      # chunks straddle the groups
+    (4, 300, 24, 8, 128, "bf16", 4, 1, None),      # ragged last chunk
+    (4, 300, 24, 8, 128, "bf16", 3, 2, None),      # whole groups: bitwise equal dK/dV
+    (4, 300, 24, 8, 128, "bf16", 9, 0, None),      # clamped to one chunk
+    (2, 257, 8, 2, 128, "bf16", 3, 1, [0, 1, 40, 300, 514]),
+    (8, 64, 64, 8, 128, "bf16", 2, 5, None),       # the UPipe head counts at small s
+    (2, 200, 8, 2, 64, "bf16", 3, 0, [0, 150, 151, 400]),
+    (2, 200, 8, 2, 64, "f32", 3, 1, None),
+    (2, 130, 8, 2, 64, "f32", 1, 0, [0, 70, 260]),
+]
+
+
+@pytest.mark.parametrize("P,s_l,Hq,Hkv,d,dt,u,rank,cu", SMALL_BWD)
+def test_chunked_bwd_small(P, s_l, Hq, Hkv, d, dt, u, rank, cu):
+    print(f"case P={P} s_l={s_l} Hq={Hq} Hkv={Hkv} d={d} {dt} u={u} rank={rank} cu={cu is not None}", flush=True)
+    cfg = W.Config("chunk_bwd_small", P=P, s_l=s_l, Hq=Hq, Hkv=Hkv, d=d, dtype=dt, amp=1.0 if dt == "bf16" else 0.5)
+    bits = {n: W.shards_of(W.gen_global(cfg, n, seed=13), P) for n in ("q", "k", "v", "do")}
+    dev = {n: [to_dev(b, dt) for b in bits[n]] for n in bits}
+    cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    o_sh, lse = _unchunked(dev["q"], dev["k"], dev["v"], rank, cfg.scale, True, cu_dev)
+    want = _unchunked_bwd(dev, o_sh, lse, rank, cfg.scale, True, cu_dev)
+    got = {n: _sentinel_like(want[n]) for n in want}
+    keep = {n: [t.clone() for t in got[n]] for n in got}
+    U.attn_bwd_chunked(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], got["dq"], got["dk"], got["dv"],
+                       rank, u, cfg.scale, True, cu_dev)
+    torch.cuda.synchronize()
+    iview = torch.int16 if dt == "bf16" else torch.int32
+    Hql, Hkvl = Hq // P, Hkv // P
+    # this rank's dQ bitwise, every other head of the shards untouched
+    for n, Hl in (("dq", Hql), ("dk", Hkvl), ("dv", Hkvl)):
+        for a, c in zip(got[n], keep[n]):
+            rest = torch.cat([a[:, :rank * Hl], a[:, (rank + 1) * Hl:]], dim=1)
+            rest_c = torch.cat([c[:, :rank * Hl], c[:, (rank + 1) * Hl:]], dim=1)
+            assert torch.equal(rest, rest_c), n
+    assert torch.equal(_rank_cat(got["dq"], rank, P).view(iview), _rank_cat(want["dq"], rank, P).view(iview))
+    if _groups_whole(Hql, Hq // Hkv, u):
+        for n in ("dk", "dv"):
+            assert torch.equal(_rank_cat(got[n], rank, P).view(iview), _rank_cat(want[n], rank, P).view(iview)), n
+
+    to64 = lambda b: W.bits_to_f64(b, dt)
+    wq, wk, wv = OC.backward(bits["q"], bits["k"], bits["v"], bits["do"], rank, u, cfg.scale, True, cu, to_f64=to64)
+    bf = dt == "bf16"
+    compare("chunked dQ", dev_to_f64(_rank_cat(got["dq"], rank, P)), wq, bf16=bf)
+    compare("chunked dK", dev_to_f64(_rank_cat(got["dk"], rank, P)), wk, bf16=bf)
+    compare("chunked dV", dev_to_f64(_rank_cat(got["dv"], rank, P)), wv, bf16=bf)
+
+
+def test_chunked_bwd_workspace_matches_query():
+    """A backward workspace one byte short is rejected before any launch; the exact size works."""
+    cfg = W.Config("chunk_bwd_ws", P=4, s_l=64, Hq=16, Hkv=4, d=128, dtype="bf16")
+    dev = {n: [to_dev(b, "bf16") for b in W.shards_of(W.gen_global(cfg, n, seed=2), cfg.P)]
+           for n in ("q", "k", "v", "do")}
+    o_sh, lse = _unchunked(dev["q"], dev["k"], dev["v"], 0, cfg.scale, True, None)
+    need = U.attn_bwd_chunked_workspace_bytes(cfg.P, cfg.s_l, cfg.Hq, cfg.Hkv, cfg.d, torch.bfloat16, 3)
+    outs = [[torch.zeros_like(t) for t in dev[n]] for n in ("q", "k", "v")]
+    short = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(U.UlyssesError):
+        U.attn_bwd_chunked(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], *outs, 0, 3, workspace=short)
+    torch.cuda.synchronize()
+    assert all(not t.float().abs().sum().item() for x in outs for t in x)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    U.attn_bwd_chunked(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], *outs, 0, 3, workspace=ws)
+    torch.cuda.synchronize()
+    assert all(t[:, :h].float().abs().sum().item() > 0 for x, h in zip(outs, (4, 1, 1)) for t in x)
+
+
+@pytest.mark.timeout(900)
+def test_chunked_bwd_full_upipe_share():
+    """Backward of the 256K UPipe share (rank 0) at u = 1 and u = 2 (every kv head summed
+    over 8 and 4 chunks): dQ bitwise equal to the unchunked attn_bwd; dK/dV within one
+    bf16 step of it (the fp32 sums are only reordered); sampled dQ rows and dK/dV keys
+    against the oracle; sum_j dV_j against the dO sums over every key; and peak
+    intermediate memory no more than the queried workspace."""
+    from tests.test_gpu_fullsize import _dv_column_sums
+    X = _upipe_inputs()
+    cfg, rank, dev, f = X["cfg"], X["rank"], X["dev"], X["f"]
+    P, s_l, s, Hl = cfg.P, cfg.s_l, cfg.s, cfg.Hq_l
+    o_sh, lse = _unchunked(dev["q"], dev["k"], dev["v"], rank, cfg.scale, True, None)
+    want = _unchunked_bwd(dev, o_sh, lse, rank, cfg.scale, True, None)
+    torch.cuda.synchronize()
+    print("unchunked backward done", flush=True)
+    ref_dkv = {n: _rank_cat(want[n], rank, P) for n in ("dk", "dv")}
+    for u in (1, 2):
+        need = U.attn_bwd_chunked_workspace_bytes(P, s_l, cfg.Hq, cfg.Hkv, cfg.d, torch.bfloat16, u)
+        got = {n: _sentinel_like(want[n]) for n in want}
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        U.attn_bwd_chunked(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], got["dq"], got["dk"], got["dv"],
+                           rank, u, cfg.scale, True)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        assert peak <= need + (1 << 20), (u, peak, need)
+        assert torch.equal(_rank_cat(got["dq"], rank, P).view(torch.int16),
+                           _rank_cat(want["dq"], rank, P).view(torch.int16))
+        for n in ("dk", "dv"):
+            a = _rank_cat(got[n], rank, P).float()
+            b = ref_dkv[n].float()
+            m = torch.maximum(a.abs(), b.abs())
+            step = torch.exp2(torch.floor(torch.log2(torch.where(m > 0, m, torch.ones_like(m)))) - 7)
+            bad = ((a - b).abs() > step + 1e-4).sum().item()
+            assert bad == 0, (u, n, bad)
+        print(f"u={u} dQ bitwise, dK/dV within one bf16 step of unchunked", flush=True)
+        if u == 1:
+            keep = got
+        else:
+            del got
+
+    rows = sample_rows(s)
+    hs = [0, Hl - 1]
+    wq, _, _ = OA.backward(f["q"][:, hs], f["k"], f["v"], f["do"][:, hs], cfg.scale, True, None,
+                           q_rows=rows, kv_cols=np.zeros(0, int))
+    ridx = torch.as_tensor(rows, device="cuda")
+    compare("upipe dQ sampled", dev_to_f64(_rank_cat(keep["dq"], rank, P)[ridx][:, hs]), wq, bf16=True)
+    keys = set(range(s - 64, s))
+    for b in range(s - 1024, s, 128):
+        keys |= {b - 1, b}
+    keys = np.array(sorted(keys))
+    _, wk, wv = OA.backward(f["q"], f["k"], f["v"], f["do"], cfg.scale, True, None,
+                            q_rows=np.zeros(0, int), kv_cols=keys)
+    kidx = torch.as_tensor(keys, device="cuda")
+    compare("upipe dK keys", dev_to_f64(_rank_cat(keep["dk"], rank, P)[kidx]), wk, bf16=True)
+    compare("upipe dV keys", dev_to_f64(_rank_cat(keep["dv"], rank, P)[kidx]), wv, bf16=True)
+    print("sampled rows and keys ok", flush=True)
+    _dv_column_sums(dev_to_f64(_rank_cat(keep["dv"], rank, P)), f["do"], cfg.G, [(0, s)])

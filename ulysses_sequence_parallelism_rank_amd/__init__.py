@@ -9,6 +9,7 @@ The names follow the C ABI in include/ulysses.h:
   attn_fwd, attn_bwd                  -- attention of one head shard
   attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq -- the phases of attn_bwd
   attn_fwd_chunked                    -- the UPipe headwise-chunked forward
+  attn_bwd_chunked                    -- its backward
 """
 from __future__ import annotations
 
@@ -49,6 +50,9 @@ SIGNATURES = {
     "attn_fwd_chunked": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                 _i32, _vp, _i32, _i32, _vp, _szp, _vp]),
     "attn_fwd_chunked_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
+    "attn_bwd_chunked": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vpp, _vpp, _vpp, _vpp, _i32, _i32, _i64, _i32,
+                                _i32, _i32, _i32, _f32, _i32, _vp, _i32, _i32, _vp, _szp, _vp]),
+    "attn_bwd_chunked_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
 }
 
 
@@ -228,3 +232,28 @@ def attn_fwd_chunked(q_shards, k_shards, v_shards, o_shards, rank, heads_per_chu
           _default_scale(d, scale), int(causal), cu, nd, heads_per_chunk, _dev(workspace), ctypes.byref(cap),
           _stream())
     return lse
+
+
+def attn_bwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, dtype, heads_per_chunk):
+    dt = dtype if isinstance(dtype, int) else _dtype(torch.empty(0, dtype=dtype))
+    return int(lib().attn_bwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, dt, heads_per_chunk))
+
+
+def attn_bwd_chunked(q_shards, k_shards, v_shards, o_shards, lse, do_shards, dq_shards, dk_shards, dv_shards,
+                     rank, heads_per_chunk, scale=None, causal=True, cu_seqlens=None, workspace=None):
+    """UPipe backward of rank `rank`: writes this rank's heads of dq_shards, dk_shards, dv_shards."""
+    P = len(q_shards)
+    s_l, Hq, d = q_shards[0].shape
+    Hkv = k_shards[0].shape[1]
+    dt = _dtype(q_shards[0])
+    need = attn_bwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, dt, heads_per_chunk)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_shards[0].device)
+    cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    keep = [_ptrs(x) for x in (q_shards, k_shards, v_shards, o_shards, do_shards, dq_shards, dk_shards, dv_shards)]
+    qp, kp, vp, op, gp, dqp, dkp, dvp = (k[0] for k in keep)
+    cu, nd = _cu(cu_seqlens)
+    _call("attn_bwd_chunked", qp, kp, vp, op, _dev(lse), gp, dqp, dkp, dvp, P, rank, s_l, Hq, Hkv, d, dt,
+          _default_scale(d, scale), int(causal), cu, nd, heads_per_chunk, _dev(workspace), ctypes.byref(cap),
+          _stream())
+    return dq_shards, dk_shards, dv_shards

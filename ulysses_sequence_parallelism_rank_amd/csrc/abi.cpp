@@ -59,6 +59,7 @@ AttnArgs make_args(int64_t s, int Hq, int Hkv, int d, float scale, int causal, c
   a.s = s;
   a.q_row = (int64_t)Hq * d;
   a.kv_row = (int64_t)Hkv * d;
+  a.dkv_row = (int64_t)Hkv * d;
   a.lse_row = s;
   a.n_heads = Hq;
   a.n_kv = Hkv;
@@ -93,6 +94,26 @@ int max_kv_span(int Hq_l, int G, int u) {
   return span;
 }
 
+}  // namespace
+
+namespace {
+
+// Byte sizes of the parts of attn_bwd_chunked's workspace (see the layout there).
+struct BwdChunkLayout {
+  size_t qc, kv, delta, acc, out, total;
+};
+BwdChunkLayout bwd_chunk_layout(int P, int64_t s_l, int Hq, int Hkv, int d, int dtype, int u) {
+  const int Hq_l = Hq / P, Hkv_l = Hkv / P, G = Hq / Hkv;
+  const size_t s = (size_t)P * (size_t)s_l, e = (size_t)esize(dtype);
+  BwdChunkLayout L;
+  L.qc = round256(s * (size_t)u * (size_t)d * e);
+  L.kv = round256(s * (size_t)max_kv_span(Hq_l, G, u) * (size_t)d * e);
+  L.delta = round256((size_t)u * s * sizeof(float));
+  L.acc = round256(s * (size_t)Hkv_l * (size_t)d * sizeof(float));
+  L.out = round256(s * (size_t)Hkv_l * (size_t)d * e);
+  L.total = 4 * L.qc + 2 * L.kv + L.delta + 2 * L.acc + 2 * L.out;
+  return L;
+}
 }  // namespace
 
 extern "C" {
@@ -345,6 +366,140 @@ int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards, c
     if (st != ULY_OK) return st;
     if ((err = launch_unpack(oc, os, P, s_l, qrow, qoff, qrun, strm)) != hipSuccess) return ULY_ERR_HIP;
   }
+  return ULY_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// Headwise-chunked backward. Workspace, in order (each part 256-byte aligned):
+//   Q, O, dO, dQ chunks        4 x [s, u, d]            element type
+//   K, V chunks                2 x [s, span, d]          element type
+//   delta of the chunk         [u, s]                    fp32
+//   dK, dV accumulators        2 x [s, Hkv/P, d]         fp32
+//   dK, dV of the rank         2 x [s, Hkv/P, d]         element type
+
+size_t attn_bwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int d, int dtype,
+                                        int heads_per_chunk) {
+  if (P < 1 || s_l < 1 || Hq < 1 || Hkv < 1 || d < 1 || heads_per_chunk < 1) return 0;
+  if (Hq % P != 0 || Hkv % P != 0 || Hq % Hkv != 0) return 0;
+  const int u = std::min(heads_per_chunk, Hq / P);
+  return bwd_chunk_layout(P, s_l, Hq, Hkv, d, dtype, u).total;
+}
+
+int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards, const void* const* v_shards,
+                     const void* const* o_shards, const float* lse, const void* const* do_shards,
+                     void* const* dq_shards, void* const* dk_shards, void* const* dv_shards, int P, int rank,
+                     int64_t s_l, int Hq, int Hkv, int d, int dtype, float scale, int causal,
+                     const int32_t* cu_seqlens, int n_docs, int heads_per_chunk, void* workspace,
+                     size_t* workspace_bytes, void* stream) {
+  if (!q_shards || !k_shards || !v_shards || !o_shards || !do_shards || !dq_shards || !dk_shards || !dv_shards)
+    return ULY_ERR_NULL;
+  int st = check_ranks(P, rank, s_l, Hq);
+  if (st != ULY_OK) return st;
+  if (Hkv < 1 || Hkv % P != 0 || Hq % Hkv != 0) return ULY_ERR_SHAPE;
+  st = check_dtype_dim(dtype, d);
+  if (st != ULY_OK) return st;
+  if (heads_per_chunk < 1) return ULY_ERR_SHAPE;
+  const int64_t s = (int64_t)P * s_l;
+  if (s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
+  if (cu_seqlens != nullptr && n_docs < 1) return ULY_ERR_SHAPE;
+  const size_t need = attn_bwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, dtype, heads_per_chunk);
+  if (workspace == nullptr) {
+    if (!workspace_bytes) return ULY_ERR_NULL;
+    *workspace_bytes = need;
+    return ULY_OK;
+  }
+  if (workspace_bytes && *workspace_bytes < need) return ULY_ERR_WORKSPACE;
+  if (!lse) return ULY_ERR_NULL;
+  if (!aligned16(lse) || !aligned16(workspace)) return ULY_ERR_ALIGN;
+  for (int p = 0; p < P; ++p) {
+    const void* ptrs[8] = {q_shards[p], k_shards[p], v_shards[p], o_shards[p], do_shards[p],
+                           dq_shards[p], dk_shards[p], dv_shards[p]};
+    for (const void* x : ptrs) {
+      if (!x) return ULY_ERR_NULL;
+      if (!aligned16(x)) return ULY_ERR_ALIGN;
+    }
+  }
+  const int Hq_l = Hq / P, Hkv_l = Hkv / P, G = Hq / Hkv;
+  const int u = std::min(heads_per_chunk, Hq_l);
+  const int64_t e = esize(dtype);
+  const int64_t qrow = (int64_t)Hq * d * e, kvrow = (int64_t)Hkv * d * e, hb = (int64_t)d * e;
+  if (!chunks_fit(P, s_l, qrow, qrow) || !chunks_fit(P, s_l, kvrow, kvrow)) return ULY_ERR_SHAPE;
+
+  const BwdChunkLayout L = bwd_chunk_layout(P, s_l, Hq, Hkv, d, dtype, u);
+  char* ws = static_cast<char*>(workspace);
+  void* qc = ws;
+  void* oc = ws + L.qc;
+  void* gc = ws + 2 * L.qc;
+  void* dqc = ws + 3 * L.qc;
+  void* kc = ws + 4 * L.qc;
+  void* vc = ws + 4 * L.qc + L.kv;
+  float* delta = reinterpret_cast<float*>(ws + 4 * L.qc + 2 * L.kv);
+  float* acc_k = reinterpret_cast<float*>(ws + 4 * L.qc + 2 * L.kv + L.delta);
+  float* acc_v = reinterpret_cast<float*>(ws + 4 * L.qc + 2 * L.kv + L.delta + L.acc);
+  char* dk_r = ws + 4 * L.qc + 2 * L.kv + L.delta + 2 * L.acc;
+  char* dv_r = dk_r + L.out;
+  const ShardPtrs qs = shard_ptrs(q_shards, P), ks = shard_ptrs(k_shards, P), vs = shard_ptrs(v_shards, P);
+  const ShardPtrs os = shard_ptrs(o_shards, P), gs = shard_ptrs(do_shards, P);
+  const ShardPtrs dqs = shard_ptrs(const_cast<const void* const*>(dq_shards), P);
+  const ShardPtrs dks = shard_ptrs(const_cast<const void* const*>(dk_shards), P);
+  const ShardPtrs dvs = shard_ptrs(const_cast<const void* const*>(dv_shards), P);
+  hipStream_t strm = as_stream(stream);
+  hipError_t err;
+
+  int kv_lo = -1, kv_hi = -1;  // local kv heads currently packed in kc / vc
+  for (int c0 = 0; c0 < Hq_l; c0 += u) {
+    const int c1 = std::min(c0 + u, Hq_l), nq = c1 - c0;
+    const int g0 = c0 / G, g1 = (c1 - 1) / G + 1;
+    if (g0 != kv_lo || g1 != kv_hi) {
+      const int64_t off = ((int64_t)rank * Hkv_l + g0) * hb, run = (int64_t)(g1 - g0) * hb;
+      if ((err = launch_pack(ks, kc, P, s_l, kvrow, off, run, strm)) != hipSuccess) return ULY_ERR_HIP;
+      if ((err = launch_pack(vs, vc, P, s_l, kvrow, off, run, strm)) != hipSuccess) return ULY_ERR_HIP;
+      kv_lo = g0;
+      kv_hi = g1;
+    }
+    const int64_t qoff = ((int64_t)rank * Hq_l + c0) * hb, qrun = (int64_t)nq * hb;
+    if ((err = launch_pack(qs, qc, P, s_l, qrow, qoff, qrun, strm)) != hipSuccess) return ULY_ERR_HIP;
+    if ((err = launch_pack(os, oc, P, s_l, qrow, qoff, qrun, strm)) != hipSuccess) return ULY_ERR_HIP;
+    if ((err = launch_pack(gs, gc, P, s_l, qrow, qoff, qrun, strm)) != hipSuccess) return ULY_ERR_HIP;
+
+    AttnArgs a = make_args(s, nq, 1, d, scale, causal, cu_seqlens, n_docs);
+    a.q_row = (int64_t)nq * d;
+    a.kv_row = (int64_t)(g1 - g0) * d;
+    a.n_heads = nq;
+    a.n_kv = g1 - g0;
+    a.G = G;
+    a.q_off = c0;   // chunk head j is local head c0 + j
+    a.kv_off = g0;  // which reads local kv head (c0 + j) / G, stored at index - g0
+    a.q = qc;
+    a.k = kc;
+    a.v = vc;
+    a.o = oc;
+    a.dout = gc;
+    a.lse_in = lse + (int64_t)c0 * s;
+    a.delta = delta;
+    // delta of the chunk's heads
+    AttnArgs pre = a;
+    pre.lse_out = delta;
+    if ((err = launch_bwd_preprocess(pre, d, dtype, strm)) != hipSuccess) return ULY_ERR_HIP;
+    // dK/dV of kv heads [g0, g1): fp32 sums carried across chunks, rounded on the last one
+    AttnArgs kvargs = a;
+    kvargs.dkv_row = (int64_t)Hkv_l * d;
+    kvargs.acc_k = acc_k + (int64_t)g0 * d;
+    kvargs.acc_v = acc_v + (int64_t)g0 * d;
+    kvargs.out_k = dk_r + (int64_t)g0 * hb;
+    kvargs.out_v = dv_r + (int64_t)g0 * hb;
+    err = dtype == ULY_BF16 ? launch_attn_dkdv_bf16(kvargs, d, strm) : launch_attn_dkdv_f32(kvargs, d, strm);
+    if (err != hipSuccess) return ULY_ERR_HIP;
+    // dQ of the chunk's heads
+    AttnArgs qargs = a;
+    qargs.out = dqc;
+    err = dtype == ULY_BF16 ? launch_attn_dq_bf16(qargs, d, strm) : launch_attn_dq_f32(qargs, d, strm);
+    if (err != hipSuccess) return ULY_ERR_HIP;
+    if ((err = launch_unpack(dqc, dqs, P, s_l, qrow, qoff, qrun, strm)) != hipSuccess) return ULY_ERR_HIP;
+  }
+  const int64_t kvoff = (int64_t)rank * Hkv_l * hb, kvrun = (int64_t)Hkv_l * hb;
+  if ((err = launch_unpack(dk_r, dks, P, s_l, kvrow, kvoff, kvrun, strm)) != hipSuccess) return ULY_ERR_HIP;
+  if ((err = launch_unpack(dv_r, dvs, P, s_l, kvrow, kvoff, kvrun, strm)) != hipSuccess) return ULY_ERR_HIP;
   return ULY_OK;
 }
 

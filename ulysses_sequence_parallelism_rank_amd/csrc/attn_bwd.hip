@@ -280,7 +280,6 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
   const int64_t s = a.s;
   const int kvh = blockIdx.x % a.n_kv;
   const int64_t n0 = (int64_t)(blockIdx.x / a.n_kv) * BNK;  // earliest keys (most rows) first
-  const int G = a.G;
   const float c = a.scale * kLog2e;
 
   // this lane's key, the rows that may see it [rlo, rhi), and its K (role 0) or V row
@@ -312,14 +311,16 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
   }
   qbeg = (qbeg / BMQ) * BMQ;
   const int ntile = qend > qbeg ? (int)((qend - qbeg + BMQ - 1) / BMQ) : 0;
-  const int nsteps = ntile * G;
+  const KvHeads kh = kv_heads_of(a, kvh);  // the launch's q heads reading this kv head
+  const int GH = kh.j1 - kh.j0;
+  const int nsteps = ntile * GH;
 
-  // Steps walk the query tiles from the last one down, the G heads of a tile back to back.
+  // Steps walk the query tiles from the last one down, the GH heads of a tile back to back.
   auto tile_row0 = [&](int tile) { return qbeg + (int64_t)(ntile - 1 - tile) * BMQ; };
   // Only the dS waves issue DMA: the P waves then never hold outstanding DMA, so nothing
   // makes them wait for it before their LDS writes of P.
   auto issue_tile = [&](int tile, int hi, const Buf& b) {
-    const int hq = kvh * G + hi;
+    const int hq = kh.j0 + hi;
     const int64_t q0 = tile_row0(tile);
     const int t2 = tid - 256;
     dma_tile<D, BMQ, 256>(static_cast<const uint16_t*>(a.q) + (int64_t)hq * D, a.q_row, q0, s, b.q, t2);
@@ -359,8 +360,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
     const Buf buf = bufs(B), nbuf = bufs(std::integral_constant<int, 1 - decltype(B)::value>{});
     wait_dma();
     __syncthreads();  // tile `step` has landed; every wave is done with tile step-1 and with P
-    const int nxt_h = cur_h + 1 == G ? 0 : cur_h + 1;
-    const int nxt_t = cur_h + 1 == G ? cur_t + 1 : cur_t;
+    const int nxt_h = cur_h + 1 == GH ? 0 : cur_h + 1;
+    const int nxt_t = cur_h + 1 == GH ? cur_t + 1 : cur_t;
     if (role == 1 && step + 1 < nsteps) issue_tile(nxt_t, nxt_h, nbuf);
     const int32_t qrel0 = (int32_t)tile_row0(cur_t) - rlo + 4 * hf;
     cur_t = nxt_t;
@@ -445,17 +446,39 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
 
   if (key < s) {
     const bool is_k = role == 1;
-    uint16_t* out = static_cast<uint16_t*>(is_k ? a.out_k : a.out_v) + (int64_t)kvh * D;
+    const int64_t off = (int64_t)kvh * D + key * a.dkv_row;
     const float f = is_k ? a.scale : 1.0f;
+    // headwise-chunked backward: fp32 sums carried across launches, rounded once at the end
+    float* accp = a.acc_k == nullptr ? nullptr : (is_k ? a.acc_k : a.acc_v) + off;
+    if (accp != nullptr && !kh.first) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[db][4 * jj + 0] * f, acc[db][4 * jj + 1] * f);
-        w[1] = pack_bf16x2(acc[db][4 * jj + 2] * f, acc[db][4 * jj + 3] * f);
-        *reinterpret_cast<u32x2*>(out + key * a.kv_row + db * 32 + 8 * jj + 4 * hf) = w;
-      }
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 prev = *reinterpret_cast<const f32x4*>(accp + db * 32 + 8 * jj + 4 * hf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[db][4 * jj + e] += prev[e];
+        }
+    }
+    if (accp != nullptr && !kh.last) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<f32x4*>(accp + db * 32 + 8 * jj + 4 * hf) =
+              f32x4{acc[db][4 * jj + 0], acc[db][4 * jj + 1], acc[db][4 * jj + 2], acc[db][4 * jj + 3]};
+    } else {
+      uint16_t* out = static_cast<uint16_t*>(is_k ? a.out_k : a.out_v) + off;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[db][4 * jj + 0] * f, acc[db][4 * jj + 1] * f);
+          w[1] = pack_bf16x2(acc[db][4 * jj + 2] * f, acc[db][4 * jj + 3] * f);
+          *reinterpret_cast<u32x2*>(out + db * 32 + 8 * jj + 4 * hf) = w;
+        }
+    }
   }
 }
 

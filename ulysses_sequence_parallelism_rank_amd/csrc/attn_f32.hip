@@ -201,8 +201,8 @@ __global__ __launch_bounds__(kRows) void f32_dkdv_kernel(AttnArgs a) {
     dk[x] = 0.f;
     dv[x] = 0.f;
   }
-  for (int g = 0; g < a.G; ++g) {
-    const int hq = kvh * a.G + g;
+  const KvHeads kh = kv_heads_of(a, kvh);  // the launch's q heads reading this kv head
+  for (int hq = kh.j0; hq < kh.j1; ++hq) {
     const float* Q = static_cast<const float*>(a.q) + (int64_t)hq * D;
     const float* dO = static_cast<const float*>(a.dout) + (int64_t)hq * D;
     for (int64_t q0 = qbeg; q0 < qend; q0 += kRows) {
@@ -239,12 +239,31 @@ __global__ __launch_bounds__(kRows) void f32_dkdv_kernel(AttnArgs a) {
     }
   }
   if (key < s) {
-    float* dK = static_cast<float*>(a.out_k) + (int64_t)kvh * D;
-    float* dV = static_cast<float*>(a.out_v) + (int64_t)kvh * D;
+    const int64_t off = (int64_t)kvh * D + key * a.dkv_row;
+    // headwise-chunked backward: sums carried across launches in fp32, scaled once at the end
+    const bool carry_in = a.acc_k != nullptr && !kh.first;
+    const bool carry_out = a.acc_k != nullptr && !kh.last;
+    if (carry_in) {
 #pragma unroll
-    for (int x = 0; x < D; ++x) {
-      dK[key * a.kv_row + x] = dk[x] * a.scale;
-      dV[key * a.kv_row + x] = dv[x];
+      for (int x = 0; x < D; ++x) {
+        dk[x] += a.acc_k[off + x];
+        dv[x] += a.acc_v[off + x];
+      }
+    }
+    if (carry_out) {
+#pragma unroll
+      for (int x = 0; x < D; ++x) {
+        a.acc_k[off + x] = dk[x];
+        a.acc_v[off + x] = dv[x];
+      }
+    } else {
+      float* dK = static_cast<float*>(a.out_k) + off;
+      float* dV = static_cast<float*>(a.out_v) + off;
+#pragma unroll
+      for (int x = 0; x < D; ++x) {
+        dK[x] = dk[x] * a.scale;
+        dV[x] = dv[x];
+      }
     }
   }
 }

@@ -14,9 +14,17 @@ struct ShardPtrs {
 
 // Attention problem description shared by the forward and backward kernels.
 //   q / o / do / dq : [s, q_heads, D], row stride q_row elements
-//   k / v / dk / dv : [s, kv_heads, D], row stride kv_row elements
-// q head h (0 <= h < n_heads of the launch) reads kv head (h + q_off) / G - kv_off.
+//   k / v           : [s, kv_heads, D], row stride kv_row elements
+//   dk / dv         : [s, kv_heads, D], row stride dkv_row elements
+// q head h (0 <= h < n_heads of the launch) reads kv head (h + q_off) / G - kv_off, so the
+// q heads of the launch that read kv head g are [max(lo, 0), min(lo + G, n_heads)) with
+// lo = (g + kv_off) G - q_off (the launch may hold a chunk of a GQA group).
 // lse / delta rows are [n_heads][s] with row stride lse_row.
+// dK/dV accumulation across launches (headwise-chunked backward): when acc_k is set, the
+// dK/dV kernel adds its sums to the fp32 arrays acc_k / acc_v ([s, kv_heads, D], row stride
+// dkv_row) unless the launch holds the first q head of the kv head's group, and writes the
+// rounded result to dk / dv only when it holds the last one (otherwise it stores the fp32
+// sum back).
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -28,6 +36,9 @@ struct AttnArgs {
   void* out;      // o (forward) or dq
   void* out_k;    // dk
   void* out_v;    // dv
+  float* acc_k;   // fp32 dK accumulator (chunked backward) or null
+  float* acc_v;   // fp32 dV accumulator
+  int64_t dkv_row;
   float* lse_out; // forward LSE / preprocess delta
   int64_t s;
   int64_t q_row, kv_row;
