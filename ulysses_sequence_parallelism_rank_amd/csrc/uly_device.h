@@ -123,50 +123,6 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t stride, in
   }
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane i writes lds_base + 16 i.
-// Issued through inline assembly so that the compiler does not track it: it then inserts no
-// wait before later LDS accesses (it would assume any of them may alias the DMA). The caller
-// must keep the DMA target disjoint from everything read or written until the wait_dma()
-// that precedes the barrier publishing the tile. lds_base must be wave-uniform.
-__device__ __forceinline__ void dma16_untracked(const void* gptr, const void* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0), "v"(gptr)
-               : "memory", "m0");
-}
-
-// 4 bytes per lane, lane i writing lds_base + 4 i; otherwise as dma16_untracked().
-__device__ __forceinline__ void dma4_untracked(const void* gptr, const void* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :
-               : "s"(m0), "v"(gptr)
-               : "memory", "m0");
-}
-
-// dma_tile() through dma16_untracked().
-template <int D, int ROWS, int NTHREADS>
-__device__ __forceinline__ void dma_tile_untracked(const uint16_t* src, int64_t stride, int64_t r0, int64_t nrows,
-                                                   uint16_t* lds_tile, int tid) {
-  constexpr int CPR = D / 8;
-  constexpr int SLOTS = ROWS * CPR;
-  static_assert(SLOTS % NTHREADS == 0, "tile must be a whole number of wave instructions");
-  const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int i = 0; i < SLOTS / NTHREADS; ++i) {
-    const int sl0 = (i * (NTHREADS / 64) + wave) * 64;
-    const int sl = sl0 + lane;
-    const int row = sl / CPR, pc = sl % CPR;
-    const int c = pc ^ swz_chunk<D>(row);
-    int64_t gr = r0 + row;
-    gr = gr < nrows ? gr : nrows - 1;
-    dma16_untracked(src + gr * stride + c * 8, lds_tile + sl0 * 8);
-  }
-}
-
 // Wait until this wave's LDS DMA (global_load_lds) has landed: s_waitcnt vmcnt(0), the other
 // counters left alone (gfx9 encoding: expcnt 7 in bits 6:4, lgkmcnt 15 in bits 11:8). A
 // workgroup barrier does not order another wave's DMA writes before this wave's LDS reads, so
