@@ -11,7 +11,13 @@ Metric: causal attention TFLOP/s, fwd+bwd counted FLOPs (4 d N fwd + 10 d N bwd 
 head, N = s^2/2 visible pairs, or sum of l^2/2 over packed documents) divided by the
 time of the whole step (permutes included). Prints ONE JSON line.
 
+The UPipe workload (--workload upipe_256k) times the headwise-chunked schedule instead:
+attn_fwd_chunked then attn_bwd_chunked (--forward-only: the forward alone) with
+--heads-per-chunk q heads per chunk, and reports the workspace bytes beside the unchunked
+intermediates.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                       [--heads-per-chunk U] [--forward-only]
 """
 import argparse
 import hashlib
@@ -145,12 +151,20 @@ def run_training_share(cfg, steps, warmup, cu_dev):
     return wall, ph.summary(steps)
 
 
-def run_upipe(cfg, steps, warmup, u):
+def run_upipe(cfg, steps, warmup, u, forward_only):
+    """The UPipe schedule on the rank-0 share: attn_fwd_chunked, then (unless forward_only)
+    attn_bwd_chunked, both on one workspace of the larger queried size."""
     _, sh = make_inputs(cfg)
     o_sh = [torch.empty_like(t) for t in sh["q"]]
+    dq_sh = [torch.empty_like(t) for t in sh["q"]]
+    dk_sh = [torch.empty_like(t) for t in sh["k"]]
+    dv_sh = [torch.empty_like(t) for t in sh["v"]]
     lse = torch.empty((cfg.Hq_l, cfg.s), dtype=torch.float32, device="cuda")
-    need = U.attn_fwd_chunked_workspace_bytes(cfg.P, cfg.s_l, cfg.Hq, cfg.Hkv, cfg.d, torch.bfloat16, u)
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    args = (cfg.P, cfg.s_l, cfg.Hq, cfg.Hkv, cfg.d, torch.bfloat16, u)
+    need = {"fwd": U.attn_fwd_chunked_workspace_bytes(*args)}
+    if not forward_only:
+        need["bwd"] = U.attn_bwd_chunked_workspace_bytes(*args)
+    ws = torch.empty(max(need.values()), dtype=torch.uint8, device="cuda")
     ph = Phases()
     for i in range(warmup + steps):
         if i == warmup:
@@ -158,6 +172,10 @@ def run_upipe(cfg, steps, warmup, u):
             t0 = time.perf_counter()
         ph.run("attn_fwd_chunked", lambda: U.attn_fwd_chunked(sh["q"], sh["k"], sh["v"], o_sh, 0, u, cfg.scale,
                                                               cfg.causal, None, ws, lse), i >= warmup)
+        if not forward_only:
+            ph.run("attn_bwd_chunked", lambda: U.attn_bwd_chunked(sh["q"], sh["k"], sh["v"], o_sh, lse, sh["do"],
+                                                                  dq_sh, dk_sh, dv_sh, 0, u, cfg.scale, cfg.causal,
+                                                                  None, ws), i >= warmup)
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps, ph.summary(steps), need
 
@@ -188,6 +206,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen_64k", choices=sorted(W.CONFIGS))
     ap.add_argument("--heads-per-chunk", type=int, default=1)
+    ap.add_argument("--forward-only", action="store_true",
+                    help="UPipe workload: time the chunked forward alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy (ulysses_pack with one rank) and exit; "
@@ -215,7 +235,8 @@ def main():
     pairs = counted_pairs(cfg, cu)
     d, Hq_l, Hkv_l, e = cfg.d, cfg.Hq_l, cfg.Hkv_l, cfg.esize
 
-    if cfg.backward:
+    chunked = bool(cfg.chunk_heads)
+    if not chunked:
         wall, ph = run_training_share(cfg, args.steps, args.warmup, cu_dev)
         flops = 14.0 * d * pairs * Hq_l
         kern = {
@@ -229,9 +250,12 @@ def main():
             "unpack_grads": ("hbm", 2.0 * cfg.s * (Hq_l + 2 * Hkv_l) * d * e),
         }
     else:
-        wall, ph, ws_bytes = run_upipe(cfg, args.steps, args.warmup, args.heads_per_chunk)
-        flops = 4.0 * d * pairs * Hq_l
-        kern = {"attn_fwd_chunked": ("mfma", flops)}
+        wall, ph, ws_bytes = run_upipe(cfg, args.steps, args.warmup, args.heads_per_chunk, args.forward_only)
+        # each call is timed whole (per chunk: permutes and attention kernels)
+        kern = {"attn_fwd_chunked": ("mfma", 4.0 * d * pairs * Hq_l)}
+        if not args.forward_only:
+            kern["attn_bwd_chunked"] = ("mfma", 10.0 * d * pairs * Hq_l)
+        flops = sum(w for _, w in kern.values())
 
     step_ms = wall * 1e3
     dom = max(ph, key=ph.get)
@@ -249,7 +273,8 @@ def main():
     roof["avg_ms"] = round(ms, 4)
     roof["traffic"] = read_traffic(dom, args.workload)
 
-    attn_ms = sum(ph.get(k, 0.0) for k in ("attn_fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "attn_fwd_chunked"))
+    attn_ms = sum(ph.get(k, 0.0) for k in ("attn_fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "attn_fwd_chunked",
+                                           "attn_bwd_chunked"))
     perm_ms = sum(ph.get(k, 0.0) for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads"))
     perm_bytes = sum(kern[k][1] for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads") if k in kern)
     value = flops / wall / 1e12
@@ -270,8 +295,8 @@ def main():
             "workload": {"qwen_64k": "Qwen3-4B-shaped SP=4 rank share at 65536 tokens",
                          "qwen_8k": "Qwen3-4B-shaped SP=4 rank share at 8192 tokens",
                          "packed_96k": "packed SFT batch at 98304 tokens (documents ~ geometric, mean 6000)",
-                         "upipe_256k": f"UPipe chunked forward, 32B-shaped SP=8 share at 262144 tokens, "
-                                       f"{args.heads_per_chunk} q heads per chunk",
+                         "upipe_256k": f"UPipe headwise-chunked {'forward' if args.forward_only else 'forward+backward'}, "
+                                       f"32B-shaped SP=8 share at 262144 tokens, {args.heads_per_chunk} q heads per chunk",
                          "tiny_f32": "tiny fp32 case"}[args.workload],
             "seq_len": cfg.s, "ranks_simulated": cfg.P, "rank": 0, "q_heads": Hq_l, "kv_heads": Hkv_l,
             "head_dim": d, "causal": cfg.causal, "packed_docs": None if cu is None else int(len(cu) - 1),
@@ -283,9 +308,12 @@ def main():
         "permute_gbs": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1) if perm_ms else None,
         "phase_ms": {k: round(v, 4) for k, v in ph.items()},
     }
-    if not cfg.backward:
+    if chunked:
+        # peak intermediate bytes: the chunked calls' workspaces against the unchunked head shards
+        # (forward: Q, O, K, V; training adds dO, dQ, dK, dV and delta)
         out["workspace_bytes"] = ws_bytes
-        out["unchunked_intermediate_bytes"] = int(2 * cfg.s * Hq_l * d * e + 2 * cfg.s * Hkv_l * d * e)
+        fwd_b = 2 * cfg.s * Hq_l * d * e + 2 * cfg.s * Hkv_l * d * e
+        out["unchunked_intermediate_bytes"] = int(fwd_b if args.forward_only else 2 * fwd_b + 4 * cfg.s * Hq_l)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)

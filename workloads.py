@@ -49,7 +49,6 @@ class Config:
     causal: bool = True
     packed_mean: float | None = None     # mean document length when packed
     chunk_heads: tuple = field(default_factory=tuple)  # q heads per chunk (UPipe)
-    backward: bool = True
 
     @property
     def s(self) -> int:
@@ -86,9 +85,9 @@ CONFIGS = {
     # packed SFT batch at 98304 tokens, documents of mean length 6000
     "packed_96k": Config("packed_96k", P=4, s_l=24576, Hq=32, Hkv=8, d=128, dtype="bf16",
                          packed_mean=6000.0),
-    # UPipe chunked forward, 32B-shaped SP=8 share at 262144 tokens
+    # UPipe headwise-chunked share, 32B-shaped SP=8 at 262144 tokens
     "upipe_256k": Config("upipe_256k", P=8, s_l=32768, Hq=64, Hkv=8, d=128, dtype="bf16",
-                         chunk_heads=(1, 2), backward=False),
+                         chunk_heads=(1, 2)),
 }
 
 
