@@ -164,11 +164,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a) {
   };
   // dS of keys kb*32 + 8jj + 4hf + e (e < 4) for this lane's row; keys outside the row's
   // range get P = 0 from an unsigned compare, so no branch surrounds the MFMAs.
-  auto soft4 = [&](int32_t krel0, int kb, int jj, const f32x16& si, const f32x16& pi, f32x4& dv) {
+  // (MASK false: every key of the half is visible to every row of the wave)
+  auto soft4 = [&](auto MASK, int32_t krel0, int kb, int jj, const f32x16& si, const f32x16& pi, f32x4& dv) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float p = fast_exp2(__builtin_fmaf(si[4 * jj + e], c, -lse2[0]));
-      p = (uint32_t)(krel0 + kb * 32 + 8 * jj + e) < width[0] ? p : 0.f;
+      if constexpr (decltype(MASK)::value) p = (uint32_t)(krel0 + kb * 32 + 8 * jj + e) < width[0] ? p : 0.f;
       dv[e] = p * (pi[4 * jj + e] - dl[0]);
     }
   };
@@ -195,6 +196,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       f32x16 sacc, pacc;
+      // raised priority through S/dP and dS: the other wave on the SIMD fills the gaps with
+      // its dQ products
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         bf16x8 kx, vx;
@@ -204,11 +208,20 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a) {
       }
       f32x4 dv[4];
       bf16x8 dsf[2];
+      auto soft_all = [&](auto MASK) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        soft4(krel0, hh, g, sacc, pacc, dv[g]);
-        if (g & 1) dsf[g / 2] = pack8(dv[g - 1], dv[g]);
-      }
+        for (int g = 0; g < 4; ++g) {
+          soft4(MASK, krel0, hh, g, sacc, pacc, dv[g]);
+          if (g & 1) dsf[g / 2] = pack8(dv[g - 1], dv[g]);
+        }
+      };
+      // the mask is applied only where some lane's row cannot see some key of the half
+      // (a wave-uniform branch around VALU work only)
+      const int32_t kr = krel0 - 4 * hf + hh * 32;
+      const bool full = (uint32_t)kr < width[0] && (uint32_t)(kr + 31) < width[0];
+      if (__ballot(!full) != 0) soft_all(std::true_type{});
+      else soft_all(std::false_type{});
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
         bf16x8 kt, unused;
@@ -374,13 +387,22 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
       constexpr int r = decltype(ROLE)::value;
       // S (role 0) or dP (role 1), row x key: the query-side operand is Q or dO
       const uint16_t* qs = r == 0 ? buf.q : buf.g;
+      // operands of k-step t+1 are read while the MFMAs of k-step t run (the scheduling
+      // barriers keep that order; left alone, the compiler reads each just before its use)
+      bf16x8 ring[2][2];
+      auto ld = [&](int t, bf16x8 (&o)[2]) {
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
+        for (int qb = 0; qb < 2; ++qb)
+          o[qb] = *reinterpret_cast<const bf16x8*>(&qs[tile_off<D>(qb * 32 + l32, 16 * t + 8 * hf)]);
+      };
+      ld(0, ring[0]);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&qs[tile_off<D>(qb * 32 + l32, 16 * t + 8 * hf)]);
-          x[qb] = mfma32x32x16(qa, kv[t], t == 0 ? f32x16{} : x[qb]);
-        }
+      for (int t = 0; t < DT; ++t) {
+        if (t + 1 < DT) ld(t + 1, ring[(t + 1) & 1]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) x[qb] = mfma32x32x16(ring[t & 1][qb], kv[t], t == 0 ? f32x16{} : x[qb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if constexpr (r == 0) {
         // P = exp2(S c - LSE log2e) on rows 32qb + 8(j/4) + 4hf + j%4, 0 outside [rlo, rhi)
 #pragma unroll
@@ -403,6 +425,14 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
     };
     auto part_b = [&](auto ROLE) {
       constexpr int r = decltype(ROLE)::value;
+      // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1): products i = (qb, tt, db), their
+      // transposed operands read two products ahead (the first two before the dS work)
+      const uint16_t* ts = r == 0 ? buf.g : buf.q;
+      constexpr int NP = 4 * DB, PF = 2;
+      bf16x8 ringb[PF + 1];
+      auto ldb = [&](int i) { return load_tr(ts, i / (2 * DB), (i / DB) % 2, i % DB); };
+#pragma unroll
+      for (int i = 0; i < PF; ++i) ringb[i] = ldb(i);
       if constexpr (r == 1) {
         // dS = P (dP - delta)
 #pragma unroll
@@ -418,20 +448,24 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
           op[qb][1] = pack8(x[qb], 1);
         }
       }
-      // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1)
-      const uint16_t* ts = r == 0 ? buf.g : buf.q;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16(load_tr(ts, qb, tt, db), op[qb][tt], acc[db]);
+      for (int i = 0; i < NP; ++i) {
+        if (i + PF < NP) ringb[(i + PF) % (PF + 1)] = ldb(i + PF);
+        acc[i % DB] = mfma32x32x16(ringb[i % (PF + 1)], op[i / (2 * DB)][(i / DB) % 2], acc[i % DB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
     if (role == 0) part_a(std::integral_constant<int, 0>{});
     else part_a(std::integral_constant<int, 1>{});
     __syncthreads();  // P of this tile is in LDS
-    if (role == 0) part_b(std::integral_constant<int, 0>{});
-    else part_b(std::integral_constant<int, 1>{});
+    // the dS waves go first in part B: their dS work is the longer path to the next barrier
+    if (role == 0) {
+      part_b(std::integral_constant<int, 0>{});
+    } else {
+      __builtin_amdgcn_s_setprio(1);
+      part_b(std::integral_constant<int, 1>{});
+      __builtin_amdgcn_s_setprio(0);
+    }
   };
 
   if (nsteps > 0) {

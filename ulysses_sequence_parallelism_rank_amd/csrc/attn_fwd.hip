@@ -251,7 +251,10 @@ __global__ __launch_bounds__(kWaves * 64, OCC) void attn_fwd_kernel(AttnArgs a) 
       __syncthreads();
       if (j + 1 < ntiles) store_v((j + 1) & 1);
       if (j + 2 < ntiles) load_tile(k0 + 2 * BN);
-      // P(j) on the VALU while the matrix cores compute S(j+1); then O^T += V(j)^T P(j)
+      // P(j) on the VALU while the matrix cores compute S(j+1); then O^T += V(j)^T P(j).
+      // Raised priority up to the PV products: the other wave on the SIMD fills the gaps
+      // with its own PV MFMAs.
+      __builtin_amdgcn_s_setprio(1);
       bf16x8 pf[RB][KB][2];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -271,6 +274,7 @@ __global__ __launch_bounds__(kWaves * 64, OCC) void attn_fwd_kernel(AttnArgs a) 
         l[rb] += ls;
       }
       qk((j + 1) & 1, sc);
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
