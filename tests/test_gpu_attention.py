@@ -32,6 +32,7 @@ CASES = [
     (257, 8, 2, 128, "bf16", True, None),
     (600, 4, 1, 128, "bf16", True, None),
     (600, 4, 2, 64, "bf16", False, None),
+    (333, 4, 2, 64, "bf16", True, [0, 50, 51, 200, 333]),
     (777, 2, 1, 128, "bf16", True, [0, 1, 2, 100, 101, 390, 777]),
     (520, 4, 2, 128, "bf16", False, [0, 300, 301, 520]),
     (1024, 8, 2, 128, "bf16", True, None),
