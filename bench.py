@@ -16,8 +16,11 @@ attn_fwd_chunked then attn_bwd_chunked (--forward-only: the forward alone) with
 --heads-per-chunk q heads per chunk, and reports the workspace bytes beside the unchunked
 intermediates.
 
+--forward-only times the forward half alone (pack Q/K/V, forward, unpack O); with --fused
+it times attn_fwd_shards instead, the forward reading and writing the shards directly.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                       [--heads-per-chunk U] [--forward-only]
+                       [--heads-per-chunk U] [--forward-only [--fused]]
 """
 import argparse
 import hashlib
@@ -151,6 +154,41 @@ def run_training_share(cfg, steps, warmup, cu_dev):
     return wall, ph.summary(steps)
 
 
+def run_forward_share(cfg, steps, warmup, cu_dev, fused):
+    """The forward half of the path for rank 0: pack Q/K/V -> attn_fwd -> unpack O, or (fused)
+    attn_fwd_shards reading the sequence shards and writing O into them directly."""
+    _, sh = make_inputs(cfg)
+    rank = 0
+    s, Hq_l, Hkv_l, d = cfg.s, cfg.Hq_l, cfg.Hkv_l, cfg.d
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q = torch.empty((s, Hq_l, d), dtype=dt, device="cuda")
+    k = torch.empty((s, Hkv_l, d), dtype=dt, device="cuda")
+    v = torch.empty_like(k)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq_l, s), dtype=torch.float32, device="cuda")
+    o_sh = [torch.empty_like(t) for t in sh["q"]]
+    ph = Phases()
+
+    def step(rec):
+        if fused:
+            ph.run("attn_fwd_shards", lambda: U.attn_fwd_shards(sh["q"], sh["k"], sh["v"], o_sh, rank, cfg.scale,
+                                                                cfg.causal, cu_dev, lse=lse), rec)
+            return
+        ph.run("pack_qkv", lambda: (U.ulysses_pack(sh["q"], rank, q), U.ulysses_pack(sh["k"], rank, k),
+                                    U.ulysses_pack(sh["v"], rank, v)), rec)
+        ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse), rec)
+        ph.run("unpack_o", lambda: U.ulysses_unpack(o, rank, o_sh), rec)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps, ph.summary(steps)
+
+
 def run_upipe(cfg, steps, warmup, u, forward_only):
     """The UPipe schedule on the rank-0 share: attn_fwd_chunked, then (unless forward_only)
     attn_bwd_chunked, both on one workspace of the larger queried size."""
@@ -207,7 +245,9 @@ def main():
     ap.add_argument("--workload", default="qwen_64k", choices=sorted(W.CONFIGS))
     ap.add_argument("--heads-per-chunk", type=int, default=1)
     ap.add_argument("--forward-only", action="store_true",
-                    help="UPipe workload: time the chunked forward alone")
+                    help="time the forward half of the path alone (UPipe workload: the chunked forward)")
+    ap.add_argument("--fused", action="store_true",
+                    help="with --forward-only: attn_fwd_shards, reading and writing the sequence shards directly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy (ulysses_pack with one rank) and exit; "
@@ -236,7 +276,14 @@ def main():
     d, Hq_l, Hkv_l, e = cfg.d, cfg.Hq_l, cfg.Hkv_l, cfg.esize
 
     chunked = bool(cfg.chunk_heads)
-    if not chunked:
+    if not chunked and args.forward_only:
+        wall, ph = run_forward_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
+        fw = 4.0 * d * pairs * Hq_l
+        kern = {"attn_fwd": ("mfma", fw), "attn_fwd_shards": ("mfma", fw),
+                "pack_qkv": ("hbm", 2.0 * cfg.s * (Hq_l + 2 * Hkv_l) * d * e),
+                "unpack_o": ("hbm", 2.0 * cfg.s * Hq_l * d * e)}
+        flops = fw
+    elif not chunked:
         wall, ph = run_training_share(cfg, args.steps, args.warmup, cu_dev)
         flops = 14.0 * d * pairs * Hq_l
         kern = {
@@ -274,12 +321,14 @@ def main():
     roof["traffic"] = read_traffic(dom, args.workload)
 
     attn_ms = sum(ph.get(k, 0.0) for k in ("attn_fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "attn_fwd_chunked",
-                                           "attn_bwd_chunked"))
+                                           "attn_bwd_chunked", "attn_fwd_shards"))
     perm_ms = sum(ph.get(k, 0.0) for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads"))
-    perm_bytes = sum(kern[k][1] for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads") if k in kern)
+    perm_bytes = sum(kern[k][1] for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads") if k in ph)
     value = flops / wall / 1e12
     out = {
-        "metric": METRIC if args.workload == "qwen_64k" else f"{METRIC} [workload {args.workload}]",
+        "metric": METRIC if args.workload == "qwen_64k" and not args.forward_only else
+        f"{METRIC} [workload {args.workload}{', forward only' if args.forward_only else ''}"
+        f"{', fused exchange' if args.fused else ''}]",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -166,6 +166,29 @@ size_t attn_fwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int
                                         int dtype, int heads_per_chunk);
 
 /* ---------------------------------------------------------------------------
+ * attn_fwd_shards -- the forward of rank `rank` with the exchange folded into the
+ * attention's own loads and stores ("Ulysses Sequence Parallelism: Training with
+ * Million-Token Contexts", how Ulysses works, steps 1-5: after the first all-to-all a
+ * rank holds every position of its heads, and the second all-to-all returns O to the
+ * sequence shards). Instead of materialising the head shard, the kernel reads the rank's
+ * Q heads and kv heads straight from the P sequence shards and writes O straight into
+ * the rank's head slice of the o shards: no intermediate buffer. Results are bitwise
+ * those of ulysses_pack + attn_fwd + ulysses_unpack.
+ *   q_shards / o_shards : host arrays of P device pointers [s_l, Hq, d] (global Hq);
+ *                        only head slice `rank` of the o shards is written
+ *   k_shards / v_shards : host arrays of P device pointers [s_l, Hkv, d]
+ *   lse : device fp32 [Hq/P, s] for this rank's heads
+ * bf16 only (ULY_ERR_UNSUPPORTED for fp32), and every workgroup's rows must lie in one
+ * shard: s_l a multiple of 128 (ULY_ERR_UNSUPPORTED otherwise). Other errors as for
+ * attn_fwd_chunked.
+ * ------------------------------------------------------------------------- */
+int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards,
+                    const void* const* v_shards, void* const* o_shards, float* lse,
+                    int P, int rank, int64_t s_l, int Hq, int Hkv, int d, int dtype,
+                    float scale, int causal, const int32_t* cu_seqlens, int n_docs,
+                    void* stream);
+
+/* ---------------------------------------------------------------------------
  * attn_bwd_chunked -- the backward of the UPipe schedule for rank `rank` (same passage
  * as attn_fwd_chunked: only some heads are resident at a time, which matters most in
  * training). For each chunk of `heads_per_chunk` local q heads: pack the chunk's Q, O and

@@ -10,6 +10,7 @@ The names follow the C ABI in include/ulysses.h:
   attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq -- the phases of attn_bwd
   attn_fwd_chunked                    -- the UPipe headwise-chunked forward
   attn_bwd_chunked                    -- its backward
+  attn_fwd_shards                     -- the forward reading and writing the sequence shards
 """
 from __future__ import annotations
 
@@ -53,6 +54,8 @@ SIGNATURES = {
     "attn_bwd_chunked": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vpp, _vpp, _vpp, _vpp, _i32, _i32, _i64, _i32,
                                 _i32, _i32, _i32, _f32, _i32, _vp, _i32, _i32, _vp, _szp, _vp]),
     "attn_bwd_chunked_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
+    "attn_fwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
+                               _i32, _vp, _i32, _vp]),
 }
 
 
@@ -257,3 +260,20 @@ def attn_bwd_chunked(q_shards, k_shards, v_shards, o_shards, lse, do_shards, dq_
           _default_scale(d, scale), int(causal), cu, nd, heads_per_chunk, _dev(workspace), ctypes.byref(cap),
           _stream())
     return dq_shards, dk_shards, dv_shards
+
+
+def attn_fwd_shards(q_shards, k_shards, v_shards, o_shards, rank, scale=None, causal=True, cu_seqlens=None,
+                    lse=None):
+    """Forward of rank `rank` straight from the sequence shards into head slice `rank` of
+    o_shards (no head-shard buffers); returns the LSE [Hq/P, s]."""
+    P = len(q_shards)
+    s_l, Hq, d = q_shards[0].shape
+    Hkv = k_shards[0].shape[1]
+    if lse is None:
+        lse = torch.empty((Hq // P, P * s_l), dtype=torch.float32, device=q_shards[0].device)
+    keep = [_ptrs(x) for x in (q_shards, k_shards, v_shards, o_shards)]
+    qp, kp, vp, op = (k[0] for k in keep)
+    cu, nd = _cu(cu_seqlens)
+    _call("attn_fwd_shards", qp, kp, vp, op, _dev(lse), P, rank, s_l, Hq, Hkv, d, _dtype(q_shards[0]),
+          _default_scale(d, scale), int(causal), cu, nd, _stream())
+    return lse

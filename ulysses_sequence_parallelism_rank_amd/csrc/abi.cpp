@@ -377,6 +377,42 @@ int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards, c
 //   dK, dV accumulators        2 x [s, Hkv/P, d]         fp32
 //   dK, dV of the rank         2 x [s, Hkv/P, d]         element type
 
+int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards, const void* const* v_shards,
+                    void* const* o_shards, float* lse, int P, int rank, int64_t s_l, int Hq, int Hkv, int d,
+                    int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs, void* stream) {
+  if (!q_shards || !k_shards || !v_shards || !o_shards || !lse) return ULY_ERR_NULL;
+  int st = check_ranks(P, rank, s_l, Hq);
+  if (st != ULY_OK) return st;
+  if (Hkv < 1 || Hkv % P != 0 || Hq % Hkv != 0) return ULY_ERR_SHAPE;
+  st = check_dtype_dim(dtype, d);
+  if (st != ULY_OK) return st;
+  if (dtype != ULY_BF16 || s_l % 128 != 0) return ULY_ERR_UNSUPPORTED;
+  const int64_t s = (int64_t)P * s_l;
+  if (s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
+  if (cu_seqlens != nullptr && n_docs < 1) return ULY_ERR_SHAPE;
+  if (!aligned16(lse)) return ULY_ERR_ALIGN;
+  const int Hq_l = Hq / P, Hkv_l = Hkv / P;
+  ShardSrc src{};
+  for (int p = 0; p < P; ++p) {
+    const void* ptrs[4] = {q_shards[p], k_shards[p], v_shards[p], o_shards[p]};
+    for (const void* x : ptrs) {
+      if (!x) return ULY_ERR_NULL;
+      if (!aligned16(x)) return ULY_ERR_ALIGN;
+    }
+    // the rank's head 0 in each shard (bf16 elements)
+    src.q[p] = static_cast<const uint16_t*>(q_shards[p]) + (int64_t)rank * Hq_l * d;
+    src.k[p] = static_cast<const uint16_t*>(k_shards[p]) + (int64_t)rank * Hkv_l * d;
+    src.v[p] = static_cast<const uint16_t*>(v_shards[p]) + (int64_t)rank * Hkv_l * d;
+    src.o[p] = static_cast<uint16_t*>(o_shards[p]) + (int64_t)rank * Hq_l * d;
+  }
+  src.s_l = s_l;
+  AttnArgs a = make_args(s, Hq_l, Hkv_l, d, scale, causal, cu_seqlens, n_docs);
+  a.q_row = (int64_t)Hq * d;  // rows of the sequence shards hold every head
+  a.kv_row = (int64_t)Hkv * d;
+  a.lse_out = lse;
+  return hip_status(launch_attn_fwd_bf16_shards(a, src, d, as_stream(stream)));
+}
+
 size_t attn_bwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int d, int dtype,
                                         int heads_per_chunk) {
   if (P < 1 || s_l < 1 || Hq < 1 || Hkv < 1 || d < 1 || heads_per_chunk < 1) return 0;

@@ -36,7 +36,7 @@ namespace {
 constexpr float kTau = 8.0f;
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc src) {
   constexpr int BM = 128, BN = 64, DT = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
@@ -49,9 +49,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const int mb = nmb - 1 - (int)(blockIdx.x / a.n_heads);
   const int64_t m0 = (int64_t)mb * BM;
   const int kvh = (h + a.q_off) / a.G - a.kv_off;
-  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + (int64_t)h * D;
-  const uint16_t* K = static_cast<const uint16_t*>(a.k) + (int64_t)kvh * D;
-  const uint16_t* V = static_cast<const uint16_t*>(a.v) + (int64_t)kvh * D;
+  // shard of the workgroup's rows (all in one) and the row offset of that shard
+  const int ps = (int)((uint32_t)m0 / (uint32_t)src.s_l);
+  const int64_t r_sh = (int64_t)ps * src.s_l;
+  const uint16_t* Q = static_cast<const uint16_t*>(src.q[ps]) + (int64_t)h * D;
   const float c = a.scale * kLog2e;
 
   const int64_t row = m0 + wave * 32 + l32;
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
     u32x4 v = {0, 0, 0, 0};
-    if (row < s) v = *reinterpret_cast<const u32x4*>(Q + row * a.q_row + 16 * t + 8 * hf);
+    if (row < s) v = *reinterpret_cast<const u32x4*>(Q + (row - r_sh) * a.q_row + 16 * t + 8 * hf);
     qf[t] = __builtin_bit_cast(bf16x8, v);
   }
 
@@ -92,9 +93,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const bool wave_has_rows = wr0 < s;
   const int ntiles = kbeg < kend ? (int)((kend - kbeg + BN - 1) / BN) : 0;
 
+  // tile k0 of K and V from its shard (rows past the sequence end read the shard's last row)
   auto issue_kv = [&](int64_t k0, int b) {
-    dma_tile<D, BN, 256>(K, a.kv_row, k0, s, sK[b], tid);
-    dma_tile<D, BN, 256>(V, a.kv_row, k0, s, sV[b], tid);
+    const int pk = (int)((uint32_t)k0 / (uint32_t)src.s_l);
+    const int64_t r0 = k0 - (int64_t)pk * src.s_l;
+    const uint16_t* K = static_cast<const uint16_t*>(src.k[pk]) + (int64_t)kvh * D;
+    const uint16_t* V = static_cast<const uint16_t*>(src.v[pk]) + (int64_t)kvh * D;
+    dma_tile<D, BN, 256>(K, a.kv_row, r0, src.s_l, sK[b], tid);
+    dma_tile<D, BN, 256>(V, a.kv_row, r0, src.s_l, sV[b], tid);
   };
   auto qk = [&](int b, int hh, f32x16& S) {
 #pragma unroll
@@ -192,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 
   const float lt = half_swap_sum(l);
   if (row < s) {
-    uint16_t* O = static_cast<uint16_t*>(a.out) + (int64_t)h * D;
+    uint16_t* O = static_cast<uint16_t*>(src.o[ps]) + (int64_t)h * D - r_sh * a.q_row;
     const float inv = 1.f / lt;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -208,19 +214,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 }
 
 template <int D>
-hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_fwd_t(const AttnArgs& a, const ShardSrc& src, hipStream_t stream) {
   const int64_t nmb = (a.s + 127) / 128;
   const int64_t blocks = nmb * a.n_heads;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a, src);
   return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_attn_fwd_bf16_shards(const AttnArgs& a, const ShardSrc& src, int d, hipStream_t stream) {
+  if (d == 128) return launch_fwd_t<128>(a, src, stream);
+  return launch_fwd_t<64>(a, src, stream);
+}
+
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream) {
-  if (d == 128) return launch_fwd_t<128>(a, stream);
-  return launch_fwd_t<64>(a, stream);
+  ShardSrc src{};
+  src.q[0] = a.q;
+  src.k[0] = a.k;
+  src.v[0] = a.v;
+  src.o[0] = a.out;
+  src.s_l = a.s;
+  return launch_attn_fwd_bf16_shards(a, src, d, stream);
 }
 
 }  // namespace uly

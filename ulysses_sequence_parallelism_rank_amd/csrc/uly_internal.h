@@ -57,7 +57,22 @@ hipError_t launch_pack(const ShardPtrs& src, void* out, int P, int64_t s_l, int6
 hipError_t launch_unpack(const void* in, const ShardPtrs& dst, int P, int64_t s_l, int64_t row_bytes,
                          int64_t off_bytes, int64_t run_bytes, hipStream_t stream);
 
+// Where the forward kernel finds Q, K, V rows and writes O rows: row r of the sequence
+// lives in shard r / s_l at row r % s_l (row strides q_row / kv_row of AttnArgs, the
+// launch's head 0 at the table entry). One packed [s, H, d] buffer is the case of one
+// shard with s_l = s; the sequence shards of the ranks are the case of P shards (every
+// workgroup's 128 rows and every 64-key tile must then lie in one shard: s_l % 128 == 0).
+struct ShardSrc {
+  const void* q[ULY_MAX_RANKS];
+  const void* k[ULY_MAX_RANKS];
+  const void* v[ULY_MAX_RANKS];
+  void* o[ULY_MAX_RANKS];
+  int64_t s_l;
+};
+
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t stream);
+// the bf16 forward reading from / writing to shards (a.q/k/v/out are ignored)
+hipError_t launch_attn_fwd_bf16_shards(const AttnArgs& a, const ShardSrc& src, int d, hipStream_t stream);
 hipError_t launch_bwd_preprocess(const AttnArgs& a, int d, int dtype, hipStream_t stream);
 hipError_t launch_attn_dkdv_bf16(const AttnArgs& a, int d, hipStream_t stream);
 hipError_t launch_attn_dq_bf16(const AttnArgs& a, int d, hipStream_t stream);
