@@ -16,8 +16,9 @@ attn_fwd_chunked then attn_bwd_chunked (--forward-only: the forward alone) with
 --heads-per-chunk q heads per chunk, and reports the workspace bytes beside the unchunked
 intermediates.
 
---forward-only times the forward half alone (pack Q/K/V, forward, unpack O); with --fused
-it times attn_fwd_shards instead, the forward reading and writing the shards directly.
+--forward-only times the forward half alone (pack Q/K/V, forward, unpack O); --fused
+replaces the permutes and head-shard buffers by attn_fwd_shards / attn_bwd_shards, which
+read and write the sequence shards directly.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                        [--heads-per-chunk U] [--forward-only [--fused]]
@@ -108,7 +109,7 @@ class Phases:
         return {k: v / steps for k, v in tot.items()}
 
 
-def run_training_share(cfg, steps, warmup, cu_dev):
+def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
     _, sh = make_inputs(cfg)
     rank = 0
     s, Hq_l, Hkv_l, d = cfg.s, cfg.Hq_l, cfg.Hkv_l, cfg.d
@@ -130,7 +131,16 @@ def run_training_share(cfg, steps, warmup, cu_dev):
     dv_sh = [torch.empty_like(t) for t in sh["v"]]
     ph = Phases()
 
+    def step_fused(rec):
+        ph.run("attn_fwd_shards", lambda: U.attn_fwd_shards(sh["q"], sh["k"], sh["v"], o_sh, rank, cfg.scale,
+                                                            cfg.causal, cu_dev, lse=lse), rec)
+        ph.run("attn_bwd_shards", lambda: U.attn_bwd_shards(sh["q"], sh["k"], sh["v"], o_sh, lse, sh["do"], dq_sh,
+                                                            dk_sh, dv_sh, rank, cfg.scale, cfg.causal, cu_dev,
+                                                            workspace=ws), rec)
+
     def step(rec):
+        if fused:
+            return step_fused(rec)
         ph.run("pack_qkv", lambda: (U.ulysses_pack(sh["q"], rank, q), U.ulysses_pack(sh["k"], rank, k),
                                     U.ulysses_pack(sh["v"], rank, v)), rec)
         ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse), rec)
@@ -247,7 +257,8 @@ def main():
     ap.add_argument("--forward-only", action="store_true",
                     help="time the forward half of the path alone (UPipe workload: the chunked forward)")
     ap.add_argument("--fused", action="store_true",
-                    help="with --forward-only: attn_fwd_shards, reading and writing the sequence shards directly")
+                    help="attn_fwd_shards / attn_bwd_shards, reading and writing the sequence shards directly "
+                         "(no head-shard buffers, no separate permutes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy (ulysses_pack with one rank) and exit; "
@@ -284,7 +295,7 @@ def main():
                 "unpack_o": ("hbm", 2.0 * cfg.s * Hq_l * d * e)}
         flops = fw
     elif not chunked:
-        wall, ph = run_training_share(cfg, args.steps, args.warmup, cu_dev)
+        wall, ph = run_training_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
         flops = 14.0 * d * pairs * Hq_l
         kern = {
             "attn_fwd": ("mfma", 4.0 * d * pairs * Hq_l),
@@ -295,6 +306,9 @@ def main():
             "pack_do": ("hbm", 2.0 * cfg.s * Hq_l * d * e),
             "bwd_preprocess": ("hbm", 2.0 * cfg.s * Hq_l * d * e + 4.0 * cfg.s * Hq_l),
             "unpack_grads": ("hbm", 2.0 * cfg.s * (Hq_l + 2 * Hkv_l) * d * e),
+            # the fused calls, timed whole (attn_bwd_shards: preprocess, dK/dV and dQ)
+            "attn_fwd_shards": ("mfma", 4.0 * d * pairs * Hq_l),
+            "attn_bwd_shards": ("mfma", 10.0 * d * pairs * Hq_l),
         }
     else:
         wall, ph, ws_bytes = run_upipe(cfg, args.steps, args.warmup, args.heads_per_chunk, args.forward_only)
@@ -321,12 +335,12 @@ def main():
     roof["traffic"] = read_traffic(dom, args.workload)
 
     attn_ms = sum(ph.get(k, 0.0) for k in ("attn_fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "attn_fwd_chunked",
-                                           "attn_bwd_chunked", "attn_fwd_shards"))
+                                           "attn_bwd_chunked", "attn_fwd_shards", "attn_bwd_shards"))
     perm_ms = sum(ph.get(k, 0.0) for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads"))
     perm_bytes = sum(kern[k][1] for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads") if k in ph)
     value = flops / wall / 1e12
     out = {
-        "metric": METRIC if args.workload == "qwen_64k" and not args.forward_only else
+        "metric": METRIC if args.workload == "qwen_64k" and not args.forward_only and not args.fused else
         f"{METRIC} [workload {args.workload}{', forward only' if args.forward_only else ''}"
         f"{', fused exchange' if args.fused else ''}]",
         "value": round(value, 2),

@@ -189,6 +189,30 @@ int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards,
                     void* stream);
 
 /* ---------------------------------------------------------------------------
+ * attn_bwd_shards -- the backward of rank `rank` with the exchange folded in, as
+ * attn_fwd_shards is for the forward (same passage: in training the backward repeats the
+ * two all-to-alls for the gradients). The kernels read Q, K, V, O and dO of the rank's
+ * heads straight from the sequence shards and write dQ, dK and dV straight into the
+ * rank's head slices of the gradient shards. Results are bitwise those of ulysses_pack +
+ * attn_bwd + ulysses_unpack.
+ *   q_shards / o_shards / do_shards / dq_shards : host arrays of P device pointers
+ *                        [s_l, Hq, d] (global Hq); o and lse as written by the forward
+ *   k_shards / v_shards / dk_shards / dv_shards : host arrays of P device pointers
+ *                        [s_l, Hkv, d]
+ *   lse : device fp32 [Hq/P, s]
+ *   workspace : delta, attn_bwd_workspace_bytes(P * s_l, Hq / P) bytes; NULL -> size
+ *               query into *workspace_bytes as for attn_bwd.
+ * bf16 only and s_l a multiple of 128 (ULY_ERR_UNSUPPORTED otherwise); other errors as
+ * for attn_bwd_chunked.
+ * ------------------------------------------------------------------------- */
+int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards,
+                    const void* const* v_shards, const void* const* o_shards, const float* lse,
+                    const void* const* do_shards, void* const* dq_shards, void* const* dk_shards,
+                    void* const* dv_shards, int P, int rank, int64_t s_l, int Hq, int Hkv, int d,
+                    int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,
+                    void* workspace, size_t* workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * attn_bwd_chunked -- the backward of the UPipe schedule for rank `rank` (same passage
  * as attn_fwd_chunked: only some heads are resident at a time, which matters most in
  * training). For each chunk of `heads_per_chunk` local q heads: pack the chunk's Q, O and

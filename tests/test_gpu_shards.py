@@ -1,10 +1,11 @@
-"""GPU parity of attn_fwd_shards: the forward that reads the rank's heads straight from the
-sequence shards and writes O straight into the rank's head slice of the output shards.
+"""GPU parity of attn_fwd_shards / attn_bwd_shards: forward and backward reading the rank's
+heads straight from the sequence shards and writing O (dQ, dK, dV) straight into the rank's
+head slice of the output shards.
 
-It runs the same per-row arithmetic as ulysses_pack -> attn_fwd -> ulysses_unpack, only
-with other addresses, so O and LSE must be bitwise equal to that path; heads of other
-ranks in the output shards must be left untouched; and the result is held to the oracle on
-the unsharded tensors at small sizes."""
+They run the same per-row arithmetic as ulysses_pack -> attn_fwd / attn_bwd ->
+ulysses_unpack, only with other addresses, so every output must be bitwise equal to that
+path; heads of other ranks in the output shards must be left untouched; and the results
+are held to the oracle on the unsharded tensors at small sizes."""
 import numpy as np
 import pytest
 import torch
@@ -63,6 +64,55 @@ def test_shards_equal_packed_path(P, s_l, Hq, Hkv, d, rank, causal, cu):
     compare("shards LSE", lse.cpu().numpy(), wl, max_abs=LSE_ABS, rel_fro=1e-4)
 
 
+def _packed_bwd(dev, o_sh, lse, rank, scale, causal, cu_dev):
+    q, k, v, o, g = (U.ulysses_pack(x, rank) for x in (dev["q"], dev["k"], dev["v"], o_sh, dev["do"]))
+    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, g, scale, causal, cu_dev)
+    out = {}
+    for n, y, like in (("dq", dq, dev["q"]), ("dk", dk, dev["k"]), ("dv", dv, dev["v"])):
+        out[n] = [torch.full_like(t, 3.0) for t in like]
+        U.ulysses_unpack(y, rank, out[n])
+    return out
+
+
+@pytest.mark.parametrize("P,s_l,Hq,Hkv,d,rank,causal,cu", CASES)
+def test_bwd_shards_equal_packed_path(P, s_l, Hq, Hkv, d, rank, causal, cu):
+    print(f"case P={P} s_l={s_l} Hq={Hq} Hkv={Hkv} d={d} rank={rank} causal={causal} cu={cu is not None}",
+          flush=True)
+    cfg = W.Config("shards_bwd", P=P, s_l=s_l, Hq=Hq, Hkv=Hkv, d=d, dtype="bf16", causal=causal)
+    bits = {n: W.gen_global(cfg, n, seed=23) for n in ("q", "k", "v", "do")}
+    dev = {n: [to_dev(b, "bf16") for b in W.shards_of(bits[n], P)] for n in bits}
+    cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    o_sh, lse = _packed_path(dev, rank, cfg.scale, causal, cu_dev)
+    want = _packed_bwd(dev, o_sh, lse, rank, cfg.scale, causal, cu_dev)
+    got = {n: [torch.full_like(t, 3.0) for t in want[n]] for n in want}
+    U.attn_bwd_shards(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], got["dq"], got["dk"], got["dv"], rank,
+                      cfg.scale, causal, cu_dev)
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv"):
+        for a, b in zip(got[n], want[n]):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), n
+    f = {n: W.bits_to_f64(W.head_slice(bits[n], P, rank), "bf16") for n in bits}
+    wq, wk, wv = OA.backward(f["q"], f["k"], f["v"], f["do"], cfg.scale, causal, cu)
+    for n, w, H in (("dq", wq, Hq), ("dk", wk, Hkv), ("dv", wv, Hkv)):
+        Hl = H // P
+        compare(f"shards {n}", dev_to_f64(torch.cat(got[n], 0)[:, rank * Hl:(rank + 1) * Hl]), w, bf16=True)
+
+
+def test_bwd_shards_workspace():
+    """A delta workspace one byte short is rejected before any launch."""
+    cfg = W.Config("shards_ws", P=2, s_l=128, Hq=4, Hkv=2, d=128, dtype="bf16")
+    dev = {n: [to_dev(b, "bf16") for b in W.shards_of(W.gen_global(cfg, n, seed=4), cfg.P)]
+           for n in ("q", "k", "v", "do")}
+    o_sh, lse = _packed_path(dev, 1, cfg.scale, True, None)
+    outs = [[torch.zeros_like(t) for t in dev[n]] for n in ("q", "k", "v")]
+    need = U.attn_bwd_workspace_bytes(cfg.s, cfg.Hq_l)
+    short = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(U.UlyssesError):
+        U.attn_bwd_shards(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], *outs, 1, workspace=short)
+    torch.cuda.synchronize()
+    assert all(not t.float().abs().sum().item() for x in outs for t in x)
+
+
 def test_shards_rejects_unsupported():
     """s_l not a multiple of 128 and fp32 are refused before any launch."""
     cfg = W.Config("shards_bad", P=2, s_l=96, Hq=4, Hkv=2, d=128, dtype="bf16")
@@ -96,3 +146,22 @@ def test_shards_qwen_64k_share(rank):
     for a, b in zip(o_sh, want_o):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(lse, want_lse)
+
+
+@pytest.mark.timeout(300)
+def test_bwd_shards_qwen_64k_share():
+    """Backward of the 64K headline share (rank 2): bitwise equal to the packed path."""
+    cfg = W.CONFIGS["qwen_64k"]
+    rank = 2
+    print("generating qwen_64k shards", flush=True)
+    dev = {n: [to_dev(W.gen_rows(cfg, n, p * cfg.s_l, (p + 1) * cfg.s_l), "bf16") for p in range(cfg.P)]
+           for n in ("q", "k", "v", "do")}
+    o_sh, lse = _packed_path(dev, rank, cfg.scale, True, None)
+    want = _packed_bwd(dev, o_sh, lse, rank, cfg.scale, True, None)
+    got = {n: [torch.full_like(t, 3.0) for t in want[n]] for n in want}
+    U.attn_bwd_shards(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], got["dq"], got["dk"], got["dv"], rank,
+                      cfg.scale, True)
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv"):
+        for a, b in zip(got[n], want[n]):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), n

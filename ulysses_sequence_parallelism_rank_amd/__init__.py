@@ -10,7 +10,7 @@ The names follow the C ABI in include/ulysses.h:
   attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq -- the phases of attn_bwd
   attn_fwd_chunked                    -- the UPipe headwise-chunked forward
   attn_bwd_chunked                    -- its backward
-  attn_fwd_shards                     -- the forward reading and writing the sequence shards
+  attn_fwd_shards, attn_bwd_shards    -- forward / backward reading and writing the sequence shards
 """
 from __future__ import annotations
 
@@ -56,6 +56,8 @@ SIGNATURES = {
     "attn_bwd_chunked_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
     "attn_fwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                _i32, _vp, _i32, _vp]),
+    "attn_bwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vpp, _vpp, _vpp, _vpp, _i32, _i32, _i64, _i32,
+                               _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _szp, _vp]),
 }
 
 
@@ -277,3 +279,23 @@ def attn_fwd_shards(q_shards, k_shards, v_shards, o_shards, rank, scale=None, ca
     _call("attn_fwd_shards", qp, kp, vp, op, _dev(lse), P, rank, s_l, Hq, Hkv, d, _dtype(q_shards[0]),
           _default_scale(d, scale), int(causal), cu, nd, _stream())
     return lse
+
+
+def attn_bwd_shards(q_shards, k_shards, v_shards, o_shards, lse, do_shards, dq_shards, dk_shards, dv_shards,
+                    rank, scale=None, causal=True, cu_seqlens=None, workspace=None):
+    """Backward of rank `rank` straight from the sequence shards into head slice `rank` of
+    the dq / dk / dv shards."""
+    P = len(q_shards)
+    s_l, Hq, d = q_shards[0].shape
+    Hkv = k_shards[0].shape[1]
+    need = attn_bwd_workspace_bytes(P * s_l, Hq // P)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_shards[0].device)
+    cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    keep = [_ptrs(x) for x in (q_shards, k_shards, v_shards, o_shards, do_shards, dq_shards, dk_shards, dv_shards)]
+    qp, kp, vp, op, gp, dqp, dkp, dvp = (k[0] for k in keep)
+    cu, nd = _cu(cu_seqlens)
+    _call("attn_bwd_shards", qp, kp, vp, op, _dev(lse), gp, dqp, dkp, dvp, P, rank, s_l, Hq, Hkv, d,
+          _dtype(q_shards[0]), _default_scale(d, scale), int(causal), cu, nd, _dev(workspace), ctypes.byref(cap),
+          _stream())
+    return dq_shards, dk_shards, dv_shards

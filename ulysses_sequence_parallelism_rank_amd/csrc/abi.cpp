@@ -413,6 +413,69 @@ int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards, co
   return hip_status(launch_attn_fwd_bf16_shards(a, src, d, as_stream(stream)));
 }
 
+int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards, const void* const* v_shards,
+                    const void* const* o_shards, const float* lse, const void* const* do_shards,
+                    void* const* dq_shards, void* const* dk_shards, void* const* dv_shards, int P, int rank,
+                    int64_t s_l, int Hq, int Hkv, int d, int dtype, float scale, int causal,
+                    const int32_t* cu_seqlens, int n_docs, void* workspace, size_t* workspace_bytes,
+                    void* stream) {
+  if (!q_shards || !k_shards || !v_shards || !o_shards || !do_shards || !dq_shards || !dk_shards || !dv_shards)
+    return ULY_ERR_NULL;
+  int st = check_ranks(P, rank, s_l, Hq);
+  if (st != ULY_OK) return st;
+  if (Hkv < 1 || Hkv % P != 0 || Hq % Hkv != 0) return ULY_ERR_SHAPE;
+  st = check_dtype_dim(dtype, d);
+  if (st != ULY_OK) return st;
+  if (dtype != ULY_BF16 || s_l % 128 != 0) return ULY_ERR_UNSUPPORTED;
+  const int64_t s = (int64_t)P * s_l;
+  if (s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
+  if (cu_seqlens != nullptr && n_docs < 1) return ULY_ERR_SHAPE;
+  const int Hq_l = Hq / P, Hkv_l = Hkv / P;
+  const size_t need = attn_bwd_workspace_bytes(s, Hq_l);
+  if (workspace == nullptr) {
+    if (!workspace_bytes) return ULY_ERR_NULL;
+    *workspace_bytes = need;
+    return ULY_OK;
+  }
+  if (workspace_bytes && *workspace_bytes < need) return ULY_ERR_WORKSPACE;
+  if (!lse) return ULY_ERR_NULL;
+  if (!aligned16(lse) || !aligned16(workspace)) return ULY_ERR_ALIGN;
+  BwdSrc src{};
+  const int64_t qo = (int64_t)rank * Hq_l * d, kvo = (int64_t)rank * Hkv_l * d;  // bf16 elements
+  for (int p = 0; p < P; ++p) {
+    const void* ptrs[8] = {q_shards[p], k_shards[p], v_shards[p], o_shards[p], do_shards[p],
+                           dq_shards[p], dk_shards[p], dv_shards[p]};
+    for (const void* x : ptrs) {
+      if (!x) return ULY_ERR_NULL;
+      if (!aligned16(x)) return ULY_ERR_ALIGN;
+    }
+    src.q.p[p] = static_cast<const uint16_t*>(q_shards[p]) + qo;
+    src.o.p[p] = static_cast<const uint16_t*>(o_shards[p]) + qo;
+    src.g.p[p] = static_cast<const uint16_t*>(do_shards[p]) + qo;
+    src.dq.p[p] = static_cast<const uint16_t*>(dq_shards[p]) + qo;
+    src.k.p[p] = static_cast<const uint16_t*>(k_shards[p]) + kvo;
+    src.v.p[p] = static_cast<const uint16_t*>(v_shards[p]) + kvo;
+    src.dk.p[p] = static_cast<const uint16_t*>(dk_shards[p]) + kvo;
+    src.dv.p[p] = static_cast<const uint16_t*>(dv_shards[p]) + kvo;
+  }
+  src.s_l = s_l;
+  float* delta = static_cast<float*>(workspace);
+  AttnArgs a = make_args(s, Hq_l, Hkv_l, d, scale, causal, cu_seqlens, n_docs);
+  a.q_row = (int64_t)Hq * d;  // rows of the sequence shards hold every head
+  a.kv_row = (int64_t)Hkv * d;
+  a.dkv_row = (int64_t)Hkv * d;
+  a.lse_in = lse;
+  a.delta = delta;
+  AttnArgs pre = a;
+  pre.lse_out = delta;
+  hipStream_t strm = as_stream(stream);
+  hipError_t err;
+  if ((err = launch_bwd_preprocess_bf16_shards(pre, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
+  if ((err = launch_attn_dkdv_bf16_shards(a, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
+  if ((err = launch_attn_dq_bf16_shards(a, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
+  return ULY_OK;
+}
+
 size_t attn_bwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int d, int dtype,
                                         int heads_per_chunk) {
   if (P < 1 || s_l < 1 || Hq < 1 || Hkv < 1 || d < 1 || heads_per_chunk < 1) return 0;

@@ -33,7 +33,7 @@ constexpr int kWaves = 4;
 // ---------------------------------------------------------------------------------------
 // delta[h, i] = sum_x dO[i, h, x] * O[i, h, x] (fp32). TPR threads per (row, head), 16 B each.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a, Shards o_sh, Shards g_sh, int64_t s_l) {
   constexpr int TPR = D * (int)sizeof(T) / 16;
   constexpr int EPV = 16 / (int)sizeof(T);
   const int64_t idx = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
@@ -42,9 +42,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
   const int h = (int)(idx % a.n_heads);
   float acc = 0.f;
   if (row < a.s) {
-    const int64_t off = row * a.q_row + (int64_t)h * D + part * EPV;
-    const u32x4 ov = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.o) + off);
-    const u32x4 gv = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dout) + off);
+    const int ps = (int)((uint32_t)row / (uint32_t)s_l);
+    const int64_t off = (row - (int64_t)ps * s_l) * a.q_row + (int64_t)h * D + part * EPV;
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(static_cast<const T*>(o_sh.p[ps]) + off);
+    const u32x4 gv = *reinterpret_cast<const u32x4*>(static_cast<const T*>(g_sh.p[ps]) + off);
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -73,7 +74,8 @@ struct DqCfg {
 };
 
 template <int D, int RB, int KB>
-__global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Shards q_sh, Shards g_sh, Shards k_sh,
+                                                                  Shards v_sh, Shards dq_sh, int64_t s_l) {
   using C = DqCfg<D, RB, KB>;
   constexpr int BM = C::BM, BN = C::BN, DT = C::DT, DB = C::DB;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
@@ -87,10 +89,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a) {
   const int mb = nmb - 1 - (int)(blockIdx.x / a.n_heads);
   const int64_t m0 = (int64_t)mb * BM;
   const int kvh = (h + a.q_off) / a.G - a.kv_off;
-  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + (int64_t)h * D;
-  const uint16_t* dO = static_cast<const uint16_t*>(a.dout) + (int64_t)h * D;
-  const uint16_t* K = static_cast<const uint16_t*>(a.k) + (int64_t)kvh * D;
-  const uint16_t* V = static_cast<const uint16_t*>(a.v) + (int64_t)kvh * D;
+  // shard of the workgroup's rows (all in one); Q, dO and dQ addressed from its first row
+  const int ps = (int)((uint32_t)m0 / (uint32_t)s_l);
+  const int64_t r_sh = (int64_t)ps * s_l;
+  const uint16_t* Q = static_cast<const uint16_t*>(q_sh.p[ps]) + (int64_t)h * D - r_sh * a.q_row;
+  const uint16_t* dO = static_cast<const uint16_t*>(g_sh.p[ps]) + (int64_t)h * D - r_sh * a.q_row;
   const float c = a.scale * kLog2e;
 
   int64_t row[RB], lo[RB], hi[RB];
@@ -144,9 +147,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a) {
   // the SIMD issues MFMAs; within a wave the two 32-key halves of a tile run one after the
   // other: S/dP, dS, dQ.
   static_assert(RB == 1 && KB == 2, "the tile is two 32-key halves of one 32-row wave tile");
+  // key tile k0 from its shard (rows past the sequence end read the shard's last row)
   auto issue_kv = [&](int64_t k0, int b) {
-    dma_tile<D, BN, kWaves * 64>(K, a.kv_row, k0, s, sK[b], tid);
-    dma_tile<D, BN, kWaves * 64>(V, a.kv_row, k0, s, sV[b], tid);
+    const int pk = (int)((uint32_t)k0 / (uint32_t)s_l);
+    const int64_t r0 = k0 - (int64_t)pk * s_l;
+    const uint16_t* K = static_cast<const uint16_t*>(k_sh.p[pk]) + (int64_t)kvh * D;
+    const uint16_t* V = static_cast<const uint16_t*>(v_sh.p[pk]) + (int64_t)kvh * D;
+    dma_tile<D, BN, kWaves * 64>(K, a.kv_row, r0, s_l, sK[b], tid);
+    dma_tile<D, BN, kWaves * 64>(V, a.kv_row, r0, s_l, sV[b], tid);
   };
   auto load_sdp = [&](int b, int kb, int t, bf16x8& kx, bf16x8& vx) {
     kx = *reinterpret_cast<const bf16x8*>(&sK[b][tile_off<D>(kb * 32 + l32, 16 * t + 8 * hf)]);
@@ -235,7 +243,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a) {
   }
 
   const int rb = 0;
-  uint16_t* dQ = static_cast<uint16_t*>(a.out) + (int64_t)h * D;
+  uint16_t* dQ = static_cast<uint16_t*>(const_cast<void*>(dq_sh.p[ps])) + (int64_t)h * D - r_sh * a.q_row;
   if (row[rb] < s) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -267,7 +275,8 @@ struct DkvSplitCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Shards q_sh, Shards g_sh, Shards k_sh,
+                                                                 Shards v_sh, Shards dk_sh, Shards dv_sh, int64_t s_l) {
   using C = DkvSplitCfg<D>;
   constexpr int BNK = C::BNK, BMQ = C::BMQ, DT = C::DT, DB = C::DB;
   // per buffer: one object for the Q and dO tiles, one for the LSE and delta rows (few DMA
@@ -306,7 +315,11 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
   if (a.causal) rlo = (int32_t)key;
   if (key >= s) rhi = rlo;  // padding key: seen by no row
   const uint32_t width = (uint32_t)(rhi - rlo);  // row r is seen iff (uint32)(r - rlo) < width
-  const uint16_t* KV = static_cast<const uint16_t*>(role == 0 ? a.k : a.v) + (int64_t)kvh * D;
+  // shard of the workgroup's keys (all in one); K/V rows and dK/dV addressed from its first row
+  const int pk = (int)((uint32_t)n0 / (uint32_t)s_l);
+  const int64_t k_sh0 = (int64_t)pk * s_l;
+  const uint16_t* KV = static_cast<const uint16_t*>(role == 0 ? k_sh.p[pk] : v_sh.p[pk]) + (int64_t)kvh * D -
+                       k_sh0 * a.kv_row;
   bf16x8 kv[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
@@ -336,8 +349,10 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
     const int hq = kh.j0 + hi;
     const int64_t q0 = tile_row0(tile);
     const int t2 = tid - 256;
-    dma_tile<D, BMQ, 256>(static_cast<const uint16_t*>(a.q) + (int64_t)hq * D, a.q_row, q0, s, b.q, t2);
-    dma_tile<D, BMQ, 256>(static_cast<const uint16_t*>(a.dout) + (int64_t)hq * D, a.q_row, q0, s, b.g, t2);
+    const int pq = (int)((uint32_t)q0 / (uint32_t)s_l);
+    const int64_t r0 = q0 - (int64_t)pq * s_l;
+    dma_tile<D, BMQ, 256>(static_cast<const uint16_t*>(q_sh.p[pq]) + (int64_t)hq * D, a.q_row, r0, s_l, b.q, t2);
+    dma_tile<D, BMQ, 256>(static_cast<const uint16_t*>(g_sh.p[pq]) + (int64_t)hq * D, a.q_row, r0, s_l, b.g, t2);
     // one fp32 per lane: lane i lands at b.l[i] (wave 4) or b.d[i] (wave 5)
     int64_t qr = q0 + (lane < BMQ ? lane : BMQ - 1);
     qr = qr < s ? qr : s - 1;
@@ -502,7 +517,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
           *reinterpret_cast<f32x4*>(accp + db * 32 + 8 * jj + 4 * hf) =
               f32x4{acc[db][4 * jj + 0], acc[db][4 * jj + 1], acc[db][4 * jj + 2], acc[db][4 * jj + 3]};
     } else {
-      uint16_t* out = static_cast<uint16_t*>(is_k ? a.out_k : a.out_v) + off;
+      uint16_t* out = static_cast<uint16_t*>(const_cast<void*>(is_k ? dk_sh.p[pk] : dv_sh.p[pk])) + off -
+                      k_sh0 * a.dkv_row;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -517,48 +533,81 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a) {
 }
 
 template <typename T, int D>
-hipError_t launch_pre_t(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_pre_t(const AttnArgs& a, const BwdSrc& src, hipStream_t stream) {
   constexpr int TPR = D * (int)sizeof(T) / 16;
   const int64_t items = a.s * a.n_heads;
   const int64_t blocks = (items + (256 / TPR) - 1) / (256 / TPR);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a, src.o, src.g, src.s_l);
   return hipGetLastError();
 }
 
 template <int D, int RB, int KB>
-hipError_t launch_dq_t(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_dq_t(const AttnArgs& a, const BwdSrc& src, hipStream_t stream) {
   using C = DqCfg<D, RB, KB>;
   const int64_t blocks = (a.s + C::BM - 1) / C::BM * a.n_heads;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_dq_kernel<D, RB, KB>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((attn_dq_kernel<D, RB, KB>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a, src.q,
+                     src.g, src.k, src.v, src.dq, src.s_l);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_dkdv_split_t(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_dkdv_split_t(const AttnArgs& a, const BwdSrc& src, hipStream_t stream) {
   using C = DkvSplitCfg<D>;
   const int64_t blocks = (a.s + C::BNK - 1) / C::BNK * a.n_kv;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_dkdv_split_kernel<D>), dim3((unsigned)blocks), dim3(C::NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((attn_dkdv_split_kernel<D>), dim3((unsigned)blocks), dim3(C::NW * 64), 0, stream, a, src.q,
+                     src.g, src.k, src.v, src.dk, src.dv, src.s_l);
   return hipGetLastError();
 }
 
 }  // namespace
 
+namespace {
+// the packed head-shard buffers of AttnArgs as one-shard tables
+BwdSrc packed_src(const AttnArgs& a) {
+  BwdSrc src{};
+  src.q.p[0] = a.q;
+  src.k.p[0] = a.k;
+  src.v.p[0] = a.v;
+  src.o.p[0] = a.o;
+  src.g.p[0] = a.dout;
+  src.dq.p[0] = a.out;
+  src.dk.p[0] = a.out_k;
+  src.dv.p[0] = a.out_v;
+  src.s_l = a.s;
+  return src;
+}
+}  // namespace
+
 hipError_t launch_bwd_preprocess(const AttnArgs& a, int d, int dtype, hipStream_t stream) {
-  if (dtype == ULY_BF16) return d == 128 ? launch_pre_t<uint16_t, 128>(a, stream) : launch_pre_t<uint16_t, 64>(a, stream);
-  return d == 128 ? launch_pre_t<float, 128>(a, stream) : launch_pre_t<float, 64>(a, stream);
+  const BwdSrc src = packed_src(a);
+  if (dtype == ULY_BF16)
+    return d == 128 ? launch_pre_t<uint16_t, 128>(a, src, stream) : launch_pre_t<uint16_t, 64>(a, src, stream);
+  return d == 128 ? launch_pre_t<float, 128>(a, src, stream) : launch_pre_t<float, 64>(a, src, stream);
 }
 
 hipError_t launch_attn_dq_bf16(const AttnArgs& a, int d, hipStream_t stream) {
-  if (d == 128) return launch_dq_t<128, 1, 2>(a, stream);
-  return launch_dq_t<64, 1, 2>(a, stream);
+  return launch_attn_dq_bf16_shards(a, packed_src(a), d, stream);
 }
 
 hipError_t launch_attn_dkdv_bf16(const AttnArgs& a, int d, hipStream_t stream) {
-  if (d == 128) return launch_dkdv_split_t<128>(a, stream);
-  return launch_dkdv_split_t<64>(a, stream);
+  return launch_attn_dkdv_bf16_shards(a, packed_src(a), d, stream);
+}
+
+hipError_t launch_bwd_preprocess_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream) {
+  return d == 128 ? launch_pre_t<uint16_t, 128>(a, src, stream) : launch_pre_t<uint16_t, 64>(a, src, stream);
+}
+
+hipError_t launch_attn_dq_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream) {
+  if (d == 128) return launch_dq_t<128, 1, 2>(a, src, stream);
+  return launch_dq_t<64, 1, 2>(a, src, stream);
+}
+
+hipError_t launch_attn_dkdv_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream) {
+  if (d == 128) return launch_dkdv_split_t<128>(a, src, stream);
+  return launch_dkdv_split_t<64>(a, src, stream);
 }
 
 }  // namespace uly

@@ -76,6 +76,22 @@ hipError_t launch_attn_fwd_bf16_shards(const AttnArgs& a, const ShardSrc& src, i
 hipError_t launch_bwd_preprocess(const AttnArgs& a, int d, int dtype, hipStream_t stream);
 hipError_t launch_attn_dkdv_bf16(const AttnArgs& a, int d, hipStream_t stream);
 hipError_t launch_attn_dq_bf16(const AttnArgs& a, int d, hipStream_t stream);
+
+// Shard tables of the backward's tensors (the layout of ShardSrc): q, k, v, o, dO read, dq,
+// dk, dv written, each at the launch's head 0; a kernel receives only the tables it uses.
+struct Shards {
+  const void* p[ULY_MAX_RANKS];
+};
+struct BwdSrc {
+  Shards q, k, v, o, g, dq, dk, dv;
+  int64_t s_l;
+};
+// the three bf16 backward phases reading / writing through shard tables (a.q, a.k, a.v, a.o,
+// a.dout, a.out, a.out_k, a.out_v are ignored); the accumulation mode of AttnArgs is not
+// supported here
+hipError_t launch_bwd_preprocess_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream);
+hipError_t launch_attn_dkdv_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream);
+hipError_t launch_attn_dq_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t stream);
 hipError_t launch_attn_dkdv_f32(const AttnArgs& a, int d, hipStream_t stream);
 hipError_t launch_attn_dq_f32(const AttnArgs& a, int d, hipStream_t stream);
