@@ -419,20 +419,33 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (r == 0) {
-        // P = exp2(S c - LSE log2e) on rows 32qb + 8(j/4) + 4hf + j%4, 0 outside [rlo, rhi)
+        // P = exp2(S c - LSE log2e) on rows 32qb + 8(j/4) + 4hf + j%4
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const f32x4 L4 = *reinterpret_cast<const f32x4*>(&buf.l[qb * 32 + 8 * jj + 4 * hf]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float p = fast_exp2(__builtin_fmaf(x[qb][4 * jj + e], c, -L4[e] * kLog2e));
-              x[qb][4 * jj + e] = (uint32_t)(qrel0 + qb * 32 + 8 * jj + e) < width ? p : 0.f;
-            }
+            for (int e = 0; e < 4; ++e) x[qb][4 * jj + e] = fast_exp2(__builtin_fmaf(x[qb][4 * jj + e], c, -L4[e] * kLog2e));
+          }
+        }
+        // 0 outside [rlo, rhi): only where some row of the tile cannot see some key of the
+        // wave (a wave-uniform branch around VALU work on P in place)
+        const int32_t qr = qrel0 - 4 * hf;
+        const bool full = (uint32_t)qr < width && (uint32_t)(qr + BMQ - 1) < width;
+        if (__ballot(!full) != 0) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              x[qb][j] = (uint32_t)(qrel0 + qb * 32 + 8 * (j / 4) + (j % 4)) < width ? x[qb][j] : 0.f;
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
             *reinterpret_cast<f32x4*>(&sP[0][0][p_off(qb, jj)]) =
                 f32x4{x[qb][4 * jj], x[qb][4 * jj + 1], x[qb][4 * jj + 2], x[qb][4 * jj + 3]};
-          }
           op[qb][0] = pack8(x[qb], 0);
           op[qb][1] = pack8(x[qb], 1);
         }
