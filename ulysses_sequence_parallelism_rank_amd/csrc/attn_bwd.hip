@@ -170,14 +170,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
     kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0v, k1v, 0, 1, 2, 3, 4, 5, 6, 7));
     (void)unused;
   };
-  // dS of keys kb*32 + 8jj + 4hf + e (e < 4) for this lane's row; keys outside the row's
-  // range get P = 0 from an unsigned compare, so no branch surrounds the MFMAs.
-  // (MASK false: every key of the half is visible to every row of the wave)
-  auto soft4 = [&](auto MASK, int32_t krel0, int kb, int jj, const f32x16& si, const f32x16& pi, f32x4& dv) {
+  // dS of keys kb*32 + 8jj + 4hf + e (e < 4) for this lane's row, before the mask (keys
+  // outside the row's range are zeroed afterwards by an unsigned compare, so no branch
+  // surrounds the MFMAs)
+  auto soft4 = [&](int kb, int jj, const f32x16& si, const f32x16& pi, f32x4& dv) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float p = fast_exp2(__builtin_fmaf(si[4 * jj + e], c, -lse2[0]));
-      if constexpr (decltype(MASK)::value) p = (uint32_t)(krel0 + kb * 32 + 8 * jj + e) < width[0] ? p : 0.f;
+      const float p = fast_exp2(__builtin_fmaf(si[4 * jj + e], c, -lse2[0]));
       dv[e] = p * (pi[4 * jj + e] - dl[0]);
     }
   };
@@ -216,19 +215,21 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
       }
       f32x4 dv[4];
       bf16x8 dsf[2];
-      auto soft_all = [&](auto MASK) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          soft4(MASK, krel0, hh, g, sacc, pacc, dv[g]);
-          if (g & 1) dsf[g / 2] = pack8(dv[g - 1], dv[g]);
-        }
-      };
-      // the mask is applied only where some lane's row cannot see some key of the half
-      // (a wave-uniform branch around VALU work only)
+      for (int g = 0; g < 4; ++g) soft4(hh, g, sacc, pacc, dv[g]);
+      // dS is 0 outside the row's key range: applied in place, only on halves where some
+      // row of the wave cannot see some key (a wave-uniform branch around VALU work)
       const int32_t kr = krel0 - 4 * hf + hh * 32;
       const bool full = (uint32_t)kr < width[0] && (uint32_t)(kr + 31) < width[0];
-      if (__ballot(!full) != 0) soft_all(std::true_type{});
-      else soft_all(std::false_type{});
+      if (__ballot(!full) != 0) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dv[g][e] = (uint32_t)(krel0 + hh * 32 + 8 * g + e) < width[0] ? dv[g][e] : 0.f;
+      }
+      dsf[0] = pack8(dv[0], dv[1]);
+      dsf[1] = pack8(dv[2], dv[3]);
       __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
