@@ -455,9 +455,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
     auto part_b = [&](auto ROLE) {
       constexpr int r = decltype(ROLE)::value;
       // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1): products i = (qb, tt, db), their
-      // transposed operands read two products ahead (the first two before the dS work)
+      // transposed operands read three products ahead (the first three before the dS work)
       const uint16_t* ts = r == 0 ? buf.g : buf.q;
-      constexpr int NP = 4 * DB, PF = 2;
+      constexpr int NP = 4 * DB, PF = 3;
       bf16x8 ringb[PF + 1];
       auto ldb = [&](int i) { return load_tr(ts, i / (2 * DB), (i / DB) % 2, i % DB); };
 #pragma unroll

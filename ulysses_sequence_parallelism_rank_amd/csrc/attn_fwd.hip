@@ -179,14 +179,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
     bf16x8 p0[2], p1[2];
     qk(b, 0, S0);
     mask_rescale(k0, S0);
-    // raised priority from S of half 1 through the softmax of half 0: the other wave on the
-    // SIMD fills the gaps with its PV products
-    __builtin_amdgcn_s_setprio(1);
     qk(b, 1, S1);
     softmax(S0, p0);
-    __builtin_amdgcn_s_setprio(0);
     pv(b, 0, p0);
     mask_rescale(k0 + 32, S1);
+    // raised priority through the second softmax, the one no MFMA of this wave overlaps
     __builtin_amdgcn_s_setprio(1);
     softmax(S1, p1);
     __builtin_amdgcn_s_setprio(0);
