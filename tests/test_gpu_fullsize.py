@@ -19,6 +19,7 @@ import numpy as np
 import pytest
 import torch
 
+import ulysses_sequence_parallelism_rank_amd as U
 import workloads as W
 from oracle import attention as OA
 from tests.helpers import LSE_ABS, compare, dev_to_f64, sample_rows, to_dev
@@ -105,3 +106,24 @@ def test_packed_96k_share():
         if b - a <= 200:
             keys |= set(range(a, b))
     _run(cfg, 0, extra, np.array(sorted(keys)), list(zip(cu[:-1], cu[1:])))
+
+
+@pytest.mark.timeout(300)
+def test_qwen_64k_deterministic():
+    """The 64K share's forward and backward, run three times on the same inputs, give the
+    same bits every time (no atomics; every LDS tile published by a barrier after its DMA
+    landed). The race this guards against showed at this size and not at small ones."""
+    cfg = W.CONFIGS["qwen_64k"]
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    mk = lambda H: torch.randn((cfg.s, H, cfg.d), device="cuda", generator=gen).to(torch.bfloat16)
+    q, k, v, do = mk(cfg.Hq_l), mk(cfg.Hkv_l), mk(cfg.Hkv_l), mk(cfg.Hq_l)
+    runs = []
+    for _ in range(3):
+        o, lse = U.attn_fwd(q, k, v, cfg.scale, True)
+        dq, dk, dv = U.attn_bwd(q, k, v, o, lse, do, cfg.scale, True)
+        torch.cuda.synchronize()
+        runs.append((o.view(torch.int16).clone(), lse.clone(), dq.view(torch.int16).clone(),
+                     dk.view(torch.int16).clone(), dv.view(torch.int16).clone()))
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b)
