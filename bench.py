@@ -228,6 +228,29 @@ def run_upipe(cfg, steps, warmup, u, forward_only):
     return (time.perf_counter() - t0) / steps, ph.summary(steps), need
 
 
+def measured_ceilings():
+    """Practical ceilings on this GPU, beside the published peaks: back-to-back bf16 MFMAs on
+    every SIMD (uly_mfma_probe, with the sustained shader clock), and a plain 1 GiB device
+    copy (ulysses_pack with one rank) for HBM."""
+    tf, clk = U.mfma_probe()
+    n = 1 << 30
+    src = torch.empty((n // 256, 1, 128), dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    U.ulysses_pack([src], 0, dst)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        U.ulysses_pack([src], 0, dst)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 3 * 2.0 * n / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    return {"mfma_bf16_tflops": round(tf, 1), "sustained_clock_mhz": round(clk, 0) if clk else None,
+            "copy_gbs": round(gbs, 1),
+            "how": "uly_mfma_probe: 512 workgroups x 4 waves x 20000 x 4 back-to-back 32x32x16 bf16 MFMAs; "
+                   "copy: 1 GiB read + 1 GiB written by ulysses_pack with one rank"}
+
+
 def cpu_baseline(cfg):
     """The oracle, untuned, on a bounded sample of the same workload: one q head (and its kv
     head) over the first `prefix` tokens of the sequence, causal forward + backward."""
@@ -377,6 +400,10 @@ def main():
         out["workspace_bytes"] = ws_bytes
         fwd_b = 2 * cfg.s * Hq_l * d * e + 2 * cfg.s * Hkv_l * d * e
         out["unchunked_intermediate_bytes"] = int(fwd_b if args.forward_only else 2 * fwd_b + 4 * cfg.s * Hq_l)
+    ceil = measured_ceilings()
+    out["measured_ceilings"] = ceil
+    roof["frac_of_measured"] = round(roof["achieved"] / (ceil["mfma_bf16_tflops"] if bound == "mfma"
+                                                         else ceil["copy_gbs"]), 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)

@@ -243,6 +243,18 @@ int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards,
 size_t attn_bwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int d,
                                         int dtype, int heads_per_chunk);
 
+/* ---------------------------------------------------------------------------
+ * uly_mfma_probe -- measurement helper, not part of the attention path: `blocks`
+ * workgroups of 4 waves each issue `iters` x 4 back-to-back v_mfma_f32_32x32x16_bf16
+ * (32768 flops each) on independent accumulators, giving the practical bf16 matrix-core
+ * ceiling that the bench reports beside the published peak. Wave 0 of workgroup 0 writes
+ * the shader clock cycles and the 100 MHz reference-counter ticks of its loop to
+ * clocks[0], clocks[1] (device memory, 2 x uint64), hence the sustained clock. `sink`: one
+ * device float, written only in a case that does not occur (it keeps the work alive).
+ * Errors: ULY_ERR_NULL, ULY_ERR_SHAPE (iters or blocks < 1), ULY_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+int uly_mfma_probe(int iters, int blocks, float* sink, uint64_t* clocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

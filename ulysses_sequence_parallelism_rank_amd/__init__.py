@@ -56,6 +56,7 @@ SIGNATURES = {
     "attn_bwd_chunked_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
     "attn_fwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                _i32, _vp, _i32, _vp]),
+    "uly_mfma_probe": (_i32, [_i32, _i32, _vp, _vp, _vp]),
     "attn_bwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vpp, _vpp, _vpp, _vpp, _i32, _i32, _i64, _i32,
                                _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _szp, _vp]),
 }
@@ -299,3 +300,20 @@ def attn_bwd_shards(q_shards, k_shards, v_shards, o_shards, lse, do_shards, dq_s
           _dtype(q_shards[0]), _default_scale(d, scale), int(causal), cu, nd, _dev(workspace), ctypes.byref(cap),
           _stream())
     return dq_shards, dk_shards, dv_shards
+
+
+def mfma_probe(iters=20000, blocks=512):
+    """Practical bf16 MFMA ceiling and sustained clock: returns (tflops, clock_mhz), timed
+    with events on the current stream."""
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    _call("uly_mfma_probe", 2, blocks, _dev(sink), _dev(clocks), _stream())  # warm-up
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    _call("uly_mfma_probe", iters, blocks, _dev(sink), _dev(clocks), _stream())
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    cyc, ref = (int(x) for x in clocks.cpu())
+    flops = float(blocks) * 4 * iters * 4 * 32768
+    return flops / (ms * 1e-3) / 1e12, (cyc / ref * 100.0 if ref > 0 else None)

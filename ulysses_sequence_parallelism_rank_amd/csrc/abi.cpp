@@ -133,6 +133,13 @@ const char* uly_status_string(int status) {
 
 int uly_abi_version(void) { return kAbiVersion; }
 
+int uly_mfma_probe(int iters, int blocks, float* sink, uint64_t* clocks, void* stream) {
+  if (!sink || !clocks) return ULY_ERR_NULL;
+  if (iters < 1 || blocks < 1) return ULY_ERR_SHAPE;
+  return hip_status(launch_mfma_probe(iters, blocks, sink, reinterpret_cast<unsigned long long*>(clocks),
+                                      as_stream(stream)));
+}
+
 int ulysses_pack(const void* const* shards, int P, int rank, int64_t s_l, int H, int d, int dtype,
                  void* out, void* stream) {
   if (!shards || !out) return ULY_ERR_NULL;

@@ -93,6 +93,7 @@ hipError_t launch_bwd_preprocess_bf16_shards(const AttnArgs& a, const BwdSrc& sr
 hipError_t launch_attn_dkdv_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream);
 hipError_t launch_attn_dq_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t stream);
+hipError_t launch_mfma_probe(int iters, int blocks, float* sink, unsigned long long* clocks, hipStream_t stream);
 hipError_t launch_attn_dkdv_f32(const AttnArgs& a, int d, hipStream_t stream);
 hipError_t launch_attn_dq_f32(const AttnArgs& a, int d, hipStream_t stream);
 
