@@ -138,3 +138,61 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         U.attn_fwd(x, x, x)
+
+
+def test_bwd_chunked_workspace_and_rejects():
+    L = U.lib()
+    MiB = 2 ** 20
+    # the 256K UPipe share: chunk buffers, delta, fp32 dK/dV sums and the rank's dK/dV
+    assert L.attn_bwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 1) == 769 * MiB
+    assert L.attn_bwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 0) == 0
+    pp, keep = _ptr_array([FAKE] * 2)
+    need = ctypes.c_size_t(0)
+
+    def call(ws=None, cap=None, P=2, rank=0, s_l=8, Hq=8, Hkv=4, d=64, dt=0, u=1, lse=FAKE):
+        return L.attn_bwd_chunked(pp, pp, pp, pp, lse, pp, pp, pp, pp, P, rank, s_l, Hq, Hkv, d, dt, 0.1, 1,
+                                  None, 0, u, ws, cap, None)
+    assert call(cap=ctypes.byref(need)) == 0 and need.value == L.attn_bwd_chunked_workspace_bytes(2, 8, 8, 4, 64,
+                                                                                                0, 1)
+    assert call(cap=ctypes.byref(need), u=0) == 2
+    assert call(cap=ctypes.byref(need), Hkv=3) == 2
+    assert call(cap=ctypes.byref(need), rank=2) == 2
+    assert call(cap=ctypes.byref(need), d=96) == 3
+    small = ctypes.c_size_t(need.value - 256)
+    assert call(ws=FAKE, cap=ctypes.byref(small)) == 5
+    assert call(ws=FAKE, cap=ctypes.byref(need), lse=None) == 1
+    assert call(ws=MIS, cap=ctypes.byref(need)) == 4
+
+
+def test_shards_rejects():
+    L = U.lib()
+    pp, keep = _ptr_array([FAKE] * 2)
+    mp, keep2 = _ptr_array([FAKE, MIS])
+
+    def fwd(q=pp, s_l=128, Hq=8, Hkv=4, d=128, dt=0, rank=0, lse=FAKE):
+        return L.attn_fwd_shards(q, pp, pp, pp, lse, 2, rank, s_l, Hq, Hkv, d, dt, 0.1, 1, None, 0, None)
+    assert fwd(s_l=96) == 3          # a workgroup's rows must lie in one shard
+    assert fwd(dt=1, d=64) == 3      # bf16 only
+    assert fwd(d=96) == 3
+    assert fwd(Hkv=3) == 2
+    assert fwd(rank=2) == 2
+    assert fwd(lse=None) == 1
+    assert fwd(q=mp) == 4
+    need = ctypes.c_size_t(0)
+
+    def bwd(ws=None, cap=None, s_l=128, dt=0, d=128):
+        return L.attn_bwd_shards(pp, pp, pp, pp, FAKE, pp, pp, pp, pp, 2, 0, s_l, 8, 4, d, dt, 0.1, 1, None, 0,
+                                 ws, cap, None)
+    assert bwd(cap=ctypes.byref(need)) == 0 and need.value == L.attn_bwd_workspace_bytes(256, 4)
+    assert bwd(cap=ctypes.byref(need), s_l=64) == 3
+    assert bwd(cap=ctypes.byref(need), dt=1, d=64) == 3
+    small = ctypes.c_size_t(need.value - 1)
+    assert bwd(ws=FAKE, cap=ctypes.byref(small)) == 5
+    assert bwd(ws=None, cap=None) == 1
+
+
+def test_probe_rejects():
+    L = U.lib()
+    assert L.uly_mfma_probe(0, 4, FAKE, FAKE, None) == 2
+    assert L.uly_mfma_probe(4, 0, FAKE, FAKE, None) == 2
+    assert L.uly_mfma_probe(4, 4, None, FAKE, None) == 1
