@@ -275,7 +275,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="qwen_64k", choices=sorted(W.CONFIGS))
+    ap.add_argument("--workload", default="qwen_64k", choices=sorted(W.WORKLOADS))
     ap.add_argument("--heads-per-chunk", type=int, default=1)
     ap.add_argument("--forward-only", action="store_true",
                     help="time the forward half of the path alone (UPipe workload: the chunked forward)")
@@ -303,7 +303,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
         return
-    cfg = W.CONFIGS[args.workload]
+    cfg = W.WORKLOADS[args.workload]
     cu = W.cu_seqlens_for(cfg)
     cu_dev = None if cu is None else torch.from_numpy(cu).to("cuda")
     pairs = counted_pairs(cfg, cu)

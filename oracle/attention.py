@@ -14,7 +14,7 @@ What is computed, and where the pages fix it:
   * Packing for SFT (same page, TRL SFTTrainer section) concatenates documents; the
     mask keeps attention inside each document.
 
-Readings taken where the pages are silent (listed in the design doc):
+Readings taken where the pages are silent:
   * S = scale * Q K^T with scale passed in (1/sqrt(d) in every workload);
   * causal self-attention over one sequence: key j is visible to row i iff j <= i;
   * packed documents: additionally lo(i) <= j, where lo(i) is the start of the

@@ -8,7 +8,7 @@ memory held by attention intermediates. The result per head is unchanged; only
 which heads are resident at once differs. So each chunk runs the same three steps
 as the unchunked layer (pack, attention, unpack) restricted to its heads.
 
-Readings (listed in the design doc): chunks cover the rank's q heads in order, u heads
+Readings: chunks cover the rank's q heads in order, u heads
 each, the last one smaller when u does not divide H_q/P; a chunk's kv heads are
 those its q heads read (h // G). In the backward, the gradient of a kv head read by
 several chunks is the sum of the chunks' contributions (the chain rule over the heads

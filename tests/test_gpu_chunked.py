@@ -103,7 +103,7 @@ def _upipe_inputs():
     local head, k and v of local kv head 0. Generated once per module."""
     if _UPIPE:
         return _UPIPE
-    cfg = W.CONFIGS["upipe_256k"]
+    cfg = W.WORKLOADS["upipe_256k"]
     rank, P, s_l, Hl = 0, cfg.P, cfg.s_l, cfg.Hq_l
     print("generating upipe_256k inputs", flush=True)
     dev = {n: [] for n in ("q", "k", "v", "do")}

@@ -87,7 +87,7 @@ def _run(cfg, rank, extra_rows, keys, segments):
 
 @pytest.mark.timeout(600)
 def test_qwen_64k_share():
-    cfg = W.CONFIGS["qwen_64k"]
+    cfg = W.WORKLOADS["qwen_64k"]
     s = cfg.s
     keys = set(range(s - 64, s))
     for b in range(s - 1024, s, 128):
@@ -97,7 +97,7 @@ def test_qwen_64k_share():
 
 @pytest.mark.timeout(600)
 def test_packed_96k_share():
-    cfg = W.CONFIGS["packed_96k"]
+    cfg = W.WORKLOADS["packed_96k"]
     cu = [int(x) for x in W.cu_seqlens_for(cfg)]
     extra = {r for c in cu[1:-1] for r in (c - 1, c, c + 1)}
     keys = set()
@@ -113,7 +113,7 @@ def test_qwen_64k_deterministic():
     """The 64K share's forward and backward, run three times on the same inputs, give the
     same bits every time (no atomics; every LDS tile published by a barrier after its DMA
     landed). The race this guards against showed at this size and not at small ones."""
-    cfg = W.CONFIGS["qwen_64k"]
+    cfg = W.WORKLOADS["qwen_64k"]
     gen = torch.Generator(device="cuda").manual_seed(5)
     mk = lambda H: torch.randn((cfg.s, H, cfg.d), device="cuda", generator=gen).to(torch.bfloat16)
     q, k, v, do = mk(cfg.Hq_l), mk(cfg.Hkv_l), mk(cfg.Hkv_l), mk(cfg.Hq_l)

@@ -51,7 +51,7 @@ def test_pack_unpack_bit_exact(P, s_l, H, d, dtype):
 
 
 def test_headline_size_pack_unpack_bit_exact():
-    cfg = W.CONFIGS["qwen_64k"]
+    cfg = W.WORKLOADS["qwen_64k"]
     print("case qwen_64k pack/unpack rank 0", flush=True)
     for name in ("q", "k"):
         g, dev = gen_shards(cfg, name)

@@ -40,7 +40,7 @@ def _cat_heads(sh, rank, P):
 
 @pytest.mark.parametrize("name,ranks", [("tiny_f32", (0, 1)), ("qwen_8k", (0, 3))])
 def test_share_matches_unsharded_oracle(name, ranks):
-    cfg = W.CONFIGS[name]
+    cfg = W.WORKLOADS[name]
     print(f"case {name} ranks {ranks}", flush=True)
     glob, shards = {}, {}
     for n in ("q", "k", "v", "do"):

@@ -134,7 +134,7 @@ def test_shards_rejects_unsupported():
 def test_shards_qwen_64k_share(rank):
     """The 64K headline share (4 shards of 16384 tokens, 32 q / 8 kv heads): bitwise equal
     to the packed path for ranks 0 and 3."""
-    cfg = W.CONFIGS["qwen_64k"]
+    cfg = W.WORKLOADS["qwen_64k"]
     print(f"generating qwen_64k shards for rank {rank}", flush=True)
     dev = {n: [to_dev(W.gen_rows(cfg, n, p * cfg.s_l, (p + 1) * cfg.s_l), "bf16") for p in range(cfg.P)]
            for n in ("q", "k", "v")}
@@ -151,7 +151,7 @@ def test_shards_qwen_64k_share(rank):
 @pytest.mark.timeout(300)
 def test_bwd_shards_qwen_64k_share():
     """Backward of the 64K headline share (rank 2): bitwise equal to the packed path."""
-    cfg = W.CONFIGS["qwen_64k"]
+    cfg = W.WORKLOADS["qwen_64k"]
     rank = 2
     print("generating qwen_64k shards", flush=True)
     dev = {n: [to_dev(W.gen_rows(cfg, n, p * cfg.s_l, (p + 1) * cfg.s_l), "bf16") for p in range(cfg.P)]

@@ -5,7 +5,7 @@ import workloads as W
 
 
 def test_rows_regenerate_exactly():
-    cfg = W.CONFIGS["qwen_8k"]
+    cfg = W.WORKLOADS["qwen_8k"]
     full = W.gen_rows(cfg, "k", 0, 9000)
     part = W.gen_rows(cfg, "k", 4000, 8200)
     np.testing.assert_array_equal(full[4000:8200], part)
@@ -13,7 +13,7 @@ def test_rows_regenerate_exactly():
 
 
 def test_f32_amplitude_and_bits():
-    cfg = W.CONFIGS["tiny_f32"]
+    cfg = W.WORKLOADS["tiny_f32"]
     q = W.gen_global(cfg, "q")
     assert q.dtype == np.uint32 and q.shape == (512, 4, 64)
     x = W.bits_to_f64(q, "f32")
@@ -40,7 +40,7 @@ def test_shards_are_contiguous_chunks():
 
 
 def test_documents_cover_the_sequence():
-    cfg = W.CONFIGS["packed_96k"]
+    cfg = W.WORKLOADS["packed_96k"]
     cu = W.cu_seqlens_for(cfg)
     assert cu[0] == 0 and cu[-1] == cfg.s and (np.diff(cu) >= 1).all()
     np.testing.assert_array_equal(cu, W.cu_seqlens_for(cfg))
@@ -51,14 +51,14 @@ def test_documents_cover_the_sequence():
 def test_packed_seed0_instance():
     """The seed-0 packed 96K instance: 11 documents, the last truncated, about a fifth of
     the dense-causal pair count."""
-    cu = W.cu_seqlens_for(W.CONFIGS["packed_96k"])
+    cu = W.cu_seqlens_for(W.WORKLOADS["packed_96k"])
     assert list(cu) == [0, 4080, 10198, 10317, 10331, 13633, 23412, 27454, 31986, 48886, 85230, 98304]
     lens = np.diff(cu).astype(np.int64)
     assert int((lens ** 2).sum()) == 1974925326
 
 
 def test_config_shapes():
-    c = W.CONFIGS["qwen_64k"]
+    c = W.WORKLOADS["qwen_64k"]
     assert (c.s, c.Hq_l, c.Hkv_l, c.G, c.d) == (65536, 8, 2, 4, 128)
-    c = W.CONFIGS["upipe_256k"]
+    c = W.WORKLOADS["upipe_256k"]
     assert (c.s, c.Hq_l, c.Hkv_l, c.G) == (262144, 8, 1, 8)

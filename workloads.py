@@ -75,7 +75,7 @@ class Config:
         return 2 if self.dtype == "bf16" else 4
 
 
-CONFIGS = {
+WORKLOADS = {
     # tiny fp32 case: 2 ranks x 256 tokens, 4 q / 4 kv heads, d 64, inputs 0.5*N(0,1)
     "tiny_f32": Config("tiny_f32", P=2, s_l=256, Hq=4, Hkv=4, d=64, dtype="f32", amp=0.5),
     # Qwen3-4B-shaped SP=4 share at 8K tokens
