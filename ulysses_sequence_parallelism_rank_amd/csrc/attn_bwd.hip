@@ -420,14 +420,15 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (r == 0) {
-        // P = exp2(S c - LSE log2e) on rows 32qb + 8(j/4) + 4hf + j%4
+        // P = exp2(S c - LSE log2e) on rows 32qb + 8(j/4) + 4hf + j%4 (the LSE rows are in
+        // log2 units in LDS already)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const f32x4 L4 = *reinterpret_cast<const f32x4*>(&buf.l[qb * 32 + 8 * jj + 4 * hf]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[qb][4 * jj + e] = fast_exp2(__builtin_fmaf(x[qb][4 * jj + e], c, -L4[e] * kLog2e));
+            for (int e = 0; e < 4; ++e) x[qb][4 * jj + e] = fast_exp2(__builtin_fmaf(x[qb][4 * jj + e], c, -L4[e]));
           }
         }
         // 0 outside [rlo, rhi): only where some row of the tile cannot see some key of the
@@ -494,11 +495,21 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
       __builtin_amdgcn_s_setprio(1);
       part_b(std::integral_constant<int, 1>{});
       __builtin_amdgcn_s_setprio(0);
+      // the wave that fetched the next tile's LSE rows turns them into log2 units once, so
+      // the P waves need no multiply per element (published by the next step's barrier)
+      if (wave == 4 && step + 1 < nsteps) {
+        wait_dma();
+        nbuf.l[lane] *= kLog2e;
+      }
     }
   };
 
   if (nsteps > 0) {
     if (role == 1) issue_tile(0, 0, bufs(std::integral_constant<int, 0>{}));
+    if (wave == 4) {  // LSE rows of the first tile in log2 units
+      wait_dma();
+      bufs(std::integral_constant<int, 0>{}).l[lane] *= kLog2e;
+    }
     for (int step = 0;;) {
       run_step(std::integral_constant<int, 0>{}, step);
       if (++step >= nsteps) break;
