@@ -13,8 +13,11 @@
  *   3. the local half of the second all-to-all: the head shard goes back to the
  *      sequence shards                                             -> ulysses_unpack
  *   4. the UPipe schedule: 1-3 run a few heads at a time so that the attention
- *      intermediates stay small                                    -> attn_fwd_chunked
+ *      intermediates stay small                    -> attn_fwd_chunked, attn_bwd_chunked
+ *   5. 1-3 with the exchange folded into the attention's own loads and stores: the
+ *      kernels read the sequence shards directly      -> attn_fwd_shards, attn_bwd_shards
  * The P ranks are P separate device buffers on one GPU; no collective runs here.
+ * uly_mfma_probe is a measurement helper outside the path.
  *
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers; arrays of pointers (the P shards) are HOST
