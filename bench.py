@@ -27,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -103,10 +104,14 @@ class Phases:
         return r
 
     def summary(self, steps):
-        tot = {}
+        """Per phase: the mean over the timed steps, and the median. The first timed step starts
+        on an idle GPU (the region opens with a synchronize), so its first phase also holds the
+        host's time to issue that call; the median is free of it."""
+        per = {}
         for name, a, b in self.marks:
-            tot[name] = tot.get(name, 0.0) + a.elapsed_time(b)
-        return {k: v / steps for k, v in tot.items()}
+            per.setdefault(name, []).append(a.elapsed_time(b))
+        mean = {k: sum(v) / steps for k, v in per.items()}
+        return mean, {k: float(statistics.median(v)) for k, v in per.items()}
 
 
 def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
@@ -141,8 +146,7 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
     def step(rec):
         if fused:
             return step_fused(rec)
-        ph.run("pack_qkv", lambda: (U.ulysses_pack(sh["q"], rank, q), U.ulysses_pack(sh["k"], rank, k),
-                                    U.ulysses_pack(sh["v"], rank, v)), rec)
+        ph.run("pack_qkv", lambda: U.ulysses_pack_group([sh["q"], sh["k"], sh["v"]], rank, [q, k, v]), rec)
         ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse), rec)
         ph.run("unpack_o", lambda: U.ulysses_unpack(o, rank, o_sh), rec)
         ph.run("pack_do", lambda: U.ulysses_pack(sh["do"], rank, do), rec)
@@ -150,8 +154,7 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
         ph.run("bwd_dkdv", lambda: U.attn_bwd_dkdv(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev,
                                                    dk=dk, dv=dv), rec)
         ph.run("bwd_dq", lambda: U.attn_bwd_dq(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev, dq=dq), rec)
-        ph.run("unpack_grads", lambda: (U.ulysses_unpack(dq, rank, dq_sh), U.ulysses_unpack(dk, rank, dk_sh),
-                                        U.ulysses_unpack(dv, rank, dv_sh)), rec)
+        ph.run("unpack_grads", lambda: U.ulysses_unpack_group([dq, dk, dv], rank, [dq_sh, dk_sh, dv_sh]), rec)
 
     for _ in range(warmup):
         step(False)
@@ -161,7 +164,7 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
         step(True)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    return wall, ph.summary(steps)
+    return (wall,) + ph.summary(steps)
 
 
 def run_forward_share(cfg, steps, warmup, cu_dev, fused):
@@ -184,8 +187,7 @@ def run_forward_share(cfg, steps, warmup, cu_dev, fused):
             ph.run("attn_fwd_shards", lambda: U.attn_fwd_shards(sh["q"], sh["k"], sh["v"], o_sh, rank, cfg.scale,
                                                                 cfg.causal, cu_dev, lse=lse), rec)
             return
-        ph.run("pack_qkv", lambda: (U.ulysses_pack(sh["q"], rank, q), U.ulysses_pack(sh["k"], rank, k),
-                                    U.ulysses_pack(sh["v"], rank, v)), rec)
+        ph.run("pack_qkv", lambda: U.ulysses_pack_group([sh["q"], sh["k"], sh["v"]], rank, [q, k, v]), rec)
         ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse), rec)
         ph.run("unpack_o", lambda: U.ulysses_unpack(o, rank, o_sh), rec)
 
@@ -196,7 +198,7 @@ def run_forward_share(cfg, steps, warmup, cu_dev, fused):
     for _ in range(steps):
         step(True)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps, ph.summary(steps)
+    return ((time.perf_counter() - t0) / steps,) + ph.summary(steps)
 
 
 def run_upipe(cfg, steps, warmup, u, forward_only):
@@ -225,7 +227,7 @@ def run_upipe(cfg, steps, warmup, u, forward_only):
                                                                   dq_sh, dk_sh, dv_sh, 0, u, cfg.scale, cfg.causal,
                                                                   None, ws), i >= warmup)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps, ph.summary(steps), need
+    return ((time.perf_counter() - t0) / steps,) + ph.summary(steps) + (need,)
 
 
 def measured_ceilings():
@@ -311,14 +313,14 @@ def main():
 
     chunked = bool(cfg.chunk_heads)
     if not chunked and args.forward_only:
-        wall, ph = run_forward_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
+        wall, ph, ph_med = run_forward_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
         fw = 4.0 * d * pairs * Hq_l
         kern = {"attn_fwd": ("mfma", fw), "attn_fwd_shards": ("mfma", fw),
                 "pack_qkv": ("hbm", 2.0 * cfg.s * (Hq_l + 2 * Hkv_l) * d * e),
                 "unpack_o": ("hbm", 2.0 * cfg.s * Hq_l * d * e)}
         flops = fw
     elif not chunked:
-        wall, ph = run_training_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
+        wall, ph, ph_med = run_training_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
         flops = 14.0 * d * pairs * Hq_l
         kern = {
             "attn_fwd": ("mfma", 4.0 * d * pairs * Hq_l),
@@ -334,7 +336,7 @@ def main():
             "attn_bwd_shards": ("mfma", 10.0 * d * pairs * Hq_l),
         }
     else:
-        wall, ph, ws_bytes = run_upipe(cfg, args.steps, args.warmup, args.heads_per_chunk, args.forward_only)
+        wall, ph, ph_med, ws_bytes = run_upipe(cfg, args.steps, args.warmup, args.heads_per_chunk, args.forward_only)
         # each call is timed whole (per chunk: permutes and attention kernels)
         kern = {"attn_fwd_chunked": ("mfma", 4.0 * d * pairs * Hq_l)}
         if not args.forward_only:
@@ -359,7 +361,9 @@ def main():
 
     attn_ms = sum(ph.get(k, 0.0) for k in ("attn_fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "attn_fwd_chunked",
                                            "attn_bwd_chunked", "attn_fwd_shards", "attn_bwd_shards"))
-    perm_ms = sum(ph.get(k, 0.0) for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads"))
+    # the permutes' rate from the per-phase medians (see Phases.summary: the first phase of the
+    # first timed step also holds a host launch latency, a sizeable part of a 0.08 ms phase)
+    perm_ms = sum(ph_med.get(k, 0.0) for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads"))
     perm_bytes = sum(kern[k][1] for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads") if k in ph)
     value = flops / wall / 1e12
     out = {
@@ -393,6 +397,7 @@ def main():
         "attention_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2) if attn_ms else None,
         "permute_gbs": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1) if perm_ms else None,
         "phase_ms": {k: round(v, 4) for k, v in ph.items()},
+        "phase_ms_median": {k: round(v, 4) for k, v in ph_med.items()},
     }
     if chunked:
         # peak intermediate bytes: the chunked calls' workspaces against the unchunked head shards

@@ -7,7 +7,8 @@
  * commentary, sections on what Ulysses changes and on activation memory):
  *   1. the local half of the first all-to-all: P sequence shards [s_l, H, d] (every
  *      head, a contiguous token chunk each) become one head shard [s, H/P, d]
- *      (every position, this rank's heads)                         -> ulysses_pack
+ *      (every position, this rank's heads)    -> ulysses_pack (several tensors at once:
+ *                                                ulysses_pack_group / ulysses_unpack_group)
  *   2. dense causal (optionally packed-document) attention over the whole sequence
  *      for the head shard, forward and backward                    -> attn_fwd, attn_bwd
  *   3. the local half of the second all-to-all: the head shard goes back to the
@@ -88,6 +89,25 @@ int ulysses_pack(const void* const* shards, int P, int rank, int64_t s_l, int H,
  * ------------------------------------------------------------------------- */
 int ulysses_unpack(const void* in, int P, int rank, int64_t s_l, int H, int d, int dtype,
                    void* const* shards, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ulysses_pack_group / ulysses_unpack_group -- the permutes of several tensors that cross
+ * the same all-to-all, in one launch. Pages: "how Ulysses works" steps 1 and 3 (the
+ * forward exchange carries Q, K and V together; the backward one carries dQ, dK and dV).
+ *   n       : number of tensors, 1..ULY_PERM_GROUP_MAX
+ *   H       : host array of n global head counts, each divisible by P
+ *   pack    : shards[i] is a host array of P device pointers [s_l, H[i], d]; out[i] is a
+ *             device [P*s_l, H[i]/P, d] buffer; out[i] = ulysses_pack(shards[i], ...)
+ *   unpack  : in[i] is a device [P*s_l, H[i]/P, d] buffer; head slice `rank` of the P shards
+ *             shards[i] is written as by ulysses_unpack(in[i], ...)
+ * Every tensor is checked as by ulysses_pack / ulysses_unpack before anything is enqueued;
+ * the results are bit-identical to n separate calls (only the launch count differs).
+ * ------------------------------------------------------------------------- */
+#define ULY_PERM_GROUP_MAX 3
+int ulysses_pack_group(int n, const void* const* const* shards, const int* H, void* const* out, int P,
+                       int rank, int64_t s_l, int d, int dtype, void* stream);
+int ulysses_unpack_group(int n, const void* const* in, const int* H, void* const* const* shards, int P,
+                         int rank, int64_t s_l, int d, int dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
  * attn_fwd -- attention forward of one head shard. Pages: "how Ulysses works" step 4

@@ -70,6 +70,49 @@ def test_pack_null_and_alignment():
     assert L.ulysses_pack(pp, 2, 0, 4, 4, 64, 0, MIS, None) == 4
 
 
+def _group(n, P, Hs, shard_vals=None, flat_vals=None, rank=0, s_l=4, d=64, dt=0):
+    """Host arrays for ulysses_pack_group / ulysses_unpack_group with fake device pointers."""
+    keep = []
+    inner = []
+    for i in range(len(Hs)):
+        pp, arr = _ptr_array(shard_vals[i] if shard_vals else [FAKE] * P)
+        keep.append(arr)
+        inner.append(ctypes.cast(pp, ctypes.c_void_p).value)
+    outer = (ctypes.c_void_p * max(len(inner), 1))(*inner)
+    heads = (ctypes.c_int * max(len(Hs), 1))(*Hs)
+    flat = (ctypes.c_void_p * max(len(Hs), 1))(*(flat_vals or [FAKE] * len(Hs)))
+    keep += [outer, heads, flat]
+    L = U.lib()
+    a = (ctypes.cast(outer, U._vpp), ctypes.cast(heads, U._i32p), ctypes.cast(flat, U._vpp))
+    got_pack = L.ulysses_pack_group(n, a[0], a[1], a[2], P, rank, s_l, d, dt, None)
+    got_unpack = L.ulysses_unpack_group(n, a[2], a[1], a[0], P, rank, s_l, d, dt, None)
+    return got_pack, got_unpack
+
+
+@pytest.mark.parametrize("n,P,Hs,kw,want", [
+    (0, 2, (4,), {}, 2),                       # no tensor
+    (4, 2, (4, 4, 4, 4), {}, 2),               # more than ULY_PERM_GROUP_MAX
+    (2, 2, (4, 3), {}, 2),                     # one head count not divisible by P
+    (3, 2, (4, 4, 4), {"rank": 2}, 2),         # rank out of range
+    (2, 2, (4, 4), {"dt": 7}, 3),              # dtype
+    (2, 2, (2, 2), {"d": 4}, 4),               # a tensor's run not a multiple of 16 bytes
+    (2, 2, (4, 4), {"s_l": 0}, 2),             # empty shards
+])
+def test_group_permute_rejects(n, P, Hs, kw, want):
+    assert _group(n, P, Hs, **kw) == (want, want)
+
+
+def test_group_permute_null_and_alignment():
+    assert _group(2, 2, (4, 4), shard_vals=[[FAKE, FAKE], [FAKE, None]]) == (1, 1)
+    assert _group(2, 2, (4, 4), flat_vals=[FAKE, None]) == (1, 1)
+    assert _group(2, 2, (4, 4), shard_vals=[[FAKE, FAKE], [MIS, FAKE]]) == (4, 4)
+    assert _group(3, 2, (4, 4, 4), flat_vals=[FAKE, FAKE, MIS]) == (4, 4)
+    L = U.lib()
+    heads = (ctypes.c_int * 1)(4)
+    assert L.ulysses_pack_group(1, None, ctypes.cast(heads, U._i32p), None, 2, 0, 4, 64, 0, None) == 1
+    assert L.ulysses_unpack_group(1, None, None, None, 2, 0, 4, 64, 0, None) == 1
+
+
 def _fwd(**kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, s=16, Hq=4, Hkv=2, d=128, dt=0, scale=0.1,
                 causal=1, cu=None, nd=0)

@@ -91,3 +91,51 @@ def test_upipe_size_pack_sampled_rows():
     for p in range(P):
         assert torch.equal(back[p][:, r * Hl:(r + 1) * Hl].view(torch.int16), dev[p][:, r * Hl:(r + 1) * Hl].view(torch.int16))
         assert not back[p][:, :r * Hl].view(torch.int16).any()
+
+
+@pytest.mark.parametrize("P,s_l,Hs,d,dtype", [
+    (4, 2048, (32, 8, 8), 128, "bf16"),   # Q, K, V of the 8K share
+    (3, 13, (6, 3, 3), 64, "bf16"),       # ragged token count, odd rank count
+    (2, 256, (4, 4), 64, "f32"),          # two tensors, fp32
+    (8, 7, (8,), 128, "f32"),             # one tensor: the grouped call equals ulysses_pack
+    (64, 3, (64, 64, 128), 64, "bf16"),   # the largest rank count, different head counts
+])
+def test_grouped_pack_unpack_bit_exact(P, s_l, Hs, d, dtype):
+    """ulysses_pack_group / ulysses_unpack_group: every tensor bit-exact against the oracle's
+    index-loop permute, for every rank; heads of other ranks untouched by the unpack."""
+    print(f"case grouped P={P} s_l={s_l} H={Hs} d={d} {dtype}", flush=True)
+    hosts, devs = zip(*[_rand_shards(P, s_l, H, d, dtype, seed=97 * i + P) for i, H in enumerate(Hs)])
+    for r in range(P):
+        ys = U.ulysses_pack_group(list(devs), r)
+        torch.cuda.synchronize()
+        for y, host in zip(ys, hosts):
+            np.testing.assert_array_equal(_bits(y), OP.pack(host, r))
+        fresh = [np.random.default_rng(r + 7 * i).integers(0, 2**16, y.shape, dtype=np.uint64).astype(hosts[i][0].dtype)
+                 for i, y in enumerate(ys)]
+        tgts = [[t.clone() for t in dev] for dev in devs]
+        U.ulysses_unpack_group([to_dev(f, dtype) for f in fresh], r, tgts)
+        torch.cuda.synchronize()
+        for f, tgt, host in zip(fresh, tgts, hosts):
+            for a, b in zip(tgt, OP.unpack(f, r, host)):
+                np.testing.assert_array_equal(_bits(a), b)
+
+
+def test_grouped_pack_headline_size_equals_single_calls():
+    """Q, K, V of the 64K share packed by one launch: bit-identical to three ulysses_pack calls,
+    and their unpack_group restores the rank's head slices."""
+    cfg = W.WORKLOADS["qwen_64k"]
+    print("case qwen_64k grouped pack/unpack rank 1", flush=True)
+    devs = [gen_shards(cfg, name)[1] for name in ("q", "k", "v")]
+    ys = U.ulysses_pack_group(devs, 1)
+    singles = [U.ulysses_pack(dev, 1) for dev in devs]
+    torch.cuda.synchronize()
+    for y, ref in zip(ys, singles):
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+    backs = [[torch.zeros_like(t) for t in dev] for dev in devs]
+    U.ulysses_unpack_group(ys, 1, backs)
+    torch.cuda.synchronize()
+    for dev, back in zip(devs, backs):
+        Hl = dev[0].shape[1] // cfg.P
+        for a, b in zip(back, dev):
+            assert torch.equal(a[:, Hl:2 * Hl].view(torch.int16), b[:, Hl:2 * Hl].view(torch.int16))
+            assert not a[:, :Hl].view(torch.int16).any() and not a[:, 2 * Hl:].view(torch.int16).any()

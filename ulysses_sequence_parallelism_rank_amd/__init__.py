@@ -6,6 +6,7 @@ library is missing, every call raises: there is no fallback path.
 
 The names follow the C ABI in include/ulysses.h:
   ulysses_pack, ulysses_unpack        -- local halves of the two all-to-alls
+  ulysses_pack_group, ulysses_unpack_group -- the same for up to three tensors in one launch
   attn_fwd, attn_bwd                  -- attention of one head shard
   attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq -- the phases of attn_bwd
   attn_fwd_chunked                    -- the UPipe headwise-chunked forward
@@ -33,12 +34,16 @@ _lib = None
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _vpp = ctypes.POINTER(ctypes.c_void_p)
 _szp = ctypes.POINTER(ctypes.c_size_t)
+_i32p = ctypes.POINTER(ctypes.c_int)
+PERM_GROUP_MAX = 3
 
 SIGNATURES = {
     "uly_status_string": (ctypes.c_char_p, [_i32]),
     "uly_abi_version": (_i32, []),
     "ulysses_pack": (_i32, [_vpp, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp]),
     "ulysses_unpack": (_i32, [_vp, _i32, _i32, _i64, _i32, _i32, _i32, _vpp, _vp]),
+    "ulysses_pack_group": (_i32, [_i32, _vpp, _i32p, _vpp, _i32, _i32, _i64, _i32, _i32, _vp]),
+    "ulysses_unpack_group": (_i32, [_i32, _vpp, _i32p, _vpp, _i32, _i32, _i64, _i32, _i32, _vp]),
     "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp]),
     "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
                         _vp, _i32, _vp, _szp, _vp]),
@@ -140,6 +145,42 @@ def ulysses_unpack(y, rank, shards):
     pp, _keep = _ptrs(shards)
     _call("ulysses_unpack", _dev(y), P, rank, s_l, H, d, _dtype(y), pp, _stream())
     return shards
+
+
+def _group_args(tensor_lists):
+    """Host arrays for the grouped permutes: one array of P device pointers per tensor, an
+    array of those arrays, and the global head counts."""
+    arrays = [_ptrs(ts) for ts in tensor_lists]
+    outer = (ctypes.c_void_p * len(arrays))(*[ctypes.cast(a, ctypes.c_void_p).value for a, _ in arrays])
+    heads = (ctypes.c_int * len(tensor_lists))(*[ts[0].shape[1] for ts in tensor_lists])
+    return ctypes.cast(outer, _vpp), ctypes.cast(heads, _i32p), (arrays, outer, heads)
+
+
+def ulysses_pack_group(shard_lists, rank, outs=None):
+    """Several tensors' P sequence shards [s_l, H_i, d] -> their head shards [P*s_l, H_i/P, d],
+    in one launch (the Q/K/V of the forward exchange)."""
+    n = len(shard_lists)
+    P = len(shard_lists[0])
+    s_l, _, d = shard_lists[0][0].shape
+    if outs is None:
+        outs = [torch.empty((P * s_l, sh[0].shape[1] // P, d), dtype=sh[0].dtype, device=sh[0].device)
+                for sh in shard_lists]
+    pp, hh, _keep = _group_args(shard_lists)
+    op, _keep2 = _ptrs(outs)
+    _call("ulysses_pack_group", n, pp, hh, op, P, rank, s_l, d, _dtype(outs[0]), _stream())
+    return outs
+
+
+def ulysses_unpack_group(ys, rank, shard_lists):
+    """Several head shards [P*s_l, H_i/P, d] -> head slice `rank` of their P shards, in one launch
+    (the dQ/dK/dV of the backward exchange)."""
+    n = len(ys)
+    P = len(shard_lists[0])
+    s_l, _, d = shard_lists[0][0].shape
+    pp, hh, _keep = _group_args(shard_lists)
+    yp, _keep2 = _ptrs(ys)
+    _call("ulysses_unpack_group", n, yp, hh, pp, P, rank, s_l, d, _dtype(ys[0]), _stream())
+    return shard_lists
 
 
 def _default_scale(d, scale):

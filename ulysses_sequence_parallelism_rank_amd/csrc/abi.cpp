@@ -179,6 +179,49 @@ int ulysses_unpack(const void* in, int P, int rank, int64_t s_l, int H, int d, i
                                   rank * run, run, as_stream(stream)));
 }
 
+// Checks shared by the grouped permutes: every tensor as ulysses_pack / ulysses_unpack
+// would check it; fills the launch segments.
+static int group_segments(int n, const void* const* const* shards, const int* H, void* const* flat, int P,
+                          int rank, int64_t s_l, int d, int dtype, PermSeg* segs) {
+  if (!shards || !H || !flat) return ULY_ERR_NULL;
+  if (n < 1 || n > ULY_PERM_GROUP_MAX) return ULY_ERR_SHAPE;
+  if (dtype != ULY_BF16 && dtype != ULY_F32) return ULY_ERR_UNSUPPORTED;
+  if (d < 1) return ULY_ERR_SHAPE;
+  for (int i = 0; i < n; ++i) {
+    int st = check_ranks(P, rank, s_l, H[i]);
+    if (st != ULY_OK) return st;
+    const int64_t Hl = H[i] / P, e = esize(dtype);
+    const int64_t run = Hl * d * e, row = (int64_t)H[i] * d * e;
+    if (run % 16 != 0) return ULY_ERR_ALIGN;
+    if (!shards[i] || !flat[i]) return ULY_ERR_NULL;
+    for (int p = 0; p < P; ++p) {
+      if (!shards[i][p]) return ULY_ERR_NULL;
+      if (!aligned16(shards[i][p])) return ULY_ERR_ALIGN;
+    }
+    if (!aligned16(flat[i])) return ULY_ERR_ALIGN;
+    if (!chunks_fit(P, s_l, run, row)) return ULY_ERR_SHAPE;
+    segs[i] = PermSeg{shard_ptrs(shards[i], P), flat[i], P, row, rank * run, run};
+  }
+  return ULY_OK;
+}
+
+int ulysses_pack_group(int n, const void* const* const* shards, const int* H, void* const* out, int P, int rank,
+                       int64_t s_l, int d, int dtype, void* stream) {
+  PermSeg segs[ULY_PERM_GROUP_MAX];
+  const int st = group_segments(n, shards, H, out, P, rank, s_l, d, dtype, segs);
+  if (st != ULY_OK) return st;
+  return hip_status(launch_pack_group(segs, n, s_l, as_stream(stream)));
+}
+
+int ulysses_unpack_group(int n, const void* const* in, const int* H, void* const* const* shards, int P, int rank,
+                         int64_t s_l, int d, int dtype, void* stream) {
+  PermSeg segs[ULY_PERM_GROUP_MAX];
+  const int st = group_segments(n, reinterpret_cast<const void* const* const*>(shards), H,
+                                const_cast<void* const*>(in), P, rank, s_l, d, dtype, segs);
+  if (st != ULY_OK) return st;
+  return hip_status(launch_unpack_group(segs, n, s_l, as_stream(stream)));
+}
+
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t s, int Hq,
              int Hkv, int d, int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,
              void* stream) {
@@ -348,8 +391,8 @@ int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards, c
     hipError_t err;
     if (g0 != kv_lo || g1 != kv_hi) {
       const int64_t off = ((int64_t)rank * Hkv_l + g0) * hb, run = (int64_t)(g1 - g0) * hb;
-      if ((err = launch_pack(ks, kc, P, s_l, kvrow, off, run, strm)) != hipSuccess) return ULY_ERR_HIP;
-      if ((err = launch_pack(vs, vc, P, s_l, kvrow, off, run, strm)) != hipSuccess) return ULY_ERR_HIP;
+      const PermSeg kv[2] = {{ks, kc, P, kvrow, off, run}, {vs, vc, P, kvrow, off, run}};
+      if ((err = launch_pack_group(kv, 2, s_l, strm)) != hipSuccess) return ULY_ERR_HIP;
       kv_lo = g0;
       kv_hi = g1;
     }
@@ -558,15 +601,14 @@ int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards, c
     const int g0 = c0 / G, g1 = (c1 - 1) / G + 1;
     if (g0 != kv_lo || g1 != kv_hi) {
       const int64_t off = ((int64_t)rank * Hkv_l + g0) * hb, run = (int64_t)(g1 - g0) * hb;
-      if ((err = launch_pack(ks, kc, P, s_l, kvrow, off, run, strm)) != hipSuccess) return ULY_ERR_HIP;
-      if ((err = launch_pack(vs, vc, P, s_l, kvrow, off, run, strm)) != hipSuccess) return ULY_ERR_HIP;
+      const PermSeg kv[2] = {{ks, kc, P, kvrow, off, run}, {vs, vc, P, kvrow, off, run}};
+      if ((err = launch_pack_group(kv, 2, s_l, strm)) != hipSuccess) return ULY_ERR_HIP;
       kv_lo = g0;
       kv_hi = g1;
     }
     const int64_t qoff = ((int64_t)rank * Hq_l + c0) * hb, qrun = (int64_t)nq * hb;
-    if ((err = launch_pack(qs, qc, P, s_l, qrow, qoff, qrun, strm)) != hipSuccess) return ULY_ERR_HIP;
-    if ((err = launch_pack(os, oc, P, s_l, qrow, qoff, qrun, strm)) != hipSuccess) return ULY_ERR_HIP;
-    if ((err = launch_pack(gs, gc, P, s_l, qrow, qoff, qrun, strm)) != hipSuccess) return ULY_ERR_HIP;
+    const PermSeg qog[3] = {{qs, qc, P, qrow, qoff, qrun}, {os, oc, P, qrow, qoff, qrun}, {gs, gc, P, qrow, qoff, qrun}};
+    if ((err = launch_pack_group(qog, 3, s_l, strm)) != hipSuccess) return ULY_ERR_HIP;
 
     AttnArgs a = make_args(s, nq, 1, d, scale, causal, cu_seqlens, n_docs);
     a.q_row = (int64_t)nq * d;
@@ -604,8 +646,8 @@ int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards, c
     if ((err = launch_unpack(dqc, dqs, P, s_l, qrow, qoff, qrun, strm)) != hipSuccess) return ULY_ERR_HIP;
   }
   const int64_t kvoff = (int64_t)rank * Hkv_l * hb, kvrun = (int64_t)Hkv_l * hb;
-  if ((err = launch_unpack(dk_r, dks, P, s_l, kvrow, kvoff, kvrun, strm)) != hipSuccess) return ULY_ERR_HIP;
-  if ((err = launch_unpack(dv_r, dvs, P, s_l, kvrow, kvoff, kvrun, strm)) != hipSuccess) return ULY_ERR_HIP;
+  const PermSeg dkv[2] = {{dks, dk_r, P, kvrow, kvoff, kvrun}, {dvs, dv_r, P, kvrow, kvoff, kvrun}};
+  if ((err = launch_unpack_group(dkv, 2, s_l, strm)) != hipSuccess) return ULY_ERR_HIP;
   return ULY_OK;
 }
 

@@ -20,52 +20,111 @@ namespace uly {
 
 constexpr int kPermThreads = 256;
 
-// gather: out[(p*s_l + t)*run + w] = shard_p[t*row_in + h_off + w]   (units of 16 B; one per thread)
-__global__ __launch_bounds__(kPermThreads) void pack_kernel(ShardPtrs src, u32x4* __restrict__ out,
-                                                            uint32_t s_l, uint32_t run, uint32_t row_in,
-                                                            uint32_t h_off, uint32_t total) {
-  const uint32_t c = blockIdx.x * kPermThreads + threadIdx.x;
-  if (c >= total) return;
-  const uint32_t row = c / run, w = c - row * run;
+// One tensor of a (grouped) permute launch, in 16-byte units: the P shards with rows of
+// row_in units, the head-shard buffer `flat` with runs of `run` units taken from offset
+// h_off of every shard row, `total` = P*s_l*run units, and the first workgroup of the launch
+// that works on it.
+struct PermSegK {
+  ShardPtrs sh;
+  u32x4* flat;
+  uint32_t run, row_in, h_off, total, block0;
+};
+// Up to kPermGroupMax tensors moved by one launch (one ramp-up and drain instead of several).
+static_assert(kPermGroupMax == 3, "pack_kernel / unpack_kernel select among three tensors");
+struct PermGroupK {
+  PermSegK seg[kPermGroupMax];
+  uint32_t s_l;
+  int n;
+};
+
+// gather: flat[(p*s_l + t)*run + w] = shard_p[t*row_in + h_off + w]   (one unit per thread)
+__device__ __forceinline__ void pack_unit(const PermSegK& g, uint32_t s_l, uint32_t c) {
+  if (c >= g.total) return;
+  const uint32_t row = c / g.run, w = c - row * g.run;
   const uint32_t p = row / s_l, t = row - p * s_l;
-  const u32x4* s = reinterpret_cast<const u32x4*>(src.p[p]);
-  __builtin_nontemporal_store(__builtin_nontemporal_load(s + (size_t)t * row_in + h_off + w), out + c);
+  const u32x4* s = reinterpret_cast<const u32x4*>(g.sh.p[p]);
+  __builtin_nontemporal_store(__builtin_nontemporal_load(s + (size_t)t * g.row_in + g.h_off + w), g.flat + c);
+}
+// scatter: shard_p[t*row_in + h_off + w] = flat[(p*s_l + t)*run + w]
+__device__ __forceinline__ void unpack_unit(const PermSegK& g, uint32_t s_l, uint32_t c) {
+  if (c >= g.total) return;
+  const uint32_t row = c / g.run, w = c - row * g.run;
+  const uint32_t p = row / s_l, t = row - p * s_l;
+  u32x4* d = reinterpret_cast<u32x4*>(const_cast<void*>(g.sh.p[p]));
+  __builtin_nontemporal_store(__builtin_nontemporal_load(g.flat + c), d + (size_t)t * g.row_in + g.h_off + w);
 }
 
-// scatter: shard_p[t*row_in + h_off + w] = in[(p*s_l + t)*run + w]
-__global__ __launch_bounds__(kPermThreads) void unpack_kernel(const u32x4* __restrict__ in, ShardPtrs dst,
-                                                              uint32_t s_l, uint32_t run, uint32_t row_in,
-                                                              uint32_t h_off, uint32_t total) {
-  const uint32_t c = blockIdx.x * kPermThreads + threadIdx.x;
-  if (c >= total) return;
-  const uint32_t row = c / run, w = c - row * run;
-  const uint32_t p = row / s_l, t = row - p * s_l;
-  u32x4* d = reinterpret_cast<u32x4*>(const_cast<void*>(dst.p[p]));
-  __builtin_nontemporal_store(__builtin_nontemporal_load(in + c), d + (size_t)t * row_in + h_off + w);
+// The workgroup's tensor is found by comparing its index with the tensors' first workgroups
+// (wave-uniform branches; each branch reads its tensor's fields at a constant index).
+__global__ __launch_bounds__(kPermThreads) void pack_kernel(PermGroupK g) {
+  const uint32_t b = blockIdx.x;
+  if (g.n > 2 && b >= g.seg[2].block0)
+    pack_unit(g.seg[2], g.s_l, (b - g.seg[2].block0) * kPermThreads + threadIdx.x);
+  else if (g.n > 1 && b >= g.seg[1].block0)
+    pack_unit(g.seg[1], g.s_l, (b - g.seg[1].block0) * kPermThreads + threadIdx.x);
+  else
+    pack_unit(g.seg[0], g.s_l, b * kPermThreads + threadIdx.x);
 }
 
-// Host launchers. Sizes are in bytes; the caller has checked alignment, that every
-// size is a multiple of 16 and that the 16-byte chunk count fits in 32 bits.
+__global__ __launch_bounds__(kPermThreads) void unpack_kernel(PermGroupK g) {
+  const uint32_t b = blockIdx.x;
+  if (g.n > 2 && b >= g.seg[2].block0)
+    unpack_unit(g.seg[2], g.s_l, (b - g.seg[2].block0) * kPermThreads + threadIdx.x);
+  else if (g.n > 1 && b >= g.seg[1].block0)
+    unpack_unit(g.seg[1], g.s_l, (b - g.seg[1].block0) * kPermThreads + threadIdx.x);
+  else
+    unpack_unit(g.seg[0], g.s_l, b * kPermThreads + threadIdx.x);
+}
+
+namespace {
+
+// Sizes are in bytes; the caller has checked alignment, that every size is a multiple of 16,
+// that each tensor's 16-byte unit count fits in 32 bits and that 1 <= n <= kPermGroupMax.
+hipError_t launch_group(bool pack, const PermSeg* segs, int n, int64_t s_l, hipStream_t stream) {
+  PermGroupK g{};
+  g.s_l = (uint32_t)s_l;
+  g.n = n;
+  uint64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    PermSegK& k = g.seg[i];
+    k.sh = segs[i].sh;
+    k.flat = reinterpret_cast<u32x4*>(segs[i].flat);
+    k.run = (uint32_t)(segs[i].run_bytes / 16);
+    k.row_in = (uint32_t)(segs[i].row_bytes / 16);
+    k.h_off = (uint32_t)(segs[i].off_bytes / 16);
+    k.total = (uint32_t)((uint64_t)segs[i].P * s_l * k.run);
+    k.block0 = (uint32_t)blocks;
+    blocks += (k.total + kPermThreads - 1) / kPermThreads;
+  }
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  if (pack)
+    hipLaunchKernelGGL(pack_kernel, dim3((uint32_t)blocks), dim3(kPermThreads), 0, stream, g);
+  else
+    hipLaunchKernelGGL(unpack_kernel, dim3((uint32_t)blocks), dim3(kPermThreads), 0, stream, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pack_group(const PermSeg* segs, int n, int64_t s_l, hipStream_t stream) {
+  return launch_group(true, segs, n, s_l, stream);
+}
+
+hipError_t launch_unpack_group(const PermSeg* segs, int n, int64_t s_l, hipStream_t stream) {
+  return launch_group(false, segs, n, s_l, stream);
+}
+
 hipError_t launch_pack(const ShardPtrs& src, void* out, int P, int64_t s_l, int64_t row_bytes,
                        int64_t off_bytes, int64_t run_bytes, hipStream_t stream) {
-  const uint64_t total = (uint64_t)P * s_l * (run_bytes / 16);
-  if (total == 0) return hipSuccess;
-  const uint32_t blocks = (uint32_t)((total + kPermThreads - 1) / kPermThreads);
-  hipLaunchKernelGGL(pack_kernel, dim3(blocks), dim3(kPermThreads), 0, stream, src,
-                     reinterpret_cast<u32x4*>(out), (uint32_t)s_l, (uint32_t)(run_bytes / 16),
-                     (uint32_t)(row_bytes / 16), (uint32_t)(off_bytes / 16), (uint32_t)total);
-  return hipGetLastError();
+  const PermSeg seg{src, out, P, row_bytes, off_bytes, run_bytes};
+  return launch_group(true, &seg, 1, s_l, stream);
 }
 
 hipError_t launch_unpack(const void* in, const ShardPtrs& dst, int P, int64_t s_l, int64_t row_bytes,
                          int64_t off_bytes, int64_t run_bytes, hipStream_t stream) {
-  const uint64_t total = (uint64_t)P * s_l * (run_bytes / 16);
-  if (total == 0) return hipSuccess;
-  const uint32_t blocks = (uint32_t)((total + kPermThreads - 1) / kPermThreads);
-  hipLaunchKernelGGL(unpack_kernel, dim3(blocks), dim3(kPermThreads), 0, stream,
-                     reinterpret_cast<const u32x4*>(in), dst, (uint32_t)s_l, (uint32_t)(run_bytes / 16),
-                     (uint32_t)(row_bytes / 16), (uint32_t)(off_bytes / 16), (uint32_t)total);
-  return hipGetLastError();
+  const PermSeg seg{dst, const_cast<void*>(in), P, row_bytes, off_bytes, run_bytes};
+  return launch_group(false, &seg, 1, s_l, stream);
 }
 
 }  // namespace uly

@@ -52,6 +52,18 @@ struct AttnArgs {
   int n_docs;
 };
 
+// One tensor of a grouped permute: its P shards (P of them used), the head-shard buffer, the
+// shard row size, the byte offset of the rank's heads in a row and the bytes per row moved.
+struct PermSeg {
+  ShardPtrs sh;
+  void* flat;
+  int P;
+  int64_t row_bytes, off_bytes, run_bytes;
+};
+constexpr int kPermGroupMax = ULY_PERM_GROUP_MAX;
+// n tensors (1 <= n <= kPermGroupMax) packed / unpacked by one launch
+hipError_t launch_pack_group(const PermSeg* segs, int n, int64_t s_l, hipStream_t stream);
+hipError_t launch_unpack_group(const PermSeg* segs, int n, int64_t s_l, hipStream_t stream);
 hipError_t launch_pack(const ShardPtrs& src, void* out, int P, int64_t s_l, int64_t row_bytes,
                        int64_t off_bytes, int64_t run_bytes, hipStream_t stream);
 hipError_t launch_unpack(const void* in, const ShardPtrs& dst, int P, int64_t s_l, int64_t row_bytes,
