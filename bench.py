@@ -43,7 +43,16 @@ import workloads as W  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 METRIC = "fwd+bwd causal attention TFLOP/s @64K (8q/2kv heads, d128); % MFMA peak"
-KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "permute.hip", "uly_device.h"]
+# the sources each timed kernel is built from: a stored counter reading is used only while they
+# are unchanged
+KERNEL_SOURCES = {
+    "attn_fwd": ["attn_fwd.hip", "uly_device.h"],
+    "bwd_dkdv": ["attn_bwd.hip", "uly_device.h"],
+    "bwd_dq": ["attn_bwd.hip", "uly_device.h"],
+    "bwd_preprocess": ["attn_bwd.hip", "uly_device.h"],
+    "permute": ["permute.hip", "uly_device.h"],
+}
+ALL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "permute.hip", "uly_device.h"]
 
 
 def counted_pairs(cfg, cu):
@@ -53,9 +62,10 @@ def counted_pairs(cfg, cu):
     return float(cfg.s) ** 2 / 2
 
 
-def source_hash():
+def source_hash(kernel=None):
+    """Hash of the sources `kernel` is built from (all kernel sources when None)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES.get(kernel, ALL_SOURCES):
         with open(os.path.join(ROOT, "ulysses_sequence_parallelism_rank_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -72,7 +82,7 @@ def read_traffic(kernel, workload):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_hash") != source_hash():
+    if vals.get("source_hash") != source_hash(kernel):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
