@@ -60,6 +60,43 @@ def test_fwd_bwd_matches_oracle(s, Hq, Hkv, d, dtype, causal, cu):
     compare("dV", dev_to_f64(dv), wv, bf16=(dtype == "bf16"))
 
 
+@pytest.mark.parametrize("s,Hq,Hkv,d,causal,cu,ramp", [
+    (600, 4, 2, 128, True, None, 8.0),                  # key scale 1 -> 76 along the sequence
+    (1000, 2, 1, 64, True, None, 2.0),                  # steeper: scores up to ~10^3 in log2 units
+    (520, 4, 2, 128, False, [0, 300, 301, 520], 4.0),   # non-causal packed documents
+    (700, 4, 4, 128, True, None, -700.0),               # decreasing scale: the first keys dominate
+])
+def test_growing_scores_match_oracle(s, Hq, Hkv, d, causal, cu, ramp):
+    """Keys scaled by 1 + j / ramp along the sequence, so a row's running maximum keeps growing
+    from tile to tile by far more than any rescale threshold (and, with ramp < 0, shrinking
+    scores after a dominant start): the forward's max tracking and O rescaling (O, LSE), and the
+    backward's P = exp(S - LSE) through dV, against the oracle. dQ and dK are not compared here:
+    with such peaked rows the backward's delta = dO . O, formed from the stored bf16 O (the
+    FlashAttention convention), carries a rounding larger than the true dS of the dominant
+    key, so their error measures that convention, not the kernels (measured: dK max error
+    2.6e-2 at the first case)."""
+    print(f"case growing scores s={s} Hq={Hq} Hkv={Hkv} d={d} causal={causal} cu={cu} ramp={ramp}", flush=True)
+    rng = np.random.default_rng(s + Hq)
+    sc = (1.0 + np.arange(s, dtype=np.float32) / np.float32(ramp))[:, None, None]
+    host = {"q": rng.standard_normal((s, Hq, d), dtype=np.float32),
+            "k": rng.standard_normal((s, Hkv, d), dtype=np.float32) * sc,
+            "v": rng.standard_normal((s, Hkv, d), dtype=np.float32),
+            "do": rng.standard_normal((s, Hq, d), dtype=np.float32)}
+    bits = {n: W.to_bf16_bits(x) for n, x in host.items()}
+    f = {n: W.bits_to_f64(b, "bf16") for n, b in bits.items()}
+    g = {n: to_dev(b, "bf16") for n, b in bits.items()}
+    scale = 1.0 / np.sqrt(d)
+    cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    o, lse = U.attn_fwd(g["q"], g["k"], g["v"], scale, causal, cu_dev)
+    dq, dk, dv = U.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale, causal, cu_dev)
+    torch.cuda.synchronize()
+    wo, wl = OA.forward(f["q"], f["k"], f["v"], scale, causal, cu)
+    compare("O", dev_to_f64(o), wo, bf16=True)
+    compare("LSE", lse.cpu().numpy(), wl, max_abs=LSE_ABS, rel_fro=1e-4)
+    _, _, wv = OA.backward(f["q"], f["k"], f["v"], f["do"], scale, causal, cu)
+    compare("dV", dev_to_f64(dv), wv, bf16=True)
+
+
 def test_deterministic():
     f, g = _inputs(700, 8, 2, 128, "bf16", seed=3)
     outs = []
