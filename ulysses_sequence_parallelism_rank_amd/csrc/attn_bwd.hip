@@ -284,7 +284,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
   // target objects keep the compiler's per-object tracking of LDS DMA exact)
   __shared__ __attribute__((aligned(16))) uint16_t sT0[2 * BMQ * D], sT1[2 * BMQ * D];
   __shared__ __attribute__((aligned(16))) float sS0[2 * BMQ], sS1[2 * BMQ];
-  // P of key group g, half qb: 64 lanes x 16 floats, 16-byte chunks XOR-swizzled by lane/4
+  // P of key group g, half qb: 4 chunks x 64 lanes x 4 floats, chunk-major, so one 16-byte
+  // access per lane of a chunk covers 1 KiB of consecutive slots (no bank conflicts)
   __shared__ __attribute__((aligned(16))) float sP[4][2][64 * 16];
   struct Buf {
     uint16_t* q;
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
     if (wave == 5) __builtin_amdgcn_global_load_lds(a.delta + (int64_t)hq * a.lse_row + qr, b.d, 4, 0, 0);
   };
   auto p_off = [&](int qb, int chunk) {  // float offset of this lane's 16-byte chunk of P
-    return ((kg * 2 + qb) * 64 + lane) * 16 + ((chunk ^ ((lane >> 2) & 3)) << 2);
+    return (((kg * 2 + qb) * 4 + chunk) * 64 + lane) * 4;
   };
   auto pack8 = [](const f32x16& x, int h) {
     u32x4 r;
