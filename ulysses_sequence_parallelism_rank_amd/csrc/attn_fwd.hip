@@ -26,6 +26,8 @@
 //     exact in the final O / l, and most halves skip the O rescale;
 //   * causal / document tiles outside a row block's range are never visited; partial
 //     halves are masked per element; workgroups with the longest key range launch first.
+#include <type_traits>
+
 #include "uly_device.h"
 #include "uly_internal.h"
 
@@ -169,9 +171,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
     }
   };
 
-  if (ntiles > 0) issue_kv(kbeg, 0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int b = t & 1;
+  // one tile; B is the buffer (compile time: the two buffers' LDS addresses then differ by an
+  // immediate offset, so no per-read address arithmetic)
+  auto tile_step = [&](auto B, int t) {
+    constexpr int b = decltype(B)::value;
     const int64_t k0 = kbeg + (int64_t)t * BN;
     wait_dma();
     __syncthreads();  // tile t has landed; every wave is done with tile t-1
@@ -190,7 +193,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
     pv(b, 1, p1);
     // the next tile's DMA after this tile's last LDS read: the wait the compiler places
     // before LDS reads that follow a DMA then falls on the next barrier
-    if (t + 1 < ntiles) issue_kv(k0 + BN, b ^ 1);
+    if (t + 1 < ntiles) issue_kv(k0 + BN, 1 - b);
+  };
+
+  if (ntiles > 0) issue_kv(kbeg, 0);
+  for (int t = 0;;) {
+    if (t >= ntiles) break;
+    tile_step(std::integral_constant<int, 0>{}, t);
+    if (++t >= ntiles) break;
+    tile_step(std::integral_constant<int, 1>{}, t);
+    ++t;
   }
 
   const float lt = half_swap_sum(l);
