@@ -76,23 +76,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
   const int64_t wr0 = m0 + wave * 32;
   const int64_t wr1 = (wr0 + 32 < s ? wr0 + 32 : s) - 1;
   const int64_t last_row = (m0 + BM < s ? m0 + BM : s) - 1;
-  int64_t kbeg = 0, kend = s, wkbeg = 0, wkend = s, w_lo_last = 0, w_hi_first = s;
+  int64_t kbeg = 0, kend = s, w_lo_last = 0, w_hi_first = s;
   if (a.cu != nullptr) {
     kbeg = a.cu[doc_of(a.cu, a.n_docs, m0)];
     kend = a.cu[doc_of(a.cu, a.n_docs, last_row) + 1];
     if (wr0 < s) {
-      wkbeg = a.cu[doc_of(a.cu, a.n_docs, wr0)];
       w_hi_first = a.cu[doc_of(a.cu, a.n_docs, wr0) + 1];
       w_lo_last = a.cu[doc_of(a.cu, a.n_docs, wr1)];
-      wkend = a.cu[doc_of(a.cu, a.n_docs, wr1) + 1];
     }
   }
-  if (a.causal) {
-    kend = kend < last_row + 1 ? kend : last_row + 1;
-    wkend = wkend < wr1 + 1 ? wkend : wr1 + 1;
-  }
+  if (a.causal) kend = kend < last_row + 1 ? kend : last_row + 1;
   kbeg = (kbeg / BN) * BN;
-  const bool wave_has_rows = wr0 < s;
+  // Halves of 32 keys from k0 that every row of this wave sees whole: full_lo <= k0 <= full_hi
+  // (keys inside the sequence, at or after the last row's document start, before the first
+  // row's document end, and, causal, at or before the first row).
+  const int64_t full_lo = w_lo_last;
+  int64_t full_hi = (s < w_hi_first ? s : w_hi_first) - 32;
+  if (a.causal) full_hi = full_hi < wr0 - 31 ? full_hi : wr0 - 31;
+  const bool any_full = wr0 < s && full_hi >= full_lo;
+  const uint32_t full_w = any_full ? (uint32_t)(full_hi - full_lo) : 0u;
   const int ntiles = kbeg < kend ? (int)((kend - kbeg + BN - 1) / BN) : 0;
 
   // tile k0 of K and V from its shard (rows past the sequence end read the shard's last row)
@@ -111,11 +113,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
       S = mfma32x32x16(kf, qf[t], t == 0 ? f32x16{} : S);
     }
   };
-  // the 32 keys from k0 need no mask for any row of this wave
-  auto half_full = [&](int64_t k0) {
-    return wave_has_rows && (k0 + 32 <= s) && (!a.causal || k0 + 31 <= wr0) && k0 + 32 > wkbeg &&
-           k0 < wkend && (a.cu == nullptr || (k0 >= w_lo_last && k0 + 32 <= w_hi_first));
-  };
+  // the 32 keys from k0 need no mask for any row of this wave (one unsigned range compare)
+  auto half_full = [&](int64_t k0) { return any_full && (uint32_t)(k0 - full_lo) <= full_w; };
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
