@@ -62,6 +62,26 @@ def counted_pairs(cfg, cu):
     return float(cfg.s) ** 2 / 2
 
 
+def training_work(cfg, pairs):
+    """Per phase of the training step: (bound, algorithmic work per launch). FLOPs count the
+    visible pairs (4 d N forward, 8 d N dK/dV, 2 d N dQ per q head, 14 d N in all); bytes are
+    the read + write of exactly the moved elements (2 s H_l d e per permuted tensor)."""
+    d, Hq_l, Hkv_l, e, s = cfg.d, cfg.Hq_l, cfg.Hkv_l, cfg.esize, cfg.s
+    return {
+        "attn_fwd": ("mfma", 4.0 * d * pairs * Hq_l),
+        "bwd_dkdv": ("mfma", 8.0 * d * pairs * Hq_l),
+        "bwd_dq": ("mfma", 2.0 * d * pairs * Hq_l),
+        "pack_qkv": ("hbm", 2.0 * s * (Hq_l + 2 * Hkv_l) * d * e),
+        "unpack_o": ("hbm", 2.0 * s * Hq_l * d * e),
+        "pack_do": ("hbm", 2.0 * s * Hq_l * d * e),
+        "bwd_preprocess": ("hbm", 2.0 * s * Hq_l * d * e + 4.0 * s * Hq_l),
+        "unpack_grads": ("hbm", 2.0 * s * (Hq_l + 2 * Hkv_l) * d * e),
+        # the fused calls, timed whole (attn_bwd_shards: preprocess, dK/dV and dQ)
+        "attn_fwd_shards": ("mfma", 4.0 * d * pairs * Hq_l),
+        "attn_bwd_shards": ("mfma", 10.0 * d * pairs * Hq_l),
+    }
+
+
 def source_hash(kernel=None):
     """Hash of the sources `kernel` is built from (all kernel sources when None)."""
     h = hashlib.sha256()
@@ -332,19 +352,7 @@ def main():
     elif not chunked:
         wall, ph, ph_med = run_training_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
         flops = 14.0 * d * pairs * Hq_l
-        kern = {
-            "attn_fwd": ("mfma", 4.0 * d * pairs * Hq_l),
-            "bwd_dkdv": ("mfma", 8.0 * d * pairs * Hq_l),
-            "bwd_dq": ("mfma", 2.0 * d * pairs * Hq_l),
-            "pack_qkv": ("hbm", 2.0 * cfg.s * (Hq_l + 2 * Hkv_l) * d * e),
-            "unpack_o": ("hbm", 2.0 * cfg.s * Hq_l * d * e),
-            "pack_do": ("hbm", 2.0 * cfg.s * Hq_l * d * e),
-            "bwd_preprocess": ("hbm", 2.0 * cfg.s * Hq_l * d * e + 4.0 * cfg.s * Hq_l),
-            "unpack_grads": ("hbm", 2.0 * cfg.s * (Hq_l + 2 * Hkv_l) * d * e),
-            # the fused calls, timed whole (attn_bwd_shards: preprocess, dK/dV and dQ)
-            "attn_fwd_shards": ("mfma", 4.0 * d * pairs * Hq_l),
-            "attn_bwd_shards": ("mfma", 10.0 * d * pairs * Hq_l),
-        }
+        kern = training_work(cfg, pairs)
     else:
         wall, ph, ph_med, ws_bytes = run_upipe(cfg, args.steps, args.warmup, args.heads_per_chunk, args.forward_only)
         # each call is timed whole (per chunk: permutes and attention kernels)
