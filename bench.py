@@ -20,8 +20,11 @@ intermediates.
 replaces the permutes and head-shard buffers by attn_fwd_shards / attn_bwd_shards, which
 read and write the sequence shards directly.
 
+--stored-ds times the training step with the stored-dS backward (dS written once by the dK/dV
+kernel, dQ formed from it; a buffer of attn_bwd_stored_ds_bytes, 34.4 GB at the 64K share).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                       [--heads-per-chunk U] [--forward-only [--fused]]
+                       [--heads-per-chunk U] [--forward-only [--fused]] [--stored-ds]
 """
 import argparse
 import hashlib
@@ -79,6 +82,9 @@ def training_work(cfg, pairs):
         # the fused calls, timed whole (attn_bwd_shards: preprocess, dK/dV and dQ)
         "attn_fwd_shards": ("mfma", 4.0 * d * pairs * Hq_l),
         "attn_bwd_shards": ("mfma", 10.0 * d * pairs * Hq_l),
+        # the stored-dS backward: the same counted FLOPs (dQ then executes only its own product)
+        "bwd_dkdv_store_ds": ("mfma", 8.0 * d * pairs * Hq_l),
+        "bwd_dq_stored_ds": ("mfma", 2.0 * d * pairs * Hq_l),
     }
 
 
@@ -144,7 +150,7 @@ class Phases:
         return mean, {k: float(statistics.median(v)) for k, v in per.items()}
 
 
-def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
+def run_training_share(cfg, steps, warmup, cu_dev, fused=False, stored_ds=False):
     _, sh = make_inputs(cfg)
     rank = 0
     s, Hq_l, Hkv_l, d = cfg.s, cfg.Hq_l, cfg.Hkv_l, cfg.d
@@ -165,6 +171,9 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
     dk_sh = [torch.empty_like(t) for t in sh["k"]]
     dv_sh = [torch.empty_like(t) for t in sh["v"]]
     ph = Phases()
+    ds = None
+    if stored_ds:
+        ds = torch.empty(U.attn_bwd_stored_ds_bytes(s, Hq_l, cfg.causal), dtype=torch.uint8, device=dev)
 
     def step_fused(rec):
         ph.run("attn_fwd_shards", lambda: U.attn_fwd_shards(sh["q"], sh["k"], sh["v"], o_sh, rank, cfg.scale,
@@ -181,9 +190,15 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
         ph.run("unpack_o", lambda: U.ulysses_unpack(o, rank, o_sh), rec)
         ph.run("pack_do", lambda: U.ulysses_pack(sh["do"], rank, do), rec)
         ph.run("bwd_preprocess", lambda: U.attn_bwd_preprocess(o, do, delta), rec)
-        ph.run("bwd_dkdv", lambda: U.attn_bwd_dkdv(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev,
-                                                   dk=dk, dv=dv), rec)
-        ph.run("bwd_dq", lambda: U.attn_bwd_dq(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev, dq=dq), rec)
+        if stored_ds:
+            ph.run("bwd_dkdv_store_ds", lambda: U.attn_bwd_dkdv_store_ds(q, k, v, lse, do, delta, ds, cfg.scale,
+                                                                         cfg.causal, dk=dk, dv=dv), rec)
+            ph.run("bwd_dq_stored_ds", lambda: U.attn_bwd_dq_stored_ds(k, ds, dq, cfg.scale, cfg.causal), rec)
+        else:
+            ph.run("bwd_dkdv", lambda: U.attn_bwd_dkdv(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev,
+                                                       dk=dk, dv=dv), rec)
+            ph.run("bwd_dq", lambda: U.attn_bwd_dq(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev, dq=dq),
+                   rec)
         ph.run("unpack_grads", lambda: U.ulysses_unpack_group([dq, dk, dv], rank, [dq_sh, dk_sh, dv_sh]), rec)
 
     for _ in range(warmup):
@@ -314,6 +329,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="attn_fwd_shards / attn_bwd_shards, reading and writing the sequence shards directly "
                          "(no head-shard buffers, no separate permutes)")
+    ap.add_argument("--stored-ds", action="store_true",
+                    help="training step with the stored-dS backward (attn_bwd_dkdv_store_ds + attn_bwd_dq_stored_ds; "
+                         "a dS buffer of attn_bwd_stored_ds_bytes, 34.4 GB at the 64K share)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy (ulysses_pack with one rank) and exit; "
@@ -337,6 +355,9 @@ def main():
         return
     cfg = W.WORKLOADS[args.workload]
     cu = W.cu_seqlens_for(cfg)
+    if args.stored_ds and (cu is not None or cfg.chunk_heads or cfg.dtype != "bf16" or args.fused or args.forward_only):
+        print("--stored-ds applies to the unpacked bf16 training step only", file=sys.stderr)
+        sys.exit(2)
     cu_dev = None if cu is None else torch.from_numpy(cu).to("cuda")
     pairs = counted_pairs(cfg, cu)
     d, Hq_l, Hkv_l, e = cfg.d, cfg.Hq_l, cfg.Hkv_l, cfg.esize
@@ -350,7 +371,7 @@ def main():
                 "unpack_o": ("hbm", 2.0 * cfg.s * Hq_l * d * e)}
         flops = fw
     elif not chunked:
-        wall, ph, ph_med = run_training_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
+        wall, ph, ph_med = run_training_share(cfg, args.steps, args.warmup, cu_dev, args.fused, args.stored_ds)
         flops = 14.0 * d * pairs * Hq_l
         kern = training_work(cfg, pairs)
     else:
@@ -378,16 +399,17 @@ def main():
     roof["traffic"] = read_traffic(dom, args.workload)
 
     attn_ms = sum(ph.get(k, 0.0) for k in ("attn_fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "attn_fwd_chunked",
-                                           "attn_bwd_chunked", "attn_fwd_shards", "attn_bwd_shards"))
+                                           "attn_bwd_chunked", "attn_fwd_shards", "attn_bwd_shards",
+                                           "bwd_dkdv_store_ds", "bwd_dq_stored_ds"))
     # the permutes' rate from the per-phase medians (see Phases.summary: the first phase of the
     # first timed step also holds a host launch latency, a sizeable part of a 0.08 ms phase)
     perm_ms = sum(ph_med.get(k, 0.0) for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads"))
     perm_bytes = sum(kern[k][1] for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads") if k in ph)
     value = flops / wall / 1e12
     out = {
-        "metric": METRIC if args.workload == "qwen_64k" and not args.forward_only and not args.fused else
+        "metric": METRIC if args.workload == "qwen_64k" and not (args.forward_only or args.fused or args.stored_ds) else
         f"{METRIC} [workload {args.workload}{', forward only' if args.forward_only else ''}"
-        f"{', fused exchange' if args.fused else ''}]",
+        f"{', fused exchange' if args.fused else ''}{', stored dS' if args.stored_ds else ''}]",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

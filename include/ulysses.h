@@ -164,6 +164,28 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                 const int32_t* cu_seqlens, int n_docs, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Stored-dS backward (opt-in; bf16, no cu_seqlens): the attention backward of "how Ulysses
+ * works" step 4 with dS computed once. attn_bwd_dkdv_store_ds does what attn_bwd_dkdv does and
+ * also writes dS = P (dP - delta) (bf16, unscaled, exactly the operand of its dK product) into
+ * `ds`; attn_bwd_dq_stored_ds then forms dQ = scale dS K from it without recomputing S and dP.
+ * Together they replace attn_bwd_dkdv + attn_bwd_dq (same inputs and outputs).
+ *   ds       : device buffer of at least attn_bwd_stored_ds_bytes(s, Hq, causal) bytes, owned
+ *              by the caller: Hq * ceil(s/128) * ceil(s/64) tiles of 16 KiB when non-causal,
+ *              about half as many when causal (34.4 GB for s = 65536, Hq = 8, causal). Its
+ *              layout is private to the two calls; it must not change between them.
+ *   ds_bytes : its size in bytes (ULY_ERR_WORKSPACE when too small)
+ *   attn_bwd_dq_stored_ds reads k [s, Hkv, d] and ds, writes dq [s, Hq, d]; scale and causal
+ *   must be those given to attn_bwd_dkdv_store_ds.
+ * ULY_ERR_UNSUPPORTED for fp32.
+ * ------------------------------------------------------------------------- */
+size_t attn_bwd_stored_ds_bytes(int64_t s, int Hq, int causal);
+int attn_bwd_dkdv_store_ds(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                           const float* delta, void* dk, void* dv, void* ds, size_t ds_bytes, int64_t s, int Hq,
+                           int Hkv, int d, int dtype, float scale, int causal, void* stream);
+int attn_bwd_dq_stored_ds(const void* k, const void* ds, size_t ds_bytes, void* dq, int64_t s, int Hq, int Hkv,
+                          int d, int dtype, float scale, int causal, void* stream);
+
+/* ---------------------------------------------------------------------------
  * attn_fwd_chunked -- the UPipe headwise-chunked forward of rank `rank` (tilnote.io
  * commentary, section on activation memory: process a few heads at a time to cut the
  * memory of attention intermediates). For each chunk of `heads_per_chunk` local q

@@ -12,6 +12,7 @@ The names follow the C ABI in include/ulysses.h:
   attn_fwd_chunked                    -- the UPipe headwise-chunked forward
   attn_bwd_chunked                    -- its backward
   attn_fwd_shards, attn_bwd_shards    -- forward / backward reading and writing the sequence shards
+  attn_bwd_dkdv_store_ds, attn_bwd_dq_stored_ds -- the backward with dS stored once (opt-in)
 """
 from __future__ import annotations
 
@@ -62,6 +63,10 @@ SIGNATURES = {
     "attn_fwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                _i32, _vp, _i32, _vp]),
     "uly_mfma_probe": (_i32, [_i32, _i32, _vp, _vp, _vp]),
+    "attn_bwd_stored_ds_bytes": (_sz, [_i64, _i32, _i32]),
+    "attn_bwd_dkdv_store_ds": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i32, _i32, _i32,
+                                      _i32, _f32, _i32, _vp]),
+    "attn_bwd_dq_stored_ds": (_i32, [_vp, _vp, _sz, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
     "attn_bwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vpp, _vpp, _vpp, _vpp, _i32, _i32, _i64, _i32,
                                _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _szp, _vp]),
 }
@@ -240,6 +245,33 @@ def attn_bwd_dkdv(q, k, v, lse, dout, delta, scale=None, causal=True, cu_seqlens
     _call("attn_bwd_dkdv", _dev(q), _dev(k), _dev(v), _dev(lse), _dev(dout), _dev(delta), _dev(dk), _dev(dv),
           s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, _stream())
     return dk, dv
+
+
+def attn_bwd_stored_ds_bytes(s, Hq, causal=True):
+    """Bytes of the dS buffer the stored-dS backward needs (s tokens, Hq local q heads)."""
+    return int(lib().attn_bwd_stored_ds_bytes(s, Hq, int(causal)))
+
+
+def attn_bwd_dkdv_store_ds(q, k, v, lse, dout, delta, ds, scale=None, causal=True, dk=None, dv=None):
+    """attn_bwd_dkdv that also writes dS into `ds` (a uint8 device tensor of at least
+    attn_bwd_stored_ds_bytes bytes) for attn_bwd_dq_stored_ds."""
+    s, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _call("attn_bwd_dkdv_store_ds", _dev(q), _dev(k), _dev(v), _dev(lse), _dev(dout), _dev(delta), _dev(dk),
+          _dev(dv), _dev(ds), ds.numel() * ds.element_size(), s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale),
+          int(causal), _stream())
+    return dk, dv
+
+
+def attn_bwd_dq_stored_ds(k, ds, dq, scale=None, causal=True):
+    """dQ [s, Hq, d] (written into dq) from the dS that attn_bwd_dkdv_store_ds stored."""
+    s, Hq, d = dq.shape
+    Hkv = k.shape[1]
+    _call("attn_bwd_dq_stored_ds", _dev(k), _dev(ds), ds.numel() * ds.element_size(), _dev(dq), s, Hq, Hkv, d,
+          _dtype(dq), _default_scale(d, scale), int(causal), _stream())
+    return dq
 
 
 def attn_bwd_dq(q, k, v, lse, dout, delta, scale=None, causal=True, cu_seqlens=None, dq=None):

@@ -299,6 +299,52 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, c
   return hip_status(e);
 }
 
+size_t attn_bwd_stored_ds_bytes(int64_t s, int Hq, int causal) {
+  if (s < 1 || Hq < 1 || s > (int64_t)INT32_MAX) return 0;
+  return (size_t)Hq * (size_t)ds_tiles_per_head(s, causal ? 1 : 0) * (128 * 64 * sizeof(uint16_t));
+}
+
+int attn_bwd_dkdv_store_ds(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                           const float* delta, void* dk, void* dv, void* ds, size_t ds_bytes, int64_t s, int Hq,
+                           int Hkv, int d, int dtype, float scale, int causal, void* stream) {
+  int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, nullptr, 0);
+  if (st != ULY_OK) return st;
+  if (dtype != ULY_BF16) return ULY_ERR_UNSUPPORTED;
+  if (!lse || !dout || !delta || !dk || !dv || !ds) return ULY_ERR_NULL;
+  if (!aligned16(lse) || !aligned16(dout) || !aligned16(delta) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(ds))
+    return ULY_ERR_ALIGN;
+  if (ds_bytes < attn_bwd_stored_ds_bytes(s, Hq, causal)) return ULY_ERR_WORKSPACE;
+  AttnArgs a = make_args(s, Hq, Hkv, d, scale, causal, nullptr, 0);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse_in = lse;
+  a.delta = delta;
+  a.out_k = dk;
+  a.out_v = dv;
+  a.ds = static_cast<uint16_t*>(ds);
+  a.ds_head_tiles = ds_tiles_per_head(s, a.causal);
+  return hip_status(launch_attn_dkdv_bf16(a, d, as_stream(stream)));
+}
+
+int attn_bwd_dq_stored_ds(const void* k, const void* ds, size_t ds_bytes, void* dq, int64_t s, int Hq, int Hkv,
+                          int d, int dtype, float scale, int causal, void* stream) {
+  int st = check_attn(k, k, k, s, Hq, Hkv, d, dtype, nullptr, 0);
+  if (st != ULY_OK) return st;
+  if (dtype != ULY_BF16) return ULY_ERR_UNSUPPORTED;
+  if (!ds || !dq) return ULY_ERR_NULL;
+  if (!aligned16(ds) || !aligned16(dq)) return ULY_ERR_ALIGN;
+  if (ds_bytes < attn_bwd_stored_ds_bytes(s, Hq, causal)) return ULY_ERR_WORKSPACE;
+  AttnArgs a = make_args(s, Hq, Hkv, d, scale, causal, nullptr, 0);
+  a.k = k;
+  a.out = dq;
+  a.ds = static_cast<uint16_t*>(const_cast<void*>(ds));
+  a.ds_head_tiles = ds_tiles_per_head(s, a.causal);
+  return hip_status(launch_attn_dq_from_ds_bf16(a, d, as_stream(stream)));
+}
+
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
              void* dq, void* dk, void* dv, int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
              const int32_t* cu_seqlens, int n_docs, void* workspace, size_t* workspace_bytes, void* stream) {
