@@ -17,6 +17,8 @@
  *      intermediates stay small                    -> attn_fwd_chunked, attn_bwd_chunked
  *   5. 1-3 with the exchange folded into the attention's own loads and stores: the
  *      kernels read the sequence shards directly      -> attn_fwd_shards, attn_bwd_shards
+ *   6. opt-in: the backward of 2 with dS computed once and stored
+ *                                        -> attn_bwd_dkdv_store_ds, attn_bwd_dq_stored_ds
  * The P ranks are P separate device buffers on one GPU; no collective runs here.
  * uly_mfma_probe is a measurement helper outside the path.
  *
