@@ -239,3 +239,28 @@ def test_probe_rejects():
     assert L.uly_mfma_probe(0, 4, FAKE, FAKE, None) == 2
     assert L.uly_mfma_probe(4, 0, FAKE, FAKE, None) == 2
     assert L.uly_mfma_probe(4, 4, None, FAKE, None) == 1
+
+
+def test_stored_ds_bytes_closed_form():
+    L = U.lib()
+    # 16 KiB tiles of 128 keys x 64 rows: causal key block kb holds query tiles [2 kb, nqt)
+    for s, Hq in ((1, 1), (64, 2), (129, 3), (600, 4), (65536, 8)):
+        nkb, nqt = -(-s // 128), -(-s // 64)
+        causal_tiles = sum(nqt - 2 * kb for kb in range(nkb))
+        assert L.attn_bwd_stored_ds_bytes(s, Hq, 1) == Hq * causal_tiles * 16384
+        assert L.attn_bwd_stored_ds_bytes(s, Hq, 0) == Hq * nkb * nqt * 16384
+    assert L.attn_bwd_stored_ds_bytes(65536, 8, 1) == 34426847232  # 34.4 GB at the 64K share
+    assert L.attn_bwd_stored_ds_bytes(0, 8, 1) == 0 and L.attn_bwd_stored_ds_bytes(16, 0, 1) == 0
+
+
+def test_stored_ds_rejects_on_the_host():
+    L = U.lib()
+    need = L.attn_bwd_stored_ds_bytes(64, 4, 1)
+    dkdv = lambda **kw: L.attn_bwd_dkdv_store_ds(*[kw.get(n, FAKE) for n in ("q", "k", "v", "lse", "do", "dl", "dk", "dv", "ds")],
+                                                  kw.get("nb", need), 64, 4, 2, 128, kw.get("dt", 0), 0.1, 1, None)
+    dq = lambda **kw: L.attn_bwd_dq_stored_ds(kw.get("k", FAKE), kw.get("ds", FAKE), kw.get("nb", need), kw.get("dq", FAKE),
+                                             64, 4, 2, 128, kw.get("dt", 0), 0.1, 1, None)
+    assert dkdv(dt=1) == 3 and dq(dt=1) == 3          # bf16 only
+    assert dkdv(ds=None) == 1 and dq(ds=None) == 1 and dq(dq=None) == 1
+    assert dkdv(ds=MIS) == 4 and dq(dq=MIS) == 4
+    assert dkdv(nb=need - 1) == 5 and dq(nb=need - 1) == 5
