@@ -20,11 +20,15 @@ intermediates.
 replaces the permutes and head-shard buffers by attn_fwd_shards / attn_bwd_shards, which
 read and write the sequence shards directly.
 
---stored-ds times the training step with the stored-dS backward (dS written once by the dK/dV
-kernel, dQ formed from it; a buffer of attn_bwd_stored_ds_bytes, 34.4 GB at the 64K share).
+The forward writes O's bf16 rounding residual (o_lo) and the backward forms delta from
+O + o_lo, as the library's tests do.
+
+Besides the step, the permutes are timed cold: each permute of the step is run alone after a
+512 MiB write that evicts the 256 MB Infinity Cache and the L2s, several times, and reported
+with median, min and max; their rate against the 8 TB/s HBM peak is `permute_roofline`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                       [--heads-per-chunk U] [--forward-only [--fused]] [--stored-ds]
+                       [--heads-per-chunk U] [--forward-only [--fused]]
 """
 import argparse
 import hashlib
@@ -77,14 +81,12 @@ def training_work(cfg, pairs):
         "pack_qkv": ("hbm", 2.0 * s * (Hq_l + 2 * Hkv_l) * d * e),
         "unpack_o": ("hbm", 2.0 * s * Hq_l * d * e),
         "pack_do": ("hbm", 2.0 * s * Hq_l * d * e),
-        "bwd_preprocess": ("hbm", 2.0 * s * Hq_l * d * e + 4.0 * s * Hq_l),
+        # O, its residual and dO read, delta written
+        "bwd_preprocess": ("hbm", (3.0 if cfg.dtype == "bf16" else 2.0) * s * Hq_l * d * e + 4.0 * s * Hq_l),
         "unpack_grads": ("hbm", 2.0 * s * (Hq_l + 2 * Hkv_l) * d * e),
         # the fused calls, timed whole (attn_bwd_shards: preprocess, dK/dV and dQ)
         "attn_fwd_shards": ("mfma", 4.0 * d * pairs * Hq_l),
         "attn_bwd_shards": ("mfma", 10.0 * d * pairs * Hq_l),
-        # the stored-dS backward: the same counted FLOPs (dQ then executes only its own product)
-        "bwd_dkdv_store_ds": ("mfma", 8.0 * d * pairs * Hq_l),
-        "bwd_dq_stored_ds": ("mfma", 2.0 * d * pairs * Hq_l),
     }
 
 
@@ -140,17 +142,18 @@ class Phases:
         return r
 
     def summary(self, steps):
-        """Per phase: the mean over the timed steps, and the median. The first timed step starts
-        on an idle GPU (the region opens with a synchronize), so its first phase also holds the
-        host's time to issue that call; the median is free of it."""
+        """Per phase: the mean over the timed steps, and the median, min and max. The first timed
+        step starts on an idle GPU (the region opens with a synchronize), so its first phase also
+        holds the host's time to issue that call; the median is free of it."""
         per = {}
         for name, a, b in self.marks:
             per.setdefault(name, []).append(a.elapsed_time(b))
         mean = {k: sum(v) / steps for k, v in per.items()}
-        return mean, {k: float(statistics.median(v)) for k, v in per.items()}
+        spread = {k: {"median": float(statistics.median(v)), "min": min(v), "max": max(v)} for k, v in per.items()}
+        return mean, spread
 
 
-def run_training_share(cfg, steps, warmup, cu_dev, fused=False, stored_ds=False):
+def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
     _, sh = make_inputs(cfg)
     rank = 0
     s, Hq_l, Hkv_l, d = cfg.s, cfg.Hq_l, cfg.Hkv_l, cfg.d
@@ -161,6 +164,7 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False, stored_ds=False)
     k = torch.empty((s, Hkv_l, d), dtype=dt, device=dev)
     v = torch.empty_like(k)
     o = torch.empty_like(q)
+    o_lo = U.new_o_lo(q) if cfg.dtype == "bf16" else None
     lse = torch.empty((Hq_l, s), dtype=torch.float32, device=dev)
     do = torch.empty_like(q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -171,34 +175,27 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False, stored_ds=False)
     dk_sh = [torch.empty_like(t) for t in sh["k"]]
     dv_sh = [torch.empty_like(t) for t in sh["v"]]
     ph = Phases()
-    ds = None
-    if stored_ds:
-        ds = torch.empty(U.attn_bwd_stored_ds_bytes(s, Hq_l, cfg.causal), dtype=torch.uint8, device=dev)
 
     def step_fused(rec):
         ph.run("attn_fwd_shards", lambda: U.attn_fwd_shards(sh["q"], sh["k"], sh["v"], o_sh, rank, cfg.scale,
-                                                            cfg.causal, cu_dev, lse=lse), rec)
+                                                            cfg.causal, cu_dev, lse=lse, o_lo=o_lo), rec)
         ph.run("attn_bwd_shards", lambda: U.attn_bwd_shards(sh["q"], sh["k"], sh["v"], o_sh, lse, sh["do"], dq_sh,
                                                             dk_sh, dv_sh, rank, cfg.scale, cfg.causal, cu_dev,
-                                                            workspace=ws), rec)
+                                                            workspace=ws, o_lo=o_lo), rec)
 
     def step(rec):
         if fused:
             return step_fused(rec)
         ph.run("pack_qkv", lambda: U.ulysses_pack_group([sh["q"], sh["k"], sh["v"]], rank, [q, k, v]), rec)
-        ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse), rec)
+        ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse, o_lo=o_lo),
+               rec)
         ph.run("unpack_o", lambda: U.ulysses_unpack(o, rank, o_sh), rec)
         ph.run("pack_do", lambda: U.ulysses_pack(sh["do"], rank, do), rec)
-        ph.run("bwd_preprocess", lambda: U.attn_bwd_preprocess(o, do, delta), rec)
-        if stored_ds:
-            ph.run("bwd_dkdv_store_ds", lambda: U.attn_bwd_dkdv_store_ds(q, k, v, lse, do, delta, ds, cfg.scale,
-                                                                         cfg.causal, dk=dk, dv=dv), rec)
-            ph.run("bwd_dq_stored_ds", lambda: U.attn_bwd_dq_stored_ds(k, ds, dq, cfg.scale, cfg.causal), rec)
-        else:
-            ph.run("bwd_dkdv", lambda: U.attn_bwd_dkdv(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev,
-                                                       dk=dk, dv=dv), rec)
-            ph.run("bwd_dq", lambda: U.attn_bwd_dq(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev, dq=dq),
-                   rec)
+        ph.run("bwd_preprocess", lambda: U.attn_bwd_preprocess(o, do, delta, o_lo=o_lo), rec)
+        ph.run("bwd_dkdv", lambda: U.attn_bwd_dkdv(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev,
+                                                   dk=dk, dv=dv), rec)
+        ph.run("bwd_dq", lambda: U.attn_bwd_dq(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev, dq=dq),
+               rec)
         ph.run("unpack_grads", lambda: U.ulysses_unpack_group([dq, dk, dv], rank, [dq_sh, dk_sh, dv_sh]), rec)
 
     for _ in range(warmup):
@@ -209,7 +206,35 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False, stored_ds=False)
         step(True)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    return (wall,) + ph.summary(steps)
+    cold = None
+    if not fused:
+        cold = cold_permutes({
+            "pack_qkv": lambda: U.ulysses_pack_group([sh["q"], sh["k"], sh["v"]], rank, [q, k, v]),
+            "unpack_o": lambda: U.ulysses_unpack(o, rank, o_sh),
+            "pack_do": lambda: U.ulysses_pack(sh["do"], rank, do),
+            "unpack_grads": lambda: U.ulysses_unpack_group([dq, dk, dv], rank, [dq_sh, dk_sh, dv_sh]),
+        })
+    return (wall,) + ph.summary(steps) + (cold,)
+
+
+def cold_permutes(calls, reps=7):
+    """Each permute alone, `reps` times, each time after a 512 MiB write that evicts the 256 MB
+    Infinity Cache and the L2s: per phase the median, min and max in ms."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    out = {}
+    for name, fn in calls.items():
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        out[name] = {"median": float(statistics.median(ts)), "min": min(ts), "max": max(ts)}
+    del flush
+    return out
 
 
 def run_forward_share(cfg, steps, warmup, cu_dev, fused):
@@ -227,13 +252,16 @@ def run_forward_share(cfg, steps, warmup, cu_dev, fused):
     o_sh = [torch.empty_like(t) for t in sh["q"]]
     ph = Phases()
 
+    o_lo = U.new_o_lo(q) if cfg.dtype == "bf16" else None
+
     def step(rec):
         if fused:
             ph.run("attn_fwd_shards", lambda: U.attn_fwd_shards(sh["q"], sh["k"], sh["v"], o_sh, rank, cfg.scale,
-                                                                cfg.causal, cu_dev, lse=lse), rec)
+                                                                cfg.causal, cu_dev, lse=lse, o_lo=o_lo), rec)
             return
         ph.run("pack_qkv", lambda: U.ulysses_pack_group([sh["q"], sh["k"], sh["v"]], rank, [q, k, v]), rec)
-        ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse), rec)
+        ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse, o_lo=o_lo),
+               rec)
         ph.run("unpack_o", lambda: U.ulysses_unpack(o, rank, o_sh), rec)
 
     for _ in range(warmup):
@@ -255,6 +283,7 @@ def run_upipe(cfg, steps, warmup, u, forward_only):
     dk_sh = [torch.empty_like(t) for t in sh["k"]]
     dv_sh = [torch.empty_like(t) for t in sh["v"]]
     lse = torch.empty((cfg.Hq_l, cfg.s), dtype=torch.float32, device="cuda")
+    o_lo = torch.empty((cfg.s, cfg.Hq_l, cfg.d), dtype=torch.bfloat16, device="cuda")
     args = (cfg.P, cfg.s_l, cfg.Hq, cfg.Hkv, cfg.d, torch.bfloat16, u)
     need = {"fwd": U.attn_fwd_chunked_workspace_bytes(*args)}
     if not forward_only:
@@ -266,11 +295,11 @@ def run_upipe(cfg, steps, warmup, u, forward_only):
             torch.cuda.synchronize()
             t0 = time.perf_counter()
         ph.run("attn_fwd_chunked", lambda: U.attn_fwd_chunked(sh["q"], sh["k"], sh["v"], o_sh, 0, u, cfg.scale,
-                                                              cfg.causal, None, ws, lse), i >= warmup)
+                                                              cfg.causal, None, ws, lse, o_lo=o_lo), i >= warmup)
         if not forward_only:
             ph.run("attn_bwd_chunked", lambda: U.attn_bwd_chunked(sh["q"], sh["k"], sh["v"], o_sh, lse, sh["do"],
                                                                   dq_sh, dk_sh, dv_sh, 0, u, cfg.scale, cfg.causal,
-                                                                  None, ws), i >= warmup)
+                                                                  None, ws, o_lo=o_lo), i >= warmup)
     torch.cuda.synchronize()
     return ((time.perf_counter() - t0) / steps,) + ph.summary(steps) + (need,)
 
@@ -298,9 +327,20 @@ def measured_ceilings():
                    "copy: 1 GiB read + 1 GiB written by ulysses_pack with one rank"}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg):
     """The oracle, untuned, on a bounded sample of the same workload: one q head (and its kv
-    head) over the first `prefix` tokens of the sequence, causal forward + backward."""
+    head) over the first `prefix` tokens of the sequence, causal forward + backward. `cores`
+    is the host cores this process may run on; the BLAS threads numpy used are listed too."""
     from threadpoolctl import threadpool_info
 
     from oracle import attention as OA
@@ -312,7 +352,8 @@ def cpu_baseline(cfg):
     dt = time.perf_counter() - t0
     flops = 14.0 * cfg.d * prefix * prefix / 2
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model(), "blas_threads": int(threads), "kind": "oracle",
             "sample": f"numpy fp64 oracle, causal fwd+bwd of 1 q head (+ its kv head) over the first {prefix} "
                       f"tokens, d={cfg.d}; {dt:.1f} s; FLOPs counted as in the metric"}
 
@@ -329,9 +370,6 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="attn_fwd_shards / attn_bwd_shards, reading and writing the sequence shards directly "
                          "(no head-shard buffers, no separate permutes)")
-    ap.add_argument("--stored-ds", action="store_true",
-                    help="training step with the stored-dS backward (attn_bwd_dkdv_store_ds + attn_bwd_dq_stored_ds; "
-                         "a dS buffer of attn_bwd_stored_ds_bytes, 34.4 GB at the 64K share)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy (ulysses_pack with one rank) and exit; "
@@ -355,27 +393,25 @@ def main():
         return
     cfg = W.WORKLOADS[args.workload]
     cu = W.cu_seqlens_for(cfg)
-    if args.stored_ds and (cu is not None or cfg.chunk_heads or cfg.dtype != "bf16" or args.fused or args.forward_only):
-        print("--stored-ds applies to the unpacked bf16 training step only", file=sys.stderr)
-        sys.exit(2)
     cu_dev = None if cu is None else torch.from_numpy(cu).to("cuda")
     pairs = counted_pairs(cfg, cu)
     d, Hq_l, Hkv_l, e = cfg.d, cfg.Hq_l, cfg.Hkv_l, cfg.esize
 
     chunked = bool(cfg.chunk_heads)
+    cold = None
     if not chunked and args.forward_only:
-        wall, ph, ph_med = run_forward_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
+        wall, ph, spread = run_forward_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
         fw = 4.0 * d * pairs * Hq_l
         kern = {"attn_fwd": ("mfma", fw), "attn_fwd_shards": ("mfma", fw),
                 "pack_qkv": ("hbm", 2.0 * cfg.s * (Hq_l + 2 * Hkv_l) * d * e),
                 "unpack_o": ("hbm", 2.0 * cfg.s * Hq_l * d * e)}
         flops = fw
     elif not chunked:
-        wall, ph, ph_med = run_training_share(cfg, args.steps, args.warmup, cu_dev, args.fused, args.stored_ds)
+        wall, ph, spread, cold = run_training_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
         flops = 14.0 * d * pairs * Hq_l
         kern = training_work(cfg, pairs)
     else:
-        wall, ph, ph_med, ws_bytes = run_upipe(cfg, args.steps, args.warmup, args.heads_per_chunk, args.forward_only)
+        wall, ph, spread, ws_bytes = run_upipe(cfg, args.steps, args.warmup, args.heads_per_chunk, args.forward_only)
         # each call is timed whole (per chunk: permutes and attention kernels)
         kern = {"attn_fwd_chunked": ("mfma", 4.0 * d * pairs * Hq_l)}
         if not args.forward_only:
@@ -399,17 +435,17 @@ def main():
     roof["traffic"] = read_traffic(dom, args.workload)
 
     attn_ms = sum(ph.get(k, 0.0) for k in ("attn_fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "attn_fwd_chunked",
-                                           "attn_bwd_chunked", "attn_fwd_shards", "attn_bwd_shards",
-                                           "bwd_dkdv_store_ds", "bwd_dq_stored_ds"))
-    # the permutes' rate from the per-phase medians (see Phases.summary: the first phase of the
-    # first timed step also holds a host launch latency, a sizeable part of a 0.08 ms phase)
-    perm_ms = sum(ph_med.get(k, 0.0) for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads"))
-    perm_bytes = sum(kern[k][1] for k in ("pack_qkv", "unpack_o", "pack_do", "unpack_grads") if k in ph)
+                                           "attn_bwd_chunked", "attn_fwd_shards", "attn_bwd_shards"))
+    # the permutes' rate inside the step from the per-phase medians (see Phases.summary: the first
+    # phase of the first timed step also holds a host launch latency)
+    perm_names = ("pack_qkv", "unpack_o", "pack_do", "unpack_grads")
+    perm_ms = sum(spread[k]["median"] for k in perm_names if k in spread)
+    perm_bytes = sum(kern[k][1] for k in perm_names if k in ph)
     value = flops / wall / 1e12
     out = {
-        "metric": METRIC if args.workload == "qwen_64k" and not (args.forward_only or args.fused or args.stored_ds) else
+        "metric": METRIC if args.workload == "qwen_64k" and not (args.forward_only or args.fused) else
         f"{METRIC} [workload {args.workload}{', forward only' if args.forward_only else ''}"
-        f"{', fused exchange' if args.fused else ''}{', stored dS' if args.stored_ds else ''}]",
+        f"{', fused exchange' if args.fused else ''}]",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -437,8 +473,20 @@ def main():
         "attention_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2) if attn_ms else None,
         "permute_gbs": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1) if perm_ms else None,
         "phase_ms": {k: round(v, 4) for k, v in ph.items()},
-        "phase_ms_median": {k: round(v, 4) for k, v in ph_med.items()},
+        "phase_ms_median": {k: round(v["median"], 4) for k, v in spread.items()},
+        "phase_ms_min": {k: round(v["min"], 4) for k, v in spread.items()},
+        "phase_ms_max": {k: round(v["max"], 4) for k, v in spread.items()},
     }
+    if cold:
+        # the permutes alone on a cold cache: HBM rate of their algorithmic bytes
+        cold_ms = sum(v["median"] for v in cold.values())
+        cold_bytes = sum(kern[k][1] for k in cold)
+        gbs = cold_bytes / (cold_ms * 1e-3) / 1e9
+        out["permute_roofline"] = {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": cold_bytes, "ms": round(cold_ms, 4),
+            "how": "each permute of the step alone after a 512 MiB cache-evicting write, 7 runs, medians",
+            "phases": {k: {m: round(x, 4) for m, x in v.items()} for k, v in cold.items()}}
     if chunked:
         # peak intermediate bytes: the chunked calls' workspaces against the unchunked head shards
         # (forward: Q, O, K, V; training adds dO, dQ, dK, dV and delta)
@@ -449,6 +497,8 @@ def main():
     out["measured_ceilings"] = ceil
     roof["frac_of_measured"] = round(roof["achieved"] / (ceil["mfma_bf16_tflops"] if bound == "mfma"
                                                          else ceil["copy_gbs"]), 4)
+    if "permute_roofline" in out:
+        out["permute_roofline"]["frac_of_measured"] = round(out["permute_roofline"]["achieved"] / ceil["copy_gbs"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)

@@ -17,8 +17,6 @@
  *      intermediates stay small                    -> attn_fwd_chunked, attn_bwd_chunked
  *   5. 1-3 with the exchange folded into the attention's own loads and stores: the
  *      kernels read the sequence shards directly      -> attn_fwd_shards, attn_bwd_shards
- *   6. opt-in: the backward of 2 with dS computed once and stored
- *                                        -> attn_bwd_dkdv_store_ds, attn_bwd_dq_stored_ds
  * The P ranks are P separate device buffers on one GPU; no collective runs here.
  * uly_mfma_probe is a measurement helper outside the path.
  *
@@ -38,6 +36,14 @@
  *     precondition and are not checked.
  *   - Base pointers must be 16-byte aligned.
  *   - Status codes are the uly_status values below; uly_status_string() names them.
+ *   - o_lo (optional, bf16 only, NULL allowed everywhere): the forward's bf16 O is O_fp32
+ *     rounded once; o_lo receives that rounding's residual, O_fp32 - bf16(O_fp32), itself
+ *     rounded to bf16, in the rank's head-shard layout [s, Hq_l, d] (Hq_l = the local q
+ *     heads) whatever layout O has. A backward given the same o_lo forms
+ *     delta_i = dO_i . (O_i + o_lo_i), i.e. from O to about 16 significant bits. Without it
+ *     delta is formed from the bf16 O (the FlashAttention convention), whose rounding
+ *     cancels against dP on rows where one key holds nearly all the softmax weight and
+ *     then dominates dS there. ULY_ERR_UNSUPPORTED for a non-NULL o_lo with ULY_F32.
  */
 #ifndef ULYSSES_H
 #define ULYSSES_H
@@ -118,6 +124,7 @@ int ulysses_unpack_group(int n, const void* const* in, const int* H, void* const
  * SFTTrainer section (packed documents).
  *   q [s, Hq, d], k, v [s, Hkv, d] : device, `dtype`; Hq = local q heads, Hq % Hkv == 0
  *   o [s, Hq, d]                   : device, `dtype`, written
+ *   o_lo [s, Hq, d]                : device bf16 or NULL: O's rounding residual (above)
  *   lse [Hq, s]                    : device fp32, written; natural-log log-sum-exp of
  *                                    each row's visible scaled scores
  *   scale  : multiplies q.k (1/sqrt(d) for the standard layer)
@@ -126,7 +133,7 @@ int ulysses_unpack_group(int n, const void* const* in, const int* H, void* const
  *                keys are then further restricted to the row's own document
  * Every row must see at least one key (true whenever causal or cu_seqlens is used).
  * ------------------------------------------------------------------------- */
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+int attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,
              int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
              const int32_t* cu_seqlens, int n_docs, void* stream);
 
@@ -135,6 +142,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * forward's o and lse. Runs attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq.
  * The gradient of a kv head sums the G = Hq/Hkv q heads that read it.
  *   q, k, v, o, lse, dout : as produced/consumed by attn_fwd (dout shaped like o)
+ *   o_lo  : the residual attn_fwd wrote, or NULL (delta then from the bf16 o)
  *   dq [s, Hq, d], dk, dv [s, Hkv, d] : device `dtype`, written (fully overwritten)
  *   workspace : device scratch of at least attn_bwd_workspace_bytes(s, Hq) bytes.
  *               If workspace == NULL the call only stores that size into
@@ -142,8 +150,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *               workspace_bytes != NULL) is the capacity and is checked.
  * Deterministic: no atomics, every output element is written by one thread.
  * ------------------------------------------------------------------------- */
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-             const void* dout, void* dq, void* dk, void* dv,
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* o_lo,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv,
              int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
              const int32_t* cu_seqlens, int n_docs,
              void* workspace, size_t* workspace_bytes, void* stream);
@@ -151,8 +159,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
 size_t attn_bwd_workspace_bytes(int64_t s, int Hq);
 
 /* The three phases of attn_bwd, exported so that each can be timed on its own.
- * delta [Hq, s] fp32: delta[h, i] = sum_x dout[i, h, x] * o[i, h, x].            */
-int attn_bwd_preprocess(const void* o, const void* dout, float* delta,
+ * delta [Hq, s] fp32: delta[h, i] = sum_x dout[i, h, x] * (o[i, h, x] + o_lo[i, h, x])
+ * (o_lo NULL: the o term alone).                                                    */
+int attn_bwd_preprocess(const void* o, const void* o_lo, const void* dout, float* delta,
                         int64_t s, int Hq, int d, int dtype, void* stream);
 /* dk, dv for every key: per kv head, loops over the rows of its G q heads.        */
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
@@ -166,28 +175,6 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                 const int32_t* cu_seqlens, int n_docs, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Stored-dS backward (opt-in; bf16, no cu_seqlens): the attention backward of "how Ulysses
- * works" step 4 with dS computed once. attn_bwd_dkdv_store_ds does what attn_bwd_dkdv does and
- * also writes dS = P (dP - delta) (bf16, unscaled, exactly the operand of its dK product) into
- * `ds`; attn_bwd_dq_stored_ds then forms dQ = scale dS K from it without recomputing S and dP.
- * Together they replace attn_bwd_dkdv + attn_bwd_dq (same inputs and outputs).
- *   ds       : device buffer of at least attn_bwd_stored_ds_bytes(s, Hq, causal) bytes, owned
- *              by the caller: Hq * ceil(s/128) * ceil(s/64) tiles of 16 KiB when non-causal,
- *              about half as many when causal (34.4 GB for s = 65536, Hq = 8, causal). Its
- *              layout is private to the two calls; it must not change between them.
- *   ds_bytes : its size in bytes (ULY_ERR_WORKSPACE when too small)
- *   attn_bwd_dq_stored_ds reads k [s, Hkv, d] and ds, writes dq [s, Hq, d]; scale and causal
- *   must be those given to attn_bwd_dkdv_store_ds.
- * ULY_ERR_UNSUPPORTED for fp32.
- * ------------------------------------------------------------------------- */
-size_t attn_bwd_stored_ds_bytes(int64_t s, int Hq, int causal);
-int attn_bwd_dkdv_store_ds(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                           const float* delta, void* dk, void* dv, void* ds, size_t ds_bytes, int64_t s, int Hq,
-                           int Hkv, int d, int dtype, float scale, int causal, void* stream);
-int attn_bwd_dq_stored_ds(const void* k, const void* ds, size_t ds_bytes, void* dq, int64_t s, int Hq, int Hkv,
-                          int d, int dtype, float scale, int causal, void* stream);
-
-/* ---------------------------------------------------------------------------
  * attn_fwd_chunked -- the UPipe headwise-chunked forward of rank `rank` (tilnote.io
  * commentary, section on activation memory: process a few heads at a time to cut the
  * memory of attention intermediates). For each chunk of `heads_per_chunk` local q
@@ -197,13 +184,14 @@ int attn_bwd_dq_stored_ds(const void* k, const void* ds, size_t ds_bytes, void* 
  * ulysses_unpack, with smaller intermediates.
  *   q_shards / o_shards : host arrays of P device pointers [s_l, Hq, d] (global Hq)
  *   k_shards / v_shards : host arrays of P device pointers [s_l, Hkv, d]
+ *   o_lo : device bf16 [s, Hq/P, d] or NULL: O's rounding residual of this rank's heads
  *   lse : device fp32 [Hq/P, s], written for this rank's heads
  *   workspace : at least attn_fwd_chunked_workspace_bytes(...) bytes; NULL -> size query
  *               into *workspace_bytes as for attn_bwd. This is the peak intermediate
  *               memory of the schedule.
  * ------------------------------------------------------------------------- */
 int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards,
-                     const void* const* v_shards, void* const* o_shards, float* lse,
+                     const void* const* v_shards, void* const* o_shards, void* o_lo, float* lse,
                      int P, int rank, int64_t s_l, int Hq, int Hkv, int d, int dtype,
                      float scale, int causal, const int32_t* cu_seqlens, int n_docs,
                      int heads_per_chunk, void* workspace, size_t* workspace_bytes,
@@ -224,13 +212,14 @@ size_t attn_fwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int
  *   q_shards / o_shards : host arrays of P device pointers [s_l, Hq, d] (global Hq);
  *                        only head slice `rank` of the o shards is written
  *   k_shards / v_shards : host arrays of P device pointers [s_l, Hkv, d]
+ *   o_lo : device bf16 [s, Hq/P, d] or NULL: O's rounding residual of this rank's heads
  *   lse : device fp32 [Hq/P, s] for this rank's heads
  * bf16 only (ULY_ERR_UNSUPPORTED for fp32), and every workgroup's rows must lie in one
  * shard: s_l a multiple of 128 (ULY_ERR_UNSUPPORTED otherwise). Other errors as for
  * attn_fwd_chunked.
  * ------------------------------------------------------------------------- */
 int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards,
-                    const void* const* v_shards, void* const* o_shards, float* lse,
+                    const void* const* v_shards, void* const* o_shards, void* o_lo, float* lse,
                     int P, int rank, int64_t s_l, int Hq, int Hkv, int d, int dtype,
                     float scale, int causal, const int32_t* cu_seqlens, int n_docs,
                     void* stream);
@@ -246,6 +235,7 @@ int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards,
  *                        [s_l, Hq, d] (global Hq); o and lse as written by the forward
  *   k_shards / v_shards / dk_shards / dv_shards : host arrays of P device pointers
  *                        [s_l, Hkv, d]
+ *   o_lo : the residual attn_fwd_shards wrote ([s, Hq/P, d]) or NULL
  *   lse : device fp32 [Hq/P, s]
  *   workspace : delta, attn_bwd_workspace_bytes(P * s_l, Hq / P) bytes; NULL -> size
  *               query into *workspace_bytes as for attn_bwd.
@@ -253,7 +243,8 @@ int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards,
  * for attn_bwd_chunked.
  * ------------------------------------------------------------------------- */
 int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards,
-                    const void* const* v_shards, const void* const* o_shards, const float* lse,
+                    const void* const* v_shards, const void* const* o_shards, const void* o_lo,
+                    const float* lse,
                     const void* const* do_shards, void* const* dq_shards, void* const* dk_shards,
                     void* const* dv_shards, int P, int rank, int64_t s_l, int Hq, int Hkv, int d,
                     int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,
@@ -272,6 +263,7 @@ int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards,
  *                        [s_l, Hq, d] (global Hq); o and lse as written by the forward
  *   k_shards / v_shards / dk_shards / dv_shards : host arrays of P device pointers
  *                        [s_l, Hkv, d]
+ *   o_lo : the residual attn_fwd_chunked wrote ([s, Hq/P, d]) or NULL
  *   lse : device fp32 [Hq/P, s] of this rank's heads
  *   dq / dk / dv shards: only this rank's head slices are written.
  *   workspace : at least attn_bwd_chunked_workspace_bytes(...) bytes; NULL -> size query
@@ -281,7 +273,8 @@ int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards,
  * Errors as for attn_fwd_chunked.
  * ------------------------------------------------------------------------- */
 int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards,
-                     const void* const* v_shards, const void* const* o_shards, const float* lse,
+                     const void* const* v_shards, const void* const* o_shards, const void* o_lo,
+                     const float* lse,
                      const void* const* do_shards, void* const* dq_shards, void* const* dk_shards,
                      void* const* dv_shards, int P, int rank, int64_t s_l, int Hq, int Hkv, int d,
                      int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,

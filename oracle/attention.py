@@ -120,7 +120,9 @@ def backward(q, k, v, do, scale, causal=True, cu_seqlens=None, q_rows=None, kv_c
     Returns (dq, dk, dv): dq [len(q_rows), Hq, d]; dk, dv [len(kv_cols), Hkv, d].
     For GQA the gradient of a kv head sums over the G q heads that read it.
     By default all rows and all keys are returned. With subsets, each returned
-    value is still exact: every row that sees a requested key is included.
+    value is still exact: every row that sees a requested key is included. dK_j and
+    dV_j use only column j of P and dS, so row blocks holding no requested dQ row
+    compute those columns alone (the forward pass still covers every key).
 
     Per row i of q head h (kv head g = h // G), with O_i and LSE_i from forward():
       P_ij  = exp(S_ij - LSE_i)  (0 where masked)
@@ -150,14 +152,20 @@ def backward(q, k, v, do, scale, causal=True, cu_seqlens=None, q_rows=None, kv_c
         pos = 0
         for br in _row_blocks(rows):
             n = len(br)
+            sel = q_pos[br] >= 0
             keys = _key_range(br, s, causal)
+            if not sel.any():
+                # no dQ row in this block: only the requested key columns of P and dS are used
+                keys = kv_cols[kv_cols < len(keys)]
+                if len(keys) == 0:
+                    pos += n
+                    continue
             S = scale * (q[br, h, :] @ k[keys, g, :].T)
             mask = allowed(br, keys, causal, cu_seqlens)
             Pm = np.where(mask, np.exp(np.where(mask, S, 0.0) - lse[h, pos:pos + n][:, None]), 0.0)
             Dv = np.sum(do[br, h, :] * o[pos:pos + n, h, :], axis=1)
             dP = do[br, h, :] @ v[keys, g, :].T
             dS = Pm * (dP - Dv[:, None])
-            sel = q_pos[br] >= 0
             if sel.any():
                 dq[q_pos[br][sel], h, :] = scale * (dS[sel] @ k[keys, g, :])
             cols = col_pos[keys]

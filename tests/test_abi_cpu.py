@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = U.lib()
-    assert L.uly_abi_version() == 1
+    assert L.uly_abi_version() == 2
     for code, name in U.STATUS.items():
         assert L.uly_status_string(code).decode() == name
 
@@ -114,12 +114,12 @@ def test_group_permute_null_and_alignment():
 
 
 def _fwd(**kw):
-    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, s=16, Hq=4, Hkv=2, d=128, dt=0, scale=0.1,
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, o_lo=None, lse=FAKE, s=16, Hq=4, Hkv=2, d=128, dt=0, scale=0.1,
                 causal=1, cu=None, nd=0)
     args.update(kw)
     a = args
-    return U.lib().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["s"], a["Hq"], a["Hkv"], a["d"],
-                            a["dt"], a["scale"], a["causal"], a["cu"], a["nd"], None)
+    return U.lib().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["o_lo"], a["lse"], a["s"], a["Hq"], a["Hkv"],
+                            a["d"], a["dt"], a["scale"], a["causal"], a["cu"], a["nd"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -127,6 +127,7 @@ def _fwd(**kw):
     (dict(Hq=3, Hkv=2), 2), (dict(s=0), 2), (dict(Hkv=0), 2), (dict(cu=FAKE, nd=0), 2),
     (dict(d=96), 3), (dict(dt=1, d=128), 3), (dict(dt=5), 3),
     (dict(k=MIS), 4), (dict(o=MIS), 4),
+    (dict(o_lo=MIS), 4), (dict(dt=1, d=64, o_lo=FAKE), 3),   # the O residual: aligned, bf16 only
 ])
 def test_attn_fwd_rejects(kw, want):
     assert _fwd(**kw) == want
@@ -135,14 +136,18 @@ def test_attn_fwd_rejects(kw, want):
 def test_bwd_workspace_query_and_checks():
     L = U.lib()
     need = ctypes.c_size_t(0)
-    z = [FAKE] * 9
+    z = [FAKE] * 10
     st = L.attn_bwd(*z, 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None, ctypes.byref(need), None)
     assert st == 0 and need.value == L.attn_bwd_workspace_bytes(1000, 8) and need.value >= 1000 * 8 * 4
     small = ctypes.c_size_t(need.value - 1)
     assert L.attn_bwd(*z, 1000, 8, 2, 128, 0, 0.1, 1, None, 0, FAKE, ctypes.byref(small), None) == 5
     assert L.attn_bwd(*z, 1000, 8, 3, 128, 0, 0.1, 1, None, 0, None, ctypes.byref(need), None) == 2
     assert L.attn_bwd(*z, 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None, None, None) == 1
-    assert L.attn_bwd_preprocess(FAKE, None, FAKE, 10, 2, 128, 0, None) == 1
+    assert L.attn_bwd_preprocess(FAKE, None, None, FAKE, 10, 2, 128, 0, None) == 1
+    assert L.attn_bwd_preprocess(FAKE, MIS, FAKE, FAKE, 10, 2, 128, 0, None) == 4
+    assert L.attn_bwd_preprocess(FAKE, FAKE, FAKE, FAKE, 10, 2, 64, 1, None) == 3
+    zl = [FAKE, FAKE, FAKE, FAKE, MIS] + [FAKE] * 5   # misaligned o_lo
+    assert L.attn_bwd(*zl, 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None, ctypes.byref(need), None) == 4
     assert L.attn_bwd_dkdv(*[FAKE] * 8, 10, 4, 3, 128, 0, 0.1, 1, None, 0, None) == 2
     assert L.attn_bwd_dq(*[FAKE] * 7, 10, 4, 2, 100, 0, 0.1, 1, None, 0, None) == 3
 
@@ -165,7 +170,7 @@ def test_chunked_rejects():
 
     def call(ws=None, cap=None, **kw):
         a = args(**kw)
-        return L.attn_fwd_chunked(pp, pp, pp, pp, FAKE, a["P"], a["rank"], a["s_l"], a["Hq"], a["Hkv"], a["d"],
+        return L.attn_fwd_chunked(pp, pp, pp, pp, None, FAKE, a["P"], a["rank"], a["s_l"], a["Hq"], a["Hkv"], a["d"],
                                   a["dt"], 0.1, 1, None, 0, a["u"], ws, cap, None)
     assert call(cap=ctypes.byref(need)) == 0 and need.value > 0
     assert call(cap=ctypes.byref(need), u=0) == 2
@@ -193,7 +198,7 @@ def test_bwd_chunked_workspace_and_rejects():
     need = ctypes.c_size_t(0)
 
     def call(ws=None, cap=None, P=2, rank=0, s_l=8, Hq=8, Hkv=4, d=64, dt=0, u=1, lse=FAKE):
-        return L.attn_bwd_chunked(pp, pp, pp, pp, lse, pp, pp, pp, pp, P, rank, s_l, Hq, Hkv, d, dt, 0.1, 1,
+        return L.attn_bwd_chunked(pp, pp, pp, pp, None, lse, pp, pp, pp, pp, P, rank, s_l, Hq, Hkv, d, dt, 0.1, 1,
                                   None, 0, u, ws, cap, None)
     assert call(cap=ctypes.byref(need)) == 0 and need.value == L.attn_bwd_chunked_workspace_bytes(2, 8, 8, 4, 64,
                                                                                                 0, 1)
@@ -212,8 +217,8 @@ def test_shards_rejects():
     pp, keep = _ptr_array([FAKE] * 2)
     mp, keep2 = _ptr_array([FAKE, MIS])
 
-    def fwd(q=pp, s_l=128, Hq=8, Hkv=4, d=128, dt=0, rank=0, lse=FAKE):
-        return L.attn_fwd_shards(q, pp, pp, pp, lse, 2, rank, s_l, Hq, Hkv, d, dt, 0.1, 1, None, 0, None)
+    def fwd(q=pp, s_l=128, Hq=8, Hkv=4, d=128, dt=0, rank=0, lse=FAKE, o_lo=None):
+        return L.attn_fwd_shards(q, pp, pp, pp, o_lo, lse, 2, rank, s_l, Hq, Hkv, d, dt, 0.1, 1, None, 0, None)
     assert fwd(s_l=96) == 3          # a workgroup's rows must lie in one shard
     assert fwd(dt=1, d=64) == 3      # bf16 only
     assert fwd(d=96) == 3
@@ -221,10 +226,11 @@ def test_shards_rejects():
     assert fwd(rank=2) == 2
     assert fwd(lse=None) == 1
     assert fwd(q=mp) == 4
+    assert fwd(o_lo=MIS) == 4
     need = ctypes.c_size_t(0)
 
     def bwd(ws=None, cap=None, s_l=128, dt=0, d=128):
-        return L.attn_bwd_shards(pp, pp, pp, pp, FAKE, pp, pp, pp, pp, 2, 0, s_l, 8, 4, d, dt, 0.1, 1, None, 0,
+        return L.attn_bwd_shards(pp, pp, pp, pp, None, FAKE, pp, pp, pp, pp, 2, 0, s_l, 8, 4, d, dt, 0.1, 1, None, 0,
                                  ws, cap, None)
     assert bwd(cap=ctypes.byref(need)) == 0 and need.value == L.attn_bwd_workspace_bytes(256, 4)
     assert bwd(cap=ctypes.byref(need), s_l=64) == 3
@@ -241,26 +247,17 @@ def test_probe_rejects():
     assert L.uly_mfma_probe(4, 4, None, FAKE, None) == 1
 
 
-def test_stored_ds_bytes_closed_form():
-    L = U.lib()
-    # 16 KiB tiles of 128 keys x 64 rows: causal key block kb holds query tiles [2 kb, nqt)
-    for s, Hq in ((1, 1), (64, 2), (129, 3), (600, 4), (65536, 8)):
-        nkb, nqt = -(-s // 128), -(-s // 64)
-        causal_tiles = sum(nqt - 2 * kb for kb in range(nkb))
-        assert L.attn_bwd_stored_ds_bytes(s, Hq, 1) == Hq * causal_tiles * 16384
-        assert L.attn_bwd_stored_ds_bytes(s, Hq, 0) == Hq * nkb * nqt * 16384
-    assert L.attn_bwd_stored_ds_bytes(65536, 8, 1) == 34426847232  # 34.4 GB at the 64K share
-    assert L.attn_bwd_stored_ds_bytes(0, 8, 1) == 0 and L.attn_bwd_stored_ds_bytes(16, 0, 1) == 0
+def test_binding_checks_shapes_before_the_call():
+    """The binding rejects a tensor whose shape or dtype does not match before any pointer
+    reaches the library (the C side cannot see a tensor's extent)."""
+    import torch
+    q = torch.zeros(16, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="k: shape"):
+        U.attn_fwd(q, torch.zeros(15, 2, 64, dtype=torch.bfloat16), torch.zeros(16, 2, 64, dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="v: dtype"):
+        U.attn_fwd(q, torch.zeros(16, 2, 64, dtype=torch.bfloat16), torch.zeros(16, 2, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="shards\\[1\\]"):
+        U.ulysses_pack([torch.zeros(8, 4, 64, dtype=torch.bfloat16), torch.zeros(8, 2, 64, dtype=torch.bfloat16)], 0)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        U._cu(torch.zeros(1, dtype=torch.int32))
 
-
-def test_stored_ds_rejects_on_the_host():
-    L = U.lib()
-    need = L.attn_bwd_stored_ds_bytes(64, 4, 1)
-    dkdv = lambda **kw: L.attn_bwd_dkdv_store_ds(*[kw.get(n, FAKE) for n in ("q", "k", "v", "lse", "do", "dl", "dk", "dv", "ds")],
-                                                  kw.get("nb", need), 64, 4, 2, 128, kw.get("dt", 0), 0.1, 1, None)
-    dq = lambda **kw: L.attn_bwd_dq_stored_ds(kw.get("k", FAKE), kw.get("ds", FAKE), kw.get("nb", need), kw.get("dq", FAKE),
-                                             64, 4, 2, 128, kw.get("dt", 0), 0.1, 1, None)
-    assert dkdv(dt=1) == 3 and dq(dt=1) == 3          # bf16 only
-    assert dkdv(ds=None) == 1 and dq(ds=None) == 1 and dq(dq=None) == 1
-    assert dkdv(ds=MIS) == 4 and dq(dq=MIS) == 4
-    assert dkdv(nb=need - 1) == 5 and dq(nb=need - 1) == 5

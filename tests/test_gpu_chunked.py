@@ -18,12 +18,13 @@ from tests.helpers import LSE_ABS, compare, dev_to_f64, sample_rows, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _unchunked(qs, ks, vs, rank, scale, causal, cu_dev):
+def _unchunked(qs, ks, vs, rank, scale, causal, cu_dev, with_lo=False):
     q, k, v = (U.ulysses_pack(x, rank) for x in (qs, ks, vs))
-    o, lse = U.attn_fwd(q, k, v, scale, causal, cu_dev)
+    o_lo = U.new_o_lo(q) if with_lo and q.dtype == torch.bfloat16 else None
+    o, lse = U.attn_fwd(q, k, v, scale, causal, cu_dev, o_lo=o_lo)
     o_sh = [torch.zeros_like(t) for t in qs]
     U.ulysses_unpack(o, rank, o_sh)
-    return o_sh, lse
+    return (o_sh, lse, o_lo) if with_lo else (o_sh, lse)
 
 
 def _sentinel_like(shards):
@@ -59,14 +60,16 @@ def test_chunked_small(P, s_l, Hq, Hkv, u, rank, cu):
     bits = {n: W.shards_of(W.gen_global(cfg, n, seed=11), P) for n in ("q", "k", "v")}
     dev = {n: [to_dev(b, "bf16") for b in bits[n]] for n in bits}
     cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
-    want_o, want_lse = _unchunked(dev["q"], dev["k"], dev["v"], rank, cfg.scale, True, cu_dev)
+    want_o, want_lse, want_lo = _unchunked(dev["q"], dev["k"], dev["v"], rank, cfg.scale, True, cu_dev, True)
     o_sh = _sentinel_like(dev["q"])
     keep = [t.clone() for t in o_sh]
-    lse = U.attn_fwd_chunked(dev["q"], dev["k"], dev["v"], o_sh, rank, u, cfg.scale, True, cu_dev)
+    o_lo = torch.full_like(want_lo, 5.0)
+    lse = U.attn_fwd_chunked(dev["q"], dev["k"], dev["v"], o_sh, rank, u, cfg.scale, True, cu_dev, o_lo=o_lo)
     torch.cuda.synchronize()
     Hl = Hq // P
     _check_rank_heads(o_sh, want_o, keep, rank, Hl)
     assert torch.equal(lse, want_lse)
+    assert torch.equal(o_lo.view(torch.int16), want_lo.view(torch.int16))  # every head's residual, bitwise
 
     to64 = lambda b: W.bits_to_f64(b, "bf16")
     zeros = [np.zeros(b.shape) for b in bits["q"]]
@@ -166,9 +169,9 @@ def test_chunked_full_upipe_share():
 # span several chunks are fp32 sums taken in another order, so they are held to the
 # oracle (and bitwise equal to the unchunked result when every chunk holds whole groups).
 
-def _unchunked_bwd(dev, o_sh, lse, rank, scale, causal, cu_dev):
+def _unchunked_bwd(dev, o_sh, lse, rank, scale, causal, cu_dev, o_lo=None):
     q, k, v, o, do = (U.ulysses_pack(x, rank) for x in (dev["q"], dev["k"], dev["v"], o_sh, dev["do"]))
-    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, do, scale, causal, cu_dev)
+    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, do, scale, causal, cu_dev, o_lo=o_lo)
     out = {}
     for n, y, like in (("dq", dq, dev["q"]), ("dk", dk, dev["k"]), ("dv", dv, dev["v"])):
         out[n] = _sentinel_like(like)
@@ -209,12 +212,12 @@ def test_chunked_bwd_small(P, s_l, Hq, Hkv, d, dt, u, rank, cu):
     bits = {n: W.shards_of(W.gen_global(cfg, n, seed=13), P) for n in ("q", "k", "v", "do")}
     dev = {n: [to_dev(b, dt) for b in bits[n]] for n in bits}
     cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
-    o_sh, lse = _unchunked(dev["q"], dev["k"], dev["v"], rank, cfg.scale, True, cu_dev)
-    want = _unchunked_bwd(dev, o_sh, lse, rank, cfg.scale, True, cu_dev)
+    o_sh, lse, o_lo = _unchunked(dev["q"], dev["k"], dev["v"], rank, cfg.scale, True, cu_dev, True)
+    want = _unchunked_bwd(dev, o_sh, lse, rank, cfg.scale, True, cu_dev, o_lo)
     got = {n: _sentinel_like(want[n]) for n in want}
     keep = {n: [t.clone() for t in got[n]] for n in got}
     U.attn_bwd_chunked(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], got["dq"], got["dk"], got["dv"],
-                       rank, u, cfg.scale, True, cu_dev)
+                       rank, u, cfg.scale, True, cu_dev, o_lo=o_lo)
     torch.cuda.synchronize()
     iview = torch.int16 if dt == "bf16" else torch.int32
     Hql, Hkvl = Hq // P, Hkv // P
@@ -261,14 +264,14 @@ def test_chunked_bwd_full_upipe_share():
     """Backward of the 256K UPipe share (rank 0) at u = 1 and u = 2 (every kv head summed
     over 8 and 4 chunks): dQ bitwise equal to the unchunked attn_bwd; dK/dV within one
     bf16 step of it (the fp32 sums are only reordered); sampled dQ rows and dK/dV keys
-    against the oracle; sum_j dV_j against the dO sums over every key; and peak
+    against the oracle; sum_j dV_j against the dO sums and sum_j dK_j = 0 over every key; and peak
     intermediate memory no more than the queried workspace."""
-    from tests.test_gpu_fullsize import _dv_column_sums
+    from tests.test_gpu_fullsize import _dk_column_sums, _dv_column_sums
     X = _upipe_inputs()
     cfg, rank, dev, f = X["cfg"], X["rank"], X["dev"], X["f"]
     P, s_l, s, Hl = cfg.P, cfg.s_l, cfg.s, cfg.Hq_l
-    o_sh, lse = _unchunked(dev["q"], dev["k"], dev["v"], rank, cfg.scale, True, None)
-    want = _unchunked_bwd(dev, o_sh, lse, rank, cfg.scale, True, None)
+    o_sh, lse, o_lo = _unchunked(dev["q"], dev["k"], dev["v"], rank, cfg.scale, True, None, True)
+    want = _unchunked_bwd(dev, o_sh, lse, rank, cfg.scale, True, None, o_lo)
     torch.cuda.synchronize()
     print("unchunked backward done", flush=True)
     ref_dkv = {n: _rank_cat(want[n], rank, P) for n in ("dk", "dv")}
@@ -279,7 +282,7 @@ def test_chunked_bwd_full_upipe_share():
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
         U.attn_bwd_chunked(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], got["dq"], got["dk"], got["dv"],
-                           rank, u, cfg.scale, True)
+                           rank, u, cfg.scale, True, o_lo=o_lo)
         torch.cuda.synchronize()
         peak = torch.cuda.max_memory_allocated() - base
         assert peak <= need + (1 << 20), (u, peak, need)
@@ -315,3 +318,4 @@ def test_chunked_bwd_full_upipe_share():
     compare("upipe dV keys", dev_to_f64(_rank_cat(keep["dv"], rank, P)[kidx]), wv, bf16=True)
     print("sampled rows and keys ok", flush=True)
     _dv_column_sums(dev_to_f64(_rank_cat(keep["dv"], rank, P)), f["do"], cfg.G, [(0, s)])
+    _dk_column_sums(dev_to_f64(_rank_cat(keep["dk"], rank, P)), [(0, s)])

@@ -14,7 +14,14 @@ one, so per kv head g (and per document) sum_j dV_j equals the sum over the grou
 heads of sum_i dO_i. On the GPU the bf16 rounding of P (relative 2^-8 per weight) and
 of the stored dV (2^-8 per element) perturb both sides by independent roundings; the
 test allows more than 8 standard deviations of that noise, 8 * 2^-8 * (||dV||_2 + ||dO||_2)
-taken over the summed elements, which a lost or doubled tile or head would exceed."""
+taken over the summed elements, which a lost or doubled tile or head would exceed.
+Likewise rows of dS sum to zero (sum_j P_ij (dP_ij - delta_i) = delta_i - delta_i), so per kv
+head (and per document) sum_j dK_j = 0; the bf16 roundings of dS and of the stored dK leave
+a noise whose size an fp64 emulation of that rounding puts at 0.6 (mean) to 2.2 (max over
+columns) times 2^-8 ||dK||_2 per column, and the test allows 8 * 2^-8 ||dK||_2.
+Finally the keys with the longest accumulations (key 0 sums every row of every q head of
+its group) are checked exactly at 64K: dK and dV of keys 0, 1, 63, 64, 127, 128, s/2 and
+s/2 + 1 of kv head 0 against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -61,6 +68,15 @@ def _dv_column_sums(dv, do, G, segments):
             assert (err <= tol).all(), f"dV column sum [{a},{b}) g={g}: err {err.max():.3e} tol {tol.min():.3e}"
 
 
+def _dk_column_sums(dk, segments):
+    """Check sum_j dK_j = 0 per kv head over each segment [a, b)."""
+    for a, b in segments:
+        for g in range(dk.shape[1]):
+            lhs = np.abs(dk[a:b, g].sum(0))
+            tol = 8 * 2.0 ** -8 * np.sqrt((dk[a:b, g] ** 2).sum(0))
+            assert (lhs <= tol).all(), f"dK column sum [{a},{b}) g={g}: |sum| {lhs.max():.3e} tol {tol.min():.3e}"
+
+
 def _run(cfg, rank, extra_rows, keys, segments):
     print(f"case {cfg.name} rank {rank}: generating", flush=True)
     shards, f = _inputs(cfg, rank)
@@ -83,6 +99,8 @@ def _run(cfg, rank, extra_rows, keys, segments):
     print("  sampled keys ok", flush=True)
     dv = _rank_heads(out["dv"], rank, cfg.P, np.arange(cfg.s))
     _dv_column_sums(dv, f["do"], cfg.G, segments)
+    _dk_column_sums(_rank_heads(out["dk"], rank, cfg.P, np.arange(cfg.s)), segments)
+    return out, f
 
 
 @pytest.mark.timeout(600)
@@ -108,6 +126,41 @@ def test_packed_96k_share():
     _run(cfg, 0, extra, np.array(sorted(keys)), list(zip(cu[:-1], cu[1:])))
 
 
+def _oracle_head_keys(f, h, g, scale, keys):
+    """dK, dV of `keys` of kv head g from q head h alone (the oracle; numpy releases the GIL
+    in its large kernels, so heads run in threads)."""
+    sl = lambda a, i: a[:, i:i + 1]
+    _, dk, dv = OA.backward(sl(f["q"], h), sl(f["k"], g), sl(f["v"], g), sl(f["do"], h), scale, True, None,
+                            q_rows=np.zeros(0, int), kv_cols=keys)
+    print(f"  oracle: q head {h} done", flush=True)
+    return dk[:, 0], dv[:, 0]
+
+
+@pytest.mark.timeout(900)
+def test_qwen_64k_early_keys_exact():
+    """The keys with the most rows: dK and dV of kv head 0 at keys 0, 1, 63, 64, 127, 128, s/2,
+    s/2 + 1 against the oracle, whose forward pass covers the whole 64K causal sequence for
+    each of the group's q heads (the GQA sum of per-head gradients)."""
+    from concurrent.futures import ThreadPoolExecutor
+    cfg = W.WORKLOADS["qwen_64k"]
+    s = cfg.s
+    keys = np.array([0, 1, 63, 64, 127, 128, s // 2, s // 2 + 1])
+    print("case qwen_64k early keys: generating", flush=True)
+    shards, f = _inputs(cfg, 0)
+    out = run_share(cfg, 0, shards, None)
+    torch.cuda.synchronize()
+    got_k = _rank_heads(out["dk"], 0, cfg.P, keys)[:, 0]
+    got_v = _rank_heads(out["dv"], 0, cfg.P, keys)[:, 0]
+    del out, shards
+    print("  GPU share done; oracle over the 4 q heads of kv head 0", flush=True)
+    with ThreadPoolExecutor(cfg.G) as ex:
+        parts = list(ex.map(lambda h: _oracle_head_keys(f, h, 0, cfg.scale, keys), range(cfg.G)))
+    wk = sum(p[0] for p in parts)
+    wv = sum(p[1] for p in parts)
+    compare("64K early keys dK", got_k, wk, bf16=True)
+    compare("64K early keys dV", got_v, wv, bf16=True)
+
+
 @pytest.mark.timeout(300)
 def test_qwen_64k_deterministic():
     """The 64K share's forward and backward, run three times on the same inputs, give the
@@ -118,9 +171,10 @@ def test_qwen_64k_deterministic():
     mk = lambda H: torch.randn((cfg.s, H, cfg.d), device="cuda", generator=gen).to(torch.bfloat16)
     q, k, v, do = mk(cfg.Hq_l), mk(cfg.Hkv_l), mk(cfg.Hkv_l), mk(cfg.Hq_l)
     runs = []
+    o_lo = U.new_o_lo(q)
     for _ in range(3):
-        o, lse = U.attn_fwd(q, k, v, cfg.scale, True)
-        dq, dk, dv = U.attn_bwd(q, k, v, o, lse, do, cfg.scale, True)
+        o, lse = U.attn_fwd(q, k, v, cfg.scale, True, o_lo=o_lo)
+        dq, dk, dv = U.attn_bwd(q, k, v, o, lse, do, cfg.scale, True, o_lo=o_lo)
         torch.cuda.synchronize()
         runs.append((o.view(torch.int16).clone(), lse.clone(), dq.view(torch.int16).clone(),
                      dk.view(torch.int16).clone(), dv.view(torch.int16).clone()))

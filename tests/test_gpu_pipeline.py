@@ -1,6 +1,8 @@
 """The whole share end to end on the GPU: pack Q/K/V -> attention forward -> unpack O;
 pack dO -> attention backward -> unpack dQ/dK/dV, against the oracle run on the
 unsharded global tensors (sharded-then-permuted must equal unsharded attention)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -14,15 +16,17 @@ pytestmark = pytest.mark.gpu
 
 
 def run_share(cfg, rank, shards, cu_dev):
-    """One rank's forward and backward through the C ABI; returns device outputs."""
+    """One rank's forward and backward through the C ABI, as the bench runs them (bf16: with
+    O's rounding residual handed from the forward to the backward); returns device outputs."""
     q = U.ulysses_pack(shards["q"], rank)
     k = U.ulysses_pack(shards["k"], rank)
     v = U.ulysses_pack(shards["v"], rank)
-    o, lse = U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev)
+    o_lo = U.new_o_lo(q) if cfg.dtype == "bf16" else None
+    o, lse = U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, o_lo=o_lo)
     o_sh = [torch.zeros_like(t) for t in shards["q"]]
     U.ulysses_unpack(o, rank, o_sh)
     do = U.ulysses_pack(shards["do"], rank)
-    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, do, cfg.scale, cfg.causal, cu_dev)
+    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, do, cfg.scale, cfg.causal, cu_dev, o_lo=o_lo)
     dq_sh = [torch.zeros_like(t) for t in shards["q"]]
     dk_sh = [torch.zeros_like(t) for t in shards["k"]]
     dv_sh = [torch.zeros_like(t) for t in shards["v"]]
@@ -38,9 +42,13 @@ def _cat_heads(sh, rank, P):
     return dev_to_f64(x[:, rank * Hl:(rank + 1) * Hl])
 
 
-@pytest.mark.parametrize("name,ranks", [("tiny_f32", (0, 1)), ("qwen_8k", (0, 3))])
+# the tiny shape also in bf16, so that its size runs through the MFMA kernels
+TINY_BF16 = dataclasses.replace(W.WORKLOADS["tiny_f32"], name="tiny_bf16", dtype="bf16")
+
+
+@pytest.mark.parametrize("name,ranks", [("tiny_f32", (0, 1)), ("tiny_bf16", (0, 1)), ("qwen_8k", (0, 3))])
 def test_share_matches_unsharded_oracle(name, ranks):
-    cfg = W.WORKLOADS[name]
+    cfg = TINY_BF16 if name == "tiny_bf16" else W.WORKLOADS[name]
     print(f"case {name} ranks {ranks}", flush=True)
     glob, shards = {}, {}
     for n in ("q", "k", "v", "do"):

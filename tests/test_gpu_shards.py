@@ -18,12 +18,13 @@ from tests.helpers import LSE_ABS, compare, dev_to_f64, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _packed_path(dev, rank, scale, causal, cu_dev):
+def _packed_path(dev, rank, scale, causal, cu_dev, with_lo=False):
     q, k, v = (U.ulysses_pack(dev[n], rank) for n in ("q", "k", "v"))
-    o, lse = U.attn_fwd(q, k, v, scale, causal, cu_dev)
+    o_lo = U.new_o_lo(q) if with_lo else None
+    o, lse = U.attn_fwd(q, k, v, scale, causal, cu_dev, o_lo=o_lo)
     o_sh = [torch.full_like(t, 3.0) for t in dev["q"]]
     U.ulysses_unpack(o, rank, o_sh)
-    return o_sh, lse
+    return (o_sh, lse, o_lo) if with_lo else (o_sh, lse)
 
 
 CASES = [
@@ -45,11 +46,13 @@ def test_shards_equal_packed_path(P, s_l, Hq, Hkv, d, rank, causal, cu):
     bits = {n: W.gen_global(cfg, n, seed=21) for n in ("q", "k", "v")}
     dev = {n: [to_dev(b, "bf16") for b in W.shards_of(bits[n], P)] for n in bits}
     cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
-    want_o, want_lse = _packed_path(dev, rank, cfg.scale, causal, cu_dev)
+    want_o, want_lse, want_lo = _packed_path(dev, rank, cfg.scale, causal, cu_dev, True)
     o_sh = [torch.full_like(t, 3.0) for t in dev["q"]]
     keep = [t.clone() for t in o_sh]
-    lse = U.attn_fwd_shards(dev["q"], dev["k"], dev["v"], o_sh, rank, cfg.scale, causal, cu_dev)
+    o_lo = torch.full_like(want_lo, 5.0)
+    lse = U.attn_fwd_shards(dev["q"], dev["k"], dev["v"], o_sh, rank, cfg.scale, causal, cu_dev, o_lo=o_lo)
     torch.cuda.synchronize()
+    assert torch.equal(o_lo.view(torch.int16), want_lo.view(torch.int16))
     Hl = Hq // P
     sl = slice(rank * Hl, (rank + 1) * Hl)
     for a, b, c in zip(o_sh, want_o, keep):
@@ -64,9 +67,9 @@ def test_shards_equal_packed_path(P, s_l, Hq, Hkv, d, rank, causal, cu):
     compare("shards LSE", lse.cpu().numpy(), wl, max_abs=LSE_ABS, rel_fro=1e-4)
 
 
-def _packed_bwd(dev, o_sh, lse, rank, scale, causal, cu_dev):
+def _packed_bwd(dev, o_sh, lse, rank, scale, causal, cu_dev, o_lo=None):
     q, k, v, o, g = (U.ulysses_pack(x, rank) for x in (dev["q"], dev["k"], dev["v"], o_sh, dev["do"]))
-    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, g, scale, causal, cu_dev)
+    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, g, scale, causal, cu_dev, o_lo=o_lo)
     out = {}
     for n, y, like in (("dq", dq, dev["q"]), ("dk", dk, dev["k"]), ("dv", dv, dev["v"])):
         out[n] = [torch.full_like(t, 3.0) for t in like]
@@ -82,11 +85,11 @@ def test_bwd_shards_equal_packed_path(P, s_l, Hq, Hkv, d, rank, causal, cu):
     bits = {n: W.gen_global(cfg, n, seed=23) for n in ("q", "k", "v", "do")}
     dev = {n: [to_dev(b, "bf16") for b in W.shards_of(bits[n], P)] for n in bits}
     cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
-    o_sh, lse = _packed_path(dev, rank, cfg.scale, causal, cu_dev)
-    want = _packed_bwd(dev, o_sh, lse, rank, cfg.scale, causal, cu_dev)
+    o_sh, lse, o_lo = _packed_path(dev, rank, cfg.scale, causal, cu_dev, True)
+    want = _packed_bwd(dev, o_sh, lse, rank, cfg.scale, causal, cu_dev, o_lo)
     got = {n: [torch.full_like(t, 3.0) for t in want[n]] for n in want}
     U.attn_bwd_shards(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], got["dq"], got["dk"], got["dv"], rank,
-                      cfg.scale, causal, cu_dev)
+                      cfg.scale, causal, cu_dev, o_lo=o_lo)
     torch.cuda.synchronize()
     for n in ("dq", "dk", "dv"):
         for a, b in zip(got[n], want[n]):
@@ -156,11 +159,11 @@ def test_bwd_shards_qwen_64k_share():
     print("generating qwen_64k shards", flush=True)
     dev = {n: [to_dev(W.gen_rows(cfg, n, p * cfg.s_l, (p + 1) * cfg.s_l), "bf16") for p in range(cfg.P)]
            for n in ("q", "k", "v", "do")}
-    o_sh, lse = _packed_path(dev, rank, cfg.scale, True, None)
-    want = _packed_bwd(dev, o_sh, lse, rank, cfg.scale, True, None)
+    o_sh, lse, o_lo = _packed_path(dev, rank, cfg.scale, True, None, True)
+    want = _packed_bwd(dev, o_sh, lse, rank, cfg.scale, True, None, o_lo)
     got = {n: [torch.full_like(t, 3.0) for t in want[n]] for n in want}
     U.attn_bwd_shards(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], got["dq"], got["dk"], got["dv"], rank,
-                      cfg.scale, True)
+                      cfg.scale, True, o_lo=o_lo)
     torch.cuda.synchronize()
     for n in ("dq", "dk", "dv"):
         for a, b in zip(got[n], want[n]):

@@ -12,7 +12,11 @@ The names follow the C ABI in include/ulysses.h:
   attn_fwd_chunked                    -- the UPipe headwise-chunked forward
   attn_bwd_chunked                    -- its backward
   attn_fwd_shards, attn_bwd_shards    -- forward / backward reading and writing the sequence shards
-  attn_bwd_dkdv_store_ds, attn_bwd_dq_stored_ds -- the backward with dS stored once (opt-in)
+
+Every tensor's shape, dtype and device are checked here before the C call (the C side
+checks sizes and alignment but cannot see a tensor's extent). `o_lo` arguments take the
+forward's bf16 rounding residual of O ([s, Hq_l, d] bf16, see include/ulysses.h);
+`new_o_lo(q)` allocates one.
 """
 from __future__ import annotations
 
@@ -45,30 +49,26 @@ SIGNATURES = {
     "ulysses_unpack": (_i32, [_vp, _i32, _i32, _i64, _i32, _i32, _i32, _vpp, _vp]),
     "ulysses_pack_group": (_i32, [_i32, _vpp, _i32p, _vpp, _i32, _i32, _i64, _i32, _i32, _vp]),
     "ulysses_unpack_group": (_i32, [_i32, _vpp, _i32p, _vpp, _i32, _i32, _i64, _i32, _i32, _vp]),
-    "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp]),
-    "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
+    "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp]),
+    "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
                         _vp, _i32, _vp, _szp, _vp]),
     "attn_bwd_workspace_bytes": (_sz, [_i64, _i32]),
-    "attn_bwd_preprocess": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
+    "attn_bwd_preprocess": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "attn_bwd_dkdv": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
                              _vp, _i32, _vp]),
     "attn_bwd_dq": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
                            _vp, _i32, _vp]),
-    "attn_fwd_chunked": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
+    "attn_fwd_chunked": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                 _i32, _vp, _i32, _i32, _vp, _szp, _vp]),
     "attn_fwd_chunked_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
-    "attn_bwd_chunked": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vpp, _vpp, _vpp, _vpp, _i32, _i32, _i64, _i32,
+    "attn_bwd_chunked": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vp, _vpp, _vpp, _vpp, _vpp, _i32, _i32, _i64, _i32,
                                 _i32, _i32, _i32, _f32, _i32, _vp, _i32, _i32, _vp, _szp, _vp]),
     "attn_bwd_chunked_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
-    "attn_fwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
+    "attn_fwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                _i32, _vp, _i32, _vp]),
-    "uly_mfma_probe": (_i32, [_i32, _i32, _vp, _vp, _vp]),
-    "attn_bwd_stored_ds_bytes": (_sz, [_i64, _i32, _i32]),
-    "attn_bwd_dkdv_store_ds": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i32, _i32, _i32,
-                                      _i32, _f32, _i32, _vp]),
-    "attn_bwd_dq_stored_ds": (_i32, [_vp, _vp, _sz, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
-    "attn_bwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vpp, _vpp, _vpp, _vpp, _i32, _i32, _i64, _i32,
+    "attn_bwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vp, _vpp, _vpp, _vpp, _vpp, _i32, _i32, _i64, _i32,
                                _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _szp, _vp]),
+    "uly_mfma_probe": (_i32, [_i32, _i32, _vp, _vp, _vp]),
 }
 
 
@@ -115,6 +115,38 @@ def _dev(t):
     return t.data_ptr()
 
 
+def _shape(t, name, shape, dtype):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+
+
+def _need(t, name, shape, dtype, device=None):
+    """Check a tensor argument before its pointer crosses the boundary."""
+    _shape(t, name, shape, dtype)
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    return _dev(t)
+
+
+def _opt(t, name, shape, dtype, device=None):
+    return None if t is None else _need(t, name, shape, dtype, device)
+
+
+def _same(ts, name):
+    """A list of shards: equal shapes, dtypes and devices; returns the first."""
+    if len(ts) < 1:
+        raise ValueError(f"{name}: no shards")
+    for i, t in enumerate(ts):
+        _shape(t, f"{name}[{i}]", ts[0].shape, ts[0].dtype)
+    for i, t in enumerate(ts):
+        _need(t, f"{name}[{i}]", ts[0].shape, ts[0].dtype, ts[0].device)
+    return ts[0]
+
+
 def _ptrs(ts):
     arr = (ctypes.c_void_p * len(ts))(*[_dev(t) for t in ts])
     return ctypes.cast(arr, _vpp), arr
@@ -124,29 +156,43 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-def _cu(cu_seqlens):
+def _cu(cu_seqlens, device=None):
     if cu_seqlens is None:
         return None, 0
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with at least two entries")
+    if device is not None and cu_seqlens.device != device:
+        raise ValueError("cu_seqlens must be on the tensors' device")
     return _dev(cu_seqlens), cu_seqlens.numel() - 1
+
+
+def new_o_lo(q, Hq_l=None):
+    """An O-residual buffer for q [s, Hq, d] (or for Hq_l local heads of sequence shards)."""
+    s, Hq, d = q.shape
+    return torch.empty((s, Hq if Hq_l is None else Hq_l, d), dtype=torch.bfloat16, device=q.device)
 
 
 def ulysses_pack(shards, rank, out=None):
     """P sequence shards [s_l, H, d] -> this rank's head shard [P*s_l, H/P, d]."""
     P = len(shards)
-    s_l, H, d = shards[0].shape
+    x = _same(shards, "shards")
+    s_l, H, d = x.shape
     if out is None:
-        out = torch.empty((P * s_l, H // P, d), dtype=shards[0].dtype, device=shards[0].device)
+        out = torch.empty((P * s_l, H // P, d), dtype=x.dtype, device=x.device)
+    _need(out, "out", (P * s_l, H // P, d), x.dtype, x.device)
     pp, _keep = _ptrs(shards)
-    _call("ulysses_pack", pp, P, rank, s_l, H, d, _dtype(shards[0]), _dev(out), _stream())
+    _call("ulysses_pack", pp, P, rank, s_l, H, d, _dtype(x), _dev(out), _stream())
     return out
 
 
 def ulysses_unpack(y, rank, shards):
     """Head shard [P*s_l, H/P, d] -> head slice `rank` of the P shards [s_l, H, d] (in place)."""
     P = len(shards)
-    s_l, H, d = shards[0].shape
+    x = _same(shards, "shards")
+    s_l, H, d = x.shape
+    _need(y, "y", (P * s_l, H // P, d), x.dtype, x.device)
     pp, _keep = _ptrs(shards)
     _call("ulysses_unpack", _dev(y), P, rank, s_l, H, d, _dtype(y), pp, _stream())
     return shards
@@ -161,6 +207,20 @@ def _group_args(tensor_lists):
     return ctypes.cast(outer, _vpp), ctypes.cast(heads, _i32p), (arrays, outer, heads)
 
 
+def _group_check(shard_lists, flats, what):
+    P = len(shard_lists[0])
+    x0 = _same(shard_lists[0], f"{what}[0]")
+    s_l, _, d = x0.shape
+    for i, (sh, f) in enumerate(zip(shard_lists, flats)):
+        if len(sh) != P:
+            raise ValueError(f"{what}[{i}]: {len(sh)} shards, expected {P}")
+        x = _same(sh, f"{what}[{i}]")
+        if x.shape[0] != s_l or x.shape[2] != d or x.dtype != x0.dtype or x.device != x0.device:
+            raise ValueError(f"{what}[{i}]: shards {tuple(x.shape)} {x.dtype} do not match {what}[0]")
+        _need(f, f"head shard {i}", (P * s_l, x.shape[1] // P, d), x0.dtype, x0.device)
+    return P, s_l, d, x0
+
+
 def ulysses_pack_group(shard_lists, rank, outs=None):
     """Several tensors' P sequence shards [s_l, H_i, d] -> their head shards [P*s_l, H_i/P, d],
     in one launch (the Q/K/V of the forward exchange)."""
@@ -170,9 +230,12 @@ def ulysses_pack_group(shard_lists, rank, outs=None):
     if outs is None:
         outs = [torch.empty((P * s_l, sh[0].shape[1] // P, d), dtype=sh[0].dtype, device=sh[0].device)
                 for sh in shard_lists]
+    if len(outs) != n:
+        raise ValueError("one output per tensor")
+    P, s_l, d, x0 = _group_check(shard_lists, outs, "shard_lists")
     pp, hh, _keep = _group_args(shard_lists)
     op, _keep2 = _ptrs(outs)
-    _call("ulysses_pack_group", n, pp, hh, op, P, rank, s_l, d, _dtype(outs[0]), _stream())
+    _call("ulysses_pack_group", n, pp, hh, op, P, rank, s_l, d, _dtype(x0), _stream())
     return outs
 
 
@@ -180,11 +243,12 @@ def ulysses_unpack_group(ys, rank, shard_lists):
     """Several head shards [P*s_l, H_i/P, d] -> head slice `rank` of their P shards, in one launch
     (the dQ/dK/dV of the backward exchange)."""
     n = len(ys)
-    P = len(shard_lists[0])
-    s_l, _, d = shard_lists[0][0].shape
+    if len(shard_lists) != n:
+        raise ValueError("one shard list per tensor")
+    P, s_l, d, x0 = _group_check(shard_lists, ys, "shard_lists")
     pp, hh, _keep = _group_args(shard_lists)
     yp, _keep2 = _ptrs(ys)
-    _call("ulysses_unpack_group", n, yp, hh, pp, P, rank, s_l, d, _dtype(ys[0]), _stream())
+    _call("ulysses_unpack_group", n, yp, hh, pp, P, rank, s_l, d, _dtype(x0), _stream())
     return shard_lists
 
 
@@ -192,15 +256,31 @@ def _default_scale(d, scale):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def attn_fwd(q, k, v, scale=None, causal=True, cu_seqlens=None, out=None, lse=None):
-    """q [s, Hq, d], k, v [s, Hkv, d] -> (o [s, Hq, d], lse [Hq, s] fp32)."""
+def _qkv(q, k, v):
+    """Shapes of a head shard's q [s, Hq, d], k, v [s, Hkv, d] (checked)."""
     s, Hq, d = q.shape
+    _dtype(q)
     Hkv = k.shape[1]
+    _shape(k, "k", (s, Hkv, d), q.dtype)
+    _shape(v, "v", (s, Hkv, d), q.dtype)
+    _dev(q)
+    _need(k, "k", (s, Hkv, d), q.dtype, q.device)
+    _need(v, "v", (s, Hkv, d), q.dtype, q.device)
+    return s, Hq, Hkv, d
+
+
+def attn_fwd(q, k, v, scale=None, causal=True, cu_seqlens=None, out=None, lse=None, o_lo=None):
+    """q [s, Hq, d], k, v [s, Hkv, d] -> (o [s, Hq, d], lse [Hq, s] fp32). When `o_lo` (bf16
+    [s, Hq, d], e.g. new_o_lo(q)) is given, O's bf16 rounding residual is written into it."""
+    s, Hq, Hkv, d = _qkv(q, k, v)
     o = torch.empty_like(q) if out is None else out
     if lse is None:
         lse = torch.empty((Hq, s), dtype=torch.float32, device=q.device)
-    cu, nd = _cu(cu_seqlens)
-    _call("attn_fwd", _dev(q), _dev(k), _dev(v), _dev(o), _dev(lse), s, Hq, Hkv, d, _dtype(q),
+    _need(o, "out", (s, Hq, d), q.dtype, q.device)
+    _need(lse, "lse", (Hq, s), torch.float32, q.device)
+    lo = _opt(o_lo, "o_lo", (s, Hq, d), torch.bfloat16, q.device)
+    cu, nd = _cu(cu_seqlens, q.device)
+    _call("attn_fwd", _dev(q), _dev(k), _dev(v), _dev(o), lo, _dev(lse), s, Hq, Hkv, d, _dtype(q),
           _default_scale(d, scale), int(causal), cu, nd, _stream())
     return o, lse
 
@@ -210,78 +290,89 @@ def attn_bwd_workspace_bytes(s, Hq):
 
 
 def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=True, cu_seqlens=None, workspace=None,
-             dq=None, dk=None, dv=None):
-    """Gradients (dq, dk, dv) of the attention forward, given its o and lse and dout."""
-    s, Hq, d = q.shape
-    Hkv = k.shape[1]
+             dq=None, dk=None, dv=None, o_lo=None):
+    """Gradients (dq, dk, dv) of the attention forward, given its o and lse and dout (and the
+    forward's o_lo, if it wrote one: delta then comes from O to about 16 bits)."""
+    s, Hq, Hkv, d = _qkv(q, k, v)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for t, n in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        _need(t, n, (s, Hq, d), q.dtype, q.device)
+    for t, n in ((dk, "dk"), (dv, "dv")):
+        _need(t, n, (s, Hkv, d), q.dtype, q.device)
+    _need(lse, "lse", (Hq, s), torch.float32, q.device)
+    lo = _opt(o_lo, "o_lo", (s, Hq, d), torch.bfloat16, q.device)
     need = attn_bwd_workspace_bytes(s, Hq)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
-    cu, nd = _cu(cu_seqlens)
-    _call("attn_bwd", _dev(q), _dev(k), _dev(v), _dev(o), _dev(lse), _dev(dout), _dev(dq), _dev(dk), _dev(dv),
+    cu, nd = _cu(cu_seqlens, q.device)
+    _call("attn_bwd", _dev(q), _dev(k), _dev(v), _dev(o), lo, _dev(lse), _dev(dout), _dev(dq), _dev(dk), _dev(dv),
           s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, _dev(workspace),
           ctypes.byref(cap), _stream())
     return dq, dk, dv
 
 
-def attn_bwd_preprocess(o, dout, delta=None):
+def attn_bwd_preprocess(o, dout, delta=None, o_lo=None):
     s, Hq, d = o.shape
+    _dtype(o)
+    _need(dout, "dout", (s, Hq, d), o.dtype, o.device)
     if delta is None:
         delta = torch.empty((Hq, s), dtype=torch.float32, device=o.device)
-    _call("attn_bwd_preprocess", _dev(o), _dev(dout), _dev(delta), s, Hq, d, _dtype(o), _stream())
+    _need(delta, "delta", (Hq, s), torch.float32, o.device)
+    lo = _opt(o_lo, "o_lo", (s, Hq, d), torch.bfloat16, o.device)
+    _call("attn_bwd_preprocess", _dev(o), lo, _dev(dout), _dev(delta), s, Hq, d, _dtype(o), _stream())
     return delta
 
 
-def attn_bwd_dkdv(q, k, v, lse, dout, delta, scale=None, causal=True, cu_seqlens=None, dk=None, dv=None):
+def _bwd_phase_checks(q, lse, dout, delta):
     s, Hq, d = q.shape
-    Hkv = k.shape[1]
+    _need(dout, "dout", (s, Hq, d), q.dtype, q.device)
+    _need(lse, "lse", (Hq, s), torch.float32, q.device)
+    _need(delta, "delta", (Hq, s), torch.float32, q.device)
+
+
+def attn_bwd_dkdv(q, k, v, lse, dout, delta, scale=None, causal=True, cu_seqlens=None, dk=None, dv=None):
+    s, Hq, Hkv, d = _qkv(q, k, v)
+    _bwd_phase_checks(q, lse, dout, delta)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    cu, nd = _cu(cu_seqlens)
+    for t, n in ((dk, "dk"), (dv, "dv")):
+        _need(t, n, (s, Hkv, d), q.dtype, q.device)
+    cu, nd = _cu(cu_seqlens, q.device)
     _call("attn_bwd_dkdv", _dev(q), _dev(k), _dev(v), _dev(lse), _dev(dout), _dev(delta), _dev(dk), _dev(dv),
           s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, _stream())
     return dk, dv
 
 
-def attn_bwd_stored_ds_bytes(s, Hq, causal=True):
-    """Bytes of the dS buffer the stored-dS backward needs (s tokens, Hq local q heads)."""
-    return int(lib().attn_bwd_stored_ds_bytes(s, Hq, int(causal)))
-
-
-def attn_bwd_dkdv_store_ds(q, k, v, lse, dout, delta, ds, scale=None, causal=True, dk=None, dv=None):
-    """attn_bwd_dkdv that also writes dS into `ds` (a uint8 device tensor of at least
-    attn_bwd_stored_ds_bytes bytes) for attn_bwd_dq_stored_ds."""
-    s, Hq, d = q.shape
-    Hkv = k.shape[1]
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    _call("attn_bwd_dkdv_store_ds", _dev(q), _dev(k), _dev(v), _dev(lse), _dev(dout), _dev(delta), _dev(dk),
-          _dev(dv), _dev(ds), ds.numel() * ds.element_size(), s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale),
-          int(causal), _stream())
-    return dk, dv
-
-
-def attn_bwd_dq_stored_ds(k, ds, dq, scale=None, causal=True):
-    """dQ [s, Hq, d] (written into dq) from the dS that attn_bwd_dkdv_store_ds stored."""
-    s, Hq, d = dq.shape
-    Hkv = k.shape[1]
-    _call("attn_bwd_dq_stored_ds", _dev(k), _dev(ds), ds.numel() * ds.element_size(), _dev(dq), s, Hq, Hkv, d,
-          _dtype(dq), _default_scale(d, scale), int(causal), _stream())
-    return dq
-
-
 def attn_bwd_dq(q, k, v, lse, dout, delta, scale=None, causal=True, cu_seqlens=None, dq=None):
-    s, Hq, d = q.shape
-    Hkv = k.shape[1]
+    s, Hq, Hkv, d = _qkv(q, k, v)
+    _bwd_phase_checks(q, lse, dout, delta)
     dq = torch.empty_like(q) if dq is None else dq
-    cu, nd = _cu(cu_seqlens)
+    _need(dq, "dq", (s, Hq, d), q.dtype, q.device)
+    cu, nd = _cu(cu_seqlens, q.device)
     _call("attn_bwd_dq", _dev(q), _dev(k), _dev(v), _dev(lse), _dev(dout), _dev(delta), _dev(dq),
           s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, _stream())
     return dq
+
+
+def _shard_sets(q_shards, k_shards, v_shards, *more_q, more_kv=()):
+    """Checks the shard lists of a rank's call: q-shaped [s_l, Hq, d] and kv-shaped [s_l, Hkv, d]
+    lists of P shards each, one dtype and device; returns (P, s_l, Hq, Hkv, d, q0)."""
+    P = len(q_shards)
+    q0 = _same(q_shards, "q_shards")
+    s_l, Hq, d = q0.shape
+    _dtype(q0)
+    Hkv = k_shards[0].shape[1]
+    for name, L, H in [("k_shards", k_shards, Hkv), ("v_shards", v_shards, Hkv)] + \
+            [(f"q-shaped shards {i}", L, Hq) for i, L in enumerate(more_q)] + \
+            [(f"kv-shaped shards {i}", L, Hkv) for i, L in enumerate(more_kv)]:
+        if len(L) != P:
+            raise ValueError(f"{name}: {len(L)} shards, expected {P}")
+        for j, t in enumerate(L):
+            _need(t, f"{name}[{j}]", (s_l, H, d), q0.dtype, q0.device)
+    return P, s_l, Hq, Hkv, d, q0
 
 
 def attn_fwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, dtype, heads_per_chunk):
@@ -290,24 +381,25 @@ def attn_fwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, dtype, heads_per_chunk)
 
 
 def attn_fwd_chunked(q_shards, k_shards, v_shards, o_shards, rank, heads_per_chunk, scale=None,
-                     causal=True, cu_seqlens=None, workspace=None, lse=None):
-    """UPipe forward of rank `rank`: writes this rank's heads of o_shards; returns lse [Hq/P, s]."""
-    P = len(q_shards)
-    s_l, Hq, d = q_shards[0].shape
-    Hkv = k_shards[0].shape[1]
+                     causal=True, cu_seqlens=None, workspace=None, lse=None, o_lo=None):
+    """UPipe forward of rank `rank`: writes this rank's heads of o_shards (and, when given, O's
+    rounding residual into o_lo [s, Hq/P, d]); returns lse [Hq/P, s]."""
+    P, s_l, Hq, Hkv, d, q0 = _shard_sets(q_shards, k_shards, v_shards, o_shards)
     s = P * s_l
     if lse is None:
-        lse = torch.empty((Hq // P, s), dtype=torch.float32, device=q_shards[0].device)
-    need = attn_fwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, _dtype(q_shards[0]), heads_per_chunk)
+        lse = torch.empty((Hq // P, s), dtype=torch.float32, device=q0.device)
+    _need(lse, "lse", (Hq // P, s), torch.float32, q0.device)
+    lo = _opt(o_lo, "o_lo", (s, Hq // P, d), torch.bfloat16, q0.device)
+    need = attn_fwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, _dtype(q0), heads_per_chunk)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q_shards[0].device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q0.device)
     cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     qp, k1 = _ptrs(q_shards)
     kp, k2 = _ptrs(k_shards)
     vp, k3 = _ptrs(v_shards)
     op, k4 = _ptrs(o_shards)
-    cu, nd = _cu(cu_seqlens)
-    _call("attn_fwd_chunked", qp, kp, vp, op, _dev(lse), P, rank, s_l, Hq, Hkv, d, _dtype(q_shards[0]),
+    cu, nd = _cu(cu_seqlens, q0.device)
+    _call("attn_fwd_chunked", qp, kp, vp, op, lo, _dev(lse), P, rank, s_l, Hq, Hkv, d, _dtype(q0),
           _default_scale(d, scale), int(causal), cu, nd, heads_per_chunk, _dev(workspace), ctypes.byref(cap),
           _stream())
     return lse
@@ -319,58 +411,61 @@ def attn_bwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, dtype, heads_per_chunk)
 
 
 def attn_bwd_chunked(q_shards, k_shards, v_shards, o_shards, lse, do_shards, dq_shards, dk_shards, dv_shards,
-                     rank, heads_per_chunk, scale=None, causal=True, cu_seqlens=None, workspace=None):
+                     rank, heads_per_chunk, scale=None, causal=True, cu_seqlens=None, workspace=None, o_lo=None):
     """UPipe backward of rank `rank`: writes this rank's heads of dq_shards, dk_shards, dv_shards."""
-    P = len(q_shards)
-    s_l, Hq, d = q_shards[0].shape
-    Hkv = k_shards[0].shape[1]
-    dt = _dtype(q_shards[0])
+    P, s_l, Hq, Hkv, d, q0 = _shard_sets(q_shards, k_shards, v_shards, o_shards, do_shards, dq_shards,
+                                         more_kv=(dk_shards, dv_shards))
+    s = P * s_l
+    _need(lse, "lse", (Hq // P, s), torch.float32, q0.device)
+    lo = _opt(o_lo, "o_lo", (s, Hq // P, d), torch.bfloat16, q0.device)
+    dt = _dtype(q0)
     need = attn_bwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, dt, heads_per_chunk)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q_shards[0].device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q0.device)
     cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     keep = [_ptrs(x) for x in (q_shards, k_shards, v_shards, o_shards, do_shards, dq_shards, dk_shards, dv_shards)]
     qp, kp, vp, op, gp, dqp, dkp, dvp = (k[0] for k in keep)
-    cu, nd = _cu(cu_seqlens)
-    _call("attn_bwd_chunked", qp, kp, vp, op, _dev(lse), gp, dqp, dkp, dvp, P, rank, s_l, Hq, Hkv, d, dt,
+    cu, nd = _cu(cu_seqlens, q0.device)
+    _call("attn_bwd_chunked", qp, kp, vp, op, lo, _dev(lse), gp, dqp, dkp, dvp, P, rank, s_l, Hq, Hkv, d, dt,
           _default_scale(d, scale), int(causal), cu, nd, heads_per_chunk, _dev(workspace), ctypes.byref(cap),
           _stream())
     return dq_shards, dk_shards, dv_shards
 
 
 def attn_fwd_shards(q_shards, k_shards, v_shards, o_shards, rank, scale=None, causal=True, cu_seqlens=None,
-                    lse=None):
+                    lse=None, o_lo=None):
     """Forward of rank `rank` straight from the sequence shards into head slice `rank` of
     o_shards (no head-shard buffers); returns the LSE [Hq/P, s]."""
-    P = len(q_shards)
-    s_l, Hq, d = q_shards[0].shape
-    Hkv = k_shards[0].shape[1]
+    P, s_l, Hq, Hkv, d, q0 = _shard_sets(q_shards, k_shards, v_shards, o_shards)
     if lse is None:
-        lse = torch.empty((Hq // P, P * s_l), dtype=torch.float32, device=q_shards[0].device)
+        lse = torch.empty((Hq // P, P * s_l), dtype=torch.float32, device=q0.device)
+    _need(lse, "lse", (Hq // P, P * s_l), torch.float32, q0.device)
+    lo = _opt(o_lo, "o_lo", (P * s_l, Hq // P, d), torch.bfloat16, q0.device)
     keep = [_ptrs(x) for x in (q_shards, k_shards, v_shards, o_shards)]
     qp, kp, vp, op = (k[0] for k in keep)
-    cu, nd = _cu(cu_seqlens)
-    _call("attn_fwd_shards", qp, kp, vp, op, _dev(lse), P, rank, s_l, Hq, Hkv, d, _dtype(q_shards[0]),
+    cu, nd = _cu(cu_seqlens, q0.device)
+    _call("attn_fwd_shards", qp, kp, vp, op, lo, _dev(lse), P, rank, s_l, Hq, Hkv, d, _dtype(q0),
           _default_scale(d, scale), int(causal), cu, nd, _stream())
     return lse
 
 
 def attn_bwd_shards(q_shards, k_shards, v_shards, o_shards, lse, do_shards, dq_shards, dk_shards, dv_shards,
-                    rank, scale=None, causal=True, cu_seqlens=None, workspace=None):
+                    rank, scale=None, causal=True, cu_seqlens=None, workspace=None, o_lo=None):
     """Backward of rank `rank` straight from the sequence shards into head slice `rank` of
     the dq / dk / dv shards."""
-    P = len(q_shards)
-    s_l, Hq, d = q_shards[0].shape
-    Hkv = k_shards[0].shape[1]
+    P, s_l, Hq, Hkv, d, q0 = _shard_sets(q_shards, k_shards, v_shards, o_shards, do_shards, dq_shards,
+                                         more_kv=(dk_shards, dv_shards))
+    _need(lse, "lse", (Hq // P, P * s_l), torch.float32, q0.device)
+    lo = _opt(o_lo, "o_lo", (P * s_l, Hq // P, d), torch.bfloat16, q0.device)
     need = attn_bwd_workspace_bytes(P * s_l, Hq // P)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q_shards[0].device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q0.device)
     cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     keep = [_ptrs(x) for x in (q_shards, k_shards, v_shards, o_shards, do_shards, dq_shards, dk_shards, dv_shards)]
     qp, kp, vp, op, gp, dqp, dkp, dvp = (k[0] for k in keep)
-    cu, nd = _cu(cu_seqlens)
-    _call("attn_bwd_shards", qp, kp, vp, op, _dev(lse), gp, dqp, dkp, dvp, P, rank, s_l, Hq, Hkv, d,
-          _dtype(q_shards[0]), _default_scale(d, scale), int(causal), cu, nd, _dev(workspace), ctypes.byref(cap),
+    cu, nd = _cu(cu_seqlens, q0.device)
+    _call("attn_bwd_shards", qp, kp, vp, op, lo, _dev(lse), gp, dqp, dkp, dvp, P, rank, s_l, Hq, Hkv, d,
+          _dtype(q0), _default_scale(d, scale), int(causal), cu, nd, _dev(workspace), ctypes.byref(cap),
           _stream())
     return dq_shards, dk_shards, dv_shards
 

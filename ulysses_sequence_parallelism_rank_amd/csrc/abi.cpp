@@ -13,7 +13,7 @@ using namespace uly;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline int esize(int dtype) { return dtype == ULY_BF16 ? 2 : 4; }
@@ -51,6 +51,13 @@ int check_attn(const void* q, const void* k, const void* v, int64_t s, int Hq, i
   if (cu != nullptr && n_docs < 1) return ULY_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ULY_ERR_ALIGN;
   return ULY_OK;
+}
+
+// O's rounding residual: bf16 only (an fp32 O has none), 16-byte aligned
+int check_o_lo(const void* o_lo, int dtype) {
+  if (o_lo == nullptr) return ULY_OK;
+  if (dtype != ULY_BF16) return ULY_ERR_UNSUPPORTED;
+  return aligned16(o_lo) ? ULY_OK : ULY_ERR_ALIGN;
 }
 
 AttnArgs make_args(int64_t s, int Hq, int Hkv, int d, float scale, int causal, const int32_t* cu,
@@ -222,18 +229,21 @@ int ulysses_unpack_group(int n, const void* const* in, const int* H, void* const
   return hip_status(launch_unpack_group(segs, n, s_l, as_stream(stream)));
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t s, int Hq,
+int attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse, int64_t s, int Hq,
              int Hkv, int d, int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,
              void* stream) {
   int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, cu_seqlens, n_docs);
   if (st != ULY_OK) return st;
   if (!o || !lse) return ULY_ERR_NULL;
   if (!aligned16(o) || !aligned16(lse)) return ULY_ERR_ALIGN;
+  if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
   AttnArgs a = make_args(s, Hq, Hkv, d, scale, causal, cu_seqlens, n_docs);
   a.q = q;
   a.k = k;
   a.v = v;
   a.out = o;
+  a.o_lo = o_lo;
+  a.lo_row = (int64_t)Hq * d;
   a.lse_out = lse;
   return fwd_dispatch(a, d, dtype, as_stream(stream));
 }
@@ -243,15 +253,18 @@ size_t attn_bwd_workspace_bytes(int64_t s, int Hq) {
   return round256((size_t)s * (size_t)Hq * sizeof(float));
 }
 
-int attn_bwd_preprocess(const void* o, const void* dout, float* delta, int64_t s, int Hq, int d, int dtype,
-                        void* stream) {
+int attn_bwd_preprocess(const void* o, const void* o_lo, const void* dout, float* delta, int64_t s, int Hq, int d,
+                        int dtype, void* stream) {
   if (!o || !dout || !delta) return ULY_ERR_NULL;
   int st = check_dtype_dim(dtype, d);
   if (st != ULY_OK) return st;
   if (s < 1 || Hq < 1 || s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
   if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return ULY_ERR_ALIGN;
+  if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
   AttnArgs a = make_args(s, Hq, Hq, d, 1.f, 1, nullptr, 0);
   a.o = o;
+  a.o_lo = const_cast<void*>(o_lo);
+  a.lo_row = (int64_t)Hq * d;
   a.dout = dout;
   a.lse_out = delta;
   return hip_status(launch_bwd_preprocess(a, d, dtype, as_stream(stream)));
@@ -299,57 +312,13 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, c
   return hip_status(e);
 }
 
-size_t attn_bwd_stored_ds_bytes(int64_t s, int Hq, int causal) {
-  if (s < 1 || Hq < 1 || s > (int64_t)INT32_MAX) return 0;
-  return (size_t)Hq * (size_t)ds_tiles_per_head(s, causal ? 1 : 0) * (128 * 64 * sizeof(uint16_t));
-}
-
-int attn_bwd_dkdv_store_ds(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                           const float* delta, void* dk, void* dv, void* ds, size_t ds_bytes, int64_t s, int Hq,
-                           int Hkv, int d, int dtype, float scale, int causal, void* stream) {
-  int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, nullptr, 0);
-  if (st != ULY_OK) return st;
-  if (dtype != ULY_BF16) return ULY_ERR_UNSUPPORTED;
-  if (!lse || !dout || !delta || !dk || !dv || !ds) return ULY_ERR_NULL;
-  if (!aligned16(lse) || !aligned16(dout) || !aligned16(delta) || !aligned16(dk) || !aligned16(dv) ||
-      !aligned16(ds))
-    return ULY_ERR_ALIGN;
-  if (ds_bytes < attn_bwd_stored_ds_bytes(s, Hq, causal)) return ULY_ERR_WORKSPACE;
-  AttnArgs a = make_args(s, Hq, Hkv, d, scale, causal, nullptr, 0);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.dout = dout;
-  a.lse_in = lse;
-  a.delta = delta;
-  a.out_k = dk;
-  a.out_v = dv;
-  a.ds = static_cast<uint16_t*>(ds);
-  a.ds_head_tiles = ds_tiles_per_head(s, a.causal);
-  return hip_status(launch_attn_dkdv_bf16(a, d, as_stream(stream)));
-}
-
-int attn_bwd_dq_stored_ds(const void* k, const void* ds, size_t ds_bytes, void* dq, int64_t s, int Hq, int Hkv,
-                          int d, int dtype, float scale, int causal, void* stream) {
-  int st = check_attn(k, k, k, s, Hq, Hkv, d, dtype, nullptr, 0);
-  if (st != ULY_OK) return st;
-  if (dtype != ULY_BF16) return ULY_ERR_UNSUPPORTED;
-  if (!ds || !dq) return ULY_ERR_NULL;
-  if (!aligned16(ds) || !aligned16(dq)) return ULY_ERR_ALIGN;
-  if (ds_bytes < attn_bwd_stored_ds_bytes(s, Hq, causal)) return ULY_ERR_WORKSPACE;
-  AttnArgs a = make_args(s, Hq, Hkv, d, scale, causal, nullptr, 0);
-  a.k = k;
-  a.out = dq;
-  a.ds = static_cast<uint16_t*>(const_cast<void*>(ds));
-  a.ds_head_tiles = ds_tiles_per_head(s, a.causal);
-  return hip_status(launch_attn_dq_from_ds_bf16(a, d, as_stream(stream)));
-}
-
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-             void* dq, void* dk, void* dv, int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
-             const int32_t* cu_seqlens, int n_docs, void* workspace, size_t* workspace_bytes, void* stream) {
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* o_lo, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int64_t s, int Hq, int Hkv, int d, int dtype, float scale,
+             int causal, const int32_t* cu_seqlens, int n_docs, void* workspace, size_t* workspace_bytes,
+             void* stream) {
   int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, cu_seqlens, n_docs);
   if (st != ULY_OK) return st;
+  if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
   const size_t need = attn_bwd_workspace_bytes(s, Hq);
   if (workspace == nullptr) {
     if (!workspace_bytes) return ULY_ERR_NULL;
@@ -362,7 +331,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
       !aligned16(dv) || !aligned16(workspace))
     return ULY_ERR_ALIGN;
   float* delta = static_cast<float*>(workspace);
-  st = attn_bwd_preprocess(o, dout, delta, s, Hq, d, dtype, stream);
+  st = attn_bwd_preprocess(o, o_lo, dout, delta, s, Hq, d, dtype, stream);
   if (st != ULY_OK) return st;
   st = attn_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens, n_docs,
                      stream);
@@ -386,8 +355,8 @@ size_t attn_fwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int
 }
 
 int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards, const void* const* v_shards,
-                     void* const* o_shards, float* lse, int P, int rank, int64_t s_l, int Hq, int Hkv, int d,
-                     int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,
+                     void* const* o_shards, void* o_lo, float* lse, int P, int rank, int64_t s_l, int Hq, int Hkv,
+                     int d, int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,
                      int heads_per_chunk, void* workspace, size_t* workspace_bytes, void* stream) {
   if (!q_shards || !k_shards || !v_shards || !o_shards) return ULY_ERR_NULL;
   int st = check_ranks(P, rank, s_l, Hq);
@@ -408,6 +377,7 @@ int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards, c
   if (workspace_bytes && *workspace_bytes < need) return ULY_ERR_WORKSPACE;
   if (!lse) return ULY_ERR_NULL;
   if (!aligned16(lse) || !aligned16(workspace)) return ULY_ERR_ALIGN;
+  if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
   for (int p = 0; p < P; ++p) {
     if (!q_shards[p] || !k_shards[p] || !v_shards[p] || !o_shards[p]) return ULY_ERR_NULL;
     if (!aligned16(q_shards[p]) || !aligned16(k_shards[p]) || !aligned16(v_shards[p]) || !aligned16(o_shards[p]))
@@ -457,6 +427,9 @@ int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards, c
     a.k = kc;
     a.v = vc;
     a.out = oc;
+    // the residual of the chunk's heads, in the rank's [s, Hq/P, d] layout
+    a.o_lo = o_lo == nullptr ? nullptr : static_cast<char*>(o_lo) + c0 * hb;
+    a.lo_row = (int64_t)Hq_l * d;
     a.lse_out = lse + (int64_t)c0 * s;
     st = fwd_dispatch(a, d, dtype, strm);
     if (st != ULY_OK) return st;
@@ -474,8 +447,9 @@ int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards, c
 //   dK, dV of the rank         2 x [s, Hkv/P, d]         element type
 
 int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards, const void* const* v_shards,
-                    void* const* o_shards, float* lse, int P, int rank, int64_t s_l, int Hq, int Hkv, int d,
-                    int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs, void* stream) {
+                    void* const* o_shards, void* o_lo, float* lse, int P, int rank, int64_t s_l, int Hq, int Hkv,
+                    int d, int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,
+                    void* stream) {
   if (!q_shards || !k_shards || !v_shards || !o_shards || !lse) return ULY_ERR_NULL;
   int st = check_ranks(P, rank, s_l, Hq);
   if (st != ULY_OK) return st;
@@ -487,6 +461,7 @@ int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards, co
   if (s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
   if (cu_seqlens != nullptr && n_docs < 1) return ULY_ERR_SHAPE;
   if (!aligned16(lse)) return ULY_ERR_ALIGN;
+  if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
   const int Hq_l = Hq / P, Hkv_l = Hkv / P;
   ShardSrc src{};
   for (int p = 0; p < P; ++p) {
@@ -505,12 +480,14 @@ int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards, co
   AttnArgs a = make_args(s, Hq_l, Hkv_l, d, scale, causal, cu_seqlens, n_docs);
   a.q_row = (int64_t)Hq * d;  // rows of the sequence shards hold every head
   a.kv_row = (int64_t)Hkv * d;
+  a.o_lo = o_lo;  // the rank's [s, Hq/P, d] layout
+  a.lo_row = (int64_t)Hq_l * d;
   a.lse_out = lse;
   return hip_status(launch_attn_fwd_bf16_shards(a, src, d, as_stream(stream)));
 }
 
 int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards, const void* const* v_shards,
-                    const void* const* o_shards, const float* lse, const void* const* do_shards,
+                    const void* const* o_shards, const void* o_lo, const float* lse, const void* const* do_shards,
                     void* const* dq_shards, void* const* dk_shards, void* const* dv_shards, int P, int rank,
                     int64_t s_l, int Hq, int Hkv, int d, int dtype, float scale, int causal,
                     const int32_t* cu_seqlens, int n_docs, void* workspace, size_t* workspace_bytes,
@@ -536,6 +513,7 @@ int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards, co
   if (workspace_bytes && *workspace_bytes < need) return ULY_ERR_WORKSPACE;
   if (!lse) return ULY_ERR_NULL;
   if (!aligned16(lse) || !aligned16(workspace)) return ULY_ERR_ALIGN;
+  if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
   BwdSrc src{};
   const int64_t qo = (int64_t)rank * Hq_l * d, kvo = (int64_t)rank * Hkv_l * d;  // bf16 elements
   for (int p = 0; p < P; ++p) {
@@ -564,6 +542,8 @@ int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards, co
   a.delta = delta;
   AttnArgs pre = a;
   pre.lse_out = delta;
+  pre.o_lo = const_cast<void*>(o_lo);  // the rank's [s, Hq/P, d] layout
+  pre.lo_row = (int64_t)Hq_l * d;
   hipStream_t strm = as_stream(stream);
   hipError_t err;
   if ((err = launch_bwd_preprocess_bf16_shards(pre, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
@@ -581,7 +561,7 @@ size_t attn_bwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int
 }
 
 int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards, const void* const* v_shards,
-                     const void* const* o_shards, const float* lse, const void* const* do_shards,
+                     const void* const* o_shards, const void* o_lo, const float* lse, const void* const* do_shards,
                      void* const* dq_shards, void* const* dk_shards, void* const* dv_shards, int P, int rank,
                      int64_t s_l, int Hq, int Hkv, int d, int dtype, float scale, int causal,
                      const int32_t* cu_seqlens, int n_docs, int heads_per_chunk, void* workspace,
@@ -606,6 +586,7 @@ int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards, c
   if (workspace_bytes && *workspace_bytes < need) return ULY_ERR_WORKSPACE;
   if (!lse) return ULY_ERR_NULL;
   if (!aligned16(lse) || !aligned16(workspace)) return ULY_ERR_ALIGN;
+  if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
   for (int p = 0; p < P; ++p) {
     const void* ptrs[8] = {q_shards[p], k_shards[p], v_shards[p], o_shards[p], do_shards[p],
                            dq_shards[p], dk_shards[p], dv_shards[p]};
@@ -674,6 +655,9 @@ int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards, c
     // delta of the chunk's heads
     AttnArgs pre = a;
     pre.lse_out = delta;
+    // the residual of the chunk's heads, in the rank's [s, Hq/P, d] layout
+    pre.o_lo = o_lo == nullptr ? nullptr : const_cast<char*>(static_cast<const char*>(o_lo)) + c0 * hb;
+    pre.lo_row = (int64_t)Hq_l * d;
     if ((err = launch_bwd_preprocess(pre, d, dtype, strm)) != hipSuccess) return ULY_ERR_HIP;
     // dK/dV of kv heads [g0, g1): fp32 sums carried across chunks, rounded on the last one
     AttnArgs kvargs = a;

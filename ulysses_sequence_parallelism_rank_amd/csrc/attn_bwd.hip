@@ -33,115 +33,6 @@ constexpr int kWaves = 4;
 // ---------------------------------------------------------------------------------------
 // delta[h, i] = sum_x dO[i, h, x] * O[i, h, x] (fp32). TPR threads per (row, head), 16 B each.
 // ---------------------------------------------------------------------------------------
-// dQ from stored dS: one workgroup = 128 query rows of one q head (4 waves x 32 rows, two
-// workgroups per CU). For each 64-key half of each key block the rows can see, the K rows and
-// the two 64-row dS tiles (written by the dK/dV kernel) arrive in LDS by DMA (double
-// buffered), and dQ^T += K^T dS^T takes both operands from transposing LDS reads:
-// 16 MFMAs per half and wave, with no S or dP recomputed. dS is already 0 wherever a row cannot
-// see a key, so no masking; the loop order is fixed (deterministic).
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_dq_from_ds_kernel(AttnArgs a) {
-  constexpr int BM = 128, BN = 64, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sS[2][2][BN * 64];  // [buffer][q tile][64-key half]
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hf = lane >> 5, gi = lane >> 4, li = lane & 15;
-  const int64_t s = a.s;
-  const int nrb = (int)((s + BM - 1) / BM);
-  const int h = blockIdx.x % a.n_heads;
-  const int rb = nrb - 1 - (int)(blockIdx.x / a.n_heads);  // longest rows first
-  const int kvh = (h + a.q_off) / a.G - a.kv_off;
-  const uint16_t* K = static_cast<const uint16_t*>(a.k) + (int64_t)kvh * D;
-  const int64_t nqt = (s + 63) / 64;
-  const int64_t it0 = 2 * (int64_t)rb;
-  // the second 64-row tile may lie past the sequence: then read the first again (its rows are
-  // never stored)
-  const int64_t it1 = it0 + 1 < nqt ? it0 + 1 : it0;
-  const int nkb = a.causal ? rb + 1 : (int)((s + 127) / 128);
-  const int nsteps = 2 * nkb;  // 64-key halves
-
-  auto issue = [&](int step, int b) {
-    const int64_t kb = step >> 1, hh = step & 1;
-    dma_tile<D, BN, 256>(K, a.kv_row, kb * 128 + hh * BN, s, sK[b], tid);
-    const uint16_t* head = a.ds + (int64_t)h * a.ds_head_tiles * (128 * 64);
-    const int64_t base = ds_tile_base(kb, nqt, a.causal) - ds_first_tile(kb, a.causal);
-    dma_tile<64, BN, 256>(head + (base + it0) * (128 * 64) + hh * BN * 64, 64, 0, BN, sS[b][0], tid);
-    dma_tile<64, BN, 256>(head + (base + it1) * (128 * 64) + hh * BN * 64, 64, 0, BN, sS[b][1], tid);
-  };
-  // transposing-read operand: 8 of the 16 keys of k-step kk (rows of the tile) for the column
-  // group starting at col (d for K^T, query row for dS^T)
-  auto load_tr = [&](const uint16_t* tile, auto DCOLS, int kk, int col0) {
-    constexpr int DC = decltype(DCOLS)::value;
-    const int kr = 16 * kk + 4 * hf + (li >> 2);
-    const int col = col0 + 16 * (gi & 1) + 4 * (li & 3);
-    const i16x4 x0 = lds_read_tr16(&tile[tile_off<DC>(kr, col)]);
-    const i16x4 x1 = lds_read_tr16(&tile[tile_off<DC>(kr + 8, col)]);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-
-  const int st = wave >> 1, c0 = 32 * (wave & 1);  // this wave's q tile and its rows in it
-  // dS^T operand of k-step kk gathered from a 64-key half of a stored tile, which holds the dS
-  // waves' accumulator layout [key group][half qb][k-step tt][lane][8 bf16] (as 64 x 64 bf16
-  // in the tile_off layout): each lane of a 16-lane group points at the 4 consecutive rows
-  // R..R+3 of key kappa that the transposing read hands to the lanes owning those rows, so
-  // lane l gets row c0 + l%32 and the keys load_tr gives the K^T operand of the same k-step
-  auto load_ds = [&](const uint16_t* tile, int kk) {
-    const int R = c0 + 16 * (gi & 1) + 4 * (li & 3);
-    const int qb = R >> 5, r = R & 31, tt = r >> 4, u = (r >> 3) & 1, hw = (r >> 2) & 1;
-    auto chunk = [&](int kappa) {
-      const int off = (((kappa >> 5) * 4 + qb * 2 + tt) * 64 + hw * 32 + (kappa & 31)) * 8 + u * 4;
-      return lds_read_tr16(&tile[tile_off<64>(off >> 6, off & 63)]);
-    };
-    const i16x4 x0 = chunk(16 * kk + 4 * hf + (li >> 2));
-    const i16x4 x1 = chunk(16 * kk + 8 + 4 * hf + (li >> 2));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-
-  f32x16 dqacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
-  if (nsteps > 0) issue(0, 0);
-  for (int step = 0; step < nsteps; ++step) {
-    const int b = step & 1;
-    wait_dma();
-    __syncthreads();  // this step's tiles have landed; every wave is done with the previous ones
-#pragma unroll
-    for (int kk = 0; kk < BN / 16; ++kk) {
-      const bf16x8 bs = load_ds(sS[b][st], kk);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 ak = load_tr(sK[b], std::integral_constant<int, D>{}, kk, db * 32);
-        dqacc[db] = mfma32x32x16(ak, bs, dqacc[db]);
-      }
-    }
-    // the next step's DMA after this step's last LDS read
-    if (step + 1 < nsteps) issue(step + 1, b ^ 1);
-  }
-
-  const int64_t row = (int64_t)rb * BM + 32 * wave + l32;
-  if (row < s) {
-    uint16_t* dQ = static_cast<uint16_t*>(a.out) + (int64_t)h * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        u32x2 w;
-        w[0] = pack_bf16x2(dqacc[db][4 * jj + 0] * a.scale, dqacc[db][4 * jj + 1] * a.scale);
-        w[1] = pack_bf16x2(dqacc[db][4 * jj + 2] * a.scale, dqacc[db][4 * jj + 3] * a.scale);
-        *reinterpret_cast<u32x2*>(dQ + row * a.q_row + db * 32 + 8 * jj + 4 * hf) = w;
-      }
-  }
-}
-
-template <int D>
-hipError_t launch_dq_from_ds_t(const AttnArgs& a, hipStream_t stream) {
-  const int64_t blocks = (a.s + 127) / 128 * a.n_heads;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_dq_from_ds_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a, Shards o_sh, Shards g_sh, int64_t s_l) {
   constexpr int TPR = D * (int)sizeof(T) / 16;
@@ -157,10 +48,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a, Shards o_sh, S
     const u32x4 ov = *reinterpret_cast<const u32x4*>(static_cast<const T*>(o_sh.p[ps]) + off);
     const u32x4 gv = *reinterpret_cast<const u32x4*>(static_cast<const T*>(g_sh.p[ps]) + off);
     if constexpr (sizeof(T) == 2) {
+      // O = bf16 O + its rounding residual when the forward wrote one (delta then carries no
+      // bf16 rounding of O, which matters on rows dominated by one key)
+      u32x4 lv = {0, 0, 0, 0};
+      if (a.o_lo != nullptr)
+        lv = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.o_lo) + row * a.lo_row + (int64_t)h * D +
+                                              part * EPV);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc += bf16_to_f32((uint16_t)(ov[i] & 0xffff)) * bf16_to_f32((uint16_t)(gv[i] & 0xffff));
-        acc += bf16_to_f32((uint16_t)(ov[i] >> 16)) * bf16_to_f32((uint16_t)(gv[i] >> 16));
+        acc += (bf16_lo(ov[i]) + bf16_lo(lv[i])) * bf16_lo(gv[i]);
+        acc += (bf16_hi(ov[i]) + bf16_hi(lv[i])) * bf16_hi(gv[i]);
       }
     } else {
       // bit-cast whole vectors: clang mis-handles __builtin_bit_cast of a vector element
@@ -220,7 +117,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
       if (a.cu != nullptr) {
         const int dk = doc_of(a.cu, a.n_docs, row[rb]);
         lo[rb] = a.cu[dk];
-        hi[rb] = a.cu[dk + 1];
+        hi[rb] = a.cu[dk + 1] < s ? a.cu[dk + 1] : s;
       }
       lse2[rb] = a.lse_in[(int64_t)h * a.lse_row + row[rb]] * kLog2e;
       dl[rb] = a.delta[(int64_t)h * a.lse_row + row[rb]];
@@ -242,8 +139,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
   const int64_t last_row = (m0 + BM < s ? m0 + BM : s) - 1;
   int64_t kbeg = 0, kend = s;
   if (a.cu != nullptr) {
+    // document bounds clamped to [0, s]: no tile outside the sequence is ever visited
     kbeg = a.cu[doc_of(a.cu, a.n_docs, m0)];
+    kbeg = kbeg > 0 ? kbeg : 0;
     kend = a.cu[doc_of(a.cu, a.n_docs, last_row) + 1];
+    kend = kend < s ? kend : s;
   }
   if (a.causal) kend = kend < last_row + 1 ? kend : last_row + 1;
   kbeg = (kbeg / BN) * BN;
@@ -385,8 +285,7 @@ struct DkvSplitCfg {
   static constexpr int DT = D / 16, DB = D / 32;
 };
 
-// STORE: also write dS (bf16, as the dK product uses it) to a.ds for the stored-dS dQ kernel.
-template <int D, bool STORE>
+template <int D>
 __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Shards q_sh, Shards g_sh, Shards k_sh,
                                                                  Shards v_sh, Shards dk_sh, Shards dv_sh, int64_t s_l) {
   using C = DkvSplitCfg<D>;
@@ -423,7 +322,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
   if (a.cu != nullptr && key < s) {
     const int dk = doc_of(a.cu, a.n_docs, key);
     rlo = a.cu[dk];
-    rhi = a.cu[dk + 1];
+    rhi = a.cu[dk + 1] < (int32_t)s ? a.cu[dk + 1] : (int32_t)s;
   }
   if (a.causal) rlo = (int32_t)key;
   if (key >= s) rhi = rlo;  // padding key: seen by no row
@@ -445,8 +344,11 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
   const int64_t last_key = (n0 + BNK < s ? n0 + BNK : s) - 1;
   int64_t qbeg = a.causal ? n0 : 0, qend = s;
   if (a.cu != nullptr) {
+    // document bounds clamped to [0, s]: no tile outside the sequence is ever visited
     qend = a.cu[doc_of(a.cu, a.n_docs, last_key) + 1];
+    qend = qend < s ? qend : s;
     if (!a.causal) qbeg = a.cu[doc_of(a.cu, a.n_docs, n0)];
+    qbeg = qbeg > 0 ? qbeg : 0;
   }
   qbeg = (qbeg / BMQ) * BMQ;
   const int ntile = qend > qbeg ? (int)((qend - qbeg + BMQ - 1) / BMQ) : 0;
@@ -505,8 +407,6 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
     const int nxt_t = cur_h + 1 == GH ? cur_t + 1 : cur_t;
     if (role == 1 && step + 1 < nsteps) issue_tile(nxt_t, nxt_h, nbuf);
     const int32_t qrel0 = (int32_t)tile_row0(cur_t) - rlo + 4 * hf;
-    const int64_t step_q0 = tile_row0(cur_t);
-    const int step_h = kh.j0 + cur_h;
     cur_t = nxt_t;
     cur_h = nxt_h;
     // The two roles run separate code, each naming its LDS objects directly (a runtime choice
@@ -590,22 +490,6 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
           }
           op[qb][0] = pack8(x[qb], 0);
           op[qb][1] = pack8(x[qb], 1);
-        }
-        if constexpr (STORE) {
-          // this step's 16 KiB tile of dS in the MFMA accumulator layout of the dS waves:
-          // [key group kg][half qb][k-step tt][lane][8 bf16], one coalesced 1 KiB store per
-          // (qb, tt) and wave (the stored-dS dQ kernel gathers its operands from this layout); issued
-          // before the dK products so they drain before the wait that precedes the next barrier
-          const int64_t kb = n0 / BNK, nqt = (s + BMQ - 1) / BMQ;
-          const int64_t tile = (int64_t)step_h * a.ds_head_tiles + ds_tile_base(kb, nqt, a.causal) +
-                               step_q0 / BMQ - ds_first_tile(kb, a.causal);
-          uint16_t* t = a.ds + tile * (BNK * BMQ) + (kg * 4 * 64 + lane) * 8;
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-              __builtin_nontemporal_store(__builtin_bit_cast(u32x4, op[qb][tt]),
-                                          reinterpret_cast<u32x4*>(t + (qb * 2 + tt) * 64 * 8));
         }
       }
 #pragma unroll
@@ -712,12 +596,8 @@ hipError_t launch_dkdv_split_t(const AttnArgs& a, const BwdSrc& src, hipStream_t
   using C = DkvSplitCfg<D>;
   const int64_t blocks = (a.s + C::BNK - 1) / C::BNK * a.n_kv;
   if (blocks == 0) return hipSuccess;
-  if (a.ds != nullptr)
-    hipLaunchKernelGGL((attn_dkdv_split_kernel<D, true>), dim3((unsigned)blocks), dim3(C::NW * 64), 0, stream, a,
-                       src.q, src.g, src.k, src.v, src.dk, src.dv, src.s_l);
-  else
-    hipLaunchKernelGGL((attn_dkdv_split_kernel<D, false>), dim3((unsigned)blocks), dim3(C::NW * 64), 0, stream, a,
-                       src.q, src.g, src.k, src.v, src.dk, src.dv, src.s_l);
+  hipLaunchKernelGGL((attn_dkdv_split_kernel<D>), dim3((unsigned)blocks), dim3(C::NW * 64), 0, stream, a, src.q,
+                     src.g, src.k, src.v, src.dk, src.dv, src.s_l);
   return hipGetLastError();
 }
 
@@ -762,11 +642,6 @@ hipError_t launch_bwd_preprocess_bf16_shards(const AttnArgs& a, const BwdSrc& sr
 hipError_t launch_attn_dq_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream) {
   if (d == 128) return launch_dq_t<128, 1, 2>(a, src, stream);
   return launch_dq_t<64, 1, 2>(a, src, stream);
-}
-
-hipError_t launch_attn_dq_from_ds_bf16(const AttnArgs& a, int d, hipStream_t stream) {
-  if (d == 128) return launch_dq_from_ds_t<128>(a, stream);
-  return launch_dq_from_ds_t<64>(a, stream);
 }
 
 hipError_t launch_attn_dkdv_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream) {

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kRows) void f32_fwd_kernel(AttnArgs a) {
   if (a.cu != nullptr && row < s) {
     const int dk = doc_of(a.cu, a.n_docs, row);
     lo = a.cu[dk];
-    hi = a.cu[dk + 1];
+    hi = a.cu[dk + 1] < s ? a.cu[dk + 1] : s;
   }
   if (a.causal) hi = hi < row + 1 ? hi : row + 1;
   const int64_t last_row = (m0 + kRows < s ? m0 + kRows : s) - 1;
@@ -42,6 +42,7 @@ __global__ __launch_bounds__(kRows) void f32_fwd_kernel(AttnArgs a) {
   if (a.cu != nullptr) {
     kbeg = a.cu[doc_of(a.cu, a.n_docs, m0)];
     kend = a.cu[doc_of(a.cu, a.n_docs, last_row) + 1];
+    kend = kend < s ? kend : s;  // document bounds clamped to the sequence
   }
   if (a.causal) kend = kend < last_row + 1 ? kend : last_row + 1;
 
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(kRows) void f32_dq_kernel(AttnArgs a) {
     if (a.cu != nullptr) {
       const int dk = doc_of(a.cu, a.n_docs, row);
       lo = a.cu[dk];
-      hi = a.cu[dk + 1];
+      hi = a.cu[dk + 1] < s ? a.cu[dk + 1] : s;
     }
     lse = a.lse_in[(int64_t)h * a.lse_row + row];
     dl = a.delta[(int64_t)h * a.lse_row + row];
@@ -125,6 +126,7 @@ __global__ __launch_bounds__(kRows) void f32_dq_kernel(AttnArgs a) {
   if (a.cu != nullptr) {
     kbeg = a.cu[doc_of(a.cu, a.n_docs, m0)];
     kend = a.cu[doc_of(a.cu, a.n_docs, last_row) + 1];
+    kend = kend < s ? kend : s;  // document bounds clamped to the sequence
   }
   if (a.causal) kend = kend < last_row + 1 ? kend : last_row + 1;
 
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(kRows) void f32_dkdv_kernel(AttnArgs a) {
   if (a.cu != nullptr && key < s) {
     const int dk = doc_of(a.cu, a.n_docs, key);
     rlo = a.cu[dk];
-    rhi = a.cu[dk + 1];
+    rhi = a.cu[dk + 1] < s ? a.cu[dk + 1] : s;
   }
   if (a.causal) rlo = key;
   if (key >= s) rhi = rlo;
@@ -190,6 +192,7 @@ __global__ __launch_bounds__(kRows) void f32_dkdv_kernel(AttnArgs a) {
   int64_t qbeg = a.causal ? n0 : 0, qend = s;
   if (a.cu != nullptr) {
     qend = a.cu[doc_of(a.cu, a.n_docs, last_key) + 1];
+    qend = qend < s ? qend : s;  // document bounds clamped to the sequence
     if (!a.causal) qbeg = a.cu[doc_of(a.cu, a.n_docs, n0)];
   }
 

@@ -22,8 +22,13 @@
 //     the row-major V tile through the transposing LDS read (ds_read_b64_tr_b16), and the
 //     O^T accumulator keeps each lane's query row, so softmax rescales stay lane-local;
 //   * the exponent is exp2 with scale*log2(e) folded into one FMA, and the running max is
-//     only moved when a row's max grows by more than kTau (2^8): P then stays <= 256,
-//     exact in the final O / l, and most halves skip the O rescale;
+//     only moved when a row's max grows by more than kTau (2^8): P then stays <= 256 and
+//     most halves skip the O rescale;
+//   * two row sums: l of the fp32 weights gives the LSE, and l' of the bf16-rounded weights
+//     (the PV operand, summed by v_dot2_f32_bf16) normalises O, so O is an exact convex
+//     combination of the V rows with the weights the MFMA used: on rows dominated by one key
+//     the weight's rounding (up to 2^-9 of it, since the lagging max leaves it unequal to 1)
+//     then cancels instead of reaching O, and delta = dO . O in the backward;
 //   * causal / document tiles outside a row block's range are never visited; partial
 //     halves are masked per element; workgroups with the longest key range launch first.
 #include <type_traits>
@@ -62,7 +67,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
   if (a.cu != nullptr && row < s) {
     const int dk = doc_of(a.cu, a.n_docs, row);
     lo = a.cu[dk];
-    hi = a.cu[dk + 1];
+    hi = a.cu[dk + 1] < s ? a.cu[dk + 1] : s;
   }
   if (a.causal) hi = hi < row + 1 ? hi : row + 1;
   bf16x8 qf[DT];
@@ -78,8 +83,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
   const int64_t last_row = (m0 + BM < s ? m0 + BM : s) - 1;
   int64_t kbeg = 0, kend = s, w_lo_last = 0, w_hi_first = s;
   if (a.cu != nullptr) {
+    // document bounds clamped to [0, s]: no tile outside the sequence is ever visited
     kbeg = a.cu[doc_of(a.cu, a.n_docs, m0)];
+    kbeg = kbeg > 0 ? kbeg : 0;
     kend = a.cu[doc_of(a.cu, a.n_docs, last_row) + 1];
+    kend = kend < s ? kend : s;
     if (wr0 < s) {
       w_hi_first = a.cu[doc_of(a.cu, a.n_docs, wr0) + 1];
       w_lo_last = a.cu[doc_of(a.cu, a.n_docs, wr1)];
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f, lr = 0.f;  // running max (log2 units), sums of fp32 / rounded weights
   // mask S of the 32 keys from k0, then rescale O if the row max grew by more than kTau
   auto mask_rescale = [&](int64_t k0, f32x16& S) {
     if (!half_full(k0)) {
@@ -138,6 +146,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
       const float alpha = need ? fast_exp2(m - mnew) : 1.f;
       m = mnew;
       l *= alpha;
+      lr *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] = mfma32x32x16(bf16x8{}, bf16x8{}, oacc[db] * alpha);
     }
@@ -154,6 +163,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
     pf[0] = to_bf16x8(S, 0);
     pf[1] = to_bf16x8(S, 1);
     l += ls;
+    // the rounded weights, two per v_dot2_f32_bf16 against (1, 1)
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 w = __builtin_bit_cast(u32x4, pf[t]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t we = w[e];
+        lr = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, we), one2, lr, false);
+      }
+    }
   };
   auto pv = [&](int b, int hh, const bf16x8 (&pf)[2]) {
 #pragma unroll
@@ -204,18 +224,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
     ++t;
   }
 
-  const float lt = half_swap_sum(l);
+  const float lt = half_swap_sum(l), lrt = half_swap_sum(lr);
   if (row < s) {
     uint16_t* O = static_cast<uint16_t*>(src.o[ps]) + (int64_t)h * D - r_sh * a.q_row;
-    const float inv = 1.f / lt;
+    // O's bf16 rounding residual, when asked for: O_fp32 - bf16(O_fp32), rounded to bf16
+    uint16_t* OL = a.o_lo != nullptr ? static_cast<uint16_t*>(a.o_lo) + (int64_t)h * D + row * a.lo_row : nullptr;
+    const float inv = 1.f / lrt;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
+        const float x0 = oacc[db][4 * jj + 0] * inv, x1 = oacc[db][4 * jj + 1] * inv;
+        const float x2 = oacc[db][4 * jj + 2] * inv, x3 = oacc[db][4 * jj + 3] * inv;
         u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
+        w[0] = pack_bf16x2(x0, x1);
+        w[1] = pack_bf16x2(x2, x3);
         *reinterpret_cast<u32x2*>(O + row * a.q_row + db * 32 + 8 * jj + 4 * hf) = w;
+        if (OL != nullptr) {
+          const uint32_t w0 = w[0], w1 = w[1];
+          u32x2 r;
+          r[0] = pack_bf16x2(x0 - bf16_lo(w0), x1 - bf16_hi(w0));
+          r[1] = pack_bf16x2(x2 - bf16_lo(w1), x3 - bf16_hi(w1));
+          *reinterpret_cast<u32x2*>(OL + db * 32 + 8 * jj + 4 * hf) = r;
+        }
       }
     if (hf == 0) a.lse_out[(int64_t)h * a.lse_row + row] = (m + log2f(lt)) * kLn2;
   }

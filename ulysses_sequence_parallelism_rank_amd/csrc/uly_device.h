@@ -60,6 +60,9 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
+// the two bf16 halves of a packed pair (low half = first element) as fp32
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 // 16 fp32 accumulator values j = 8t..8t+7 -> one bf16x8 MFMA operand.
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& a, int t) {

@@ -40,6 +40,11 @@ struct AttnArgs {
   float* acc_v;   // fp32 dV accumulator
   int64_t dkv_row;
   float* lse_out; // forward LSE / preprocess delta
+  // O's bf16 rounding residual ([s, n_heads, D] bf16 at the launch's head 0, row stride lo_row):
+  // the bf16 forward writes O_fp32 - bf16(O_fp32) rounded to bf16 here when it is set, and the
+  // preprocess then forms delta from O + o_lo; null: not written / delta from O alone
+  void* o_lo;
+  int64_t lo_row;
   int64_t s;
   int64_t q_row, kv_row;
   int64_t lse_row;
@@ -50,24 +55,7 @@ struct AttnArgs {
   int causal;
   const int32_t* cu;
   int n_docs;
-  // stored-dS backward: the dK/dV kernel also writes dS (bf16) here in tiles of 128 keys x 64
-  // rows ([key][row], rows fastest), ds_head_tiles tiles per q head (see ds_tile_index)
-  uint16_t* ds;
-  int64_t ds_head_tiles;
 };
-
-// Stored-dS tiles of one q head (no cu_seqlens): key block kb (128 keys) holds the 64-row query
-// tiles the dK/dV kernel visits for it, [2 kb, nqt) when causal, [0, nqt) otherwise, where
-// nqt = ceil(s / 64); tile (kb, it) is the head's tile number ds_tile_base(kb) + it - first.
-__host__ __device__ inline int64_t ds_tile_base(int64_t kb, int64_t nqt, int causal) {
-  return causal ? kb * nqt - kb * (kb - 1) : kb * nqt;
-}
-__host__ __device__ inline int64_t ds_first_tile(int64_t kb, int causal) { return causal ? 2 * kb : 0; }
-inline int64_t ds_tiles_per_head(int64_t s, int causal) {
-  const int64_t nkb = (s + 127) / 128, nqt = (s + 63) / 64;
-  return ds_tile_base(nkb, nqt, causal);
-}
-hipError_t launch_attn_dq_from_ds_bf16(const AttnArgs& a, int d, hipStream_t stream);
 
 // One tensor of a grouped permute: its P shards (P of them used), the head-shard buffer, the
 // shard row size, the byte offset of the rank's heads in a row and the bytes per row moved.
