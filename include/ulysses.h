@@ -158,6 +158,24 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
 
 size_t attn_bwd_workspace_bytes(int64_t s, int Hq);
 
+/* ---------------------------------------------------------------------------
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, and the same kernels, so the results are bitwise those
+ * of attn_bwd. delta lives in a static device array of ULY_NOALLOC_MAX_DELTA floats
+ * (16 MiB) that each GPU the library runs on holds until the process ends; the call
+ * allocates nothing. s * Hq above ULY_NOALLOC_MAX_DELTA -> ULY_ERR_WORKSPACE; the array's
+ * address not obtainable -> ULY_ERR_HIP. Every call on one GPU uses that GPU's one array:
+ * calls that overlap on a GPU (other streams, other host threads) race and must be ordered
+ * by the caller. Devices are numbered below ULY_MAX_DEVICES.
+ * ------------------------------------------------------------------------- */
+#define ULY_NOALLOC_MAX_DELTA (1 << 22)
+#define ULY_MAX_DEVICES 64
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* o_lo,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
+                     const int32_t* cu_seqlens, int n_docs, void* stream);
+
 /* The three phases of attn_bwd, exported so that each can be timed on its own.
  * delta [Hq, s] fp32: delta[h, i] = sum_x dout[i, h, x] * (o[i, h, x] + o_lo[i, h, x])
  * (o_lo NULL: the o term alone).                                                    */

@@ -261,3 +261,15 @@ def test_binding_checks_shapes_before_the_call():
     with pytest.raises(ValueError, match="cu_seqlens"):
         U._cu(torch.zeros(1, dtype=torch.int32))
 
+
+def test_bwd_noalloc_rejects_on_the_host():
+    """The allocation-free backward refuses a delta larger than its static array, and the usual
+    argument errors, before touching the device."""
+    L = U.lib()
+    z = [FAKE] * 10
+    too_big = (U.NOALLOC_MAX_DELTA // 8) + 1
+    assert L.attn_bwd_noalloc(*z, too_big, 8, 2, 128, 0, 0.1, 1, None, 0, None) == 5
+    assert L.attn_bwd_noalloc(*z, 1000, 8, 3, 128, 0, 0.1, 1, None, 0, None) == 2
+    assert L.attn_bwd_noalloc(None, *z[1:], 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None) == 1
+    assert L.attn_bwd_noalloc(*z[:4], MIS, *z[5:], 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None) == 4
+

@@ -53,6 +53,8 @@ SIGNATURES = {
     "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
                         _vp, _i32, _vp, _szp, _vp]),
     "attn_bwd_workspace_bytes": (_sz, [_i64, _i32]),
+    "attn_bwd_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32,
+                                _i32, _vp, _i32, _vp]),
     "attn_bwd_preprocess": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "attn_bwd_dkdv": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
                              _vp, _i32, _vp]),
@@ -311,6 +313,29 @@ def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=True, cu_seqlens=None, wo
     _call("attn_bwd", _dev(q), _dev(k), _dev(v), _dev(o), lo, _dev(lse), _dev(dout), _dev(dq), _dev(dk), _dev(dv),
           s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, _dev(workspace),
           ctypes.byref(cap), _stream())
+    return dq, dk, dv
+
+
+NOALLOC_MAX_DELTA = 1 << 22
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, scale=None, causal=True, cu_seqlens=None, dq=None, dk=None, dv=None,
+                     o_lo=None):
+    """attn_bwd without a workspace: delta lives in the library's static per-device array
+    (s * Hq <= NOALLOC_MAX_DELTA). Calls that overlap on one GPU race."""
+    s, Hq, Hkv, d = _qkv(q, k, v)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        _need(t, n, (s, Hq, d), q.dtype, q.device)
+    for t, n in ((dk, "dk"), (dv, "dv")):
+        _need(t, n, (s, Hkv, d), q.dtype, q.device)
+    _need(lse, "lse", (Hq, s), torch.float32, q.device)
+    lo = _opt(o_lo, "o_lo", (s, Hq, d), torch.bfloat16, q.device)
+    cu, nd = _cu(cu_seqlens, q.device)
+    _call("attn_bwd_noalloc", _dev(q), _dev(k), _dev(v), _dev(o), lo, _dev(lse), _dev(dout), _dev(dq), _dev(dk),
+          _dev(dv), s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, _stream())
     return dq, dk, dv
 
 

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "uly_internal.h"
 #include "ulysses.h"
@@ -338,6 +339,47 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (st != ULY_OK) return st;
   return attn_bwd_dq(q, k, v, lse, dout, delta, dq, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens, n_docs,
                      stream);
+}
+
+// ---- attn_bwd without a caller workspace ---------------------------------------------
+// delta lives in a file-scope device array; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name in host code is a
+// host-side stand-in, not a device address).
+static __device__ __align__(256) float scratch[ULY_NOALLOC_MAX_DELTA];
+
+static std::mutex g_scratch_mu;
+static float* g_scratch_ptr[ULY_MAX_DEVICES];
+
+// this device's copy of `scratch`, looked up once per device (null on failure)
+static float* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= ULY_MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  return g_scratch_ptr[dev];
+}
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* o_lo, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int64_t s, int Hq, int Hkv, int d, int dtype,
+                     float scale, int causal, const int32_t* cu_seqlens, int n_docs, void* stream) {
+  int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, cu_seqlens, n_docs);
+  if (st != ULY_OK) return st;
+  if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
+  if (!o || !lse || !dout || !dq || !dk || !dv) return ULY_ERR_NULL;
+  if (!aligned16(o) || !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return ULY_ERR_ALIGN;
+  if (Hq < 1 || (uint64_t)s * (uint64_t)Hq > (uint64_t)ULY_NOALLOC_MAX_DELTA) return ULY_ERR_WORKSPACE;
+  // every argument is checked: only now is the device touched
+  float* delta = device_scratch();
+  if (delta == nullptr) return ULY_ERR_HIP;
+  size_t cap = (size_t)ULY_NOALLOC_MAX_DELTA * sizeof(float);
+  // every element of delta the kernels read is written by the preprocess first: nothing to clear
+  return attn_bwd(q, k, v, o, o_lo, lse, dout, dq, dk, dv, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens, n_docs,
+                  delta, &cap, stream);
 }
 
 // ---- UPipe headwise-chunked forward ------------------------------------------------
