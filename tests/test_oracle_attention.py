@@ -215,3 +215,34 @@ def test_planted_gqa_map_is_caught(monkeypatch):
     assert not np.allclose(o, ob)
     o_ok, _ = attention.forward(q, k, v, 0.5)
     assert np.allclose(o_ok, ob, rtol=1e-12)
+
+
+@pytest.mark.parametrize("P,Hq,Hkv", [(4, 8, 2), (8, 8, 1), (4, 8, 4)])
+def test_replicated_then_sharded_equals_unsharded(P, Hq, Hkv):
+    """Kv heads fewer than the ranks (replicated: each kv head goes to the P / Hkv ranks whose q
+    heads read it), the exchange as send-side permute + all-to-all + receive-side permute: every
+    rank's local attention, with the gradients of a replicated kv head summed over its ranks on
+    the way back, equals attention on the unsharded tensors (float64)."""
+    from oracle import permute
+    rng = np.random.default_rng(P + Hq + Hkv)
+    s_l, d = 5, 4
+    s = P * s_l
+    glob = {n: rng.standard_normal((s, H, d)) for n, H in (("q", Hq), ("k", Hkv), ("v", Hkv), ("do", Hq))}
+    shards = {n: [g[p * s_l:(p + 1) * s_l] for p in range(P)] for n, g in glob.items()}
+    exch = lambda bufs: [np.stack([bufs[p][r] for p in range(P)]) for r in range(P)]
+    recv = {n: exch([permute.send_pack(x, P) for x in shards[n]]) for n in shards}
+    heads = lambda n, r: recv[n][r].reshape(s, recv[n][r].shape[2], d)
+    o_h, dq_h, dk_h, dv_h = [], [], [], []
+    for r in range(P):
+        q, k, v, do = (heads(n, r) for n in ("q", "k", "v", "do"))
+        o_h.append(attention.forward(q, k, v, 0.5, True)[0])
+        dq, dk, dv = attention.backward(q, k, v, do, 0.5, True)
+        dq_h.append(dq), dk_h.append(dk), dv_h.append(dv)
+    back = lambda outs, H: np.concatenate([permute.recv_unpack(b, P, H)
+                                           for b in exch([x.reshape(P, s_l, x.shape[1], d) for x in outs])])
+    wo, _ = attention.forward(glob["q"], glob["k"], glob["v"], 0.5, True)
+    wq, wk, wv = attention.backward(glob["q"], glob["k"], glob["v"], glob["do"], 0.5, True)
+    np.testing.assert_allclose(back(o_h, Hq), wo, atol=1e-12)
+    np.testing.assert_allclose(back(dq_h, Hq), wq, atol=1e-12)
+    np.testing.assert_allclose(back(dk_h, Hkv), wk, atol=1e-12)
+    np.testing.assert_allclose(back(dv_h, Hkv), wv, atol=1e-12)
