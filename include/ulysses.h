@@ -13,6 +13,8 @@
  *      for the head shard, forward and backward                    -> attn_fwd, attn_bwd
  *   3. the local half of the second all-to-all: the head shard goes back to the
  *      sequence shards                                             -> ulysses_unpack
+ *      (the send-side and receive-side permutes of a real all-to-all, with kv heads
+ *      replicated when there are fewer than ranks -> ulysses_send_pack, ulysses_recv_unpack)
  *   4. the UPipe schedule: 1-3 run a few heads at a time so that the attention
  *      intermediates stay small                    -> attn_fwd_chunked, attn_bwd_chunked
  *   5. 1-3 with the exchange folded into the attention's own loads and stores: the
@@ -116,6 +118,31 @@ int ulysses_pack_group(int n, const void* const* const* shards, const int* H, vo
                        int rank, int64_t s_l, int d, int dtype, void* stream);
 int ulysses_unpack_group(int n, const void* const* in, const int* H, void* const* const* shards, int P,
                          int rank, int64_t s_l, int d, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ulysses_send_pack / ulysses_recv_unpack -- the local permutes of one rank as a real
+ * all-to-all needs them ("how Ulysses works", steps 1, 3 and 5): send_pack turns the rank's
+ * sequence shard into P contiguous per-destination blocks, and recv_unpack turns the P blocks
+ * a rank received back into its sequence shard. The collective between them moves block r of
+ * rank p's send buffer to block p of rank r's receive buffer; on one GPU the ranks' buffers
+ * are separate allocations and that move is the caller's. send_pack of every rank, the
+ * exchange, and the receiving rank's buffer read as [P*s_l, H_l, d] give exactly
+ * ulysses_pack's head shard.
+ *   H heads over P ranks, H % P == 0 or P % H == 0 (ULY_ERR_SHAPE otherwise). Rank r receives
+ *   H_l = H/P heads from r*H/P, or, when H < P, the one head r / (P/H): a head fewer than the
+ *   ranks (the kv heads of a GQA model at large SP; the comparison table on the first page
+ *   asks num_heads >= sp_size) is replicated to P/H ranks.
+ *   send_pack   : shard [s_l, H, d] -> out [P, s_l, H_l, d]; out[r, t, j] = shard[t, first(r)+j]
+ *   recv_unpack : in [P, s_l, H_l, d] -> shard [s_l, H, d]; shard[t, h] = in[r, t, h - first(r)]
+ *                 for the rank r holding h (the bits unchanged), or, for a replicated head,
+ *                 the sum over its P/H holders in rank order, in fp32 from +0, rounded once
+ *                 to nearest even (the gradient of a head read by several ranks).
+ *   d * element size must be a multiple of 16 (ULY_ERR_ALIGN); base pointers 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+int ulysses_send_pack(const void* shard, int P, int64_t s_l, int H, int d, int dtype, void* out,
+                      void* stream);
+int ulysses_recv_unpack(const void* in, int P, int64_t s_l, int H, int d, int dtype, void* shard,
+                        void* stream);
 
 /* ---------------------------------------------------------------------------
  * attn_fwd -- attention forward of one head shard. Pages: "how Ulysses works" step 4

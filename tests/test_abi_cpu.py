@@ -273,3 +273,20 @@ def test_bwd_noalloc_rejects_on_the_host():
     assert L.attn_bwd_noalloc(None, *z[1:], 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None) == 1
     assert L.attn_bwd_noalloc(*z[:4], MIS, *z[5:], 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None) == 4
 
+
+@pytest.mark.parametrize("P,s_l,H,d,dt,want", [
+    (0, 4, 4, 64, 0, 2), (65, 4, 4, 64, 0, 2), (4, 0, 4, 64, 0, 2), (4, 4, 3, 64, 0, 2), (3, 4, 2, 64, 0, 2),
+    (4, 4, 4, 64, 7, 3), (4, 4, 2, 4, 0, 4),
+])
+def test_send_recv_reject_on_the_host(P, s_l, H, d, dt, want):
+    L = U.lib()
+    assert L.ulysses_send_pack(FAKE, P, s_l, H, d, dt, FAKE, None) == want
+    assert L.ulysses_recv_unpack(FAKE, P, s_l, H, d, dt, FAKE, None) == want
+
+
+def test_send_recv_null_and_alignment():
+    L = U.lib()
+    assert L.ulysses_send_pack(None, 4, 4, 8, 64, 0, FAKE, None) == 1
+    assert L.ulysses_recv_unpack(FAKE, 4, 4, 8, 64, 0, None, None) == 1
+    assert L.ulysses_send_pack(MIS, 4, 4, 8, 64, 0, FAKE, None) == 4
+    assert L.ulysses_recv_unpack(FAKE, 4, 4, 2, 64, 0, MIS, None) == 4

@@ -7,6 +7,8 @@ library is missing, every call raises: there is no fallback path.
 The names follow the C ABI in include/ulysses.h:
   ulysses_pack, ulysses_unpack        -- local halves of the two all-to-alls
   ulysses_pack_group, ulysses_unpack_group -- the same for up to three tensors in one launch
+  ulysses_send_pack, ulysses_recv_unpack -- one rank's send-side / receive-side permutes of a
+                                        real all-to-all (kv heads replicated when fewer than ranks)
   attn_fwd, attn_bwd                  -- attention of one head shard
   attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq -- the phases of attn_bwd
   attn_fwd_chunked                    -- the UPipe headwise-chunked forward
@@ -47,6 +49,8 @@ SIGNATURES = {
     "uly_abi_version": (_i32, []),
     "ulysses_pack": (_i32, [_vpp, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp]),
     "ulysses_unpack": (_i32, [_vp, _i32, _i32, _i64, _i32, _i32, _i32, _vpp, _vp]),
+    "ulysses_send_pack": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp]),
+    "ulysses_recv_unpack": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp]),
     "ulysses_pack_group": (_i32, [_i32, _vpp, _i32p, _vpp, _i32, _i32, _i64, _i32, _i32, _vp]),
     "ulysses_unpack_group": (_i32, [_i32, _vpp, _i32p, _vpp, _i32, _i32, _i64, _i32, _i32, _vp]),
     "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp]),
@@ -198,6 +202,35 @@ def ulysses_unpack(y, rank, shards):
     pp, _keep = _ptrs(shards)
     _call("ulysses_unpack", _dev(y), P, rank, s_l, H, d, _dtype(y), pp, _stream())
     return shards
+
+
+def rank_heads(r, P, H):
+    """(first head, count) rank r receives of H heads over P ranks (replicated when H < P)."""
+    return (r * H // P, H // P) if H % P == 0 else (r // (P // H), 1)
+
+
+def ulysses_send_pack(shard, P, out=None):
+    """One rank's sequence shard [s_l, H, d] -> its all-to-all send buffer [P, s_l, H_l, d]."""
+    s_l, H, d = shard.shape
+    nh = rank_heads(0, P, H)[1]
+    if out is None:
+        out = torch.empty((P, s_l, nh, d), dtype=shard.dtype, device=shard.device)
+    _need(out, "out", (P, s_l, nh, d), shard.dtype, shard.device)
+    _call("ulysses_send_pack", _dev(shard), P, s_l, H, d, _dtype(shard), _dev(out), _stream())
+    return out
+
+
+def ulysses_recv_unpack(buf, H, shard=None):
+    """One rank's all-to-all receive buffer [P, s_l, H_l, d] -> its sequence shard [s_l, H, d]
+    (replicated heads summed over their ranks)."""
+    P, s_l, nh, d = buf.shape
+    if shard is None:
+        shard = torch.empty((s_l, H, d), dtype=buf.dtype, device=buf.device)
+    _need(shard, "shard", (s_l, H, d), buf.dtype, buf.device)
+    if H % P == 0 or P % H == 0:
+        _shape(buf, "buf", (P, s_l, rank_heads(0, P, H)[1], d), buf.dtype)
+    _call("ulysses_recv_unpack", _dev(buf), P, s_l, H, d, _dtype(buf), _dev(shard), _stream())
+    return shard
 
 
 def _group_args(tensor_lists):

@@ -187,6 +187,32 @@ int ulysses_unpack(const void* in, int P, int rank, int64_t s_l, int H, int d, i
                                   rank * run, run, as_stream(stream)));
 }
 
+// Checks shared by the send-side and receive-side permutes of one rank.
+static int check_send_recv(const void* a, const void* b, int P, int64_t s_l, int H, int d, int dtype) {
+  if (!a || !b) return ULY_ERR_NULL;
+  if (P < 1 || P > ULY_MAX_RANKS || s_l < 1 || H < 1 || d < 1) return ULY_ERR_SHAPE;
+  if (H % P != 0 && P % H != 0) return ULY_ERR_SHAPE;
+  if (dtype != ULY_BF16 && dtype != ULY_F32) return ULY_ERR_UNSUPPORTED;
+  if (((int64_t)d * esize(dtype)) % 16 != 0) return ULY_ERR_ALIGN;
+  if (!aligned16(a) || !aligned16(b)) return ULY_ERR_ALIGN;
+  const uint64_t units = (uint64_t)s_l * (uint64_t)std::max(H, P) * (uint64_t)(d * esize(dtype) / 16);
+  if (units >= (1ull << 32)) return ULY_ERR_SHAPE;
+  return ULY_OK;
+}
+
+int ulysses_send_pack(const void* shard, int P, int64_t s_l, int H, int d, int dtype, void* out, void* stream) {
+  const int st = check_send_recv(shard, out, P, s_l, H, d, dtype);
+  if (st != ULY_OK) return st;
+  return hip_status(launch_send_pack(shard, out, P, s_l, H, (int64_t)d * esize(dtype), as_stream(stream)));
+}
+
+int ulysses_recv_unpack(const void* in, int P, int64_t s_l, int H, int d, int dtype, void* shard, void* stream) {
+  const int st = check_send_recv(in, shard, P, s_l, H, d, dtype);
+  if (st != ULY_OK) return st;
+  return hip_status(launch_recv_unpack(in, shard, P, s_l, H, (int64_t)d * esize(dtype), dtype == ULY_BF16 ? 1 : 0,
+                                       as_stream(stream)));
+}
+
 // Checks shared by the grouped permutes: every tensor as ulysses_pack / ulysses_unpack
 // would check it; fills the launch segments.
 static int group_segments(int n, const void* const* const* shards, const int* H, void* const* flat, int P,

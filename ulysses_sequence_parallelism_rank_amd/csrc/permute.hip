@@ -76,6 +76,82 @@ __global__ __launch_bounds__(kPermThreads) void unpack_kernel(PermGroupK g) {
     unpack_unit(g.seg[0], g.s_l, b * kPermThreads + threadIdx.x);
 }
 
+// ---------------------------------------------------------------------------------------
+// The exchange as a real all-to-all performs it (pages: "how Ulysses works", steps 1, 3 and 5;
+// the comparison table's num_heads >= sp_size): every source rank permutes its sequence shard
+// into P contiguous per-destination blocks, the collective swaps blocks, and every destination
+// rank permutes what it received back into its sequence shard. With fewer heads than ranks
+// (P a multiple of H) each head goes to the R = P / H ranks r with r / R == head, and on the way
+// back the R copies of a head's gradient are summed in fp32 in rank order (from +0, so the sign
+// of a zero sum is +), then rounded once.
+struct SendK {
+  const u32x4* shard;  // [s_l, H, d]
+  u32x4* out;          // [P, s_l, H_l, d]
+  uint32_t s_l, run, row_in, head_units, total, per_rank_heads, rep;
+};
+// out[(r*s_l + t)*run + w] = shard[t*row_in + first(r)*head_units + w]
+__global__ __launch_bounds__(kPermThreads) void send_pack_kernel(SendK g) {
+  const uint32_t c = blockIdx.x * kPermThreads + threadIdx.x;
+  if (c >= g.total) return;
+  const uint32_t row = c / g.run, w = c - row * g.run;
+  const uint32_t r = row / g.s_l, t = row - r * g.s_l;
+  const uint32_t first = g.rep > 1 ? r / g.rep : r * g.per_rank_heads;
+  __builtin_nontemporal_store(
+      __builtin_nontemporal_load(g.shard + (size_t)t * g.row_in + (size_t)first * g.head_units + w), g.out + c);
+}
+
+struct RecvK {
+  const u32x4* in;  // [P, s_l, H_l, d]
+  u32x4* shard;     // [s_l, H, d]
+  uint32_t s_l, run, row_out, head_units, total, per_rank_heads, rep;
+  int bf16;
+};
+// shard[t*row_out + h*head_units + w] = sum over the holders r of head h of
+// in[(r*s_l + t)*run + (h - first(r))*head_units + w]
+__global__ __launch_bounds__(kPermThreads) void recv_unpack_kernel(RecvK g) {
+  const uint32_t c = blockIdx.x * kPermThreads + threadIdx.x;
+  if (c >= g.total) return;
+  const uint32_t t = c / g.row_out, rem = c - t * g.row_out;
+  const uint32_t h = rem / g.head_units, w = rem - h * g.head_units;
+  if (g.rep <= 1) {  // one holder: the bits move unchanged
+    const uint32_t r = h / g.per_rank_heads, j = h - r * g.per_rank_heads;
+    __builtin_nontemporal_store(
+        __builtin_nontemporal_load(g.in + ((size_t)r * g.s_l + t) * g.run + (size_t)j * g.head_units + w),
+        g.shard + c);
+    return;
+  }
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (uint32_t k = 0; k < g.rep; ++k) {
+    const uint32_t r = h * g.rep + k;
+    const u32x4 x = __builtin_nontemporal_load(g.in + ((size_t)r * g.s_l + t) * g.run + w);
+    if (g.bf16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t xi = x[i];
+        acc[2 * i] += bf16_lo(xi);
+        acc[2 * i + 1] += bf16_hi(xi);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t xi = x[i];
+        acc[i] += __builtin_bit_cast(float, xi);
+      }
+    }
+  }
+  u32x4 o;
+  if (g.bf16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __builtin_bit_cast(uint32_t, acc[i]);
+  }
+  __builtin_nontemporal_store(o, g.shard + c);
+}
+
 namespace {
 
 // Sizes are in bytes; the caller has checked alignment, that every size is a multiple of 16,
@@ -113,6 +189,47 @@ hipError_t launch_pack_group(const PermSeg* segs, int n, int64_t s_l, hipStream_
 
 hipError_t launch_unpack_group(const PermSeg* segs, int n, int64_t s_l, hipStream_t stream) {
   return launch_group(false, segs, n, s_l, stream);
+}
+
+// Sizes in bytes, checked by the caller: P % H == 0 or H % P == 0, head_bytes a multiple of 16,
+// the 16-byte unit counts within 32 bits.
+hipError_t launch_send_pack(const void* shard, void* out, int P, int64_t s_l, int H, int64_t head_bytes,
+                            hipStream_t stream) {
+  SendK g{};
+  const int rep = H < P ? P / H : 1, nh = H < P ? 1 : H / P;
+  g.shard = static_cast<const u32x4*>(shard);
+  g.out = static_cast<u32x4*>(out);
+  g.s_l = (uint32_t)s_l;
+  g.head_units = (uint32_t)(head_bytes / 16);
+  g.run = (uint32_t)(nh * g.head_units);
+  g.row_in = (uint32_t)(H * g.head_units);
+  g.total = (uint32_t)((uint64_t)P * s_l * g.run);
+  g.per_rank_heads = (uint32_t)nh;
+  g.rep = (uint32_t)rep;
+  const uint32_t blocks = (g.total + kPermThreads - 1) / kPermThreads;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(send_pack_kernel, dim3(blocks), dim3(kPermThreads), 0, stream, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_recv_unpack(const void* in, void* shard, int P, int64_t s_l, int H, int64_t head_bytes, int bf16,
+                              hipStream_t stream) {
+  RecvK g{};
+  const int rep = H < P ? P / H : 1, nh = H < P ? 1 : H / P;
+  g.in = static_cast<const u32x4*>(in);
+  g.shard = static_cast<u32x4*>(shard);
+  g.s_l = (uint32_t)s_l;
+  g.head_units = (uint32_t)(head_bytes / 16);
+  g.run = (uint32_t)(nh * g.head_units);
+  g.row_out = (uint32_t)(H * g.head_units);
+  g.total = (uint32_t)((uint64_t)s_l * g.row_out);
+  g.per_rank_heads = (uint32_t)nh;
+  g.rep = (uint32_t)rep;
+  g.bf16 = bf16;
+  const uint32_t blocks = (g.total + kPermThreads - 1) / kPermThreads;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(recv_unpack_kernel, dim3(blocks), dim3(kPermThreads), 0, stream, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(const ShardPtrs& src, void* out, int P, int64_t s_l, int64_t row_bytes,

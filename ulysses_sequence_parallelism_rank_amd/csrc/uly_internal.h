@@ -69,6 +69,11 @@ constexpr int kPermGroupMax = ULY_PERM_GROUP_MAX;
 // n tensors (1 <= n <= kPermGroupMax) packed / unpacked by one launch
 hipError_t launch_pack_group(const PermSeg* segs, int n, int64_t s_l, hipStream_t stream);
 hipError_t launch_unpack_group(const PermSeg* segs, int n, int64_t s_l, hipStream_t stream);
+// send-side / receive-side permutes of one rank (head_bytes = d * element size, a multiple of 16)
+hipError_t launch_send_pack(const void* shard, void* out, int P, int64_t s_l, int H, int64_t head_bytes,
+                            hipStream_t stream);
+hipError_t launch_recv_unpack(const void* in, void* shard, int P, int64_t s_l, int H, int64_t head_bytes, int bf16,
+                              hipStream_t stream);
 hipError_t launch_pack(const ShardPtrs& src, void* out, int P, int64_t s_l, int64_t row_bytes,
                        int64_t off_bytes, int64_t run_bytes, hipStream_t stream);
 hipError_t launch_unpack(const void* in, const ShardPtrs& dst, int P, int64_t s_l, int64_t row_bytes,
