@@ -29,6 +29,9 @@ namespace uly {
 namespace {
 
 constexpr int kWaves = 4;
+// dQ kernel: LDS operand read-ahead of the S/dP products (k-steps) and the dQ products (products):
+// left alone, the compiler reads each operand just before its MFMA (2% of the kernel at 64K)
+constexpr int kDqPfA = 2, kDqPfB = 3;
 
 // ---------------------------------------------------------------------------------------
 // delta[h, i] = sum_x dO[i, h, x] * O[i, h, x] (fp32). TPR threads per (row, head), 16 B each.
@@ -216,12 +219,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
       // raised priority through S/dP and dS: the other wave on the SIMD fills the gaps with
       // its dQ products
       __builtin_amdgcn_s_setprio(1);
+      {
+        // K and V operands kDqPfA k-steps ahead of their products, behind scheduling barriers
+        bf16x8 rk[kDqPfA + 1], rv[kDqPfA + 1];
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        bf16x8 kx, vx;
-        load_sdp(buf, hh, t, kx, vx);
-        sacc = mfma32x32x16(kx, qf[0][t], t == 0 ? f32x16{} : sacc);
-        pacc = mfma32x32x16(vx, gf[0][t], t == 0 ? f32x16{} : pacc);
+        for (int t = 0; t < kDqPfA; ++t) load_sdp(buf, hh, t, rk[t], rv[t]);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          if (t + kDqPfA < DT) load_sdp(buf, hh, t + kDqPfA, rk[(t + kDqPfA) % (kDqPfA + 1)], rv[(t + kDqPfA) % (kDqPfA + 1)]);
+          sacc = mfma32x32x16(rk[t % (kDqPfA + 1)], qf[0][t], t == 0 ? f32x16{} : sacc);
+          pacc = mfma32x32x16(rv[t % (kDqPfA + 1)], gf[0][t], t == 0 ? f32x16{} : pacc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       f32x4 dv[4];
       bf16x8 dsf[2];
@@ -241,11 +250,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
       dsf[0] = pack8(dv[0], dv[1]);
       dsf[1] = pack8(dv[2], dv[3]);
       __builtin_amdgcn_s_setprio(0);
+      {
+        // K^T operands kDqPfB products ahead
+        bf16x8 rk[kDqPfB + 1], unused;
 #pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        bf16x8 kt, unused;
-        load_dq(buf, hh, i, kt, unused);
-        dqacc[i % DB] = mfma32x32x16(kt, dsf[i / DB], dqacc[i % DB]);
+        for (int i = 0; i < kDqPfB; ++i) load_dq(buf, hh, i, rk[i], unused);
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          if (i + kDqPfB < NC) load_dq(buf, hh, i + kDqPfB, rk[(i + kDqPfB) % (kDqPfB + 1)], unused);
+          dqacc[i % DB] = mfma32x32x16(rk[i % (kDqPfB + 1)], dsf[i / DB], dqacc[i % DB]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     // the next tile's DMA after this tile's last LDS read: the wait the compiler places

@@ -41,6 +41,8 @@ namespace uly {
 namespace {
 
 constexpr float kTau = 8.0f;
+// LDS operand read-ahead of the S^T and O^T products (k-steps / products ahead)
+constexpr int kPfS = 3, kPfV = 2;
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc src) {
@@ -114,11 +116,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
     dma_tile<D, BN, 256>(K, a.kv_row, r0, src.s_l, sK[b], tid);
     dma_tile<D, BN, 256>(V, a.kv_row, r0, src.s_l, sV[b], tid);
   };
+  // S^T of one half: the K operand of k-step t is read kPfS steps ahead (a ring of kPfS + 1
+  // registers), each product behind a scheduling barrier; left alone, the compiler reads
+  // each operand just before its MFMA and waits for it (4% of the kernel at 64K)
   auto qk = [&](int b, int hh, f32x16& S) {
+    bf16x8 ring[kPfS + 1];
+    auto ld = [&](int t) {
+      return *reinterpret_cast<const bf16x8*>(&sK[b][tile_off<D>(hh * 32 + l32, 16 * t + 8 * hf)]);
+    };
+#pragma unroll
+    for (int t = 0; t < kPfS; ++t) ring[t] = ld(t);
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[b][tile_off<D>(hh * 32 + l32, 16 * t + 8 * hf)]);
-      S = mfma32x32x16(kf, qf[t], t == 0 ? f32x16{} : S);
+      if (t + kPfS < DT) ring[(t + kPfS) % (kPfS + 1)] = ld(t + kPfS);
+      S = mfma32x32x16(ring[t % (kPfS + 1)], qf[t], t == 0 ? f32x16{} : S);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // the 32 keys from k0 need no mask for any row of this wave (one unsigned range compare)
@@ -175,18 +187,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
       }
     }
   };
+  // O^T += V^T P^T for one half: product i = (tt, db); its V^T operand (two transposing
+  // reads) is read kPfV products ahead, as the K operands are
   auto pv = [&](int b, int hh, const bf16x8 (&pf)[2]) {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    constexpr int NPV = 2 * DB;
+    auto ld = [&](int i) {
+      const int tt = i / DB, db = i % DB;
       const int kr = hh * 32 + 16 * tt + 4 * hf + (li >> 2);
+      const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
+      const i16x4 v0 = lds_read_tr16(&sV[b][tile_off<D>(kr, col)]);
+      const i16x4 v1 = lds_read_tr16(&sV[b][tile_off<D>(kr + 8, col)]);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 ring[kPfV + 1];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
-        const i16x4 v0 = lds_read_tr16(&sV[b][tile_off<D>(kr, col)]);
-        const i16x4 v1 = lds_read_tr16(&sV[b][tile_off<D>(kr + 8, col)]);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = mfma32x32x16(vf, pf[tt], oacc[db]);
-      }
+    for (int i = 0; i < kPfV; ++i) ring[i] = ld(i);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      if (i + kPfV < NPV) ring[(i + kPfV) % (kPfV + 1)] = ld(i + kPfV);
+      oacc[i % DB] = mfma32x32x16(ring[i % (kPfV + 1)], pf[i / DB], oacc[i % DB]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
