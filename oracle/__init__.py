@@ -9,8 +9,9 @@ Parts:
   attention -- plain masked softmax attention forward and backward in float64
   brute     -- scalar-loop attention and finite differences for tiny inputs
   chunked   -- the headwise-chunked (UPipe) forward as a loop over head chunks
+  ring      -- Ring Attention over P ranks: per-hop partial attention and an LSE merge
 
 Every function is pinned by tests under tests/ (test_oracle_*.py) against
 brute force, closed forms, invariants and library routines.
 """
-from . import permute, attention, brute, chunked  # noqa: F401
+from . import permute, attention, brute, chunked, ring  # noqa: F401
