@@ -19,6 +19,7 @@
  *      intermediates stay small                    -> attn_fwd_chunked, attn_bwd_chunked
  *   5. 1-3 with the exchange folded into the attention's own loads and stores: the
  *      kernels read the sequence shards directly      -> attn_fwd_shards, attn_bwd_shards
+ *   6. the pages' comparison workload, Ring Attention   -> ring_attn_fwd, ring_attn_bwd
  * The P ranks are P separate device buffers on one GPU; no collective runs here.
  * uly_mfma_probe is a measurement helper outside the path.
  *
@@ -327,6 +328,45 @@ int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards,
 
 size_t attn_bwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int d,
                                         int dtype, int heads_per_chunk);
+
+/* ---------------------------------------------------------------------------
+ * ring_attn_fwd / ring_attn_bwd -- Ring Attention, the pages' comparison workload
+ * ("Ulysses Sequence Parallelism: Training with Million-Token Contexts", sections on
+ * communication complexity and on Ulysses compared with Ring Attention): every rank keeps its
+ * token block of Q, K and V with all heads, and the K/V blocks travel round a ring of P ranks;
+ * at hop i rank r attends to the block of rank (r - i) mod P and the partial outputs are merged
+ * by their log-sum-exps, which gives attention over the whole sequence. On one GPU the ring's
+ * point-to-point sends are reads of the other ranks' buffers. causal: the rank's own block is
+ * causal inside, earlier blocks fully visible, later blocks skipped. bf16 only.
+ *   q_shards, k_shards, v_shards : host arrays of P device pointers [s_l, Hq | Hkv, d]
+ *   Hq, Hkv : all the heads (no head sharding), Hq % Hkv == 0
+ * ring_attn_fwd: o [s_l, Hq, d] (rank's block of O), o_lo (NULL or its residual, as for
+ *   attn_fwd), lse [Hq, s_l]. Each hop runs the attention forward on the pair of blocks, writing
+ *   the partial O with its residual, and a merge folds it into an fp32 running output in
+ *   ring order. workspace: ring_attn_fwd_workspace_bytes(s_l, Hq, d) (partial O, residual,
+ *   LSE, fp32 running output and LSE); NULL -> size query into *workspace_bytes.
+ * ring_attn_bwd: rank r's backward given its merged o (+ o_lo), lse and dout: writes dq
+ *   [s_l, Hq, d] (summed over its hops in fp32, rounded once), and adds its contribution to
+ *   the fp32 dK/dV sums of every block it attended to. dk_acc, dv_acc: device fp32
+ *   [P, s_l, Hkv, d], the sums that travel with the K/V blocks in a real ring; the rank that
+ *   attends first to a block (causal: its owner; else rank 0) starts them, and rank P - 1
+ *   rounds them into that block's dk_shards / dv_shards [s_l, Hkv, d]. So the P ranks' calls
+ *   must run in rank order on one stream. workspace: ring_attn_bwd_workspace_bytes(s_l, Hq, d)
+ *   (delta and the fp32 dQ sums).
+ * Deterministic (fixed hop and rank order, no atomics).
+ * ------------------------------------------------------------------------- */
+size_t ring_attn_fwd_workspace_bytes(int64_t s_l, int Hq, int d);
+size_t ring_attn_bwd_workspace_bytes(int64_t s_l, int Hq, int d);
+int ring_attn_fwd(const void* const* q_shards, const void* const* k_shards,
+                  const void* const* v_shards, void* o, void* o_lo, float* lse, int P, int rank,
+                  int64_t s_l, int Hq, int Hkv, int d, int dtype, float scale, int causal,
+                  void* workspace, size_t* workspace_bytes, void* stream);
+int ring_attn_bwd(const void* const* q_shards, const void* const* k_shards,
+                  const void* const* v_shards, const void* o, const void* o_lo, const float* lse,
+                  const void* dout, void* dq, float* dk_acc, float* dv_acc, void* const* dk_shards,
+                  void* const* dv_shards, int P, int rank, int64_t s_l, int Hq, int Hkv, int d,
+                  int dtype, float scale, int causal, void* workspace, size_t* workspace_bytes,
+                  void* stream);
 
 /* ---------------------------------------------------------------------------
  * uly_mfma_probe -- measurement helper, not part of the attention path: `blocks`

@@ -290,3 +290,30 @@ def test_send_recv_null_and_alignment():
     assert L.ulysses_recv_unpack(FAKE, 4, 4, 8, 64, 0, None, None) == 1
     assert L.ulysses_send_pack(MIS, 4, 4, 8, 64, 0, FAKE, None) == 4
     assert L.ulysses_recv_unpack(FAKE, 4, 4, 2, 64, 0, MIS, None) == 4
+
+
+def test_ring_rejects_on_the_host():
+    L = U.lib()
+    pp, keep = _ptr_array([FAKE] * 4)
+    need = ctypes.c_size_t(0)
+
+    def fwd(P=4, rank=1, s_l=64, Hq=8, Hkv=2, d=128, dt=0, ws=None, cap=None, o=FAKE, q=pp):
+        return L.ring_attn_fwd(q, pp, pp, o, None, FAKE, P, rank, s_l, Hq, Hkv, d, dt, 0.1, 1, ws, cap, None)
+    assert fwd(cap=ctypes.byref(need)) == 0 and need.value == L.ring_attn_fwd_workspace_bytes(64, 8, 128)
+    assert fwd(rank=4, cap=ctypes.byref(need)) == 2
+    assert fwd(Hkv=3, cap=ctypes.byref(need)) == 2
+    assert fwd(dt=1, d=64, cap=ctypes.byref(need)) == 3
+    small = ctypes.c_size_t(need.value - 1)
+    assert fwd(ws=FAKE, cap=ctypes.byref(small)) == 5
+    assert fwd(ws=FAKE, cap=ctypes.byref(need), o=None) == 1
+    mp, keep2 = _ptr_array([FAKE, FAKE, MIS, FAKE])
+    assert fwd(q=mp, cap=ctypes.byref(need)) == 4
+
+    def bwd(ws=FAKE, cap=None, acc=FAKE, rank=3):
+        return L.ring_attn_bwd(pp, pp, pp, FAKE, None, FAKE, FAKE, FAKE, acc, FAKE, pp, pp, 4, rank, 64, 8, 2, 128, 0,
+                               0.1, 1, ws, cap, None)
+    nb = ctypes.c_size_t(0)
+    assert bwd(ws=None, cap=ctypes.byref(nb)) == 0 and nb.value == L.ring_attn_bwd_workspace_bytes(64, 8, 128)
+    assert bwd(cap=ctypes.byref(nb), acc=None) == 1
+    assert bwd(cap=ctypes.byref(nb), acc=MIS) == 4
+    assert bwd(cap=ctypes.byref(nb), rank=-1) == 2

@@ -14,6 +14,7 @@ The names follow the C ABI in include/ulysses.h:
   attn_fwd_chunked                    -- the UPipe headwise-chunked forward
   attn_bwd_chunked                    -- its backward
   attn_fwd_shards, attn_bwd_shards    -- forward / backward reading and writing the sequence shards
+  ring_attn_fwd, ring_attn_bwd        -- Ring Attention over the P ranks (the comparison workload)
 
 Every tensor's shape, dtype and device are checked here before the C call (the C side
 checks sizes and alignment but cannot see a tensor's extent). `o_lo` arguments take the
@@ -74,6 +75,12 @@ SIGNATURES = {
                                _i32, _vp, _i32, _vp]),
     "attn_bwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vp, _vpp, _vpp, _vpp, _vpp, _i32, _i32, _i64, _i32,
                                _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _szp, _vp]),
+    "ring_attn_fwd_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "ring_attn_bwd_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "ring_attn_fwd": (_i32, [_vpp, _vpp, _vpp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
+                             _vp, _szp, _vp]),
+    "ring_attn_bwd": (_i32, [_vpp, _vpp, _vpp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vpp, _vpp, _i32, _i32, _i64, _i32,
+                             _i32, _i32, _i32, _f32, _i32, _vp, _szp, _vp]),
     "uly_mfma_probe": (_i32, [_i32, _i32, _vp, _vp, _vp]),
 }
 
@@ -526,6 +533,53 @@ def attn_bwd_shards(q_shards, k_shards, v_shards, o_shards, lse, do_shards, dq_s
           _dtype(q0), _default_scale(d, scale), int(causal), cu, nd, _dev(workspace), ctypes.byref(cap),
           _stream())
     return dq_shards, dk_shards, dv_shards
+
+
+def ring_attn_fwd(q_shards, k_shards, v_shards, rank, scale=None, causal=True, out=None, lse=None, o_lo=None,
+                  workspace=None):
+    """Ring Attention forward of rank `rank` (its token block of every head): returns (o, lse),
+    o [s_l, Hq, d], lse [Hq, s_l]; o_lo (bf16 [s_l, Hq, d]) receives O's residual when given."""
+    P, s_l, Hq, Hkv, d, q0 = _shard_sets(q_shards, k_shards, v_shards)
+    o = torch.empty_like(q0) if out is None else out
+    if lse is None:
+        lse = torch.empty((Hq, s_l), dtype=torch.float32, device=q0.device)
+    _need(o, "out", (s_l, Hq, d), q0.dtype, q0.device)
+    _need(lse, "lse", (Hq, s_l), torch.float32, q0.device)
+    lo = _opt(o_lo, "o_lo", (s_l, Hq, d), torch.bfloat16, q0.device)
+    need = int(lib().ring_attn_fwd_workspace_bytes(s_l, Hq, d))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q0.device)
+    cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    keep = [_ptrs(x) for x in (q_shards, k_shards, v_shards)]
+    qp, kp, vp = (k[0] for k in keep)
+    _call("ring_attn_fwd", qp, kp, vp, _dev(o), lo, _dev(lse), P, rank, s_l, Hq, Hkv, d, _dtype(q0),
+          _default_scale(d, scale), int(causal), _dev(workspace), ctypes.byref(cap), _stream())
+    return o, lse
+
+
+def ring_attn_bwd(q_shards, k_shards, v_shards, o, lse, dout, rank, dk_acc, dv_acc, dk_shards, dv_shards,
+                  scale=None, causal=True, dq=None, o_lo=None, workspace=None):
+    """Ring Attention backward of rank `rank`: returns its dq [s_l, Hq, d] and adds its share to
+    the fp32 dK/dV sums dk_acc, dv_acc [P, s_l, Hkv, d]; the call of rank P - 1 rounds them into
+    dk_shards / dv_shards. Ranks must be called in order on one stream."""
+    P, s_l, Hq, Hkv, d, q0 = _shard_sets(q_shards, k_shards, v_shards, more_kv=(dk_shards, dv_shards))
+    dq = torch.empty_like(q0) if dq is None else dq
+    for t, n in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        _need(t, n, (s_l, Hq, d), q0.dtype, q0.device)
+    _need(lse, "lse", (Hq, s_l), torch.float32, q0.device)
+    for t, n in ((dk_acc, "dk_acc"), (dv_acc, "dv_acc")):
+        _need(t, n, (P, s_l, Hkv, d), torch.float32, q0.device)
+    lo = _opt(o_lo, "o_lo", (s_l, Hq, d), torch.bfloat16, q0.device)
+    need = int(lib().ring_attn_bwd_workspace_bytes(s_l, Hq, d))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q0.device)
+    cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    keep = [_ptrs(x) for x in (q_shards, k_shards, v_shards, dk_shards, dv_shards)]
+    qp, kp, vp, dkp, dvp = (k[0] for k in keep)
+    _call("ring_attn_bwd", qp, kp, vp, _dev(o), lo, _dev(lse), _dev(dout), _dev(dq), _dev(dk_acc), _dev(dv_acc),
+          dkp, dvp, P, rank, s_l, Hq, Hkv, d, _dtype(q0), _default_scale(d, scale), int(causal), _dev(workspace),
+          ctypes.byref(cap), _stream())
+    return dq
 
 
 def mfma_probe(iters=20000, blocks=512):

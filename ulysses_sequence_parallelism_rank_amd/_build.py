@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libulysses.so")
-SOURCES = ["permute.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_f32.hip", "probe.hip", "abi.cpp"]
+SOURCES = ["permute.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_f32.hip", "ring.hip", "probe.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 

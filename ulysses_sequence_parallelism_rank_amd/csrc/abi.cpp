@@ -78,6 +78,8 @@ AttnArgs make_args(int64_t s, int Hq, int Hkv, int d, float scale, int causal, c
   a.causal = causal ? 1 : 0;
   a.cu = cu;
   a.n_docs = cu ? n_docs : 0;
+  a.acc_init = -1;
+  a.acc_final = -1;
   return a;
 }
 
@@ -617,6 +619,166 @@ int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards, co
   if ((err = launch_bwd_preprocess_bf16_shards(pre, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
   if ((err = launch_attn_dkdv_bf16_shards(a, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
   if ((err = launch_attn_dq_bf16_shards(a, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
+  return ULY_OK;
+}
+
+// ---- Ring Attention (the pages' comparison workload) -----------------------------------
+// Hop i of rank r attends to the K/V block of rank (r - i) mod P; causal: the own block is
+// causal inside, earlier blocks are fully visible, later ones are skipped.
+
+namespace {
+int ring_hops(int P, int rank, int causal, int* srcs) {
+  int n = 0;
+  for (int i = 0; i < P; ++i) {
+    const int src = ((rank - i) % P + P) % P;
+    if (causal && src > rank) continue;
+    srcs[n++] = src;
+  }
+  return n;
+}
+
+struct RingFwdLayout {
+  size_t part, part_lo, part_lse, acc, acc_lse, total;
+};
+RingFwdLayout ring_fwd_layout(int64_t s_l, int Hq, int d) {
+  RingFwdLayout L;
+  const size_t n = (size_t)s_l * (size_t)Hq * (size_t)d;
+  L.part = round256(n * 2);
+  L.part_lo = round256(n * 2);
+  L.part_lse = round256((size_t)s_l * Hq * sizeof(float));
+  L.acc = round256(n * sizeof(float));
+  L.acc_lse = round256((size_t)s_l * Hq * sizeof(float));
+  L.total = L.part + L.part_lo + L.part_lse + L.acc + L.acc_lse;
+  return L;
+}
+
+// checks shared by the ring calls: P shards of Q, K, V (all heads), bf16
+int check_ring(const void* const* qs, const void* const* ks, const void* const* vs, int P, int rank, int64_t s_l,
+               int Hq, int Hkv, int d, int dtype) {
+  if (!qs || !ks || !vs) return ULY_ERR_NULL;
+  if (P < 1 || P > ULY_MAX_RANKS || rank < 0 || rank >= P || s_l < 1) return ULY_ERR_SHAPE;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ULY_ERR_SHAPE;
+  if (s_l > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
+  int st = check_dtype_dim(dtype, d);
+  if (st != ULY_OK) return st;
+  if (dtype != ULY_BF16) return ULY_ERR_UNSUPPORTED;
+  for (int p = 0; p < P; ++p) {
+    if (!qs[p] || !ks[p] || !vs[p]) return ULY_ERR_NULL;
+    if (!aligned16(qs[p]) || !aligned16(ks[p]) || !aligned16(vs[p])) return ULY_ERR_ALIGN;
+  }
+  return ULY_OK;
+}
+}  // namespace
+
+size_t ring_attn_fwd_workspace_bytes(int64_t s_l, int Hq, int d) {
+  if (s_l < 1 || Hq < 1 || d < 1) return 0;
+  return ring_fwd_layout(s_l, Hq, d).total;
+}
+
+int ring_attn_fwd(const void* const* q_shards, const void* const* k_shards, const void* const* v_shards, void* o,
+                  void* o_lo, float* lse, int P, int rank, int64_t s_l, int Hq, int Hkv, int d, int dtype, float scale,
+                  int causal, void* workspace, size_t* workspace_bytes, void* stream) {
+  int st = check_ring(q_shards, k_shards, v_shards, P, rank, s_l, Hq, Hkv, d, dtype);
+  if (st != ULY_OK) return st;
+  const RingFwdLayout L = ring_fwd_layout(s_l, Hq, d);
+  if (workspace == nullptr) {
+    if (!workspace_bytes) return ULY_ERR_NULL;
+    *workspace_bytes = L.total;
+    return ULY_OK;
+  }
+  if (workspace_bytes && *workspace_bytes < L.total) return ULY_ERR_WORKSPACE;
+  if (!o || !lse) return ULY_ERR_NULL;
+  if (!aligned16(o) || !aligned16(lse) || !aligned16(workspace)) return ULY_ERR_ALIGN;
+  if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  void* part = ws;
+  void* part_lo = ws + L.part;
+  float* part_lse = reinterpret_cast<float*>(ws + L.part + L.part_lo);
+  float* acc = reinterpret_cast<float*>(ws + L.part + L.part_lo + L.part_lse);
+  float* acc_lse = reinterpret_cast<float*>(ws + L.part + L.part_lo + L.part_lse + L.acc);
+  int srcs[ULY_MAX_RANKS];
+  const int n = ring_hops(P, rank, causal, srcs);
+  hipStream_t strm = as_stream(stream);
+  for (int i = 0; i < n; ++i) {
+    const int src = srcs[i];
+    AttnArgs a = make_args(s_l, Hq, Hkv, d, scale, causal && src == rank, nullptr, 0);
+    a.q = q_shards[rank];
+    a.k = k_shards[src];
+    a.v = v_shards[src];
+    a.out = part;
+    a.o_lo = part_lo;
+    a.lo_row = (int64_t)Hq * d;
+    a.lse_out = part_lse;
+    if ((st = fwd_dispatch(a, d, dtype, strm)) != ULY_OK) return st;
+    const hipError_t e = launch_ring_merge(part, part_lo, part_lse, acc, acc_lse, o, o_lo, lse, s_l, Hq, d, i == 0,
+                                           i == n - 1, strm);
+    if (e != hipSuccess) return ULY_ERR_HIP;
+  }
+  return ULY_OK;
+}
+
+size_t ring_attn_bwd_workspace_bytes(int64_t s_l, int Hq, int d) {
+  if (s_l < 1 || Hq < 1 || d < 1) return 0;
+  return round256((size_t)s_l * Hq * sizeof(float)) + round256((size_t)s_l * Hq * d * sizeof(float));
+}
+
+int ring_attn_bwd(const void* const* q_shards, const void* const* k_shards, const void* const* v_shards,
+                  const void* o, const void* o_lo, const float* lse, const void* dout, void* dq, float* dk_acc,
+                  float* dv_acc, void* const* dk_shards, void* const* dv_shards, int P, int rank, int64_t s_l, int Hq,
+                  int Hkv, int d, int dtype, float scale, int causal, void* workspace, size_t* workspace_bytes,
+                  void* stream) {
+  int st = check_ring(q_shards, k_shards, v_shards, P, rank, s_l, Hq, Hkv, d, dtype);
+  if (st != ULY_OK) return st;
+  const size_t need = ring_attn_bwd_workspace_bytes(s_l, Hq, d);
+  if (workspace == nullptr) {
+    if (!workspace_bytes) return ULY_ERR_NULL;
+    *workspace_bytes = need;
+    return ULY_OK;
+  }
+  if (workspace_bytes && *workspace_bytes < need) return ULY_ERR_WORKSPACE;
+  if (!o || !lse || !dout || !dq || !dk_acc || !dv_acc || !dk_shards || !dv_shards) return ULY_ERR_NULL;
+  if (!aligned16(o) || !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk_acc) ||
+      !aligned16(dv_acc) || !aligned16(workspace))
+    return ULY_ERR_ALIGN;
+  if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
+  for (int p = 0; p < P; ++p) {
+    if (!dk_shards[p] || !dv_shards[p]) return ULY_ERR_NULL;
+    if (!aligned16(dk_shards[p]) || !aligned16(dv_shards[p])) return ULY_ERR_ALIGN;
+  }
+  float* delta = static_cast<float*>(workspace);
+  float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)s_l * Hq * sizeof(float)));
+  hipStream_t strm = as_stream(stream);
+  if ((st = attn_bwd_preprocess(o, o_lo, dout, delta, s_l, Hq, d, dtype, stream)) != ULY_OK) return st;
+  int srcs[ULY_MAX_RANKS];
+  const int n = ring_hops(P, rank, causal, srcs);
+  const size_t blk = (size_t)s_l * Hkv * d;  // fp32 elements of one block's dK (dV) sums
+  for (int i = 0; i < n; ++i) {
+    const int src = srcs[i];
+    AttnArgs a = make_args(s_l, Hq, Hkv, d, scale, causal && src == rank, nullptr, 0);
+    a.q = q_shards[rank];
+    a.k = k_shards[src];
+    a.v = v_shards[src];
+    a.dout = dout;
+    a.lse_in = lse;
+    a.delta = delta;
+    // block src's dK/dV sums travel with its K/V: the first rank to attend to it starts them,
+    // the last rank of the ring rounds them into the block's gradient shards
+    AttnArgs kv = a;
+    kv.acc_k = dk_acc + (size_t)src * blk;
+    kv.acc_v = dv_acc + (size_t)src * blk;
+    kv.acc_init = rank == (causal ? src : 0) ? 1 : 0;
+    kv.acc_final = rank == P - 1 ? 1 : 0;
+    kv.out_k = dk_shards[src];
+    kv.out_v = dv_shards[src];
+    if (launch_attn_dkdv_bf16(kv, d, strm) != hipSuccess) return ULY_ERR_HIP;
+    // this rank's dQ: summed over its hops
+    AttnArgs qa = a;
+    qa.out = dq;
+    qa.acc_q = dq_acc;
+    qa.acc_init = i == 0 ? 1 : 0;
+    qa.acc_final = i == n - 1 ? 1 : 0;
+    if (launch_attn_dq_bf16(qa, d, strm) != hipSuccess) return ULY_ERR_HIP;
+  }
   return ULY_OK;
 }
 

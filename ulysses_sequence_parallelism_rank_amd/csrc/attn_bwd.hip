@@ -270,6 +270,30 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
 
   const int rb = 0;
   uint16_t* dQ = static_cast<uint16_t*>(const_cast<void*>(dq_sh.p[ps])) + (int64_t)h * D - r_sh * a.q_row;
+  if (a.acc_q != nullptr && row[rb] < s) {
+    // sums carried across launches (Ring Attention's hops): add the previous fp32 sums unless
+    // this launch starts them, store them back unless it ends them
+    float* accp = a.acc_q + row[rb] * a.q_row + (int64_t)h * D;
+    if (a.acc_init == 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 prev = *reinterpret_cast<const f32x4*>(accp + db * 32 + 8 * jj + 4 * hf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dqacc[db][4 * jj + e] += prev[e];
+        }
+    }
+    if (a.acc_final == 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<f32x4*>(accp + db * 32 + 8 * jj + 4 * hf) =
+              f32x4{dqacc[db][4 * jj + 0], dqacc[db][4 * jj + 1], dqacc[db][4 * jj + 2], dqacc[db][4 * jj + 3]};
+      return;
+    }
+  }
   if (row[rb] < s) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -553,7 +577,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
     const float f = is_k ? a.scale : 1.0f;
     // headwise-chunked backward: fp32 sums carried across launches, rounded once at the end
     float* accp = a.acc_k == nullptr ? nullptr : (is_k ? a.acc_k : a.acc_v) + off;
-    if (accp != nullptr && !kh.first) {
+    const bool acc_first = a.acc_init >= 0 ? a.acc_init != 0 : kh.first;
+    const bool acc_last = a.acc_final >= 0 ? a.acc_final != 0 : kh.last;
+    if (accp != nullptr && !acc_first) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -563,7 +589,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
           for (int e = 0; e < 4; ++e) acc[db][4 * jj + e] += prev[e];
         }
     }
-    if (accp != nullptr && !kh.last) {
+    if (accp != nullptr && !acc_last) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -55,6 +55,12 @@ struct AttnArgs {
   int causal;
   const int32_t* cu;
   int n_docs;
+  // accumulation across launches, when acc_k / acc_v (dK/dV) or acc_q (dQ, [s, n_heads, D] fp32
+  // with row stride q_row) are set: acc_init / acc_final say whether this launch starts the sums
+  // (does not read them) and ends them (rounds into the output instead of storing fp32); -1 in
+  // the dK/dV kernel means "from the launch's q heads" (the headwise-chunked rule above)
+  float* acc_q;
+  int acc_init, acc_final;
 };
 
 // One tensor of a grouped permute: its P shards (P of them used), the head-shard buffer, the
@@ -115,6 +121,11 @@ hipError_t launch_bwd_preprocess_bf16_shards(const AttnArgs& a, const BwdSrc& sr
 hipError_t launch_attn_dkdv_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream);
 hipError_t launch_attn_dq_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t stream);
+// Ring Attention: merge one hop's partial (O bf16 + residual, LSE) into the fp32 running output;
+// the last hop writes O (bf16), its residual (if out_lo) and the LSE
+hipError_t launch_ring_merge(const void* part, const void* part_lo, const float* part_lse, float* acc, float* acc_lse,
+                             void* out, void* out_lo, float* out_lse, int64_t s_l, int H, int d, int first, int last,
+                             hipStream_t stream);
 hipError_t launch_mfma_probe(int iters, int blocks, float* sink, unsigned long long* clocks, hipStream_t stream);
 hipError_t launch_attn_dkdv_f32(const AttnArgs& a, int d, hipStream_t stream);
 hipError_t launch_attn_dq_f32(const AttnArgs& a, int d, hipStream_t stream);
