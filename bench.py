@@ -488,11 +488,18 @@ def main():
             "how": "each permute of the step alone after a 512 MiB cache-evicting write, 7 runs, medians",
             "phases": {k: {m: round(x, 4) for m, x in v.items()} for k, v in cold.items()}}
     if chunked:
-        # peak intermediate bytes: the chunked calls' workspaces against the unchunked head shards
-        # (forward: Q, O, K, V; training adds dO, dQ, dK, dV and delta)
+        # peak intermediate bytes: the chunked calls' workspaces (the chunks read the shards, so
+        # the forward needs none and the backward delta and fp32 dK/dV sums), and the buffers a
+        # multi-GPU all-to-all would have to deliver -- staged per chunk (Q/O of u heads, K/V of
+        # their kv heads) against unchunked (every local head): the UPipe accounting
         out["workspace_bytes"] = ws_bytes
+        u = min(args.heads_per_chunk, Hq_l)
+        span = max((min(c0 + u, Hq_l) - 1) // cfg.G - c0 // cfg.G + 1 for c0 in range(0, Hq_l, u))
+        staged = 2 * cfg.s * u * d * e + 2 * cfg.s * span * d * e
         fwd_b = 2 * cfg.s * Hq_l * d * e + 2 * cfg.s * Hkv_l * d * e
+        out["staged_chunk_bytes"] = int(staged)
         out["unchunked_intermediate_bytes"] = int(fwd_b if args.forward_only else 2 * fwd_b + 4 * cfg.s * Hq_l)
+        out["staged_reduction_q_shaped"] = round(1 - u / Hq_l, 4)
     ceil = measured_ceilings()
     out["measured_ceilings"] = ceil
     roof["frac_of_measured"] = round(roof["achieved"] / (ceil["mfma_bf16_tflops"] if bound == "mfma"

@@ -232,9 +232,13 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
  *   k_shards / v_shards : host arrays of P device pointers [s_l, Hkv, d]
  *   o_lo : device bf16 [s, Hq/P, d] or NULL: O's rounding residual of this rank's heads
  *   lse : device fp32 [Hq/P, s], written for this rank's heads
- *   workspace : at least attn_fwd_chunked_workspace_bytes(...) bytes; NULL -> size query
- *               into *workspace_bytes as for attn_bwd. This is the peak intermediate
- *               memory of the schedule.
+ *   workspace : at least attn_fwd_chunked_workspace_bytes(...) bytes; NULL with a non-NULL
+ *               workspace_bytes -> size query as for attn_bwd. This is the peak intermediate
+ *               memory of the schedule. For bf16 with s_l a multiple of 128 the chunks read
+ *               the shards and write the o shards directly (the shard-reading kernels of
+ *               attn_fwd_shards with head sub-ranges), so the size is 0 and the call runs
+ *               with workspace == NULL and workspace_bytes == NULL; otherwise each chunk's
+ *               Q/O and its kv heads' K/V are packed into the workspace.
  * ------------------------------------------------------------------------- */
 int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards,
                      const void* const* v_shards, void* const* o_shards, void* o_lo, float* lse,
@@ -313,9 +317,11 @@ int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards,
  *   lse : device fp32 [Hq/P, s] of this rank's heads
  *   dq / dk / dv shards: only this rank's head slices are written.
  *   workspace : at least attn_bwd_chunked_workspace_bytes(...) bytes; NULL -> size query
- *               into *workspace_bytes as for attn_bwd: the chunk buffers (Q, O, dO, dQ
- *               of u heads, K and V of the kv heads they read, delta) plus fp32 dK/dV
- *               sums and the rank's dK/dV.
+ *               into *workspace_bytes as for attn_bwd. For bf16 with s_l a multiple of 128
+ *               the chunks read and write the shards directly and the workspace is delta of
+ *               a chunk and the fp32 dK/dV sums of the rank's kv heads; otherwise it also
+ *               holds the chunk buffers (Q, O, dO, dQ of u heads, K and V of the kv heads
+ *               they read) and the rank's dK/dV.
  * Errors as for attn_fwd_chunked.
  * ------------------------------------------------------------------------- */
 int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards,

@@ -155,11 +155,20 @@ def test_bwd_workspace_query_and_checks():
 def test_chunked_workspace_matches_upipe_accounting():
     L = U.lib()
     MiB = 2 ** 20
-    # 262144 tokens, 64 q / 8 kv heads, P = 8, d = 128, bf16
-    assert L.attn_fwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 1) == 256 * MiB
-    assert L.attn_fwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 2) == 384 * MiB
-    assert L.attn_fwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 8) == 1152 * MiB
+    # 262144 tokens, 64 q / 8 kv heads, P = 8, d = 128, bf16: the chunks read the shards directly
+    for u in (1, 2, 8):
+        assert L.attn_fwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, u) == 0
     assert L.attn_fwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 0) == 0
+    # shards whose length is not a multiple of 128 stage each chunk: Q and O of u heads plus K and
+    # V of the kv heads they read, [s, ., d] bf16 each (the UPipe accounting: 87.5% less than the
+    # 8 q heads' Q and O at u = 1)
+    s_l = 32760
+    s = 8 * s_l
+    r256 = lambda b: (b + 255) // 256 * 256
+    for u, span in ((1, 1), (2, 1), (8, 1)):
+        want = 2 * r256(s * u * 128 * 2) + 2 * r256(s * span * 128 * 2)
+        assert L.attn_fwd_chunked_workspace_bytes(8, s_l, 64, 8, 128, 0, u) == want
+    assert L.attn_fwd_chunked_workspace_bytes(8, s_l, 64, 8, 128, 0, 1) < 257 * MiB
 
 
 def test_chunked_rejects():
@@ -191,8 +200,14 @@ def test_binding_refuses_cpu_tensors():
 def test_bwd_chunked_workspace_and_rejects():
     L = U.lib()
     MiB = 2 ** 20
-    # the 256K UPipe share: chunk buffers, delta, fp32 dK/dV sums and the rank's dK/dV
-    assert L.attn_bwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 1) == 769 * MiB
+    # the 256K UPipe share read from the shards: delta of a one-head chunk (1 MiB) and the fp32
+    # dK/dV sums of the rank's kv head (2 x 128 MiB)
+    assert L.attn_bwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 1) == 257 * MiB
+    # staged chunks (shards not a multiple of 128): also Q, O, dO, dQ of the chunk, K/V and dK/dV
+    s = 8 * 32760
+    r256 = lambda b: (b + 255) // 256 * 256
+    staged = 4 * r256(s * 256) + 2 * r256(s * 256) + r256(s * 4) + 2 * r256(s * 512) + 2 * r256(s * 256)
+    assert L.attn_bwd_chunked_workspace_bytes(8, 32760, 64, 8, 128, 0, 1) == staged
     assert L.attn_bwd_chunked_workspace_bytes(8, 32768, 64, 8, 128, 0, 0) == 0
     pp, keep = _ptr_array([FAKE] * 2)
     need = ctypes.c_size_t(0)

@@ -50,6 +50,11 @@ SMALL = [
     (4, 300, 24, 8, 9, 0, None),        # u beyond H_q/P is clamped to one chunk
     (2, 257, 8, 2, 3, 1, [0, 1, 40, 300, 514]),
     (8, 64, 64, 8, 2, 5, None),         # the UPipe head counts (8 q / 1 kv per rank) at small s
+    # shards a multiple of 128 long: the chunks read the shards directly (no workspace)
+    (4, 256, 24, 8, 1, 0, None),
+    (4, 128, 24, 8, 4, 3, None),        # ragged last chunk
+    (2, 384, 8, 2, 3, 1, [0, 1, 40, 300, 768]),
+    (8, 128, 64, 8, 2, 5, None),
 ]
 
 
@@ -82,7 +87,8 @@ def test_chunked_small(P, s_l, Hq, Hkv, u, rank, cu):
 
 
 def test_chunked_workspace_matches_query():
-    """A workspace one byte short is rejected before any launch; the exact size works."""
+    """A workspace one byte short is rejected before any launch; the exact size works (shards
+    of 64 tokens: chunks staged in the workspace)."""
     cfg = W.Config("chunk_ws", P=4, s_l=64, Hq=16, Hkv=4, d=128, dtype="bf16")
     dev = {n: [to_dev(b, "bf16") for b in W.shards_of(W.gen_global(cfg, n, seed=2), cfg.P)]
            for n in ("q", "k", "v")}
@@ -128,7 +134,7 @@ def _upipe_inputs():
 def test_chunked_full_upipe_share():
     """The 256K UPipe share (8 ranks x 32768 tokens, 64 q / 8 kv heads, rank 0) at u = 1
     and u = 2: bitwise equal to the unchunked path, sampled rows of two heads against
-    the oracle, and the workspace (peak intermediate bytes) as the analysis predicts."""
+    the oracle, and no intermediate memory beyond the LSE (the chunks read the shards)."""
     X = _upipe_inputs()
     cfg, rank, dev, f = X["cfg"], X["rank"], X["dev"], X["f"]
     P, s_l, Hl = cfg.P, cfg.s_l, cfg.Hq_l
@@ -138,7 +144,7 @@ def test_chunked_full_upipe_share():
     print("unchunked done", flush=True)
     for u in (1, 2):
         need = U.attn_fwd_chunked_workspace_bytes(P, s_l, cfg.Hq, cfg.Hkv, cfg.d, torch.bfloat16, u)
-        assert need == {1: 256, 2: 384}[u] * 2 ** 20
+        assert need == 0
         o_sh = _sentinel_like(dev["q"])
         keep = [t.clone() for t in o_sh]
         torch.cuda.synchronize()
@@ -202,6 +208,12 @@ SMALL_BWD = [
     (2, 200, 8, 2, 64, "bf16", 3, 0, [0, 150, 151, 400]),
     (2, 200, 8, 2, 64, "f32", 3, 1, None),
     (2, 130, 8, 2, 64, "f32", 1, 0, [0, 70, 260]),
+    # read straight from the shards (bf16, s_l a multiple of 128)
+    (4, 256, 24, 8, 128, "bf16", 1, 0, None),      # every kv head summed over three chunks
+    (4, 128, 24, 8, 128, "bf16", 2, 3, None),      # chunks straddle the groups
+    (4, 256, 24, 8, 128, "bf16", 3, 2, None),      # whole groups: bitwise equal dK/dV
+    (2, 384, 8, 2, 64, "bf16", 3, 0, [0, 150, 151, 768]),
+    (8, 128, 64, 8, 128, "bf16", 2, 5, None),
 ]
 
 

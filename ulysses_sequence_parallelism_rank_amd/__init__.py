@@ -456,17 +456,20 @@ def attn_fwd_chunked(q_shards, k_shards, v_shards, o_shards, rank, heads_per_chu
     _need(lse, "lse", (Hq // P, s), torch.float32, q0.device)
     lo = _opt(o_lo, "o_lo", (s, Hq // P, d), torch.bfloat16, q0.device)
     need = attn_fwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, _dtype(q0), heads_per_chunk)
-    if workspace is None:
+    if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q0.device)
-    cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    if workspace is None or workspace.numel() == 0:   # none needed: NULL workspace and size
+        ws_ptr, cap_ref = None, None
+    else:
+        cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+        ws_ptr, cap_ref = _dev(workspace), ctypes.byref(cap)
     qp, k1 = _ptrs(q_shards)
     kp, k2 = _ptrs(k_shards)
     vp, k3 = _ptrs(v_shards)
     op, k4 = _ptrs(o_shards)
     cu, nd = _cu(cu_seqlens, q0.device)
     _call("attn_fwd_chunked", qp, kp, vp, op, lo, _dev(lse), P, rank, s_l, Hq, Hkv, d, _dtype(q0),
-          _default_scale(d, scale), int(causal), cu, nd, heads_per_chunk, _dev(workspace), ctypes.byref(cap),
-          _stream())
+          _default_scale(d, scale), int(causal), cu, nd, heads_per_chunk, ws_ptr, cap_ref, _stream())
     return lse
 
 

@@ -68,6 +68,7 @@ AttnArgs make_args(int64_t s, int Hq, int Hkv, int d, float scale, int causal, c
   a.q_row = (int64_t)Hq * d;
   a.kv_row = (int64_t)Hkv * d;
   a.dkv_row = (int64_t)Hkv * d;
+  a.acc_row = (int64_t)Hkv * d;
   a.lse_row = s;
   a.n_heads = Hq;
   a.n_kv = Hkv;
@@ -112,6 +113,11 @@ namespace {
 struct BwdChunkLayout {
   size_t qc, kv, delta, acc, out, total;
 };
+// the shard-reading chunked backward: delta of a chunk and the fp32 dK/dV sums of the rank's kv heads
+size_t bwd_shard_chunk_bytes(int P, int64_t s_l, int Hq, int Hkv, int d, int u) {
+  const size_t s = (size_t)P * (size_t)s_l;
+  return round256((size_t)u * s * sizeof(float)) + 2 * round256(s * (size_t)(Hkv / P) * (size_t)d * sizeof(float));
+}
 BwdChunkLayout bwd_chunk_layout(int P, int64_t s_l, int Hq, int Hkv, int d, int dtype, int u) {
   const int Hq_l = Hq / P, Hkv_l = Hkv / P, G = Hq / Hkv;
   const size_t s = (size_t)P * (size_t)s_l, e = (size_t)esize(dtype);
@@ -412,10 +418,15 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
 
 // ---- UPipe headwise-chunked forward ------------------------------------------------
 
+// The chunked schedules read the sequence shards directly (no chunk buffers) when the
+// shard-reading kernels apply: bf16 and every workgroup's rows inside one shard.
+static bool chunks_read_shards(int dtype, int64_t s_l) { return dtype == ULY_BF16 && s_l % 128 == 0; }
+
 size_t attn_fwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int d, int dtype,
                                         int heads_per_chunk) {
   if (P < 1 || s_l < 1 || Hq < 1 || Hkv < 1 || d < 1 || heads_per_chunk < 1) return 0;
   if (Hq % P != 0 || Hkv % P != 0 || Hq % Hkv != 0) return 0;
+  if (chunks_read_shards(dtype, s_l)) return 0;
   const int Hq_l = Hq / P, G = Hq / Hkv;
   const int u = std::min(heads_per_chunk, Hq_l);
   const size_t s = (size_t)P * (size_t)s_l, e = (size_t)esize(dtype);
@@ -439,14 +450,14 @@ int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards, c
   if (s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
   if (cu_seqlens != nullptr && n_docs < 1) return ULY_ERR_SHAPE;
   const size_t need = attn_fwd_chunked_workspace_bytes(P, s_l, Hq, Hkv, d, dtype, heads_per_chunk);
-  if (workspace == nullptr) {
-    if (!workspace_bytes) return ULY_ERR_NULL;
+  if (workspace == nullptr && workspace_bytes != nullptr) {  // size query
     *workspace_bytes = need;
     return ULY_OK;
   }
+  if (workspace == nullptr && need > 0) return ULY_ERR_NULL;  // both NULL: runs only when none is needed
   if (workspace_bytes && *workspace_bytes < need) return ULY_ERR_WORKSPACE;
   if (!lse) return ULY_ERR_NULL;
-  if (!aligned16(lse) || !aligned16(workspace)) return ULY_ERR_ALIGN;
+  if (!aligned16(lse) || (workspace != nullptr && !aligned16(workspace))) return ULY_ERR_ALIGN;
   if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
   for (int p = 0; p < P; ++p) {
     if (!q_shards[p] || !k_shards[p] || !v_shards[p] || !o_shards[p]) return ULY_ERR_NULL;
@@ -459,6 +470,35 @@ int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards, c
   const int64_t qrow = (int64_t)Hq * d * e, kvrow = (int64_t)Hkv * d * e, hb = (int64_t)d * e;
   if (!chunks_fit(P, s_l, qrow, qrow) || !chunks_fit(P, s_l, kvrow, kvrow)) return ULY_ERR_SHAPE;
 
+  hipStream_t strm = as_stream(stream);
+  if (chunks_read_shards(dtype, s_l)) {
+    // each chunk's heads straight from the shards into the o shards: no buffers at all
+    for (int c0 = 0; c0 < Hq_l; c0 += u) {
+      const int c1 = std::min(c0 + u, Hq_l), nq = c1 - c0;
+      const int g0 = c0 / G, g1 = (c1 - 1) / G + 1;
+      ShardSrc src{};
+      for (int p = 0; p < P; ++p) {
+        src.q[p] = static_cast<const uint16_t*>(q_shards[p]) + ((int64_t)rank * Hq_l + c0) * d;
+        src.k[p] = static_cast<const uint16_t*>(k_shards[p]) + ((int64_t)rank * Hkv_l + g0) * d;
+        src.v[p] = static_cast<const uint16_t*>(v_shards[p]) + ((int64_t)rank * Hkv_l + g0) * d;
+        src.o[p] = static_cast<uint16_t*>(o_shards[p]) + ((int64_t)rank * Hq_l + c0) * d;
+      }
+      src.s_l = s_l;
+      AttnArgs a = make_args(s, nq, 1, d, scale, causal, cu_seqlens, n_docs);
+      a.q_row = (int64_t)Hq * d;  // rows of the sequence shards hold every head
+      a.kv_row = (int64_t)Hkv * d;
+      a.n_heads = nq;
+      a.n_kv = g1 - g0;
+      a.G = G;
+      a.q_off = c0;
+      a.kv_off = g0;
+      a.o_lo = o_lo == nullptr ? nullptr : static_cast<char*>(o_lo) + c0 * hb;
+      a.lo_row = (int64_t)Hq_l * d;
+      a.lse_out = lse + (int64_t)c0 * s;
+      if (launch_attn_fwd_bf16_shards(a, src, d, strm) != hipSuccess) return ULY_ERR_HIP;
+    }
+    return ULY_OK;
+  }
   const int span = max_kv_span(Hq_l, G, u);
   char* ws = static_cast<char*>(workspace);
   const size_t qo = round256((size_t)s * u * d * e);
@@ -468,7 +508,6 @@ int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards, c
   void* vc = ws + 2 * qo + round256((size_t)s * span * d * e);
   const ShardPtrs qs = shard_ptrs(q_shards, P), ks = shard_ptrs(k_shards, P), vs = shard_ptrs(v_shards, P);
   const ShardPtrs os = shard_ptrs(const_cast<const void* const*>(o_shards), P);
-  hipStream_t strm = as_stream(stream);
 
   int kv_lo = -1, kv_hi = -1;  // local kv heads currently packed in kc / vc
   for (int c0 = 0; c0 < Hq_l; c0 += u) {
@@ -787,6 +826,7 @@ size_t attn_bwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int
   if (P < 1 || s_l < 1 || Hq < 1 || Hkv < 1 || d < 1 || heads_per_chunk < 1) return 0;
   if (Hq % P != 0 || Hkv % P != 0 || Hq % Hkv != 0) return 0;
   const int u = std::min(heads_per_chunk, Hq / P);
+  if (chunks_read_shards(dtype, s_l)) return bwd_shard_chunk_bytes(P, s_l, Hq, Hkv, d, u);
   return bwd_chunk_layout(P, s_l, Hq, Hkv, d, dtype, u).total;
 }
 
@@ -831,6 +871,56 @@ int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards, c
   const int64_t qrow = (int64_t)Hq * d * e, kvrow = (int64_t)Hkv * d * e, hb = (int64_t)d * e;
   if (!chunks_fit(P, s_l, qrow, qrow) || !chunks_fit(P, s_l, kvrow, kvrow)) return ULY_ERR_SHAPE;
 
+  hipStream_t strm = as_stream(stream);
+  hipError_t err;
+  if (chunks_read_shards(dtype, s_l)) {
+    // each chunk's heads read from the shards and dQ written into them; dK/dV of a kv head summed
+    // in fp32 across the chunks that read it and rounded, by its last one, straight into the shards
+    char* ws = static_cast<char*>(workspace);
+    float* delta = reinterpret_cast<float*>(ws);
+    float* acc_k = reinterpret_cast<float*>(ws + round256((size_t)u * s * sizeof(float)));
+    float* acc_v = acc_k + round256(s * (size_t)Hkv_l * d * sizeof(float)) / sizeof(float);
+    for (int c0 = 0; c0 < Hq_l; c0 += u) {
+      const int c1 = std::min(c0 + u, Hq_l), nq = c1 - c0;
+      const int g0 = c0 / G, g1 = (c1 - 1) / G + 1;
+      BwdSrc src{};
+      const int64_t qo = ((int64_t)rank * Hq_l + c0) * d, kvo = ((int64_t)rank * Hkv_l + g0) * d;
+      for (int p = 0; p < P; ++p) {
+        src.q.p[p] = static_cast<const uint16_t*>(q_shards[p]) + qo;
+        src.o.p[p] = static_cast<const uint16_t*>(o_shards[p]) + qo;
+        src.g.p[p] = static_cast<const uint16_t*>(do_shards[p]) + qo;
+        src.dq.p[p] = static_cast<const uint16_t*>(dq_shards[p]) + qo;
+        src.k.p[p] = static_cast<const uint16_t*>(k_shards[p]) + kvo;
+        src.v.p[p] = static_cast<const uint16_t*>(v_shards[p]) + kvo;
+        src.dk.p[p] = static_cast<const uint16_t*>(dk_shards[p]) + kvo;
+        src.dv.p[p] = static_cast<const uint16_t*>(dv_shards[p]) + kvo;
+      }
+      src.s_l = s_l;
+      AttnArgs a = make_args(s, nq, 1, d, scale, causal, cu_seqlens, n_docs);
+      a.q_row = (int64_t)Hq * d;
+      a.kv_row = (int64_t)Hkv * d;
+      a.dkv_row = (int64_t)Hkv * d;
+      a.n_heads = nq;
+      a.n_kv = g1 - g0;
+      a.G = G;
+      a.q_off = c0;
+      a.kv_off = g0;
+      a.lse_in = lse + (int64_t)c0 * s;
+      a.delta = delta;
+      AttnArgs pre = a;
+      pre.lse_out = delta;
+      pre.o_lo = o_lo == nullptr ? nullptr : const_cast<char*>(static_cast<const char*>(o_lo)) + c0 * hb;
+      pre.lo_row = (int64_t)Hq_l * d;
+      if ((err = launch_bwd_preprocess_bf16_shards(pre, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
+      AttnArgs kv = a;
+      kv.acc_k = acc_k + (int64_t)g0 * d;
+      kv.acc_v = acc_v + (int64_t)g0 * d;
+      kv.acc_row = (int64_t)Hkv_l * d;
+      if ((err = launch_attn_dkdv_bf16_shards(kv, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
+      if ((err = launch_attn_dq_bf16_shards(a, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
+    }
+    return ULY_OK;
+  }
   const BwdChunkLayout L = bwd_chunk_layout(P, s_l, Hq, Hkv, d, dtype, u);
   char* ws = static_cast<char*>(workspace);
   void* qc = ws;
@@ -849,8 +939,6 @@ int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards, c
   const ShardPtrs dqs = shard_ptrs(const_cast<const void* const*>(dq_shards), P);
   const ShardPtrs dks = shard_ptrs(const_cast<const void* const*>(dk_shards), P);
   const ShardPtrs dvs = shard_ptrs(const_cast<const void* const*>(dv_shards), P);
-  hipStream_t strm = as_stream(stream);
-  hipError_t err;
 
   int kv_lo = -1, kv_hi = -1;  // local kv heads currently packed in kc / vc
   for (int c0 = 0; c0 < Hq_l; c0 += u) {
@@ -892,6 +980,7 @@ int attn_bwd_chunked(const void* const* q_shards, const void* const* k_shards, c
     // dK/dV of kv heads [g0, g1): fp32 sums carried across chunks, rounded on the last one
     AttnArgs kvargs = a;
     kvargs.dkv_row = (int64_t)Hkv_l * d;
+    kvargs.acc_row = (int64_t)Hkv_l * d;
     kvargs.acc_k = acc_k + (int64_t)g0 * d;
     kvargs.acc_v = acc_v + (int64_t)g0 * d;
     kvargs.out_k = dk_r + (int64_t)g0 * hb;

@@ -576,7 +576,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
     const int64_t off = (int64_t)kvh * D + key * a.dkv_row;
     const float f = is_k ? a.scale : 1.0f;
     // headwise-chunked backward: fp32 sums carried across launches, rounded once at the end
-    float* accp = a.acc_k == nullptr ? nullptr : (is_k ? a.acc_k : a.acc_v) + off;
+    float* accp = a.acc_k == nullptr ? nullptr
+                                     : (is_k ? a.acc_k : a.acc_v) + (int64_t)kvh * D + key * a.acc_row;
     const bool acc_first = a.acc_init >= 0 ? a.acc_init != 0 : kh.first;
     const bool acc_last = a.acc_final >= 0 ? a.acc_final != 0 : kh.last;
     if (accp != nullptr && !acc_first) {

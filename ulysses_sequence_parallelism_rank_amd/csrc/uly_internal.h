@@ -22,7 +22,7 @@ struct ShardPtrs {
 // lse / delta rows are [n_heads][s] with row stride lse_row.
 // dK/dV accumulation across launches (headwise-chunked backward): when acc_k is set, the
 // dK/dV kernel adds its sums to the fp32 arrays acc_k / acc_v ([s, kv_heads, D], row stride
-// dkv_row) unless the launch holds the first q head of the kv head's group, and writes the
+// acc_row) unless the launch holds the first q head of the kv head's group, and writes the
 // rounded result to dk / dv only when it holds the last one (otherwise it stores the fp32
 // sum back).
 struct AttnArgs {
@@ -38,6 +38,7 @@ struct AttnArgs {
   void* out_v;    // dv
   float* acc_k;   // fp32 dK accumulator (chunked backward) or null
   float* acc_v;   // fp32 dV accumulator
+  int64_t acc_row;
   int64_t dkv_row;
   float* lse_out; // forward LSE / preprocess delta
   // O's bf16 rounding residual ([s, n_heads, D] bf16 at the launch's head 0, row stride lo_row):
@@ -115,8 +116,7 @@ struct BwdSrc {
   int64_t s_l;
 };
 // the three bf16 backward phases reading / writing through shard tables (a.q, a.k, a.v, a.o,
-// a.dout, a.out, a.out_k, a.out_v are ignored); the accumulation mode of AttnArgs is not
-// supported here
+// a.dout, a.out, a.out_k, a.out_v are ignored)
 hipError_t launch_bwd_preprocess_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream);
 hipError_t launch_attn_dkdv_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream);
 hipError_t launch_attn_dq_bf16_shards(const AttnArgs& a, const BwdSrc& src, int d, hipStream_t stream);
