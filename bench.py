@@ -168,8 +168,11 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
     lse = torch.empty((Hq_l, s), dtype=torch.float32, device=dev)
     do = torch.empty_like(q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(U.attn_bwd_workspace_bytes(s, Hq_l), dtype=torch.uint8, device=dev)
+    ws = torch.empty(U.delta_bytes(s, Hq_l), dtype=torch.uint8, device=dev)
     delta = ws.view(torch.float32)[: Hq_l * s].view(Hq_l, s)
+    # room for dK/dV's partial sums when the key blocks split (short sequences; none at 64K)
+    dkdv_need = U.attn_bwd_dkdv_workspace_bytes(s, Hkv_l, d)
+    dkdv_ws = torch.empty(dkdv_need, dtype=torch.uint8, device=dev) if dkdv_need else None
     o_sh = [torch.empty_like(t) for t in sh["q"]]
     dq_sh = [torch.empty_like(t) for t in sh["q"]]
     dk_sh = [torch.empty_like(t) for t in sh["k"]]
@@ -193,7 +196,7 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
         ph.run("pack_do", lambda: U.ulysses_pack(sh["do"], rank, do), rec)
         ph.run("bwd_preprocess", lambda: U.attn_bwd_preprocess(o, do, delta, o_lo=o_lo), rec)
         ph.run("bwd_dkdv", lambda: U.attn_bwd_dkdv(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev,
-                                                   dk=dk, dv=dv), rec)
+                                                   dk=dk, dv=dv, workspace=dkdv_ws), rec)
         ph.run("bwd_dq", lambda: U.attn_bwd_dq(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev, dq=dq),
                rec)
         ph.run("unpack_grads", lambda: U.ulysses_unpack_group([dq, dk, dv], rank, [dq_sh, dk_sh, dv_sh]), rec)

@@ -172,7 +172,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_lo, f
  *   q, k, v, o, lse, dout : as produced/consumed by attn_fwd (dout shaped like o)
  *   o_lo  : the residual attn_fwd wrote, or NULL (delta then from the bf16 o)
  *   dq [s, Hq, d], dk, dv [s, Hkv, d] : device `dtype`, written (fully overwritten)
- *   workspace : device scratch of at least attn_bwd_workspace_bytes(s, Hq) bytes.
+ *   workspace : device scratch of attn_bwd_workspace_bytes(s, Hq, Hkv, d) bytes: delta
+ *               [Hq, s] fp32 (rounded up to 256 bytes; required) followed by room for the dK/dV
+ *               partial sums of a split run (see attn_bwd_dkdv; optional: a workspace that
+ *               holds delta only runs dK/dV unsplit).
  *               If workspace == NULL the call only stores that size into
  *               *workspace_bytes and returns ULY_OK. Otherwise *workspace_bytes (if
  *               workspace_bytes != NULL) is the capacity and is checked.
@@ -184,13 +187,14 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const int32_t* cu_seqlens, int n_docs,
              void* workspace, size_t* workspace_bytes, void* stream);
 
-size_t attn_bwd_workspace_bytes(int64_t s, int Hq);
+size_t attn_bwd_workspace_bytes(int64_t s, int Hq, int Hkv, int d);
 
 /* ---------------------------------------------------------------------------
  * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
- * arguments without the workspace, and the same kernels, so the results are bitwise those
- * of attn_bwd. delta lives in a static device array of ULY_NOALLOC_MAX_DELTA floats
+ * arguments without the workspace, and the same kernels (dK/dV unsplit), so the results are
+ * bitwise those of attn_bwd wherever attn_bwd runs them unsplit (at least 256 key blocks x kv
+ * heads, i.e. s * Hkv >= 32768). delta lives in a static device array of ULY_NOALLOC_MAX_DELTA floats
  * (16 MiB) that each GPU the library runs on holds until the process ends; the call
  * allocates nothing. s * Hq above ULY_NOALLOC_MAX_DELTA -> ULY_ERR_WORKSPACE; the array's
  * address not obtainable -> ULY_ERR_HIP. Every call on one GPU uses that GPU's one array:
@@ -209,11 +213,19 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
  * (o_lo NULL: the o term alone).                                                    */
 int attn_bwd_preprocess(const void* o, const void* o_lo, const void* dout, float* delta,
                         int64_t s, int Hq, int d, int dtype, void* stream);
-/* dk, dv for every key: per kv head, loops over the rows of its G q heads.        */
+/* dk, dv for every key: per kv head, loops over the rows of its G q heads. A workgroup
+ * holds 128 keys of one kv head and fills a CU; when fewer than 256 such workgroups would run
+ * (short sequences) and a workspace of attn_bwd_dkdv_workspace_bytes(s, Hkv, d) bytes is
+ * given (bf16), each key block's rows are split over up to 8 workgroups (aiming at 512) that
+ * store fp32 partial sums, and a second kernel adds them in split order and rounds once:
+ * still deterministic; the sums' order, and so the last bits, differ from the unsplit run.
+ * The size is 0 when no split applies; workspace NULL runs unsplit.                     */
+size_t attn_bwd_dkdv_workspace_bytes(int64_t s, int Hkv, int d);
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                   const void* dout, const float* delta, void* dk, void* dv,
                   int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
-                  const int32_t* cu_seqlens, int n_docs, void* stream);
+                  const int32_t* cu_seqlens, int n_docs, void* workspace, size_t workspace_bytes,
+                  void* stream);
 /* dq for every row: loops over the visible keys.                                   */
 int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                 const void* dout, const float* delta, void* dq,
@@ -287,8 +299,8 @@ int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards,
  *                        [s_l, Hkv, d]
  *   o_lo : the residual attn_fwd_shards wrote ([s, Hq/P, d]) or NULL
  *   lse : device fp32 [Hq/P, s]
- *   workspace : delta, attn_bwd_workspace_bytes(P * s_l, Hq / P) bytes; NULL -> size
- *               query into *workspace_bytes as for attn_bwd.
+ *   workspace : delta, 4 * P * s_l * (Hq / P) bytes rounded up to a multiple of 256; NULL ->
+ *               size query into *workspace_bytes as for attn_bwd (dK/dV run unsplit).
  * bf16 only and s_l a multiple of 128 (ULY_ERR_UNSUPPORTED otherwise); other errors as
  * for attn_bwd_chunked.
  * ------------------------------------------------------------------------- */

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = U.lib()
-    assert L.uly_abi_version() == 2
+    assert L.uly_abi_version() == 3
     for code, name in U.STATUS.items():
         assert L.uly_status_string(code).decode() == name
 
@@ -138,8 +138,8 @@ def test_bwd_workspace_query_and_checks():
     need = ctypes.c_size_t(0)
     z = [FAKE] * 10
     st = L.attn_bwd(*z, 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None, ctypes.byref(need), None)
-    assert st == 0 and need.value == L.attn_bwd_workspace_bytes(1000, 8) and need.value >= 1000 * 8 * 4
-    small = ctypes.c_size_t(need.value - 1)
+    assert st == 0 and need.value == L.attn_bwd_workspace_bytes(1000, 8, 2, 128) and need.value >= 1000 * 8 * 4
+    small = ctypes.c_size_t(1000 * 8 * 4 - 1)   # less than delta
     assert L.attn_bwd(*z, 1000, 8, 2, 128, 0, 0.1, 1, None, 0, FAKE, ctypes.byref(small), None) == 5
     assert L.attn_bwd(*z, 1000, 8, 3, 128, 0, 0.1, 1, None, 0, None, ctypes.byref(need), None) == 2
     assert L.attn_bwd(*z, 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None, None, None) == 1
@@ -148,7 +148,8 @@ def test_bwd_workspace_query_and_checks():
     assert L.attn_bwd_preprocess(FAKE, FAKE, FAKE, FAKE, 10, 2, 64, 1, None) == 3
     zl = [FAKE, FAKE, FAKE, FAKE, MIS] + [FAKE] * 5   # misaligned o_lo
     assert L.attn_bwd(*zl, 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None, ctypes.byref(need), None) == 4
-    assert L.attn_bwd_dkdv(*[FAKE] * 8, 10, 4, 3, 128, 0, 0.1, 1, None, 0, None) == 2
+    assert L.attn_bwd_dkdv(*[FAKE] * 8, 10, 4, 3, 128, 0, 0.1, 1, None, 0, None, 0, None) == 2
+    assert L.attn_bwd_dkdv(*[FAKE] * 8, 10, 4, 2, 128, 0, 0.1, 1, None, 0, MIS, 1 << 20, None) == 4
     assert L.attn_bwd_dq(*[FAKE] * 7, 10, 4, 2, 100, 0, 0.1, 1, None, 0, None) == 3
 
 
@@ -247,7 +248,7 @@ def test_shards_rejects():
     def bwd(ws=None, cap=None, s_l=128, dt=0, d=128):
         return L.attn_bwd_shards(pp, pp, pp, pp, None, FAKE, pp, pp, pp, pp, 2, 0, s_l, 8, 4, d, dt, 0.1, 1, None, 0,
                                  ws, cap, None)
-    assert bwd(cap=ctypes.byref(need)) == 0 and need.value == L.attn_bwd_workspace_bytes(256, 4)
+    assert bwd(cap=ctypes.byref(need)) == 0 and need.value == U.delta_bytes(256, 4)
     assert bwd(cap=ctypes.byref(need), s_l=64) == 3
     assert bwd(cap=ctypes.byref(need), dt=1, d=64) == 3
     small = ctypes.c_size_t(need.value - 1)
@@ -332,3 +333,17 @@ def test_ring_rejects_on_the_host():
     assert bwd(cap=ctypes.byref(nb), acc=None) == 1
     assert bwd(cap=ctypes.byref(nb), acc=MIS) == 4
     assert bwd(cap=ctypes.byref(nb), rank=-1) == 2
+
+
+def test_dkdv_split_accounting():
+    """Key blocks split over workgroups only while the grid is under the CUs: 8K share (2 kv
+    heads) -> 4 splits and 64 MiB of fp32 partials; 64K share -> none."""
+    L = U.lib()
+    MiB = 2 ** 20
+    assert L.attn_bwd_dkdv_workspace_bytes(8192, 2, 128) == 2 * 64 * 4 * 2 * 128 * 128 * 4 == 64 * MiB
+    assert L.attn_bwd_dkdv_workspace_bytes(65536, 2, 128) == 0
+    assert L.attn_bwd_dkdv_workspace_bytes(32768, 1, 128) == 0      # 256 blocks: full
+    assert L.attn_bwd_dkdv_workspace_bytes(128, 1, 64) == 1 * 1 * 8 * 2 * 128 * 64 * 4   # capped at 8
+    delta = U.delta_bytes(8192, 8)
+    assert L.attn_bwd_workspace_bytes(8192, 8, 2, 128) == delta + 64 * MiB
+    assert L.attn_bwd_workspace_bytes(65536, 8, 2, 128) == U.delta_bytes(65536, 8)

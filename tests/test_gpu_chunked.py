@@ -177,7 +177,7 @@ def test_chunked_full_upipe_share():
 
 def _unchunked_bwd(dev, o_sh, lse, rank, scale, causal, cu_dev, o_lo=None):
     q, k, v, o, do = (U.ulysses_pack(x, rank) for x in (dev["q"], dev["k"], dev["v"], o_sh, dev["do"]))
-    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, do, scale, causal, cu_dev, o_lo=o_lo)
+    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, do, scale, causal, cu_dev, o_lo=o_lo, split=False)
     out = {}
     for n, y, like in (("dq", dq, dev["q"]), ("dk", dk, dev["k"]), ("dv", dv, dev["v"])):
         out[n] = _sentinel_like(like)

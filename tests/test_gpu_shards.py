@@ -69,7 +69,7 @@ def test_shards_equal_packed_path(P, s_l, Hq, Hkv, d, rank, causal, cu):
 
 def _packed_bwd(dev, o_sh, lse, rank, scale, causal, cu_dev, o_lo=None):
     q, k, v, o, g = (U.ulysses_pack(x, rank) for x in (dev["q"], dev["k"], dev["v"], o_sh, dev["do"]))
-    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, g, scale, causal, cu_dev, o_lo=o_lo)
+    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, g, scale, causal, cu_dev, o_lo=o_lo, split=False)
     out = {}
     for n, y, like in (("dq", dq, dev["q"]), ("dk", dk, dev["k"]), ("dv", dv, dev["v"])):
         out[n] = [torch.full_like(t, 3.0) for t in like]
@@ -108,7 +108,7 @@ def test_bwd_shards_workspace():
            for n in ("q", "k", "v", "do")}
     o_sh, lse = _packed_path(dev, 1, cfg.scale, True, None)
     outs = [[torch.zeros_like(t) for t in dev[n]] for n in ("q", "k", "v")]
-    need = U.attn_bwd_workspace_bytes(cfg.s, cfg.Hq_l)
+    need = U.delta_bytes(cfg.s, cfg.Hq_l)
     short = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
     with pytest.raises(U.UlyssesError):
         U.attn_bwd_shards(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], *outs, 1, workspace=short)

@@ -57,12 +57,13 @@ SIGNATURES = {
     "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp]),
     "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
                         _vp, _i32, _vp, _szp, _vp]),
-    "attn_bwd_workspace_bytes": (_sz, [_i64, _i32]),
+    "attn_bwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
+    "attn_bwd_dkdv_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "attn_bwd_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32,
                                 _i32, _vp, _i32, _vp]),
     "attn_bwd_preprocess": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "attn_bwd_dkdv": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
-                             _vp, _i32, _vp]),
+                             _vp, _i32, _vp, _sz, _vp]),
     "attn_bwd_dq": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
                            _vp, _i32, _vp]),
     "attn_fwd_chunked": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
@@ -327,14 +328,24 @@ def attn_fwd(q, k, v, scale=None, causal=True, cu_seqlens=None, out=None, lse=No
     return o, lse
 
 
-def attn_bwd_workspace_bytes(s, Hq):
-    return int(lib().attn_bwd_workspace_bytes(s, Hq))
+def attn_bwd_workspace_bytes(s, Hq, Hkv, d):
+    return int(lib().attn_bwd_workspace_bytes(s, Hq, Hkv, d))
+
+
+def attn_bwd_dkdv_workspace_bytes(s, Hkv, d):
+    return int(lib().attn_bwd_dkdv_workspace_bytes(s, Hkv, d))
+
+
+def delta_bytes(s, Hq):
+    """Bytes of delta [Hq, s] fp32 rounded up to 256 (the shard-reading backward's workspace)."""
+    return (s * Hq * 4 + 255) // 256 * 256
 
 
 def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=True, cu_seqlens=None, workspace=None,
-             dq=None, dk=None, dv=None, o_lo=None):
+             dq=None, dk=None, dv=None, o_lo=None, split=True):
     """Gradients (dq, dk, dv) of the attention forward, given its o and lse and dout (and the
-    forward's o_lo, if it wrote one: delta then comes from O to about 16 bits)."""
+    forward's o_lo, if it wrote one: delta then comes from O to about 16 bits). split=False
+    allocates room for delta only, so dK/dV run unsplit on short sequences too."""
     s, Hq, Hkv, d = _qkv(q, k, v)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -345,7 +356,7 @@ def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=True, cu_seqlens=None, wo
         _need(t, n, (s, Hkv, d), q.dtype, q.device)
     _need(lse, "lse", (Hq, s), torch.float32, q.device)
     lo = _opt(o_lo, "o_lo", (s, Hq, d), torch.bfloat16, q.device)
-    need = attn_bwd_workspace_bytes(s, Hq)
+    need = attn_bwd_workspace_bytes(s, Hq, Hkv, d) if split else delta_bytes(s, Hq)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
@@ -398,16 +409,25 @@ def _bwd_phase_checks(q, lse, dout, delta):
     _need(delta, "delta", (Hq, s), torch.float32, q.device)
 
 
-def attn_bwd_dkdv(q, k, v, lse, dout, delta, scale=None, causal=True, cu_seqlens=None, dk=None, dv=None):
+def attn_bwd_dkdv(q, k, v, lse, dout, delta, scale=None, causal=True, cu_seqlens=None, dk=None, dv=None,
+                  workspace=None, split=True):
+    """dK, dV. On short sequences the key blocks split over several workgroups when a workspace
+    of attn_bwd_dkdv_workspace_bytes is given (allocated here unless split=False)."""
     s, Hq, Hkv, d = _qkv(q, k, v)
     _bwd_phase_checks(q, lse, dout, delta)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for t, n in ((dk, "dk"), (dv, "dv")):
         _need(t, n, (s, Hkv, d), q.dtype, q.device)
+    if workspace is None and split:
+        need = attn_bwd_dkdv_workspace_bytes(s, Hkv, d)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws, cap = (None, 0) if workspace is None or not split else (_dev(workspace),
+                                                                 workspace.numel() * workspace.element_size())
     cu, nd = _cu(cu_seqlens, q.device)
     _call("attn_bwd_dkdv", _dev(q), _dev(k), _dev(v), _dev(lse), _dev(dout), _dev(delta), _dev(dk), _dev(dv),
-          s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, _stream())
+          s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, ws, cap, _stream())
     return dk, dv
 
 
@@ -525,7 +545,7 @@ def attn_bwd_shards(q_shards, k_shards, v_shards, o_shards, lse, do_shards, dq_s
                                          more_kv=(dk_shards, dv_shards))
     _need(lse, "lse", (Hq // P, P * s_l), torch.float32, q0.device)
     lo = _opt(o_lo, "o_lo", (P * s_l, Hq // P, d), torch.bfloat16, q0.device)
-    need = attn_bwd_workspace_bytes(P * s_l, Hq // P)
+    need = delta_bytes(P * s_l, Hq // P)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q0.device)
     cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())

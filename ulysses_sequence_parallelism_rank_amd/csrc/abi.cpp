@@ -14,7 +14,7 @@ using namespace uly;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline int esize(int dtype) { return dtype == ULY_BF16 ? 2 : 4; }
@@ -81,6 +81,7 @@ AttnArgs make_args(int64_t s, int Hq, int Hkv, int d, float scale, int causal, c
   a.n_docs = cu ? n_docs : 0;
   a.acc_init = -1;
   a.acc_final = -1;
+  a.nsplit = 1;
   return a;
 }
 
@@ -283,9 +284,20 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_lo, f
   return fwd_dispatch(a, d, dtype, as_stream(stream));
 }
 
-size_t attn_bwd_workspace_bytes(int64_t s, int Hq) {
+// delta [Hq, s] fp32 of the backward
+static size_t delta_bytes(int64_t s, int Hq) {
   if (s < 1 || Hq < 1) return 0;
   return round256((size_t)s * (size_t)Hq * sizeof(float));
+}
+
+size_t attn_bwd_dkdv_workspace_bytes(int64_t s, int Hkv, int d) {
+  if (s < 1 || Hkv < 1 || d < 1) return 0;
+  return dkdv_part_bytes(s, Hkv, d);
+}
+
+size_t attn_bwd_workspace_bytes(int64_t s, int Hq, int Hkv, int d) {
+  if (s < 1 || Hq < 1 || Hkv < 1 || d < 1) return 0;
+  return delta_bytes(s, Hq) + round256(attn_bwd_dkdv_workspace_bytes(s, Hkv, d));
 }
 
 int attn_bwd_preprocess(const void* o, const void* o_lo, const void* dout, float* delta, int64_t s, int Hq, int d,
@@ -307,12 +319,16 @@ int attn_bwd_preprocess(const void* o, const void* o_lo, const void* dout, float
 
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                   const float* delta, void* dk, void* dv, int64_t s, int Hq, int Hkv, int d, int dtype,
-                  float scale, int causal, const int32_t* cu_seqlens, int n_docs, void* stream) {
+                  float scale, int causal, const int32_t* cu_seqlens, int n_docs, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, cu_seqlens, n_docs);
   if (st != ULY_OK) return st;
   if (!lse || !dout || !delta || !dk || !dv) return ULY_ERR_NULL;
   if (!aligned16(lse) || !aligned16(dout) || !aligned16(delta) || !aligned16(dk) || !aligned16(dv))
     return ULY_ERR_ALIGN;
+  if (workspace != nullptr && !aligned16(workspace)) return ULY_ERR_ALIGN;
+  const size_t part = attn_bwd_dkdv_workspace_bytes(s, Hkv, d);
+  const bool split = dtype == ULY_BF16 && part > 0 && workspace != nullptr && workspace_bytes >= part;
   AttnArgs a = make_args(s, Hq, Hkv, d, scale, causal, cu_seqlens, n_docs);
   a.q = q;
   a.k = k;
@@ -322,6 +338,10 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
   a.delta = delta;
   a.out_k = dk;
   a.out_v = dv;
+  if (split) {  // small grid: each key block's rows over several workgroups, partials reduced in order
+    a.nsplit = dkdv_split_count(s, Hkv);
+    a.dkv_part = static_cast<float*>(workspace);
+  }
   const hipError_t e = dtype == ULY_BF16 ? launch_attn_dkdv_bf16(a, d, as_stream(stream))
                                          : launch_attn_dkdv_f32(a, d, as_stream(stream));
   return hip_status(e);
@@ -354,13 +374,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, cu_seqlens, n_docs);
   if (st != ULY_OK) return st;
   if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
-  const size_t need = attn_bwd_workspace_bytes(s, Hq);
+  const size_t need = attn_bwd_workspace_bytes(s, Hq, Hkv, d);
   if (workspace == nullptr) {
     if (!workspace_bytes) return ULY_ERR_NULL;
     *workspace_bytes = need;
     return ULY_OK;
   }
-  if (workspace_bytes && *workspace_bytes < need) return ULY_ERR_WORKSPACE;
+  // delta is required; the dK/dV partial sums are optional (dK/dV run split only with room for them)
+  const size_t cap = workspace_bytes ? *workspace_bytes : need;
+  if (cap < delta_bytes(s, Hq)) return ULY_ERR_WORKSPACE;
   if (!o || !lse || !dout || !dq || !dk || !dv) return ULY_ERR_NULL;
   if (!aligned16(o) || !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv) || !aligned16(workspace))
@@ -368,8 +390,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   float* delta = static_cast<float*>(workspace);
   st = attn_bwd_preprocess(o, o_lo, dout, delta, s, Hq, d, dtype, stream);
   if (st != ULY_OK) return st;
+  const size_t dpart = delta_bytes(s, Hq);
   st = attn_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens, n_docs,
-                     stream);
+                     static_cast<char*>(workspace) + dpart, cap - dpart, stream);
   if (st != ULY_OK) return st;
   return attn_bwd_dq(q, k, v, lse, dout, delta, dq, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens, n_docs,
                      stream);
@@ -410,10 +433,13 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
   // every argument is checked: only now is the device touched
   float* delta = device_scratch();
   if (delta == nullptr) return ULY_ERR_HIP;
-  size_t cap = (size_t)ULY_NOALLOC_MAX_DELTA * sizeof(float);
-  // every element of delta the kernels read is written by the preprocess first: nothing to clear
-  return attn_bwd(q, k, v, o, o_lo, lse, dout, dq, dk, dv, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens, n_docs,
-                  delta, &cap, stream);
+  // every element of delta the kernels read is written by the preprocess first: nothing to clear;
+  // dK/dV run unsplit (no partial sums, which would need more than the array)
+  if ((st = attn_bwd_preprocess(o, o_lo, dout, delta, s, Hq, d, dtype, stream)) != ULY_OK) return st;
+  if ((st = attn_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens,
+                          n_docs, nullptr, 0, stream)) != ULY_OK)
+    return st;
+  return attn_bwd_dq(q, k, v, lse, dout, delta, dq, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens, n_docs, stream);
 }
 
 // ---- UPipe headwise-chunked forward ------------------------------------------------
@@ -613,7 +639,7 @@ int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards, co
   if (s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
   if (cu_seqlens != nullptr && n_docs < 1) return ULY_ERR_SHAPE;
   const int Hq_l = Hq / P, Hkv_l = Hkv / P;
-  const size_t need = attn_bwd_workspace_bytes(s, Hq_l);
+  const size_t need = delta_bytes(s, Hq_l);
   if (workspace == nullptr) {
     if (!workspace_bytes) return ULY_ERR_NULL;
     *workspace_bytes = need;

@@ -352,7 +352,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
   const int l32 = lane & 31, hf = lane >> 5, gi = lane >> 4, li = lane & 15;
   const int64_t s = a.s;
   const int kvh = blockIdx.x % a.n_kv;
-  const int64_t n0 = (int64_t)(blockIdx.x / a.n_kv) * BNK;  // earliest keys (most rows) first
+  const int sp = (int)((blockIdx.x / a.n_kv) % a.nsplit);                 // split of the key block
+  const int64_t kb = (int64_t)(blockIdx.x / a.n_kv) / a.nsplit;
+  const int64_t n0 = kb * BNK;  // earliest keys (most rows) first
   const float c = a.scale * kLog2e;
 
   // this lane's key, the rows that may see it [rlo, rhi), and its K (role 0) or V row
@@ -393,7 +395,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
   const int ntile = qend > qbeg ? (int)((qend - qbeg + BMQ - 1) / BMQ) : 0;
   const KvHeads kh = kv_heads_of(a, kvh);  // the launch's q heads reading this kv head
   const int GH = kh.j1 - kh.j0;
-  const int nsteps = ntile * GH;
+  // steps [st0, st0 + nsteps) of the block's ntile * GH (all of them unless split)
+  const int st0 = (int)((int64_t)ntile * GH * sp / a.nsplit);
+  const int nsteps = (int)((int64_t)ntile * GH * (sp + 1) / a.nsplit) - st0;
 
   // Steps walk the query tiles from the last one down, the GH heads of a tile back to back.
   auto tile_row0 = [&](int tile) { return qbeg + (int64_t)(ntile - 1 - tile) * BMQ; };
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  int cur_t = 0, cur_h = 0;  // tile and head of this step
+  int cur_t = st0 / (GH > 0 ? GH : 1), cur_h = st0 - cur_t * GH;  // tile and head of this step
   auto run_step = [&](auto B, int step) {
     const Buf buf = bufs(B), nbuf = bufs(std::integral_constant<int, 1 - decltype(B)::value>{});
     wait_dma();
@@ -558,7 +562,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
   };
 
   if (nsteps > 0) {
-    if (role == 1) issue_tile(0, 0, bufs(std::integral_constant<int, 0>{}));
+    if (role == 1) issue_tile(cur_t, cur_h, bufs(std::integral_constant<int, 0>{}));
     if (wave == 4) {  // LSE rows of the first tile in log2 units
       wait_dma();
       bufs(std::integral_constant<int, 0>{}).l[lane] *= kLog2e;
@@ -571,6 +575,20 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
     }
   }
 
+  if (a.nsplit > 1) {
+    // this split's fp32 partial sums (unscaled) into its slot; the reduce kernel finishes them
+    if (key < s) {
+      float* slot = a.dkv_part + ((((int64_t)kvh * ((s + BNK - 1) / BNK) + kb) * a.nsplit + sp) * 2 + role) *
+                                     (BNK * D) + (int64_t)(kg * 32 + l32) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<f32x4*>(slot + db * 32 + 8 * jj + 4 * hf) =
+              f32x4{acc[db][4 * jj + 0], acc[db][4 * jj + 1], acc[db][4 * jj + 2], acc[db][4 * jj + 3]};
+    }
+    return;
+  }
   if (key < s) {
     const bool is_k = role == 1;
     const int64_t off = (int64_t)kvh * D + key * a.dkv_row;
@@ -633,17 +651,71 @@ hipError_t launch_dq_t(const AttnArgs& a, const BwdSrc& src, hipStream_t stream)
   return hipGetLastError();
 }
 
+// dK/dV of split key blocks: for 8 consecutive elements of one key and kv head, the nsplit
+// partial sums in split order (from +0), scaled (dK) and rounded once, one thread each
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnArgs a, Shards dk_sh, Shards dv_sh, int64_t s_l) {
+  constexpr int BNK = 128, PER = D / 8;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t s = a.s, nkb = (s + BNK - 1) / BNK;
+  const int64_t total = 2 * (int64_t)a.n_kv * s * PER;
+  if (c >= total) return;
+  const int part8 = (int)(c % PER);
+  const int64_t key = (c / PER) % s;
+  const int64_t rest = c / PER / s;
+  const int kvh = (int)(rest % a.n_kv), is_k = (int)(rest / a.n_kv);
+  const int64_t kb = key / BNK;
+  const float* slot0 = a.dkv_part + ((((int64_t)kvh * nkb + kb) * a.nsplit) * 2 + is_k) * (BNK * D) +
+                       (key - kb * BNK) * D + part8 * 8;
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const float* p = slot0 + (int64_t)sp * 2 * (BNK * D);
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p), hi = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] += lo[e];
+      x[4 + e] += hi[e];
+    }
+  }
+  const float f = is_k ? a.scale : 1.0f;
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[2 * i] * f, x[2 * i + 1] * f);
+  const int pk = (int)((uint32_t)key / (uint32_t)s_l);
+  uint16_t* out = static_cast<uint16_t*>(const_cast<void*>(is_k ? dk_sh.p[pk] : dv_sh.p[pk])) +
+                  (key - (int64_t)pk * s_l) * a.dkv_row + (int64_t)kvh * D + part8 * 8;
+  *reinterpret_cast<u32x4*>(out) = w;
+}
+
 template <int D>
 hipError_t launch_dkdv_split_t(const AttnArgs& a, const BwdSrc& src, hipStream_t stream) {
   using C = DkvSplitCfg<D>;
-  const int64_t blocks = (a.s + C::BNK - 1) / C::BNK * a.n_kv;
+  const int64_t blocks = (a.s + C::BNK - 1) / C::BNK * a.n_kv * (a.nsplit > 1 ? a.nsplit : 1);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((attn_dkdv_split_kernel<D>), dim3((unsigned)blocks), dim3(C::NW * 64), 0, stream, a, src.q,
                      src.g, src.k, src.v, src.dk, src.dv, src.s_l);
+  if (a.nsplit > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t items = 2 * (int64_t)a.n_kv * a.s * (D / 8);
+    hipLaunchKernelGGL((dkdv_reduce_kernel<D>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a, src.dk,
+                       src.dv, src.s_l);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
+
+int dkdv_split_count(int64_t s, int n_kv) {
+  // one eight-wave workgroup per CU: split the key blocks' rows while the grid is under the
+  // 256 CUs, aiming at 512 workgroups, at most 8 per block
+  const int64_t wg = (s + 127) / 128 * n_kv;
+  if (wg >= 256 || wg < 1) return 1;
+  const int64_t ns = (512 + wg - 1) / wg;
+  return (int)(ns < 8 ? ns : 8);
+}
 
 namespace {
 // the packed head-shard buffers of AttnArgs as one-shard tables

@@ -62,7 +62,20 @@ struct AttnArgs {
   // the dK/dV kernel means "from the launch's q heads" (the headwise-chunked rule above)
   float* acc_q;
   int acc_init, acc_final;
+  // dK/dV of one key block split over nsplit workgroups (small grids): workgroup sp walks its
+  // share of the block's steps and stores fp32 partial sums (dV then dK, [128 keys][D] each) in
+  // slot ((kv head * key blocks + block) * nsplit + sp) of dkv_part; a reduce kernel sums the
+  // slots in split order and rounds. nsplit 1: no partials (and no accumulation across launches
+  // combined with a split).
+  int nsplit;
+  float* dkv_part;
 };
+// dK/dV workgroups split per key block for a grid of n_kv * ceil(s/128) blocks (1 = no split)
+int dkdv_split_count(int64_t s, int n_kv);
+inline size_t dkdv_part_bytes(int64_t s, int n_kv, int d) {
+  const int ns = dkdv_split_count(s, n_kv);
+  return ns <= 1 ? 0 : (size_t)n_kv * (size_t)((s + 127) / 128) * (size_t)ns * 2 * 128 * (size_t)d * sizeof(float);
+}
 
 // One tensor of a grouped permute: its P shards (P of them used), the head-shard buffer, the
 // shard row size, the byte offset of the rank's heads in a row and the bytes per row moved.
