@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hf = lane >> 5, gi = lane >> 4, li = lane & 15;
   const int64_t s = a.s;
   const int nmb = (int)((s + BM - 1) / BM);
@@ -160,14 +160,21 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
   // the SIMD issues MFMAs; within a wave the two 32-key halves of a tile run one after the
   // other: S/dP, dS, dQ.
   static_assert(RB == 1 && KB == 2, "the tile is two 32-key halves of one 32-row wave tile");
-  // key tile k0 from its shard (rows past the sequence end read the shard's last row)
+  // key tile k0 from its shard (rows past the sequence end read the shard's last row); K and V
+  // share the row stride, so one lane offset serves both
+  const uint32_t kv_off = dma_lane_offset<D, kWaves * 64>(a.kv_row, tid);
   auto issue_kv = [&](int64_t k0, int b) {
     const int pk = (int)((uint32_t)k0 / (uint32_t)s_l);
     const int64_t r0 = k0 - (int64_t)pk * s_l;
     const uint16_t* K = static_cast<const uint16_t*>(k_sh.p[pk]) + (int64_t)kvh * D;
     const uint16_t* V = static_cast<const uint16_t*>(v_sh.p[pk]) + (int64_t)kvh * D;
-    dma_tile<D, BN, kWaves * 64>(K, a.kv_row, r0, s_l, sK[b], tid);
-    dma_tile<D, BN, kWaves * 64>(V, a.kv_row, r0, s_l, sV[b], tid);
+    if (r0 + BN <= s_l) {
+      dma_tile_whole<D, BN, kWaves * 64>(K + r0 * a.kv_row, a.kv_row, kv_off, sK[b], wave);
+      dma_tile_whole<D, BN, kWaves * 64>(V + r0 * a.kv_row, a.kv_row, kv_off, sV[b], wave);
+    } else {
+      dma_tile<D, BN, kWaves * 64>(K, a.kv_row, r0, s_l, sK[b], tid);
+      dma_tile<D, BN, kWaves * 64>(V, a.kv_row, r0, s_l, sV[b], tid);
+    }
   };
   auto load_sdp = [&](int b, int kb, int t, bf16x8& kx, bf16x8& vx) {
     kx = *reinterpret_cast<const bf16x8*>(&sK[b][tile_off<D>(kb * 32 + l32, 16 * t + 8 * hf)]);
@@ -207,9 +214,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
   for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
 
   constexpr int NC = 2 * DB;  // dQ products per half (tt, db)
-  if (kbeg < kend) issue_kv(kbeg, 0);
-  int buf = 0;
-  for (int64_t k0 = kbeg; k0 < kend; k0 += BN, buf ^= 1) {
+  // one key tile; B is the buffer (compile time, as in the forward: the two buffers' LDS
+  // addresses then differ by an immediate offset, so no per-read address arithmetic)
+  auto tile_step = [&](auto B, int64_t k0) {
+    constexpr int buf = decltype(B)::value;
     wait_dma();
     __syncthreads();  // tile k0 has landed and every wave is done with the previous tile
     const int32_t krel0 = (int32_t)(k0 - lo[0]) + 4 * hf;
@@ -266,6 +274,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
     // the next tile's DMA after this tile's last LDS read: the wait the compiler places
     // before LDS reads that follow a DMA then falls on the next barrier
     if (k0 + BN < kend) issue_kv(k0 + BN, buf ^ 1);
+  };
+  if (kbeg < kend) issue_kv(kbeg, 0);
+  for (int64_t k0 = kbeg;;) {
+    if (k0 >= kend) break;
+    tile_step(std::integral_constant<int, 0>{}, k0);
+    k0 += BN;
+    if (k0 >= kend) break;
+    tile_step(std::integral_constant<int, 1>{}, k0);
+    k0 += BN;
   }
 
   const int rb = 0;

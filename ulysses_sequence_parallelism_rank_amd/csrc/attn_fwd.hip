@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hf = lane >> 5, gi = lane >> 4, li = lane & 15;
   const int64_t s = a.s;
   const int nmb = (int)((s + BM - 1) / BM);
@@ -107,14 +107,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
   const uint32_t full_w = any_full ? (uint32_t)(full_hi - full_lo) : 0u;
   const int ntiles = kbeg < kend ? (int)((kend - kbeg + BN - 1) / BN) : 0;
 
-  // tile k0 of K and V from its shard (rows past the sequence end read the shard's last row)
+  // tile k0 of K and V from its shard (rows past the sequence end read the shard's last row);
+  // K and V share the row stride, so one set of lane offsets serves both
+  const uint32_t kv_off = dma_lane_offset<D, 256>(a.kv_row, tid);
   auto issue_kv = [&](int64_t k0, int b) {
     const int pk = (int)((uint32_t)k0 / (uint32_t)src.s_l);
     const int64_t r0 = k0 - (int64_t)pk * src.s_l;
     const uint16_t* K = static_cast<const uint16_t*>(src.k[pk]) + (int64_t)kvh * D;
     const uint16_t* V = static_cast<const uint16_t*>(src.v[pk]) + (int64_t)kvh * D;
-    dma_tile<D, BN, 256>(K, a.kv_row, r0, src.s_l, sK[b], tid);
-    dma_tile<D, BN, 256>(V, a.kv_row, r0, src.s_l, sV[b], tid);
+    if (r0 + BN <= src.s_l) {
+      dma_tile_whole<D, BN, 256>(K + r0 * a.kv_row, a.kv_row, kv_off, sK[b], wave);
+      dma_tile_whole<D, BN, 256>(V + r0 * a.kv_row, a.kv_row, kv_off, sV[b], wave);
+    } else {
+      dma_tile<D, BN, 256>(K, a.kv_row, r0, src.s_l, sK[b], tid);
+      dma_tile<D, BN, 256>(V, a.kv_row, r0, src.s_l, sV[b], tid);
+    }
   };
   // S^T of one half: the K operand of k-step t is read kPfS steps ahead (a ring of kPfS + 1
   // registers), each product behind a scheduling barrier; left alone, the compiler reads

@@ -126,6 +126,39 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t stride, in
   }
 }
 
+// The lane-dependent part of dma_tile's addresses: the byte offset of this lane's 16-byte chunk
+// in the tile's first wave instruction (row stride `stride` elements). Instruction i reads the
+// rows NTHREADS / (D / 8) * i further on, a multiple of the swizzle's 16-row period, so its
+// lanes keep the same chunk order and only a wave-uniform row step is added. Computed once per
+// kernel: a tile whose rows all lie inside the matrix then costs scalar address arithmetic only.
+template <int D, int NTHREADS>
+__device__ __forceinline__ uint32_t dma_lane_offset(int64_t stride, int tid) {
+  constexpr int CPR = D / 8;
+  static_assert((NTHREADS / CPR) % 16 == 0, "rows per wave instruction must be a multiple of 16");
+  const int sl = (tid >> 6) * 64 + (tid & 63);
+  const int row = sl / CPR, pc = sl % CPR;
+  return (uint32_t)(row * stride + (pc ^ swz_chunk<D>(row)) * 8) * 2u;
+}
+// dma_tile for a tile whose ROWS rows all lie inside the matrix: `tile` is the wave-uniform
+// address of its first row, `off` this lane's dma_lane_offset, `wave` the wave index (uniform).
+template <int D, int ROWS, int NTHREADS>
+__device__ __forceinline__ void dma_tile_whole(const uint16_t* tile, int64_t stride, uint32_t off, uint16_t* lds_tile,
+                                               int wave) {
+  constexpr int CPR = D / 8, RPI = NTHREADS / CPR;
+  static_assert(ROWS % RPI == 0, "tile must be a whole number of wave instructions");
+#pragma unroll
+  for (int i = 0; i < ROWS / RPI; ++i) {
+    const int sl0 = (i * (NTHREADS / 64) + wave) * 64;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(tile + (int64_t)i * RPI * stride) + off,
+                                     lds_tile + sl0 * 8, 16, 0, 0);
+  }
+}
+
+// The wave index as a wave-uniform value: tid >> 6 is the same on every lane of a wave, but the
+// compiler cannot see that, and values derived from it would otherwise live in vector registers
+// (branches on them turned into per-lane selects, LDS DMA bases moved to scalars per use).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+
 // Wait until this wave's LDS DMA (global_load_lds) has landed: s_waitcnt vmcnt(0), the other
 // counters left alone (gfx9 encoding: expcnt 7 in bits 6:4, lgkmcnt 15 in bits 11:8). A
 // workgroup barrier does not order another wave's DMA writes before this wave's LDS reads, so
