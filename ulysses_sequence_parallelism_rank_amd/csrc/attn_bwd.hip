@@ -420,14 +420,27 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
   auto tile_row0 = [&](int tile) { return qbeg + (int64_t)(ntile - 1 - tile) * BMQ; };
   // Only the dS waves issue DMA: the P waves then never hold outstanding DMA, so nothing
   // makes them wait for it before their LDS writes of P.
+  // Q and dO share the row stride: one lane offset (of the dS waves' 256 threads) serves both
+  const uint32_t qg_off = dma_lane_offset<D, 256>(a.q_row, tid & 255);
   auto issue_tile = [&](int tile, int hi, const Buf& b) {
     const int hq = kh.j0 + hi;
     const int64_t q0 = tile_row0(tile);
-    const int t2 = tid - 256;
     const int pq = (int)((uint32_t)q0 / (uint32_t)s_l);
     const int64_t r0 = q0 - (int64_t)pq * s_l;
-    dma_tile<D, BMQ, 256>(static_cast<const uint16_t*>(q_sh.p[pq]) + (int64_t)hq * D, a.q_row, r0, s_l, b.q, t2);
-    dma_tile<D, BMQ, 256>(static_cast<const uint16_t*>(g_sh.p[pq]) + (int64_t)hq * D, a.q_row, r0, s_l, b.g, t2);
+    const uint16_t* Qh = static_cast<const uint16_t*>(q_sh.p[pq]) + (int64_t)hq * D;
+    const uint16_t* Gh = static_cast<const uint16_t*>(g_sh.p[pq]) + (int64_t)hq * D;
+    if (r0 + BMQ <= s_l) {
+      const int w4 = __builtin_amdgcn_readfirstlane(wave - 4);
+      dma_tile_whole<D, BMQ, 256>(Qh + r0 * a.q_row, a.q_row, qg_off, b.q, w4);
+      dma_tile_whole<D, BMQ, 256>(Gh + r0 * a.q_row, a.q_row, qg_off, b.g, w4);
+    } else {
+      // a shard's ragged last tile: the thread index through an empty asm, so this rare path's
+      // address arithmetic is formed here rather than hoisted into registers for the whole loop
+      int t2 = tid - 256;
+      asm volatile("" : "+v"(t2));
+      dma_tile<D, BMQ, 256>(Qh, a.q_row, r0, s_l, b.q, t2);
+      dma_tile<D, BMQ, 256>(Gh, a.q_row, r0, s_l, b.g, t2);
+    }
     // one fp32 per lane: lane i lands at b.l[i] (wave 4) or b.d[i] (wave 5)
     int64_t qr = q0 + (lane < BMQ ? lane : BMQ - 1);
     qr = qr < s ? qr : s - 1;
