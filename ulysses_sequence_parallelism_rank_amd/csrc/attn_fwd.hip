@@ -7,30 +7,32 @@
 // compute stays O(n^2)): the kernel streams K/V tiles past resident Q rows with an
 // online softmax, so the s x s score matrix never exists.
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one q head, two
+// Work decomposition (one workgroup = 4 waves = 128 query rows of one q head, three
 // workgroups per CU):
 //   * each wave owns 32 query rows; its Q rows stay in VGPRs for the whole key loop as
 //     MFMA B operands;
-//   * K/V tiles of 64 keys arrive in LDS by DMA (global_load_lds, XOR-swizzled rows,
+//   * K/V tiles of 32 keys arrive in LDS by DMA (global_load_lds, XOR-swizzled rows,
 //     double buffered; the next tile is requested after the current tile's last LDS read)
-//     and are shared by the 4 waves; a tile is processed as two 32-key halves, S of the
-//     second half issued with the softmax of the first;
+//     and are shared by the 4 waves; a tile is S (8 MFMAs), its softmax, then PV (8 MFMAs);
+//   * three waves per SIMD (at most 168 VGPRs, 32 KiB of LDS per workgroup): a wave's VALU
+//     work does not overlap its own MFMAs, so the softmax of one wave runs beside the
+//     products of the others, and a third wave leaves that overlap less often empty than two;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 leaves each lane one query row and 16 of
-//     the half's keys, so the row max and row sum are lane-local plus one swap with the
+//     the tile's keys, so the row max and row sum are lane-local plus one swap with the
 //     lane 32 away;
 //   * O^T += V^T P^T: P (bf16) is already in B-operand layout, V^T comes straight from
 //     the row-major V tile through the transposing LDS read (ds_read_b64_tr_b16), and the
 //     O^T accumulator keeps each lane's query row, so softmax rescales stay lane-local;
 //   * the exponent is exp2 with scale*log2(e) folded into one FMA, and the running max is
 //     only moved when a row's max grows by more than kTau (2^8): P then stays <= 256 and
-//     most halves skip the O rescale;
+//     most tiles skip the O rescale;
 //   * two row sums: l of the fp32 weights gives the LSE, and l' of the bf16-rounded weights
 //     (the PV operand, summed by v_dot2_f32_bf16) normalises O, so O is an exact convex
 //     combination of the V rows with the weights the MFMA used: on rows dominated by one key
 //     the weight's rounding (up to 2^-9 of it, since the lagging max leaves it unequal to 1)
 //     then cancels instead of reaching O, and delta = dO . O in the backward;
 //   * causal / document tiles outside a row block's range are never visited; partial
-//     halves are masked per element; workgroups with the longest key range launch first.
+//     tiles are masked per element; workgroups with the longest key range launch first.
 #include <type_traits>
 
 #include "uly_device.h"
@@ -42,11 +44,11 @@ namespace {
 
 constexpr float kTau = 8.0f;
 // LDS operand read-ahead of the S^T and O^T products (k-steps / products ahead)
-constexpr int kPfS = 3, kPfV = 2;
+constexpr int kPfS = 2, kPfV = 2;
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc src) {
-  constexpr int BM = 128, BN = 64, DT = D / 16, DB = D / 32;
+__global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a, ShardSrc src) {
+  constexpr int BM = 128, BN = 32, DT = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
 
@@ -65,13 +67,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
   const float c = a.scale * kLog2e;
 
   const int64_t row = m0 + wave * 32 + l32;
-  int64_t lo = 0, hi = s;
+  // this row's key range [lo, hi) (positions fit in 32 bits: s < 2^31 is checked on the host)
+  int32_t lo = 0, hi = (int32_t)s;
   if (a.cu != nullptr && row < s) {
     const int dk = doc_of(a.cu, a.n_docs, row);
     lo = a.cu[dk];
-    hi = a.cu[dk + 1] < s ? a.cu[dk + 1] : s;
+    hi = a.cu[dk + 1] < (int32_t)s ? a.cu[dk + 1] : (int32_t)s;
   }
-  if (a.causal) hi = hi < row + 1 ? hi : row + 1;
+  if (a.causal) hi = hi < (int32_t)row + 1 ? hi : (int32_t)row + 1;
   bf16x8 qf[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
@@ -97,12 +100,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
   }
   if (a.causal) kend = kend < last_row + 1 ? kend : last_row + 1;
   kbeg = (kbeg / BN) * BN;
-  // Halves of 32 keys from k0 that every row of this wave sees whole: full_lo <= k0 <= full_hi
+  // Tiles of 32 keys from k0 that every row of this wave sees whole: full_lo <= k0 <= full_hi
   // (keys inside the sequence, at or after the last row's document start, before the first
   // row's document end, and, causal, at or before the first row).
   const int64_t full_lo = w_lo_last;
-  int64_t full_hi = (s < w_hi_first ? s : w_hi_first) - 32;
-  if (a.causal) full_hi = full_hi < wr0 - 31 ? full_hi : wr0 - 31;
+  int64_t full_hi = (s < w_hi_first ? s : w_hi_first) - BN;
+  if (a.causal) full_hi = full_hi < wr0 - (BN - 1) ? full_hi : wr0 - (BN - 1);
   const bool any_full = wr0 < s && full_hi >= full_lo;
   const uint32_t full_w = any_full ? (uint32_t)(full_hi - full_lo) : 0u;
   const int ntiles = kbeg < kend ? (int)((kend - kbeg + BN - 1) / BN) : 0;
@@ -119,17 +122,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
       dma_tile_whole<D, BN, 256>(K + r0 * a.kv_row, a.kv_row, kv_off, sK[b], wave);
       dma_tile_whole<D, BN, 256>(V + r0 * a.kv_row, a.kv_row, kv_off, sV[b], wave);
     } else {
-      dma_tile<D, BN, 256>(K, a.kv_row, r0, src.s_l, sK[b], tid);
-      dma_tile<D, BN, 256>(V, a.kv_row, r0, src.s_l, sV[b], tid);
+      // a shard's ragged last tile: the thread index through an empty asm, so this rare path's
+      // address arithmetic is formed here rather than hoisted into registers for the whole loop
+      int t1 = tid;
+      asm volatile("" : "+v"(t1));
+      dma_tile<D, BN, 256>(K, a.kv_row, r0, src.s_l, sK[b], t1);
+      dma_tile<D, BN, 256>(V, a.kv_row, r0, src.s_l, sV[b], t1);
     }
   };
-  // S^T of one half: the K operand of k-step t is read kPfS steps ahead (a ring of kPfS + 1
-  // registers), each product behind a scheduling barrier; left alone, the compiler reads
-  // each operand just before its MFMA and waits for it (4% of the kernel at 64K)
-  auto qk = [&](int b, int hh, f32x16& S) {
+  // S^T of the tile in buffer b: the K operand of k-step t is read kPfS steps ahead (a ring
+  // of kPfS + 1 registers), each product behind a scheduling barrier; left alone, the compiler
+  // reads each operand just before its MFMA and waits for it
+  auto qk = [&](int b, f32x16& S) {
     bf16x8 ring[kPfS + 1];
     auto ld = [&](int t) {
-      return *reinterpret_cast<const bf16x8*>(&sK[b][tile_off<D>(hh * 32 + l32, 16 * t + 8 * hf)]);
+      return *reinterpret_cast<const bf16x8*>(&sK[b][tile_off<D>(l32, 16 * t + 8 * hf)]);
     };
 #pragma unroll
     for (int t = 0; t < kPfS; ++t) ring[t] = ld(t);
@@ -141,17 +148,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
     }
   };
   // the 32 keys from k0 need no mask for any row of this wave (one unsigned range compare)
-  auto half_full = [&](int64_t k0) { return any_full && (uint32_t)(k0 - full_lo) <= full_w; };
+  auto tile_full = [&](int64_t k0) { return any_full && (uint32_t)(k0 - full_lo) <= full_w; };
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m = -INFINITY, l = 0.f, lr = 0.f;  // running max (log2 units), sums of fp32 / rounded weights
   // mask S of the 32 keys from k0, then rescale O if the row max grew by more than kTau
   auto mask_rescale = [&](int64_t k0, f32x16& S) {
-    if (!half_full(k0)) {
+    if (!tile_full(k0)) {
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
-        const int64_t key = k0 + 8 * (jj / 4) + 4 * hf + (jj % 4);
+        const int32_t key = (int32_t)k0 + 8 * (jj / 4) + 4 * hf + (jj % 4);
         if (key < lo || key >= hi) S[jj] = -INFINITY;
       }
     }
@@ -194,13 +201,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
       }
     }
   };
-  // O^T += V^T P^T for one half: product i = (tt, db); its V^T operand (two transposing
-  // reads) is read kPfV products ahead, as the K operands are
-  auto pv = [&](int b, int hh, const bf16x8 (&pf)[2]) {
+  // O^T += V^T P^T for the tile in buffer b: product i = (tt, db); its V^T operand (two
+  // transposing reads) is read kPfV products ahead, as the K operands are
+  auto pv = [&](int b, const bf16x8 (&pf)[2]) {
     constexpr int NPV = 2 * DB;
     auto ld = [&](int i) {
       const int tt = i / DB, db = i % DB;
-      const int kr = hh * 32 + 16 * tt + 4 * hf + (li >> 2);
+      const int kr = 16 * tt + 4 * hf + (li >> 2);
       const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
       const i16x4 v0 = lds_read_tr16(&sV[b][tile_off<D>(kr, col)]);
       const i16x4 v1 = lds_read_tr16(&sV[b][tile_off<D>(kr + 8, col)]);
@@ -224,19 +231,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, ShardSrc s
     const int64_t k0 = kbeg + (int64_t)t * BN;
     wait_dma();
     __syncthreads();  // tile t has landed; every wave is done with tile t-1
-    f32x16 S0, S1;
-    bf16x8 p0[2], p1[2];
-    qk(b, 0, S0);
-    mask_rescale(k0, S0);
-    qk(b, 1, S1);
-    softmax(S0, p0);
-    pv(b, 0, p0);
-    mask_rescale(k0 + 32, S1);
-    // raised priority through the second softmax, the one no MFMA of this wave overlaps
+    f32x16 S;
+    bf16x8 p[2];
+    qk(b, S);
+    mask_rescale(k0, S);
+    // raised priority through the softmax: the other waves' products fill the matrix core
     __builtin_amdgcn_s_setprio(1);
-    softmax(S1, p1);
+    softmax(S, p);
     __builtin_amdgcn_s_setprio(0);
-    pv(b, 1, p1);
+    pv(b, p);
     // the next tile's DMA after this tile's last LDS read: the wait the compiler places
     // before LDS reads that follow a DMA then falls on the next barrier
     if (t + 1 < ntiles) issue_kv(k0 + BN, 1 - b);
