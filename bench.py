@@ -31,6 +31,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--
                        [--heads-per-chunk U] [--forward-only [--fused]]
 """
 import argparse
+import contextlib
+import gc
 import hashlib
 import json
 import os
@@ -125,6 +127,19 @@ def make_inputs(cfg, seed=0):
     return glob, shards
 
 
+@contextlib.contextmanager
+def no_gc():
+    """Python's cyclic garbage collector off for a timed region (collected just before): a
+    collection pass stalls the host thread for milliseconds while the GPU waits for its next
+    launch. All the work still runs inside the region."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
+
+
 class Phases:
     """HIP events around every phase of every timed step, on the stream the library uses."""
 
@@ -203,12 +218,13 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
 
     for _ in range(warmup):
         step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step(True)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
+    with no_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(True)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
     cold = None
     if not fused:
         cold = cold_permutes({
@@ -269,12 +285,14 @@ def run_forward_share(cfg, steps, warmup, cu_dev, fused):
 
     for _ in range(warmup):
         step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step(True)
-    torch.cuda.synchronize()
-    return ((time.perf_counter() - t0) / steps,) + ph.summary(steps)
+    with no_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(True)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+    return (wall,) + ph.summary(steps)
 
 
 def run_upipe(cfg, steps, warmup, u, forward_only):
@@ -293,24 +311,27 @@ def run_upipe(cfg, steps, warmup, u, forward_only):
         need["bwd"] = U.attn_bwd_chunked_workspace_bytes(*args)
     ws = torch.empty(max(need.values()), dtype=torch.uint8, device="cuda")
     ph = Phases()
-    for i in range(warmup + steps):
-        if i == warmup:
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-        ph.run("attn_fwd_chunked", lambda: U.attn_fwd_chunked(sh["q"], sh["k"], sh["v"], o_sh, 0, u, cfg.scale,
-                                                              cfg.causal, None, ws, lse, o_lo=o_lo), i >= warmup)
-        if not forward_only:
-            ph.run("attn_bwd_chunked", lambda: U.attn_bwd_chunked(sh["q"], sh["k"], sh["v"], o_sh, lse, sh["do"],
-                                                                  dq_sh, dk_sh, dv_sh, 0, u, cfg.scale, cfg.causal,
-                                                                  None, ws, o_lo=o_lo), i >= warmup)
-    torch.cuda.synchronize()
-    return ((time.perf_counter() - t0) / steps,) + ph.summary(steps) + (need,)
+    with no_gc():
+        for i in range(warmup + steps):
+            if i == warmup:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+            ph.run("attn_fwd_chunked", lambda: U.attn_fwd_chunked(sh["q"], sh["k"], sh["v"], o_sh, 0, u, cfg.scale,
+                                                                  cfg.causal, None, ws, lse, o_lo=o_lo), i >= warmup)
+            if not forward_only:
+                ph.run("attn_bwd_chunked", lambda: U.attn_bwd_chunked(sh["q"], sh["k"], sh["v"], o_sh, lse, sh["do"],
+                                                                      dq_sh, dk_sh, dv_sh, 0, u, cfg.scale,
+                                                                      cfg.causal, None, ws, o_lo=o_lo), i >= warmup)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+    return (wall,) + ph.summary(steps) + (need,)
 
 
 def measured_ceilings():
     """Practical ceilings on this GPU, beside the published peaks: back-to-back bf16 MFMAs on
-    every SIMD (uly_mfma_probe, with the sustained shader clock), and a plain 1 GiB device
-    copy (ulysses_pack with one rank) for HBM."""
+    every SIMD (uly_mfma_probe, with the sustained shader clock), the attention kernels'
+    inner-loop instruction mix at 2 and 3 waves per SIMD (uly_mix_probe), and a plain 1 GiB
+    device copy (ulysses_pack with one rank) for HBM."""
     tf, clk = U.mfma_probe()
     n = 1 << 30
     src = torch.empty((n // 256, 1, 128), dtype=torch.bfloat16, device="cuda")
@@ -324,9 +345,14 @@ def measured_ceilings():
     torch.cuda.synchronize()
     gbs = 3 * 2.0 * n / (a.elapsed_time(b) * 1e-3) / 1e9
     del src, dst
+    # the kernels' inner-loop instruction mix (an LDS operand per product, plus the softmax's VALU
+    # work) at the occupancies they run: 2 waves per SIMD (backward kernels) and 3 (forward)
+    mix = {f"{U.MIX_KINDS[k]} @{w} waves/SIMD": round(U.mix_probe(k, w), 1) for k in (0, 1, 2) for w in (2, 3)}
     return {"mfma_bf16_tflops": round(tf, 1), "sustained_clock_mhz": round(clk, 0) if clk else None,
-            "copy_gbs": round(gbs, 1),
+            "copy_gbs": round(gbs, 1), "mix_tflops": mix,
             "how": "uly_mfma_probe: 512 workgroups x 4 waves x 20000 x 4 back-to-back 32x32x16 bf16 MFMAs; "
+                   "uly_mix_probe: 256 x W workgroups of 4 waves, 4000 rounds of 16 MFMAs each with its "
+                   "first operand read from LDS and the listed fp32 FMAs / exp2 after it; "
                    "copy: 1 GiB read + 1 GiB written by ulysses_pack with one rank"}
 
 

@@ -21,7 +21,7 @@
  *      kernels read the sequence shards directly      -> attn_fwd_shards, attn_bwd_shards
  *   6. the pages' comparison workload, Ring Attention   -> ring_attn_fwd, ring_attn_bwd
  * The P ranks are P separate device buffers on one GPU; no collective runs here.
- * uly_mfma_probe is a measurement helper outside the path.
+ * uly_mfma_probe and uly_mix_probe are measurement helpers outside the path.
  *
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers; arrays of pointers (the P shards) are HOST
@@ -397,6 +397,19 @@ int ring_attn_bwd(const void* const* q_shards, const void* const* k_shards,
  * Errors: ULY_ERR_NULL, ULY_ERR_SHAPE (iters or blocks < 1), ULY_ERR_HIP.
  * ------------------------------------------------------------------------- */
 int uly_mfma_probe(int iters, int blocks, float* sink, uint64_t* clocks, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * uly_mix_probe -- measurement helper, not part of the attention path: the ceiling of the
+ * attention kernels' inner-loop instruction mix. `blocks` workgroups of 4 waves each run
+ * `iters` rounds of 16 v_mfma_f32_32x32x16_bf16 (32768 flops each), every product's first
+ * operand a 1 KiB LDS read (ds_read_b128), followed by, for `kind` 0: nothing; 1: 2 fp32
+ * FMAs and 1 v_exp_f32; 2: 4 fp32 FMAs and 1 v_exp_f32, on registers of their own. The
+ * kernel fits 4 workgroups per CU, so 256 * W blocks run W waves on every SIMD. `sink`: one
+ * device float, written only in a case that does not occur.
+ * Errors: ULY_ERR_NULL, ULY_ERR_SHAPE (iters or blocks < 1), ULY_ERR_UNSUPPORTED (kind not
+ * 0..2), ULY_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+int uly_mix_probe(int kind, int iters, int blocks, float* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = U.lib()
-    assert L.uly_abi_version() == 3
+    assert L.uly_abi_version() == 4
     for code, name in U.STATUS.items():
         assert L.uly_status_string(code).decode() == name
 
@@ -261,6 +261,11 @@ def test_probe_rejects():
     assert L.uly_mfma_probe(0, 4, FAKE, FAKE, None) == 2
     assert L.uly_mfma_probe(4, 0, FAKE, FAKE, None) == 2
     assert L.uly_mfma_probe(4, 4, None, FAKE, None) == 1
+    assert L.uly_mix_probe(0, 0, 4, FAKE, None) == 2
+    assert L.uly_mix_probe(0, 4, 0, FAKE, None) == 2
+    assert L.uly_mix_probe(3, 4, 4, FAKE, None) == 3
+    assert L.uly_mix_probe(-1, 4, 4, FAKE, None) == 3
+    assert L.uly_mix_probe(1, 4, 4, None, None) == 1
 
 
 def test_binding_checks_shapes_before_the_call():

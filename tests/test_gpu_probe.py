@@ -1,5 +1,5 @@
-"""The measurement helper uly_mfma_probe: a plausible practical MFMA ceiling and sustained
-clock, and its argument checks."""
+"""The measurement helpers uly_mfma_probe (a plausible practical MFMA ceiling and sustained
+clock) and uly_mix_probe (the inner-loop instruction mix), and their argument checks."""
 import pytest
 import torch
 
@@ -22,3 +22,15 @@ def test_mfma_probe_rejects_bad_arguments():
         U._call("uly_mfma_probe", 0, 4, U._dev(sink), U._dev(clocks), U._stream())
     with pytest.raises(U.UlyssesError):
         U._call("uly_mfma_probe", 4, 4, None, U._dev(clocks), U._stream())
+
+
+def test_mix_probe_plausible():
+    r = {(k, w): U.mix_probe(k, w, iters=1000) for k in (0, 2) for w in (2, 3)}
+    for key, tf in r.items():
+        assert 100.0 < tf < 2700.0, (key, tf)
+    # the VALU work per product costs rate at a fixed occupancy
+    assert r[(2, 2)] < r[(0, 2)], r
+    with pytest.raises(ValueError):
+        U.mix_probe(3, 2)
+    with pytest.raises(ValueError):
+        U.mix_probe(0, 5)

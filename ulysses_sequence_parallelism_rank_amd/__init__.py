@@ -83,6 +83,7 @@ SIGNATURES = {
     "ring_attn_bwd": (_i32, [_vpp, _vpp, _vpp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vpp, _vpp, _i32, _i32, _i64, _i32,
                              _i32, _i32, _i32, _f32, _i32, _vp, _szp, _vp]),
     "uly_mfma_probe": (_i32, [_i32, _i32, _vp, _vp, _vp]),
+    "uly_mix_probe": (_i32, [_i32, _i32, _i32, _vp, _vp]),
 }
 
 
@@ -603,6 +604,25 @@ def ring_attn_bwd(q_shards, k_shards, v_shards, o, lse, dout, rank, dk_acc, dv_a
           dkp, dvp, P, rank, s_l, Hq, Hkv, d, _dtype(q0), _default_scale(d, scale), int(causal), _dev(workspace),
           ctypes.byref(cap), _stream())
     return dq
+
+
+MIX_KINDS = {0: "mfma+lds", 1: "mfma+lds+2fma+1exp", 2: "mfma+lds+4fma+1exp"}
+
+
+def mix_probe(kind, waves_per_simd, iters=4000):
+    """Rate (TFLOP/s) of the inner-loop instruction mix `kind` (MIX_KINDS) with
+    `waves_per_simd` (1..4) waves on every SIMD, timed with events on the current stream."""
+    if kind not in MIX_KINDS or not 1 <= waves_per_simd <= 4:
+        raise ValueError("kind must be 0..2 and waves_per_simd 1..4")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    blocks = 256 * waves_per_simd
+    _call("uly_mix_probe", kind, 2, blocks, _dev(sink), _stream())  # warm-up
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    _call("uly_mix_probe", kind, iters, blocks, _dev(sink), _stream())
+    b.record()
+    torch.cuda.synchronize()
+    return float(blocks) * 4 * iters * 16 * 32768 / (a.elapsed_time(b) * 1e-3) / 1e12
 
 
 def mfma_probe(iters=20000, blocks=512):

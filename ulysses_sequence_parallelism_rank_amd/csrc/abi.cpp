@@ -14,7 +14,7 @@ using namespace uly;
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline int esize(int dtype) { return dtype == ULY_BF16 ? 2 : 4; }
@@ -155,6 +155,13 @@ int uly_mfma_probe(int iters, int blocks, float* sink, uint64_t* clocks, void* s
   if (iters < 1 || blocks < 1) return ULY_ERR_SHAPE;
   return hip_status(launch_mfma_probe(iters, blocks, sink, reinterpret_cast<unsigned long long*>(clocks),
                                       as_stream(stream)));
+}
+
+int uly_mix_probe(int kind, int iters, int blocks, float* sink, void* stream) {
+  if (!sink) return ULY_ERR_NULL;
+  if (iters < 1 || blocks < 1) return ULY_ERR_SHAPE;
+  if (kind < 0 || kind > 2) return ULY_ERR_UNSUPPORTED;
+  return hip_status(launch_mix_probe(kind, iters, blocks, sink, as_stream(stream)));
 }
 
 int ulysses_pack(const void* const* shards, int P, int rank, int64_t s_l, int H, int d, int dtype,

@@ -140,6 +140,8 @@ hipError_t launch_ring_merge(const void* part, const void* part_lo, const float*
                              void* out, void* out_lo, float* out_lse, int64_t s_l, int H, int d, int first, int last,
                              hipStream_t stream);
 hipError_t launch_mfma_probe(int iters, int blocks, float* sink, unsigned long long* clocks, hipStream_t stream);
+// kind 0: MFMA + LDS operand; 1: + 2 FMAs + 1 exp per product; 2: + 4 FMAs + 1 exp per product
+hipError_t launch_mix_probe(int kind, int iters, int blocks, float* sink, hipStream_t stream);
 hipError_t launch_attn_dkdv_f32(const AttnArgs& a, int d, hipStream_t stream);
 hipError_t launch_attn_dq_f32(const AttnArgs& a, int d, hipStream_t stream);
 
