@@ -197,3 +197,35 @@ def test_q_zero_gives_prefix_means():
     for h in range(2):
         compare(f"O head {h}", dev_to_f64(o)[:, h], want, bf16=True)
     np.testing.assert_allclose(lse.cpu().numpy(), np.log(np.arange(1, s + 1))[None, :].repeat(2, 0), atol=1e-4)
+
+
+@pytest.mark.parametrize("d,causal,cu", [
+    (128, True, [0, 37, 38, 700, 1333, 2100]),
+    (64, True, None),
+    (128, False, [0, 1000, 2100]),
+])
+def test_forward_key_tile_sizes_agree(d, causal, cu):
+    """The forward takes 32-key tiles (three workgroups per CU) on grids of at least 768
+    workgroups and 64-key tiles (two per CU) on smaller ones; both perform the same per-half
+    operations in the same order. 48 q heads over 2100 tokens (17 row blocks: 816 workgroups)
+    run with 32-key tiles, their first 8 heads alone (136 workgroups) with 64-key tiles: O, its
+    rounding residual and the LSE agree bitwise (ragged tail, documents not aligned to either
+    tile), and the 8-head run matches the oracle."""
+    s, Hq, Hkv = 2100, 48, 12
+    print(f"case d={d} causal={causal} cu={cu is not None}", flush=True)
+    f, g = _inputs(s, Hq, Hkv, d, "bf16", seed=d + 7)
+    scale = 1.0 / np.sqrt(d)
+    cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    lo48 = U.new_o_lo(g["q"])
+    o48, l48 = U.attn_fwd(g["q"], g["k"], g["v"], scale, causal, cu_dev, o_lo=lo48)
+    q8, k2, v2 = (g[n][:, :h].contiguous() for n, h in (("q", 8), ("k", 2), ("v", 2)))
+    lo8 = U.new_o_lo(q8)
+    o8, l8 = U.attn_fwd(q8, k2, v2, scale, causal, cu_dev, o_lo=lo8)
+    torch.cuda.synchronize()
+    bits = lambda t: t.contiguous().view(torch.int16)
+    assert torch.equal(bits(o48[:, :8]), bits(o8))
+    assert torch.equal(bits(lo48[:, :8]), bits(lo8))
+    assert torch.equal(l48[:8].contiguous().view(torch.int32), l8.view(torch.int32))
+    wo, wl = OA.forward(f["q"][:, :8], f["k"][:, :2], f["v"][:, :2], scale, causal, cu)
+    compare("O", dev_to_f64(o8), wo, bf16=True)
+    compare("LSE", l8.cpu().numpy(), wl, max_abs=LSE_ABS, rel_fro=1e-4)

@@ -8,7 +8,7 @@
 // online softmax, so the s x s score matrix never exists.
 //
 // Work decomposition (one workgroup = 4 waves = 128 query rows of one q head, three
-// workgroups per CU):
+// workgroups per CU; grids too small to fill three per CU take 64-key tiles at two per CU):
 //   * each wave owns 32 query rows; its Q rows stay in VGPRs for the whole key loop as
 //     MFMA B operands;
 //   * K/V tiles of 32 keys arrive in LDS by DMA (global_load_lds, XOR-swizzled rows,
@@ -46,9 +46,13 @@ constexpr float kTau = 8.0f;
 // LDS operand read-ahead of the S^T and O^T products (k-steps / products ahead)
 constexpr int kPfS = 2, kPfV = 2;
 
-template <int D>
-__global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a, ShardSrc src) {
-  constexpr int BM = 128, BN = 32, DT = D / 16, DB = D / 32;
+// Key tiles of BN = 32 (three workgroups per CU) or 64 keys (two): a tile is processed as
+// BN / 32 halves of 32 keys, each S, its softmax and PV in turn, so both tile sizes perform the
+// same operations in the same order and give bitwise-identical results.
+template <int D, int BN>
+__global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void attn_fwd_kernel(AttnArgs a, ShardSrc src) {
+  constexpr int BM = 128, DT = D / 16, DB = D / 32;
+  static_assert(BN == 32 || BN == 64, "key tile");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
 
@@ -100,12 +104,12 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a, ShardSrc s
   }
   if (a.causal) kend = kend < last_row + 1 ? kend : last_row + 1;
   kbeg = (kbeg / BN) * BN;
-  // Tiles of 32 keys from k0 that every row of this wave sees whole: full_lo <= k0 <= full_hi
+  // Halves of 32 keys from k0 that every row of this wave sees whole: full_lo <= k0 <= full_hi
   // (keys inside the sequence, at or after the last row's document start, before the first
   // row's document end, and, causal, at or before the first row).
   const int64_t full_lo = w_lo_last;
-  int64_t full_hi = (s < w_hi_first ? s : w_hi_first) - BN;
-  if (a.causal) full_hi = full_hi < wr0 - (BN - 1) ? full_hi : wr0 - (BN - 1);
+  int64_t full_hi = (s < w_hi_first ? s : w_hi_first) - 32;
+  if (a.causal) full_hi = full_hi < wr0 - 31 ? full_hi : wr0 - 31;
   const bool any_full = wr0 < s && full_hi >= full_lo;
   const uint32_t full_w = any_full ? (uint32_t)(full_hi - full_lo) : 0u;
   const int ntiles = kbeg < kend ? (int)((kend - kbeg + BN - 1) / BN) : 0;
@@ -130,13 +134,13 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a, ShardSrc s
       dma_tile<D, BN, 256>(V, a.kv_row, r0, src.s_l, sV[b], t1);
     }
   };
-  // S^T of the tile in buffer b: the K operand of k-step t is read kPfS steps ahead (a ring
-  // of kPfS + 1 registers), each product behind a scheduling barrier; left alone, the compiler
-  // reads each operand just before its MFMA and waits for it
-  auto qk = [&](int b, f32x16& S) {
+  // S^T of half hh of the tile in buffer b: the K operand of k-step t is read kPfS steps ahead
+  // (a ring of kPfS + 1 registers), each product behind a scheduling barrier; left alone, the
+  // compiler reads each operand just before its MFMA and waits for it
+  auto qk = [&](int b, int hh, f32x16& S) {
     bf16x8 ring[kPfS + 1];
     auto ld = [&](int t) {
-      return *reinterpret_cast<const bf16x8*>(&sK[b][tile_off<D>(l32, 16 * t + 8 * hf)]);
+      return *reinterpret_cast<const bf16x8*>(&sK[b][tile_off<D>(hh * 32 + l32, 16 * t + 8 * hf)]);
     };
 #pragma unroll
     for (int t = 0; t < kPfS; ++t) ring[t] = ld(t);
@@ -148,14 +152,14 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a, ShardSrc s
     }
   };
   // the 32 keys from k0 need no mask for any row of this wave (one unsigned range compare)
-  auto tile_full = [&](int64_t k0) { return any_full && (uint32_t)(k0 - full_lo) <= full_w; };
+  auto half_full = [&](int64_t k0) { return any_full && (uint32_t)(k0 - full_lo) <= full_w; };
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m = -INFINITY, l = 0.f, lr = 0.f;  // running max (log2 units), sums of fp32 / rounded weights
   // mask S of the 32 keys from k0, then rescale O if the row max grew by more than kTau
   auto mask_rescale = [&](int64_t k0, f32x16& S) {
-    if (!tile_full(k0)) {
+    if (!half_full(k0)) {
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const int32_t key = (int32_t)k0 + 8 * (jj / 4) + 4 * hf + (jj % 4);
@@ -201,13 +205,13 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a, ShardSrc s
       }
     }
   };
-  // O^T += V^T P^T for the tile in buffer b: product i = (tt, db); its V^T operand (two
-  // transposing reads) is read kPfV products ahead, as the K operands are
-  auto pv = [&](int b, const bf16x8 (&pf)[2]) {
+  // O^T += V^T P^T for half hh of the tile in buffer b: product i = (tt, db); its V^T operand
+  // (two transposing reads) is read kPfV products ahead, as the K operands are
+  auto pv = [&](int b, int hh, const bf16x8 (&pf)[2]) {
     constexpr int NPV = 2 * DB;
     auto ld = [&](int i) {
       const int tt = i / DB, db = i % DB;
-      const int kr = 16 * tt + 4 * hf + (li >> 2);
+      const int kr = hh * 32 + 16 * tt + 4 * hf + (li >> 2);
       const int col = db * 32 + 16 * (gi & 1) + 4 * (li & 3);
       const i16x4 v0 = lds_read_tr16(&sV[b][tile_off<D>(kr, col)]);
       const i16x4 v1 = lds_read_tr16(&sV[b][tile_off<D>(kr + 8, col)]);
@@ -231,15 +235,18 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a, ShardSrc s
     const int64_t k0 = kbeg + (int64_t)t * BN;
     wait_dma();
     __syncthreads();  // tile t has landed; every wave is done with tile t-1
-    f32x16 S;
-    bf16x8 p[2];
-    qk(b, S);
-    mask_rescale(k0, S);
-    // raised priority through the softmax: the other waves' products fill the matrix core
-    __builtin_amdgcn_s_setprio(1);
-    softmax(S, p);
-    __builtin_amdgcn_s_setprio(0);
-    pv(b, p);
+#pragma unroll
+    for (int hh = 0; hh < BN / 32; ++hh) {
+      f32x16 S;
+      bf16x8 p[2];
+      qk(b, hh, S);
+      mask_rescale(k0 + 32 * hh, S);
+      // raised priority through the softmax: the other waves' products fill the matrix core
+      __builtin_amdgcn_s_setprio(1);
+      softmax(S, p);
+      __builtin_amdgcn_s_setprio(0);
+      pv(b, hh, p);
+    }
     // the next tile's DMA after this tile's last LDS read: the wait the compiler places
     // before LDS reads that follow a DMA then falls on the next barrier
     if (t + 1 < ntiles) issue_kv(k0 + BN, 1 - b);
@@ -282,12 +289,20 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a, ShardSrc s
   }
 }
 
+// Grids of at least three workgroups per CU (256 CUs) take 32-key tiles and three workgroups
+// per CU; smaller grids, which would leave that third slot empty, take 64-key tiles (fewer
+// barriers and tile requests per key) at two per CU.
+constexpr int64_t kFwdSmallGrid = 3 * 256;
+
 template <int D>
 hipError_t launch_fwd_t(const AttnArgs& a, const ShardSrc& src, hipStream_t stream) {
   const int64_t nmb = (a.s + 127) / 128;
   const int64_t blocks = nmb * a.n_heads;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a, src);
+  if (blocks >= kFwdSmallGrid)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, 32>), dim3((unsigned)blocks), dim3(256), 0, stream, a, src);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, 64>), dim3((unsigned)blocks), dim3(256), 0, stream, a, src);
   return hipGetLastError();
 }
 
