@@ -71,6 +71,9 @@ typedef enum {
 } uly_status;
 
 #define ULY_MAX_RANKS 64
+/* Largest head count (global or local) any call accepts: the kernels address a tile's rows
+   (at most 128 rows of one tensor) with 32-bit byte offsets. Larger counts: ULY_ERR_SHAPE. */
+#define ULY_MAX_HEADS 4096
 
 /* Name of a status code (static string). */
 const char* uly_status_string(int status);

@@ -51,6 +51,7 @@ def _ptr_array(vals):
 @pytest.mark.parametrize("P,rank,s_l,H,d,dt,want", [
     (0, 0, 4, 4, 64, 0, 2), (65, 0, 4, 65, 64, 0, 2), (2, 2, 4, 4, 64, 0, 2), (2, -1, 4, 4, 64, 0, 2),
     (2, 0, 0, 4, 64, 0, 2), (3, 0, 4, 4, 64, 0, 2), (2, 0, 4, 4, 64, 7, 3), (2, 0, 4, 2, 4, 0, 4),
+    (2, 0, 4, 4098, 64, 0, 2),   # more heads than ULY_MAX_HEADS
 ])
 def test_pack_rejects(P, rank, s_l, H, d, dt, want):
     L = U.lib()
@@ -125,6 +126,7 @@ def _fwd(**kw):
 @pytest.mark.parametrize("kw,want", [
     (dict(q=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
     (dict(Hq=3, Hkv=2), 2), (dict(s=0), 2), (dict(Hkv=0), 2), (dict(cu=FAKE, nd=0), 2),
+    (dict(Hq=4097 * 2, Hkv=2), 2),   # more heads than ULY_MAX_HEADS
     (dict(d=96), 3), (dict(dt=1, d=128), 3), (dict(dt=5), 3),
     (dict(k=MIS), 4), (dict(o=MIS), 4),
     (dict(o_lo=MIS), 4), (dict(dt=1, d=64, o_lo=FAKE), 3),   # the O residual: aligned, bf16 only
@@ -297,7 +299,7 @@ def test_bwd_noalloc_rejects_on_the_host():
 
 @pytest.mark.parametrize("P,s_l,H,d,dt,want", [
     (0, 4, 4, 64, 0, 2), (65, 4, 4, 64, 0, 2), (4, 0, 4, 64, 0, 2), (4, 4, 3, 64, 0, 2), (3, 4, 2, 64, 0, 2),
-    (4, 4, 4, 64, 7, 3), (4, 4, 2, 4, 0, 4),
+    (4, 4, 4, 64, 7, 3), (4, 4, 2, 4, 0, 4), (4, 4, 4100, 64, 0, 2),
 ])
 def test_send_recv_reject_on_the_host(P, s_l, H, d, dt, want):
     L = U.lib()
@@ -323,6 +325,7 @@ def test_ring_rejects_on_the_host():
     assert fwd(cap=ctypes.byref(need)) == 0 and need.value == L.ring_attn_fwd_workspace_bytes(64, 8, 128)
     assert fwd(rank=4, cap=ctypes.byref(need)) == 2
     assert fwd(Hkv=3, cap=ctypes.byref(need)) == 2
+    assert fwd(Hq=8192, cap=ctypes.byref(need)) == 2   # more heads than ULY_MAX_HEADS
     assert fwd(dt=1, d=64, cap=ctypes.byref(need)) == 3
     small = ctypes.c_size_t(need.value - 1)
     assert fwd(ws=FAKE, cap=ctypes.byref(small)) == 5

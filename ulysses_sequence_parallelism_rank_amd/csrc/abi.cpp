@@ -31,7 +31,7 @@ int check_dtype_dim(int dtype, int d) {
 // P, rank, s_l, H checks shared by the permutes and the chunked forward.
 int check_ranks(int P, int rank, int64_t s_l, int H) {
   if (P < 1 || P > ULY_MAX_RANKS || rank < 0 || rank >= P) return ULY_ERR_SHAPE;
-  if (s_l < 1 || H < 1 || H % P != 0) return ULY_ERR_SHAPE;
+  if (s_l < 1 || H < 1 || H > ULY_MAX_HEADS || H % P != 0) return ULY_ERR_SHAPE;
   return ULY_OK;
 }
 
@@ -47,7 +47,7 @@ int check_attn(const void* q, const void* k, const void* v, int64_t s, int Hq, i
   if (!q || !k || !v) return ULY_ERR_NULL;
   int st = check_dtype_dim(dtype, d);
   if (st != ULY_OK) return st;
-  if (s < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ULY_ERR_SHAPE;
+  if (s < 1 || Hq < 1 || Hkv < 1 || Hq > ULY_MAX_HEADS || Hq % Hkv != 0) return ULY_ERR_SHAPE;
   if (s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;  // cu_seqlens are int32
   if (cu != nullptr && n_docs < 1) return ULY_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ULY_ERR_ALIGN;
@@ -206,7 +206,7 @@ int ulysses_unpack(const void* in, int P, int rank, int64_t s_l, int H, int d, i
 // Checks shared by the send-side and receive-side permutes of one rank.
 static int check_send_recv(const void* a, const void* b, int P, int64_t s_l, int H, int d, int dtype) {
   if (!a || !b) return ULY_ERR_NULL;
-  if (P < 1 || P > ULY_MAX_RANKS || s_l < 1 || H < 1 || d < 1) return ULY_ERR_SHAPE;
+  if (P < 1 || P > ULY_MAX_RANKS || s_l < 1 || H < 1 || H > ULY_MAX_HEADS || d < 1) return ULY_ERR_SHAPE;
   if (H % P != 0 && P % H != 0) return ULY_ERR_SHAPE;
   if (dtype != ULY_BF16 && dtype != ULY_F32) return ULY_ERR_UNSUPPORTED;
   if (((int64_t)d * esize(dtype)) % 16 != 0) return ULY_ERR_ALIGN;
@@ -729,7 +729,7 @@ int check_ring(const void* const* qs, const void* const* ks, const void* const* 
                int Hq, int Hkv, int d, int dtype) {
   if (!qs || !ks || !vs) return ULY_ERR_NULL;
   if (P < 1 || P > ULY_MAX_RANKS || rank < 0 || rank >= P || s_l < 1) return ULY_ERR_SHAPE;
-  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ULY_ERR_SHAPE;
+  if (Hq < 1 || Hkv < 1 || Hq > ULY_MAX_HEADS || Hq % Hkv != 0) return ULY_ERR_SHAPE;
   if (s_l > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
   int st = check_dtype_dim(dtype, d);
   if (st != ULY_OK) return st;
