@@ -11,15 +11,16 @@
 // workgroups per CU; grids too small to fill three per CU take 64-key tiles at two per CU):
 //   * each wave owns 32 query rows; its Q rows stay in VGPRs for the whole key loop as
 //     MFMA B operands;
-//   * K/V tiles of 32 keys arrive in LDS by DMA (global_load_lds, XOR-swizzled rows,
-//     double buffered; the next tile is requested after the current tile's last LDS read)
-//     and are shared by the 4 waves; a tile is S (8 MFMAs), its softmax, then PV (8 MFMAs);
+//   * K/V tiles of 32 (or 64) keys arrive in LDS by DMA (global_load_lds, XOR-swizzled
+//     rows, double buffered; the next tile is requested after the current tile's last LDS
+//     read) and are shared by the 4 waves; each 32 keys of a tile are S (8 MFMAs), their
+//     softmax, then PV (8 MFMAs);
 //   * three waves per SIMD (at most 168 VGPRs, 32 KiB of LDS per workgroup): a wave's VALU
 //     work does not overlap its own MFMAs, so the softmax of one wave runs beside the
 //     products of the others, and a third wave leaves that overlap less often empty than two;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 leaves each lane one query row and 16 of
-//     the tile's keys, so the row max and row sum are lane-local plus one swap with the
-//     lane 32 away;
+//     the 32 keys, so the row max and row sum are lane-local plus one swap with the lane 32
+//     away;
 //   * O^T += V^T P^T: P (bf16) is already in B-operand layout, V^T comes straight from
 //     the row-major V tile through the transposing LDS read (ds_read_b64_tr_b16), and the
 //     O^T accumulator keeps each lane's query row, so softmax rescales stay lane-local;

@@ -57,9 +57,6 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return a + b;
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __builtin_bit_cast(float, (uint32_t)b << 16);
-}
 // the two bf16 halves of a packed pair (low half = first element) as fp32
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
@@ -164,11 +161,6 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // workgroup barrier does not order another wave's DMA writes before this wave's LDS reads, so
 // every wave waits for its own DMA before the barrier that publishes a DMA'd tile.
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
 
 // q heads [j0, j1) of a launch that read its kv head g (see AttnArgs), and whether the launch
 // holds the first (lo >= 0) and the last (lo + G <= n_heads) q head of that kv head's group.
