@@ -14,7 +14,10 @@ time of the whole step (permutes included). Prints ONE JSON line.
 The UPipe workload (--workload upipe_256k) times the headwise-chunked schedule instead:
 attn_fwd_chunked then attn_bwd_chunked (--forward-only: the forward alone) with
 --heads-per-chunk q heads per chunk, and reports the workspace bytes beside the unchunked
-intermediates.
+intermediates; --unchunked runs the same share without chunking (every local head packed,
+attended and unpacked at once) for comparison. `memory` gives the intermediates' device bytes
+as torch's allocator counts them and the peak the library's calls added (none: they never
+allocate).
 
 --forward-only times the forward half alone (pack Q/K/V, forward, unpack O); --fused
 replaces the permutes and head-shard buffers by attn_fwd_shards / attn_bwd_shards, which
@@ -28,7 +31,7 @@ Besides the step, the permutes are timed cold: each permute of the step is run a
 with median, min and max; their rate against the 8 TB/s HBM peak is `permute_roofline`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                       [--heads-per-chunk U] [--forward-only [--fused]]
+                       [--heads-per-chunk U] [--unchunked] [--forward-only [--fused]]
 """
 import argparse
 import contextlib
@@ -140,6 +143,17 @@ def no_gc():
         gc.enable()
 
 
+def alloc_bytes(fn):
+    """Device bytes `fn` leaves allocated (torch's caching allocator, so the intermediates the
+    caller holds), and the peak above the starting point while it ran."""
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    r = fn()
+    torch.cuda.synchronize()
+    return r, torch.cuda.memory_allocated() - base, torch.cuda.max_memory_allocated() - base
+
+
 class Phases:
     """HIP events around every phase of every timed step, on the stream the library uses."""
 
@@ -174,16 +188,18 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
     s, Hq_l, Hkv_l, d = cfg.s, cfg.Hq_l, cfg.Hkv_l, cfg.d
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     dev = "cuda"
-    # intermediates, allocated once
-    q = torch.empty((s, Hq_l, d), dtype=dt, device=dev)
-    k = torch.empty((s, Hkv_l, d), dtype=dt, device=dev)
-    v = torch.empty_like(k)
-    o = torch.empty_like(q)
-    o_lo = U.new_o_lo(q) if cfg.dtype == "bf16" else None
+    o_lo = torch.empty((s, Hq_l, d), dtype=torch.bfloat16, device=dev) if cfg.dtype == "bf16" else None
     lse = torch.empty((Hq_l, s), dtype=torch.float32, device=dev)
-    do = torch.empty_like(q)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(U.delta_bytes(s, Hq_l), dtype=torch.uint8, device=dev)
+
+    def heads():  # the head-shard intermediates and the backward's delta, allocated once
+        ws = torch.empty(U.delta_bytes(s, Hq_l), dtype=torch.uint8, device=dev)
+        if fused:  # the shard-reading kernels need no head shards
+            return (None,) * 8 + (ws,)
+        q = torch.empty((s, Hq_l, d), dtype=dt, device=dev)
+        k = torch.empty((s, Hkv_l, d), dtype=dt, device=dev)
+        return (q, k, torch.empty_like(k), torch.empty_like(q), torch.empty_like(q), torch.empty_like(q),
+                torch.empty_like(k), torch.empty_like(k), ws)
+    (q, k, v, o, do, dq, dk, dv, ws), inter, _ = alloc_bytes(heads)
     delta = ws.view(torch.float32)[: Hq_l * s].view(Hq_l, s)
     # room for dK/dV's partial sums when the key blocks split (short sequences; none at 64K)
     dkdv_need = U.attn_bwd_dkdv_workspace_bytes(s, Hkv_l, d)
@@ -220,11 +236,15 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
         step(False)
     with no_gc():
         torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
         t0 = time.perf_counter()
         for _ in range(steps):
             step(True)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
+        call_peak = torch.cuda.max_memory_allocated() - base
+    mem = {"intermediate_bytes": int(inter), "calls_peak_alloc_bytes": int(call_peak)}
     cold = None
     if not fused:
         cold = cold_permutes({
@@ -233,7 +253,7 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
             "pack_do": lambda: U.ulysses_pack(sh["do"], rank, do),
             "unpack_grads": lambda: U.ulysses_unpack_group([dq, dk, dv], rank, [dq_sh, dk_sh, dv_sh]),
         })
-    return (wall,) + ph.summary(steps) + (cold,)
+    return (wall,) + ph.summary(steps) + (cold, mem)
 
 
 def cold_permutes(calls, reps=7):
@@ -263,15 +283,19 @@ def run_forward_share(cfg, steps, warmup, cu_dev, fused):
     rank = 0
     s, Hq_l, Hkv_l, d = cfg.s, cfg.Hq_l, cfg.Hkv_l, cfg.d
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    q = torch.empty((s, Hq_l, d), dtype=dt, device="cuda")
-    k = torch.empty((s, Hkv_l, d), dtype=dt, device="cuda")
-    v = torch.empty_like(k)
-    o = torch.empty_like(q)
-    lse = torch.empty((Hq_l, s), dtype=torch.float32, device="cuda")
     o_sh = [torch.empty_like(t) for t in sh["q"]]
+    lse = torch.empty((Hq_l, s), dtype=torch.float32, device="cuda")
+
+    def heads():  # the head-shard intermediates of the unchunked forward (not needed fused)
+        if fused:
+            return None, None, None, None
+        q = torch.empty((s, Hq_l, d), dtype=dt, device="cuda")
+        k = torch.empty((s, Hkv_l, d), dtype=dt, device="cuda")
+        return q, k, torch.empty_like(k), torch.empty_like(q)
+    (q, k, v, o), inter, _ = alloc_bytes(heads)
     ph = Phases()
 
-    o_lo = U.new_o_lo(q) if cfg.dtype == "bf16" else None
+    o_lo = torch.empty((s, Hq_l, d), dtype=torch.bfloat16, device="cuda") if cfg.dtype == "bf16" else None
 
     def step(rec):
         if fused:
@@ -287,12 +311,15 @@ def run_forward_share(cfg, steps, warmup, cu_dev, fused):
         step(False)
     with no_gc():
         torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
         t0 = time.perf_counter()
         for _ in range(steps):
             step(True)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
-    return (wall,) + ph.summary(steps)
+        call_peak = torch.cuda.max_memory_allocated() - base
+    return (wall,) + ph.summary(steps) + ({"intermediate_bytes": int(inter), "calls_peak_alloc_bytes": int(call_peak)},)
 
 
 def run_upipe(cfg, steps, warmup, u, forward_only):
@@ -315,6 +342,8 @@ def run_upipe(cfg, steps, warmup, u, forward_only):
         for i in range(warmup + steps):
             if i == warmup:
                 torch.cuda.synchronize()
+                torch.cuda.reset_peak_memory_stats()
+                base = torch.cuda.memory_allocated()
                 t0 = time.perf_counter()
             ph.run("attn_fwd_chunked", lambda: U.attn_fwd_chunked(sh["q"], sh["k"], sh["v"], o_sh, 0, u, cfg.scale,
                                                                   cfg.causal, None, ws, lse, o_lo=o_lo), i >= warmup)
@@ -324,6 +353,7 @@ def run_upipe(cfg, steps, warmup, u, forward_only):
                                                                       cfg.causal, None, ws, o_lo=o_lo), i >= warmup)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
+        need["calls_peak_alloc_bytes"] = int(torch.cuda.max_memory_allocated() - base)
     return (wall,) + ph.summary(steps) + (need,)
 
 
@@ -396,6 +426,9 @@ def main():
     ap.add_argument("--heads-per-chunk", type=int, default=1)
     ap.add_argument("--forward-only", action="store_true",
                     help="time the forward half of the path alone (UPipe workload: the chunked forward)")
+    ap.add_argument("--unchunked", action="store_true",
+                    help="UPipe workload: the same share without chunking (pack, attention and unpack of every "
+                         "local head at once), for comparison")
     ap.add_argument("--fused", action="store_true",
                     help="attn_fwd_shards / attn_bwd_shards, reading and writing the sequence shards directly "
                          "(no head-shard buffers, no separate permutes)")
@@ -405,8 +438,8 @@ def main():
                          "its FETCH_SIZE/WRITE_SIZE counters scale the traffic of other kernels")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the layer on one GPU; runs on more than one GPU are "
-              "not part of this build (the P ranks are simulated as buffers on one device).", file=sys.stderr)
+        print("bench.py measures one GPU's share of the layer and runs on one GPU only (the P ranks are "
+              "simulated as buffers on one device).", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -426,17 +459,17 @@ def main():
     pairs = counted_pairs(cfg, cu)
     d, Hq_l, Hkv_l, e = cfg.d, cfg.Hq_l, cfg.Hkv_l, cfg.esize
 
-    chunked = bool(cfg.chunk_heads)
-    cold = None
+    chunked = bool(cfg.chunk_heads) and not args.unchunked
+    cold = mem = None
     if not chunked and args.forward_only:
-        wall, ph, spread = run_forward_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
+        wall, ph, spread, mem = run_forward_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
         fw = 4.0 * d * pairs * Hq_l
         kern = {"attn_fwd": ("mfma", fw), "attn_fwd_shards": ("mfma", fw),
                 "pack_qkv": ("hbm", 2.0 * cfg.s * (Hq_l + 2 * Hkv_l) * d * e),
                 "unpack_o": ("hbm", 2.0 * cfg.s * Hq_l * d * e)}
         flops = fw
     elif not chunked:
-        wall, ph, spread, cold = run_training_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
+        wall, ph, spread, cold, mem = run_training_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
         flops = 14.0 * d * pairs * Hq_l
         kern = training_work(cfg, pairs)
     else:
@@ -473,8 +506,8 @@ def main():
     value = flops / wall / 1e12
     out = {
         "metric": METRIC if args.workload == "qwen_64k" and not (args.forward_only or args.fused) else
-        f"{METRIC} [workload {args.workload}{', forward only' if args.forward_only else ''}"
-        f"{', fused exchange' if args.fused else ''}]",
+        f"{METRIC} [workload {args.workload}{', unchunked' if args.unchunked else ''}"
+        f"{', forward only' if args.forward_only else ''}{', fused exchange' if args.fused else ''}]",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -490,8 +523,11 @@ def main():
             "workload": {"qwen_64k": "Qwen3-4B-shaped SP=4 rank share at 65536 tokens",
                          "qwen_8k": "Qwen3-4B-shaped SP=4 rank share at 8192 tokens",
                          "packed_96k": "packed SFT batch at 98304 tokens (documents ~ geometric, mean 6000)",
-                         "upipe_256k": f"UPipe headwise-chunked {'forward' if args.forward_only else 'forward+backward'}, "
-                                       f"32B-shaped SP=8 share at 262144 tokens, {args.heads_per_chunk} q heads per chunk",
+                         "upipe_256k": (f"UPipe headwise-chunked {'forward' if args.forward_only else 'forward+backward'}, "
+                                        f"32B-shaped SP=8 share at 262144 tokens, {args.heads_per_chunk} q heads per "
+                                        "chunk") if chunked else
+                         (f"unchunked {'forward' if args.forward_only else 'forward+backward'} of the 32B-shaped "
+                          "SP=8 share at 262144 tokens (every local head at once)"),
                          "tiny_f32": "tiny fp32 case"}[args.workload],
             "seq_len": cfg.s, "ranks_simulated": cfg.P, "rank": 0, "q_heads": Hq_l, "kv_heads": Hkv_l,
             "head_dim": d, "causal": cfg.causal, "packed_docs": None if cu is None else int(len(cu) - 1),
@@ -516,12 +552,18 @@ def main():
             "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": cold_bytes, "ms": round(cold_ms, 4),
             "how": "each permute of the step alone after a 512 MiB cache-evicting write, 7 runs, medians",
             "phases": {k: {m: round(x, 4) for m, x in v.items()} for k, v in cold.items()}}
+    if mem is not None:
+        # device memory of the share's intermediates (head shards, delta), measured with torch's
+        # allocator, and the peak the library's calls added (they allocate nothing)
+        out["memory"] = mem
     if chunked:
         # peak intermediate bytes: the chunked calls' workspaces (the chunks read the shards, so
         # the forward needs none and the backward delta and fp32 dK/dV sums), and the buffers a
         # multi-GPU all-to-all would have to deliver -- staged per chunk (Q/O of u heads, K/V of
         # their kv heads) against unchunked (every local head): the UPipe accounting
-        out["workspace_bytes"] = ws_bytes
+        out["memory"] = {"workspace_bytes": int(max(v for k, v in ws_bytes.items() if k != "calls_peak_alloc_bytes")),
+                         "calls_peak_alloc_bytes": ws_bytes["calls_peak_alloc_bytes"]}
+        out["workspace_bytes"] = {k: v for k, v in ws_bytes.items() if k != "calls_peak_alloc_bytes"}
         u = min(args.heads_per_chunk, Hq_l)
         span = max((min(c0 + u, Hq_l) - 1) // cfg.G - c0 // cfg.G + 1 for c0 in range(0, Hq_l, u))
         staged = 2 * cfg.s * u * d * e + 2 * cfg.s * span * d * e
