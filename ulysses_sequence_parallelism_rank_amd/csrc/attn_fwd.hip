@@ -158,6 +158,7 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void attn_fwd_kernel(AttnArg
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m = -INFINITY, l = 0.f, lr = 0.f;  // running max (log2 units), sums of fp32 / rounded weights
+  float nms = 0.f;  // the exponent offset -m, 0 while m is -inf (kept beside m, set when m moves)
   // mask S of the 32 keys from k0, then rescale O if the row max grew by more than kTau
   auto mask_rescale = [&](int64_t k0, f32x16& S) {
     if (!half_full(k0)) {
@@ -167,15 +168,18 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void attn_fwd_kernel(AttnArg
         if (key < lo || key >= hi) S[jj] = -INFINITY;
       }
     }
+    // the NaN-propagating maximum (v_maximum3_f32, three values per instruction): unlike fmaxf
+    // it needs no quieting of the MFMA results first
     float mx = S[0];
 #pragma unroll
-    for (int jj = 1; jj < 16; ++jj) mx = fmaxf(mx, S[jj]);
+    for (int jj = 1; jj < 16; ++jj) mx = __builtin_elementwise_maximum(mx, S[jj]);
     const float tmax = half_swap_max(mx) * c;
     const bool need = tmax > m + kTau;
     if (__ballot(need) != 0) {  // wave-uniform
       const float mnew = need ? tmax : m;
       const float alpha = need ? fast_exp2(m - mnew) : 1.f;
       m = mnew;
+      nms = need ? -tmax : nms;  // a row whose max moved has a finite one
       l *= alpha;
       lr *= alpha;
 #pragma unroll
@@ -183,11 +187,11 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void attn_fwd_kernel(AttnArg
     }
   };
   auto softmax = [&](f32x16& S, bf16x8 (&pf)[2]) {
-    const float ms = m == -INFINITY ? 0.f : m;
-    float ls = 0.f;
+    S[0] = fast_exp2(__builtin_fmaf(S[0], c, nms));
+    float ls = S[0];  // the weights are >= +0: starting the sum at the first one is exact
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const float pj = fast_exp2(__builtin_fmaf(S[jj], c, -ms));
+    for (int jj = 1; jj < 16; ++jj) {
+      const float pj = fast_exp2(__builtin_fmaf(S[jj], c, nms));
       S[jj] = pj;
       ls += pj;
     }

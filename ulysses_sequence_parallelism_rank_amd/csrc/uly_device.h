@@ -49,7 +49,7 @@ __device__ __forceinline__ void half_swap(float x, float& a, float& b) {
 __device__ __forceinline__ float half_swap_max(float x) {
   float a, b;
   half_swap(x, a, b);
-  return fmaxf(a, b);
+  return __builtin_elementwise_maximum(a, b);  // NaN-propagating: no quieting of a and b first
 }
 __device__ __forceinline__ float half_swap_sum(float x) {
   float a, b;
