@@ -340,6 +340,9 @@ struct DkvSplitCfg {
   static constexpr int BNK = 128, BMQ = 64, NW = 8;
   static constexpr int DT = D / 16, DB = D / 32;
 };
+// k-step of part A at which the dS waves issue the next tile's DMA (it must land by the barrier
+// that ends part A: issued later than this, its latency shows there)
+constexpr int kDkvDmaAt = 2;
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Shards q_sh, Shards g_sh, Shards k_sh,
@@ -478,7 +481,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
     __syncthreads();  // tile `step` has landed; every wave is done with tile step-1 and with P
     const int nxt_h = cur_h + 1 == GH ? 0 : cur_h + 1;
     const int nxt_t = cur_h + 1 == GH ? cur_t + 1 : cur_t;
-    if (role == 1 && step + 1 < nsteps) issue_tile(nxt_t, nxt_h, nbuf);
+    const bool issue_next = role == 1 && step + 1 < nsteps;  // the next tile's DMA (in part A)
     const int32_t qrel0 = (int32_t)tile_row0(cur_t) - rlo + 4 * hf;
     cur_t = nxt_t;
     cur_h = nxt_h;
@@ -502,6 +505,11 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         if (t + 1 < DT) ld(t + 1, ring[(t + 1) & 1]);
+        // the dS waves request the next tile after their first kDkvDmaAt k-steps: issued at the
+        // step's start, the DMA instructions held up the wave's first products
+        if constexpr (r == 1) {
+          if (t == kDkvDmaAt && issue_next) issue_tile(nxt_t, nxt_h, nbuf);
+        }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) x[qb] = mfma32x32x16(ring[t & 1][qb], kv[t], t == 0 ? f32x16{} : x[qb]);
         __builtin_amdgcn_sched_barrier(0);
