@@ -411,10 +411,22 @@ def cpu_baseline(cfg):
     dt = time.perf_counter() - t0
     flops = 14.0 * cfg.d * prefix * prefix / 2
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    # the permute oracle (a Python loop over rows and heads) on the Q pack of rank 0, the first
+    # rows of each shard, as the algorithmic bytes it moves per second
+    from oracle import permute as OP
+    rows = min(cfg.s_l, 4096)
+    shards = [W.gen_rows(cfg, "q", p * cfg.s_l, p * cfg.s_l + rows) for p in range(cfg.P)]
+    t1 = time.perf_counter()
+    y = OP.pack(shards, 0)
+    dtp = time.perf_counter() - t1
+    moved = 2 * y.nbytes
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
             "cpu_model": cpu_model(), "blas_threads": int(threads), "kind": "oracle",
             "sample": f"numpy fp64 oracle, causal fwd+bwd of 1 q head (+ its kv head) over the first {prefix} "
-                      f"tokens, d={cfg.d}; {dt:.1f} s; FLOPs counted as in the metric"}
+                      f"tokens, d={cfg.d}; {dt:.1f} s; FLOPs counted as in the metric",
+            "permute": {"value": round(moved / dtp / 1e9, 4), "unit": "GB/s", "kind": "oracle",
+                        "sample": f"oracle pack of Q for rank 0 from the first {rows} rows of each of the {cfg.P} "
+                                  f"shards ({moved / 2**20:.1f} MiB read + written, one thread); {dtp:.2f} s"}}
 
 
 def main():
