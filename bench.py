@@ -549,6 +549,7 @@ def main():
         "mfma_frac_of_step": round(value / PEAK_BF16_TFLOPS, 4),
         "attention_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2) if attn_ms else None,
         "permute_gbs": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1) if perm_ms else None,
+        "permute_frac_of_step": round(perm_ms / step_ms, 4) if perm_ms and step_ms else None,
         "phase_ms": {k: round(v, 4) for k, v in ph.items()},
         "phase_ms_median": {k: round(v["median"], 4) for k, v in spread.items()},
         "phase_ms_min": {k: round(v["min"], 4) for k, v in spread.items()},
