@@ -229,3 +229,29 @@ def test_forward_key_tile_sizes_agree(d, causal, cu):
     wo, wl = OA.forward(f["q"][:, :8], f["k"][:, :2], f["v"][:, :2], scale, causal, cu)
     compare("O", dev_to_f64(o8), wo, bf16=True)
     compare("LSE", l8.cpu().numpy(), wl, max_abs=LSE_ABS, rel_fro=1e-4)
+
+
+@pytest.mark.parametrize("cu", [
+    [0, 37, 1200, 1201, 1900, 3000, 3001, 4096],            # key blocks launched longest first
+    [int(x) for x in np.linspace(0, 4096, 71).round()],      # 70 documents: launched in order
+])
+def test_packed_dkdv_unsplit_matches_oracle(cu):
+    """dK/dV with one workgroup per key block (no split): a causal packed sequence of at most 64
+    documents launches its key blocks longest first, so every block must still be visited
+    exactly once. Every element is compared; the outputs start as NaN, so a block never
+    visited fails."""
+    s, Hq, Hkv, d = 4096, 4, 2, 64
+    print(f"case packed unsplit dK/dV s={s} docs={len(cu) - 1}", flush=True)
+    f, g = _inputs(s, Hq, Hkv, d, "bf16", seed=11)
+    scale = 1.0 / np.sqrt(d)
+    cu_dev = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    o_lo = U.new_o_lo(g["q"])
+    o, lse = U.attn_fwd(g["q"], g["k"], g["v"], scale, True, cu_dev, o_lo=o_lo)
+    delta = U.attn_bwd_preprocess(o, g["do"], o_lo=o_lo)
+    dk = torch.full_like(g["k"], float("nan"))
+    dv = torch.full_like(g["v"], float("nan"))
+    U.attn_bwd_dkdv(g["q"], g["k"], g["v"], lse, g["do"], delta, scale, True, cu_dev, dk=dk, dv=dv, split=False)
+    torch.cuda.synchronize()
+    _, wk, wv = OA.backward(f["q"], f["k"], f["v"], f["do"], scale, True, cu)
+    compare("dK", dev_to_f64(dk), wk, bf16=True)
+    compare("dV", dev_to_f64(dv), wv, bf16=True)

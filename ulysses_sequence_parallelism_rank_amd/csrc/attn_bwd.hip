@@ -340,6 +340,54 @@ struct DkvSplitCfg {
   static constexpr int BNK = 128, BMQ = 64, NW = 8;
   static constexpr int DT = D / 16, DB = D / 32;
 };
+// Launch order of the key blocks of a causal packed sequence (at most 64 documents): longest
+// first, i.e. by decreasing count of query tiles, ties by position, so that the blocks at the
+// start of a long document do not wait behind the short blocks before it. A block whose last
+// key lies in document d (blocks floor(cu[d]/128) .. floor(cu[d+1]/128) - 1) sees the query
+// tiles from its own first row to the document's end E_d: A_d - 2 kb of them, A_d = ceil(E_d/64).
+// Every wave finds the block of rank r itself: lane d holds document d, a binary search over the
+// tile count t on C(t) = #{blocks with at least t tiles} (a wave-wide sum) finds the count of
+// rank r, and the block is the (r - C(t+1))-th document, in order, with a block of exactly t
+// tiles (at most one per document). Bitwise-neutral: only the order of the workgroups changes.
+__device__ int lpt_key_block(const int32_t* cu, int n_docs, int s, int nkb, int r) {
+  const int lane = threadIdx.x & 63;
+  const bool on = lane < n_docs;
+  const int c0 = on ? cu[lane] : s, c1 = on ? cu[lane + 1] : s;
+  const int a0 = c0 >= s ? nkb : c0 / 128;      // first block of the document
+  const int b1 = (c1 >= s ? nkb : c1 / 128) - 1;  // last block of the document
+  const int e = c1 < s ? c1 : s;
+  const int A = (e + 63) / 64;
+  auto count = [&](int t) {  // blocks of this lane's document with at least t tiles
+    if (!on || b1 < a0 || A < t) return 0;
+    const int hi = (A - t) / 2 < b1 ? (A - t) / 2 : b1;
+    return hi >= a0 ? hi - a0 + 1 : 0;
+  };
+  auto wsum = [](int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+  };
+  int tmax = on ? A : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int u = __shfl_xor(tmax, o);
+    tmax = u > tmax ? u : tmax;
+  }
+  int lo = 1, hi = tmax + 1;  // C(lo) > r >= C(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (wsum(count(mid)) > r) lo = mid;
+    else hi = mid;
+  }
+  int m = r - wsum(count(lo + 1));
+  const int kbd = (A - lo) / 2;
+  const bool has = on && A >= lo && ((A - lo) & 1) == 0 && kbd >= a0 && kbd <= b1;
+  uint64_t mask = __ballot(has);
+  for (; m > 0; --m) mask &= mask - 1;
+  // the same on every lane: made wave-uniform, so what derives from it stays in scalar registers
+  return __builtin_amdgcn_readfirstlane(__shfl(kbd, __builtin_ctzll(mask)));
+}
+
 // k-step of part A at which the dS waves issue the next tile's DMA (it must land by the barrier
 // that ends part A: issued later than this, its latency shows there)
 constexpr int kDkvDmaAt = 2;
@@ -373,8 +421,10 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_split_kernel(AttnArgs a, Sha
   const int64_t s = a.s;
   const int kvh = blockIdx.x % a.n_kv;
   const int sp = (int)((blockIdx.x / a.n_kv) % a.nsplit);                 // split of the key block
-  const int64_t kb = (int64_t)(blockIdx.x / a.n_kv) / a.nsplit;
-  const int64_t n0 = kb * BNK;  // earliest keys (most rows) first
+  int64_t kb = (int64_t)(blockIdx.x / a.n_kv) / a.nsplit;  // earliest keys (most rows) first
+  if (a.cu != nullptr && a.causal && a.nsplit == 1 && a.n_docs <= 64)
+    kb = lpt_key_block(a.cu, a.n_docs, (int)s, (int)((s + BNK - 1) / BNK), (int)kb);
+  const int64_t n0 = kb * BNK;
   const float c = a.scale * kLog2e;
 
   // this lane's key, the rows that may see it [rlo, rhi), and its K (role 0) or V row
