@@ -383,9 +383,10 @@ __device__ int lpt_key_block(const int32_t* cu, int n_docs, int s, int nkb, int 
   const int kbd = (A - lo) / 2;
   const bool has = on && A >= lo && ((A - lo) & 1) == 0 && kbd >= a0 && kbd <= b1;
   uint64_t mask = __ballot(has);
-  for (; m > 0; --m) mask &= mask - 1;
-  // the same on every lane: made wave-uniform, so what derives from it stays in scalar registers
-  return __builtin_amdgcn_readfirstlane(__shfl(kbd, __builtin_ctzll(mask)));
+  for (; m > 0 && mask != 0; --m) mask &= mask - 1;
+  const int res = mask != 0 ? __shfl(kbd, __builtin_ctzll(mask)) : -1;
+  // a block in range whatever cu holds, made wave-uniform (what derives from it stays scalar)
+  return __builtin_amdgcn_readfirstlane(res >= 0 && res < nkb ? res : r);
 }
 
 // k-step of part A at which the dS waves issue the next tile's DMA (it must land by the barrier
