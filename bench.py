@@ -201,9 +201,10 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
                 torch.empty_like(k), torch.empty_like(k), ws)
     (q, k, v, o, do, dq, dk, dv, ws), inter, _ = alloc_bytes(heads)
     delta = ws.view(torch.float32)[: Hq_l * s].view(Hq_l, s)
-    # room for dK/dV's partial sums when the key blocks split (short sequences; none at 64K)
-    dkdv_need = U.attn_bwd_dkdv_workspace_bytes(s, Hkv_l, d)
-    dkdv_ws = torch.empty(dkdv_need, dtype=torch.uint8, device=dev) if dkdv_need else None
+    # room for the partial sums of dK/dV's split key blocks and of dQ's split row blocks (short
+    # sequences only; none at 64K); the two phases run in turn on one stream and share it
+    part_need = max(U.attn_bwd_dkdv_workspace_bytes(s, Hkv_l, d), U.attn_bwd_dq_workspace_bytes(s, Hq_l, d))
+    part_ws = torch.empty(part_need, dtype=torch.uint8, device=dev) if part_need else None
     o_sh = [torch.empty_like(t) for t in sh["q"]]
     dq_sh = [torch.empty_like(t) for t in sh["q"]]
     dk_sh = [torch.empty_like(t) for t in sh["k"]]
@@ -227,9 +228,9 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
         ph.run("pack_do", lambda: U.ulysses_pack(sh["do"], rank, do), rec)
         ph.run("bwd_preprocess", lambda: U.attn_bwd_preprocess(o, do, delta, o_lo=o_lo), rec)
         ph.run("bwd_dkdv", lambda: U.attn_bwd_dkdv(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev,
-                                                   dk=dk, dv=dv, workspace=dkdv_ws), rec)
-        ph.run("bwd_dq", lambda: U.attn_bwd_dq(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev, dq=dq),
-               rec)
+                                                   dk=dk, dv=dv, workspace=part_ws), rec)
+        ph.run("bwd_dq", lambda: U.attn_bwd_dq(q, k, v, lse, do, delta, cfg.scale, cfg.causal, cu_dev, dq=dq,
+                                               workspace=part_ws), rec)
         ph.run("unpack_grads", lambda: U.ulysses_unpack_group([dq, dk, dv], rank, [dq_sh, dk_sh, dv_sh]), rec)
 
     for _ in range(warmup):

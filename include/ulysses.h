@@ -176,9 +176,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_lo, f
  *   o_lo  : the residual attn_fwd wrote, or NULL (delta then from the bf16 o)
  *   dq [s, Hq, d], dk, dv [s, Hkv, d] : device `dtype`, written (fully overwritten)
  *   workspace : device scratch of attn_bwd_workspace_bytes(s, Hq, Hkv, d) bytes: delta
- *               [Hq, s] fp32 (rounded up to 256 bytes; required) followed by room for the dK/dV
- *               partial sums of a split run (see attn_bwd_dkdv; optional: a workspace that
- *               holds delta only runs dK/dV unsplit).
+ *               [Hq, s] fp32 (rounded up to 256 bytes; required) followed by room for the
+ *               partial sums of a split run (attn_bwd_dkdv's, then attn_bwd_dq's in the same
+ *               bytes; optional: a workspace that holds delta only runs both unsplit).
  *               If workspace == NULL the call only stores that size into
  *               *workspace_bytes and returns ULY_OK. Otherwise *workspace_bytes (if
  *               workspace_bytes != NULL) is the capacity and is checked.
@@ -195,9 +195,10 @@ size_t attn_bwd_workspace_bytes(int64_t s, int Hq, int Hkv, int d);
 /* ---------------------------------------------------------------------------
  * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
- * arguments without the workspace, and the same kernels (dK/dV unsplit), so the results are
- * bitwise those of attn_bwd wherever attn_bwd runs them unsplit (at least 256 key blocks x kv
- * heads, i.e. s * Hkv >= 32768). delta lives in a static device array of ULY_NOALLOC_MAX_DELTA floats
+ * arguments without the workspace, and the same kernels (dK/dV and dQ unsplit), so the
+ * results are bitwise those of attn_bwd wherever attn_bwd runs both unsplit (at least 256 key
+ * blocks x kv heads, i.e. s * Hkv >= 32768, and more than 512 row blocks x q heads, i.e.
+ * ceil(s / 128) * Hq > 512). delta lives in a static device array of ULY_NOALLOC_MAX_DELTA floats
  * (16 MiB) that each GPU the library runs on holds until the process ends; the call
  * allocates nothing. s * Hq above ULY_NOALLOC_MAX_DELTA -> ULY_ERR_WORKSPACE; the array's
  * address not obtainable -> ULY_ERR_HIP. Every call on one GPU uses that GPU's one array:
@@ -229,11 +230,20 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                   int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
                   const int32_t* cu_seqlens, int n_docs, void* workspace, size_t workspace_bytes,
                   void* stream);
-/* dq for every row: loops over the visible keys.                                   */
+/* dq for every row: loops over the visible keys. A workgroup holds 128 rows of one q head,
+ * two share a CU; when at most 512 such workgroups would run (short sequences: the longest row
+ * block, which sees every key, then sets the time) and a workspace of
+ * attn_bwd_dq_workspace_bytes(s, Hq, d) bytes is given (bf16), each row block's key tiles are
+ * split over up to 8 workgroups (aiming at 1024) that store fp32 partial sums, and a second
+ * kernel adds them in split order, scales and rounds once: deterministic; the sums' order,
+ * and so the last bits, differ from the unsplit run. The size is 0 when no split applies;
+ * workspace NULL runs unsplit.                                                        */
+size_t attn_bwd_dq_workspace_bytes(int64_t s, int Hq, int d);
 int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                 const void* dout, const float* delta, void* dq,
                 int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
-                const int32_t* cu_seqlens, int n_docs, void* stream);
+                const int32_t* cu_seqlens, int n_docs, void* workspace, size_t workspace_bytes,
+                void* stream);
 
 /* ---------------------------------------------------------------------------
  * attn_fwd_chunked -- the UPipe headwise-chunked forward of rank `rank` (tilnote.io

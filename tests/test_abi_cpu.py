@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = U.lib()
-    assert L.uly_abi_version() == 4
+    assert L.uly_abi_version() == 5
     for code, name in U.STATUS.items():
         assert L.uly_status_string(code).decode() == name
 
@@ -152,7 +152,8 @@ def test_bwd_workspace_query_and_checks():
     assert L.attn_bwd(*zl, 1000, 8, 2, 128, 0, 0.1, 1, None, 0, None, ctypes.byref(need), None) == 4
     assert L.attn_bwd_dkdv(*[FAKE] * 8, 10, 4, 3, 128, 0, 0.1, 1, None, 0, None, 0, None) == 2
     assert L.attn_bwd_dkdv(*[FAKE] * 8, 10, 4, 2, 128, 0, 0.1, 1, None, 0, MIS, 1 << 20, None) == 4
-    assert L.attn_bwd_dq(*[FAKE] * 7, 10, 4, 2, 100, 0, 0.1, 1, None, 0, None) == 3
+    assert L.attn_bwd_dq(*[FAKE] * 7, 10, 4, 2, 100, 0, 0.1, 1, None, 0, None, 0, None) == 3
+    assert L.attn_bwd_dq(*[FAKE] * 7, 10, 4, 2, 128, 0, 0.1, 1, None, 0, MIS, 1 << 20, None) == 4
 
 
 def test_chunked_workspace_matches_upipe_accounting():
@@ -355,3 +356,23 @@ def test_dkdv_split_accounting():
     delta = U.delta_bytes(8192, 8)
     assert L.attn_bwd_workspace_bytes(8192, 8, 2, 128) == delta + 64 * MiB
     assert L.attn_bwd_workspace_bytes(65536, 8, 2, 128) == U.delta_bytes(65536, 8)
+
+
+def test_dq_split_accounting():
+    """dQ row blocks split while at most 512 workgroups (128 rows x q head) would run, aiming at
+    1024, at most 8 per block: 8K share (8 q heads) -> 2 splits, 64 MiB of fp32 partials, the
+    same bytes the dK/dV split needs, so attn_bwd's workspace is delta + their maximum; 64K
+    share -> none."""
+    L = U.lib()
+    MiB = 2 ** 20
+    assert L.attn_bwd_dq_workspace_bytes(8192, 8, 128) == 8 * 64 * 2 * 128 * 128 * 4 == 64 * MiB
+    assert L.attn_bwd_dq_workspace_bytes(65536, 8, 128) == 0
+    assert L.attn_bwd_dq_workspace_bytes(8192, 16, 128) == 0         # 1024 workgroups: full
+    assert L.attn_bwd_dq_workspace_bytes(4096, 8, 64) == 8 * 32 * 4 * 128 * 64 * 4   # 256 -> 4 splits
+    assert L.attn_bwd_dq_workspace_bytes(128, 1, 64) == 1 * 1 * 8 * 128 * 64 * 4     # capped at 8
+    assert L.attn_bwd_dq_workspace_bytes(0, 8, 128) == 0
+    # 4K, 8 q heads, 1 kv head: dQ needs 4 splits of 32 x 8 blocks, dK/dV 8 of 32 x 1
+    delta = U.delta_bytes(4096, 8)
+    dq_part = 8 * 32 * 4 * 128 * 128 * 4
+    dkdv_part = 1 * 32 * 8 * 2 * 128 * 128 * 4
+    assert L.attn_bwd_workspace_bytes(4096, 8, 1, 128) == delta + max(dq_part, dkdv_part)

@@ -255,3 +255,35 @@ def test_packed_dkdv_unsplit_matches_oracle(cu):
     _, wk, wv = OA.backward(f["q"], f["k"], f["v"], f["do"], scale, True, cu)
     compare("dK", dev_to_f64(dk), wk, bf16=True)
     compare("dV", dev_to_f64(dv), wv, bf16=True)
+
+
+@pytest.mark.parametrize("s,Hq,Hkv,d,causal,cu", [
+    (128, 1, 1, 64, True, None),                                   # 8 splits of 2 key tiles: 6 empty
+    (1800, 4, 2, 128, True, [0, 1, 2, 333, 334, 1000, 1799, 1800]),  # 8 splits, packed, ragged tail
+    (3000, 8, 2, 64, False, None),                                 # 6 uneven splits of 47 tiles
+    (4096, 8, 2, 128, True, None),                                 # 4 splits
+])
+def test_dq_split_matches_oracle(s, Hq, Hkv, d, causal, cu):
+    """dQ with each 128-row block's key tiles split over several workgroups (grids of at most
+    512 workgroups) and the fp32 partials summed in split order by a second kernel: every
+    element against the oracle, next to the unsplit run. dQ starts as NaN, so a row the reduce
+    never writes fails."""
+    ns_bytes = U.attn_bwd_dq_workspace_bytes(s, Hq, d)
+    assert ns_bytes > 0
+    print(f"case split dQ s={s} Hq={Hq} d={d} causal={causal} docs={None if cu is None else len(cu) - 1}",
+          flush=True)
+    f, g = _inputs(s, Hq, Hkv, d, "bf16", seed=s + d)
+    scale = 1.0 / np.sqrt(d)
+    cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    o_lo = U.new_o_lo(g["q"])
+    o, lse = U.attn_fwd(g["q"], g["k"], g["v"], scale, causal, cu_dev, o_lo=o_lo)
+    delta = U.attn_bwd_preprocess(o, g["do"], o_lo=o_lo)
+    dq = torch.full_like(g["q"], float("nan"))
+    dq1 = torch.full_like(g["q"], float("nan"))
+    ws = torch.full((ns_bytes,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN partials if unwritten
+    U.attn_bwd_dq(g["q"], g["k"], g["v"], lse, g["do"], delta, scale, causal, cu_dev, dq=dq, workspace=ws)
+    U.attn_bwd_dq(g["q"], g["k"], g["v"], lse, g["do"], delta, scale, causal, cu_dev, dq=dq1, split=False)
+    torch.cuda.synchronize()
+    wq, _, _ = OA.backward(f["q"], f["k"], f["v"], f["do"], scale, causal, cu, kv_cols=np.zeros(0, int))
+    compare("dQ split", dev_to_f64(dq), wq, bf16=True)
+    compare("dQ unsplit", dev_to_f64(dq1), wq, bf16=True)

@@ -65,7 +65,8 @@ SIGNATURES = {
     "attn_bwd_dkdv": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
                              _vp, _i32, _vp, _sz, _vp]),
     "attn_bwd_dq": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
-                           _vp, _i32, _vp]),
+                           _vp, _i32, _vp, _sz, _vp]),
+    "attn_bwd_dq_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "attn_fwd_chunked": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                 _i32, _vp, _i32, _i32, _vp, _szp, _vp]),
     "attn_fwd_chunked_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
@@ -337,6 +338,10 @@ def attn_bwd_dkdv_workspace_bytes(s, Hkv, d):
     return int(lib().attn_bwd_dkdv_workspace_bytes(s, Hkv, d))
 
 
+def attn_bwd_dq_workspace_bytes(s, Hq, d):
+    return int(lib().attn_bwd_dq_workspace_bytes(s, Hq, d))
+
+
 def delta_bytes(s, Hq):
     """Bytes of delta [Hq, s] fp32 rounded up to 256 (the shard-reading backward's workspace)."""
     return (s * Hq * 4 + 255) // 256 * 256
@@ -346,7 +351,7 @@ def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=True, cu_seqlens=None, wo
              dq=None, dk=None, dv=None, o_lo=None, split=True):
     """Gradients (dq, dk, dv) of the attention forward, given its o and lse and dout (and the
     forward's o_lo, if it wrote one: delta then comes from O to about 16 bits). split=False
-    allocates room for delta only, so dK/dV run unsplit on short sequences too."""
+    allocates room for delta only, so dK/dV and dQ run unsplit on short sequences too."""
     s, Hq, Hkv, d = _qkv(q, k, v)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -432,14 +437,23 @@ def attn_bwd_dkdv(q, k, v, lse, dout, delta, scale=None, causal=True, cu_seqlens
     return dk, dv
 
 
-def attn_bwd_dq(q, k, v, lse, dout, delta, scale=None, causal=True, cu_seqlens=None, dq=None):
+def attn_bwd_dq(q, k, v, lse, dout, delta, scale=None, causal=True, cu_seqlens=None, dq=None,
+                workspace=None, split=True):
+    """dQ. On short sequences each row block's keys split over several workgroups when a
+    workspace of attn_bwd_dq_workspace_bytes is given (allocated here unless split=False)."""
     s, Hq, Hkv, d = _qkv(q, k, v)
     _bwd_phase_checks(q, lse, dout, delta)
     dq = torch.empty_like(q) if dq is None else dq
     _need(dq, "dq", (s, Hq, d), q.dtype, q.device)
+    if workspace is None and split:
+        need = attn_bwd_dq_workspace_bytes(s, Hq, d)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws, cap = (None, 0) if workspace is None or not split else (_dev(workspace),
+                                                                 workspace.numel() * workspace.element_size())
     cu, nd = _cu(cu_seqlens, q.device)
     _call("attn_bwd_dq", _dev(q), _dev(k), _dev(v), _dev(lse), _dev(dout), _dev(delta), _dev(dq),
-          s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, _stream())
+          s, Hq, Hkv, d, _dtype(q), _default_scale(d, scale), int(causal), cu, nd, ws, cap, _stream())
     return dq
 
 

@@ -14,7 +14,7 @@ using namespace uly;
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline int esize(int dtype) { return dtype == ULY_BF16 ? 2 : 4; }
@@ -82,6 +82,7 @@ AttnArgs make_args(int64_t s, int Hq, int Hkv, int d, float scale, int causal, c
   a.acc_init = -1;
   a.acc_final = -1;
   a.nsplit = 1;
+  a.nsplit_q = 1;
   return a;
 }
 
@@ -302,9 +303,17 @@ size_t attn_bwd_dkdv_workspace_bytes(int64_t s, int Hkv, int d) {
   return dkdv_part_bytes(s, Hkv, d);
 }
 
+size_t attn_bwd_dq_workspace_bytes(int64_t s, int Hq, int d) {
+  if (s < 1 || Hq < 1 || d < 1) return 0;
+  return dq_part_bytes(s, Hq, d);
+}
+
 size_t attn_bwd_workspace_bytes(int64_t s, int Hq, int Hkv, int d) {
   if (s < 1 || Hq < 1 || Hkv < 1 || d < 1) return 0;
-  return delta_bytes(s, Hq) + round256(attn_bwd_dkdv_workspace_bytes(s, Hkv, d));
+  // the dK/dV and the dQ partial sums share one region: the dK/dV reduce has read the first
+  // before the dQ kernel, later on the same stream, writes the second
+  const size_t part = std::max(attn_bwd_dkdv_workspace_bytes(s, Hkv, d), attn_bwd_dq_workspace_bytes(s, Hq, d));
+  return delta_bytes(s, Hq) + round256(part);
 }
 
 int attn_bwd_preprocess(const void* o, const void* o_lo, const void* dout, float* delta, int64_t s, int Hq, int d,
@@ -356,12 +365,20 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
 
 int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                 const float* delta, void* dq, int64_t s, int Hq, int Hkv, int d, int dtype, float scale,
-                int causal, const int32_t* cu_seqlens, int n_docs, void* stream) {
+                int causal, const int32_t* cu_seqlens, int n_docs, void* workspace, size_t workspace_bytes,
+                void* stream) {
   int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, cu_seqlens, n_docs);
   if (st != ULY_OK) return st;
   if (!lse || !dout || !delta || !dq) return ULY_ERR_NULL;
   if (!aligned16(lse) || !aligned16(dout) || !aligned16(delta) || !aligned16(dq)) return ULY_ERR_ALIGN;
+  if (workspace != nullptr && !aligned16(workspace)) return ULY_ERR_ALIGN;
+  const size_t part = attn_bwd_dq_workspace_bytes(s, Hq, d);
+  const bool split = dtype == ULY_BF16 && part > 0 && workspace != nullptr && workspace_bytes >= part;
   AttnArgs a = make_args(s, Hq, Hkv, d, scale, causal, cu_seqlens, n_docs);
+  if (split) {  // small grid: each row block's key tiles over several workgroups, partials reduced in order
+    a.nsplit_q = dq_split_count(s, Hq);
+    a.dq_part = static_cast<float*>(workspace);
+  }
   a.q = q;
   a.k = k;
   a.v = v;
@@ -402,7 +419,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
                      static_cast<char*>(workspace) + dpart, cap - dpart, stream);
   if (st != ULY_OK) return st;
   return attn_bwd_dq(q, k, v, lse, dout, delta, dq, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens, n_docs,
-                     stream);
+                     static_cast<char*>(workspace) + dpart, cap - dpart, stream);
 }
 
 // ---- attn_bwd without a caller workspace ---------------------------------------------
@@ -441,12 +458,13 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
   float* delta = device_scratch();
   if (delta == nullptr) return ULY_ERR_HIP;
   // every element of delta the kernels read is written by the preprocess first: nothing to clear;
-  // dK/dV run unsplit (no partial sums, which would need more than the array)
+  // dK/dV and dQ run unsplit (no partial sums, which would need more than the array)
   if ((st = attn_bwd_preprocess(o, o_lo, dout, delta, s, Hq, d, dtype, stream)) != ULY_OK) return st;
   if ((st = attn_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens,
                           n_docs, nullptr, 0, stream)) != ULY_OK)
     return st;
-  return attn_bwd_dq(q, k, v, lse, dout, delta, dq, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens, n_docs, stream);
+  return attn_bwd_dq(q, k, v, lse, dout, delta, dq, s, Hq, Hkv, d, dtype, scale, causal, cu_seqlens, n_docs,
+                     nullptr, 0, stream);
 }
 
 // ---- UPipe headwise-chunked forward ------------------------------------------------

@@ -96,7 +96,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
   const int64_t s = a.s;
   const int nmb = (int)((s + BM - 1) / BM);
   const int h = blockIdx.x % a.n_heads;
-  const int mb = nmb - 1 - (int)(blockIdx.x / a.n_heads);
+  const int nsq = a.nsplit_q > 1 ? a.nsplit_q : 1;  // workgroups per row block (small grids)
+  const int sp = (int)((blockIdx.x / a.n_heads) % nsq);
+  const int mb = nmb - 1 - (int)(blockIdx.x / a.n_heads / nsq);
   const int64_t m0 = (int64_t)mb * BM;
   const int kvh = (h + a.q_off) / a.G - a.kv_off;
   // shard of the workgroup's rows (all in one); Q, dO and dQ addressed from its first row
@@ -150,6 +152,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
   }
   if (a.causal) kend = kend < last_row + 1 ? kend : last_row + 1;
   kbeg = (kbeg / BN) * BN;
+  if (nsq > 1) {  // this split's share of the block's key tiles
+    const int64_t nt = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+    const int64_t t0 = nt * sp / nsq, t1 = nt * (sp + 1) / nsq;
+    const int64_t e = kbeg + t1 * BN;
+    kend = e < kend ? e : kend;
+    kbeg += t0 * BN;
+  }
   // key k is seen by row rb of this lane iff (uint32)(k - lo[rb]) < width[rb]
   uint32_t width[RB];
 #pragma unroll
@@ -286,6 +295,19 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_dq_kernel(AttnArgs a, Sha
   }
 
   const int rb = 0;
+  if (nsq > 1) {
+    // this split's fp32 partial sums (unscaled) into its slot; the reduce kernel finishes them
+    if (row[rb] < s) {
+      float* slot = a.dq_part + (((int64_t)h * nmb + mb) * nsq + sp) * (BM * D) + (int64_t)(wave * 32 + l32) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<f32x4*>(slot + db * 32 + 8 * jj + 4 * hf) =
+              f32x4{dqacc[db][4 * jj + 0], dqacc[db][4 * jj + 1], dqacc[db][4 * jj + 2], dqacc[db][4 * jj + 3]};
+    }
+    return;
+  }
   uint16_t* dQ = static_cast<uint16_t*>(const_cast<void*>(dq_sh.p[ps])) + (int64_t)h * D - r_sh * a.q_row;
   if (a.acc_q != nullptr && row[rb] < s) {
     // sums carried across launches (Ring Attention's hops): add the previous fp32 sums unless
@@ -730,13 +752,55 @@ hipError_t launch_pre_t(const AttnArgs& a, const BwdSrc& src, hipStream_t stream
   return hipGetLastError();
 }
 
+// dQ of split row blocks: for 8 consecutive elements of one row and q head, the nsplit_q partial
+// sums in split order (from +0), scaled and rounded once, one thread each
+template <int D>
+__global__ __launch_bounds__(256) void dq_reduce_kernel(AttnArgs a, Shards dq_sh, int64_t s_l) {
+  constexpr int BM = 128, PER = D / 8;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t s = a.s, nmb = (s + BM - 1) / BM;
+  const int64_t total = (int64_t)a.n_heads * s * PER;
+  if (c >= total) return;
+  const int part8 = (int)(c % PER);
+  const int64_t row = (c / PER) % s;
+  const int h = (int)(c / PER / s);
+  const int ns = a.nsplit_q;
+  const int64_t mb = row / BM;
+  const float* src = a.dq_part + ((int64_t)h * nmb + mb) * ns * (BM * D) + (row - mb * BM) * D + part8 * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < ns; ++sp) {
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (int64_t)sp * (BM * D));
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + (int64_t)sp * (BM * D) + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += x0[e];
+      acc[4 + e] += x1[e];
+    }
+  }
+  const int p = (int)((uint32_t)row / (uint32_t)s_l);
+  uint16_t* out = static_cast<uint16_t*>(const_cast<void*>(dq_sh.p[p])) + (row - (int64_t)p * s_l) * a.q_row +
+                  (int64_t)h * D + part8 * 8;
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[2 * e] * a.scale, acc[2 * e + 1] * a.scale);
+  *reinterpret_cast<u32x4*>(out) = w;
+}
+
 template <int D, int RB, int KB>
 hipError_t launch_dq_t(const AttnArgs& a, const BwdSrc& src, hipStream_t stream) {
   using C = DqCfg<D, RB, KB>;
-  const int64_t blocks = (a.s + C::BM - 1) / C::BM * a.n_heads;
+  const int nsq = a.nsplit_q > 1 ? a.nsplit_q : 1;
+  const int64_t blocks = (a.s + C::BM - 1) / C::BM * a.n_heads * nsq;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((attn_dq_kernel<D, RB, KB>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a, src.q,
                      src.g, src.k, src.v, src.dq, src.s_l);
+  if (nsq > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t items = (int64_t)a.n_heads * a.s * (D / 8);
+    hipLaunchKernelGGL((dq_reduce_kernel<D>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a, src.dq,
+                       src.s_l);
+  }
   return hipGetLastError();
 }
 
@@ -796,6 +860,16 @@ hipError_t launch_dkdv_split_t(const AttnArgs& a, const BwdSrc& src, hipStream_t
 }
 
 }  // namespace
+
+int dq_split_count(int64_t s, int n_heads) {
+  // two four-wave workgroups per CU: while the grid is at most one round of them (512), its
+  // longest row block sets the time (twice the mean for one causal sequence); split every
+  // block's key tiles, aiming at 1024 workgroups, at most 8 per block
+  const int64_t wg = (s + 127) / 128 * n_heads;
+  if (wg > 512 || wg < 1) return 1;
+  const int64_t ns = (1024 + wg - 1) / wg;
+  return (int)(ns < 8 ? ns : 8);
+}
 
 int dkdv_split_count(int64_t s, int n_kv) {
   // one eight-wave workgroup per CU: split the key blocks' rows while the grid is under the

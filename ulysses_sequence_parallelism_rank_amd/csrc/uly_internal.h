@@ -69,9 +69,22 @@ struct AttnArgs {
   // combined with a split).
   int nsplit;
   float* dkv_part;
+  // dQ of one 128-row block split over nsplit_q workgroups (small grids): workgroup sp walks its
+  // share of the block's key tiles and stores its fp32 partial sums (unscaled, [128 rows][D]) in
+  // slot ((q head * row blocks + block) * nsplit_q + sp) of dq_part; a reduce kernel sums the
+  // slots in split order, scales and rounds. Values below 2: no split (no accumulation across
+  // launches is combined with a split).
+  int nsplit_q;
+  float* dq_part;
 };
 // dK/dV workgroups split per key block for a grid of n_kv * ceil(s/128) blocks (1 = no split)
 int dkdv_split_count(int64_t s, int n_kv);
+// dQ workgroups split per row block for a grid of n_heads * ceil(s/128) blocks (1 = no split)
+int dq_split_count(int64_t s, int n_heads);
+inline size_t dq_part_bytes(int64_t s, int n_heads, int d) {
+  const int ns = dq_split_count(s, n_heads);
+  return ns <= 1 ? 0 : (size_t)n_heads * (size_t)((s + 127) / 128) * (size_t)ns * 128 * (size_t)d * sizeof(float);
+}
 inline size_t dkdv_part_bytes(int64_t s, int n_kv, int d) {
   const int ns = dkdv_split_count(s, n_kv);
   return ns <= 1 ? 0 : (size_t)n_kv * (size_t)((s + 127) / 128) * (size_t)ns * 2 * 128 * (size_t)d * sizeof(float);
