@@ -193,18 +193,20 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
 
     def heads():  # the head-shard intermediates and the backward's delta, allocated once
         ws = torch.empty(U.delta_bytes(s, Hq_l), dtype=torch.uint8, device=dev)
-        if fused:  # the shard-reading kernels need no head shards
-            return (None,) * 8 + (ws,)
+        if fused:  # the shard-reading kernels need no head shards (and run unsplit)
+            return (None,) * 8 + (ws, None)
         q = torch.empty((s, Hq_l, d), dtype=dt, device=dev)
         k = torch.empty((s, Hkv_l, d), dtype=dt, device=dev)
+        # room for the partial results of the split runs on short sequences (none at 64K): the
+        # forward's row blocks, dK/dV's key blocks, dQ's row blocks; the three run in turn on one
+        # stream, each consuming its partials before the next starts, so they share it
+        part_need = max(U.attn_fwd_workspace_bytes(s, Hq_l, d), U.attn_bwd_dkdv_workspace_bytes(s, Hkv_l, d),
+                        U.attn_bwd_dq_workspace_bytes(s, Hq_l, d))
+        part = torch.empty(part_need, dtype=torch.uint8, device=dev) if part_need else None
         return (q, k, torch.empty_like(k), torch.empty_like(q), torch.empty_like(q), torch.empty_like(q),
-                torch.empty_like(k), torch.empty_like(k), ws)
-    (q, k, v, o, do, dq, dk, dv, ws), inter, _ = alloc_bytes(heads)
+                torch.empty_like(k), torch.empty_like(k), ws, part)
+    (q, k, v, o, do, dq, dk, dv, ws, part_ws), inter, _ = alloc_bytes(heads)
     delta = ws.view(torch.float32)[: Hq_l * s].view(Hq_l, s)
-    # room for the partial sums of dK/dV's split key blocks and of dQ's split row blocks (short
-    # sequences only; none at 64K); the two phases run in turn on one stream and share it
-    part_need = max(U.attn_bwd_dkdv_workspace_bytes(s, Hkv_l, d), U.attn_bwd_dq_workspace_bytes(s, Hq_l, d))
-    part_ws = torch.empty(part_need, dtype=torch.uint8, device=dev) if part_need else None
     o_sh = [torch.empty_like(t) for t in sh["q"]]
     dq_sh = [torch.empty_like(t) for t in sh["q"]]
     dk_sh = [torch.empty_like(t) for t in sh["k"]]
@@ -222,8 +224,8 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
         if fused:
             return step_fused(rec)
         ph.run("pack_qkv", lambda: U.ulysses_pack_group([sh["q"], sh["k"], sh["v"]], rank, [q, k, v]), rec)
-        ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse, o_lo=o_lo),
-               rec)
+        ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse, o_lo=o_lo,
+                                              workspace=part_ws), rec)
         ph.run("unpack_o", lambda: U.ulysses_unpack(o, rank, o_sh), rec)
         ph.run("pack_do", lambda: U.ulysses_pack(sh["do"], rank, do), rec)
         ph.run("bwd_preprocess", lambda: U.attn_bwd_preprocess(o, do, delta, o_lo=o_lo), rec)
@@ -289,11 +291,13 @@ def run_forward_share(cfg, steps, warmup, cu_dev, fused):
 
     def heads():  # the head-shard intermediates of the unchunked forward (not needed fused)
         if fused:
-            return None, None, None, None
+            return None, None, None, None, None
         q = torch.empty((s, Hq_l, d), dtype=dt, device="cuda")
         k = torch.empty((s, Hkv_l, d), dtype=dt, device="cuda")
-        return q, k, torch.empty_like(k), torch.empty_like(q)
-    (q, k, v, o), inter, _ = alloc_bytes(heads)
+        need = U.attn_fwd_workspace_bytes(s, Hq_l, d)  # the split forward's partials (short sequences)
+        part = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+        return q, k, torch.empty_like(k), torch.empty_like(q), part
+    (q, k, v, o, part_ws), inter, _ = alloc_bytes(heads)
     ph = Phases()
 
     o_lo = torch.empty((s, Hq_l, d), dtype=torch.bfloat16, device="cuda") if cfg.dtype == "bf16" else None
@@ -304,8 +308,8 @@ def run_forward_share(cfg, steps, warmup, cu_dev, fused):
                                                                 cfg.causal, cu_dev, lse=lse, o_lo=o_lo), rec)
             return
         ph.run("pack_qkv", lambda: U.ulysses_pack_group([sh["q"], sh["k"], sh["v"]], rank, [q, k, v]), rec)
-        ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse, o_lo=o_lo),
-               rec)
+        ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse, o_lo=o_lo,
+                                              workspace=part_ws), rec)
         ph.run("unpack_o", lambda: U.ulysses_unpack(o, rank, o_sh), rec)
 
     for _ in range(warmup):

@@ -162,11 +162,22 @@ int ulysses_recv_unpack(const void* in, int P, int64_t s_l, int H, int d, int dt
  *   causal : 1 -> key j visible to row i iff j <= i; 0 -> all keys
  *   cu_seqlens : NULL, or device int32 [n_docs + 1], 0 = cu[0] < ... < cu[n_docs] = s;
  *                keys are then further restricted to the row's own document
+ *   workspace : NULL, or device scratch (16-byte aligned, else ULY_ERR_ALIGN) of
+ *               workspace_bytes bytes. A workgroup holds 128 rows of one q head; below 768
+ *               of them (short sequences: one round in which the last row block, which sees
+ *               every key, sets the time) and given attn_fwd_workspace_bytes(s, Hq, d) bytes
+ *               (bf16), each row block's key tiles are split over up to 8 workgroups (aiming
+ *               at 1024) that store fp32 partial results (O sums, running max, weight sums),
+ *               and a second kernel merges them in split order: deterministic; the last bits
+ *               differ from the unsplit run. A smaller or NULL workspace runs unsplit. The
+ *               size is 0 where no split applies.
  * Every row must see at least one key (true whenever causal or cu_seqlens is used).
  * ------------------------------------------------------------------------- */
+size_t attn_fwd_workspace_bytes(int64_t s, int Hq, int d);
 int attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,
              int64_t s, int Hq, int Hkv, int d, int dtype, float scale, int causal,
-             const int32_t* cu_seqlens, int n_docs, void* stream);
+             const int32_t* cu_seqlens, int n_docs, void* workspace, size_t workspace_bytes,
+             void* stream);
 
 /* ---------------------------------------------------------------------------
  * attn_bwd -- attention backward of one head shard: dq, dk, dv from dout, given the

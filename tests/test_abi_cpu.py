@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = U.lib()
-    assert L.uly_abi_version() == 5
+    assert L.uly_abi_version() == 6
     for code, name in U.STATUS.items():
         assert L.uly_status_string(code).decode() == name
 
@@ -120,7 +120,8 @@ def _fwd(**kw):
     args.update(kw)
     a = args
     return U.lib().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["o_lo"], a["lse"], a["s"], a["Hq"], a["Hkv"],
-                            a["d"], a["dt"], a["scale"], a["causal"], a["cu"], a["nd"], None)
+                            a["d"], a["dt"], a["scale"], a["causal"], a["cu"], a["nd"], a.get("ws"), a.get("cap", 0),
+                            None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -130,6 +131,7 @@ def _fwd(**kw):
     (dict(d=96), 3), (dict(dt=1, d=128), 3), (dict(dt=5), 3),
     (dict(k=MIS), 4), (dict(o=MIS), 4),
     (dict(o_lo=MIS), 4), (dict(dt=1, d=64, o_lo=FAKE), 3),   # the O residual: aligned, bf16 only
+    (dict(ws=MIS, cap=1 << 20), 4),                          # a workspace must be 16-byte aligned
 ])
 def test_attn_fwd_rejects(kw, want):
     assert _fwd(**kw) == want
@@ -356,6 +358,20 @@ def test_dkdv_split_accounting():
     delta = U.delta_bytes(8192, 8)
     assert L.attn_bwd_workspace_bytes(8192, 8, 2, 128) == delta + 64 * MiB
     assert L.attn_bwd_workspace_bytes(65536, 8, 2, 128) == U.delta_bytes(65536, 8)
+
+
+def test_fwd_split_accounting():
+    """Forward row blocks split below 768 workgroups (128 rows x q head), aiming at 1024, at most
+    8 per block; each split keeps fp32 O sums (128 x d) and 4 floats of row statistics per row:
+    8K share (8 q heads, 512 workgroups) -> 2 splits; 64K share and 768 workgroups -> none."""
+    L = U.lib()
+    assert L.attn_fwd_workspace_bytes(8192, 8, 128) == 8 * 64 * 2 * 128 * (128 + 4) * 4
+    assert L.attn_fwd_workspace_bytes(65536, 8, 128) == 0
+    assert L.attn_fwd_workspace_bytes(8192, 12, 128) == 0            # 768 workgroups: no split
+    assert L.attn_fwd_workspace_bytes(8192, 11, 128) == 11 * 64 * 2 * 128 * (128 + 4) * 4   # 704 -> 2
+    assert L.attn_fwd_workspace_bytes(4096, 8, 64) == 8 * 32 * 4 * 128 * (64 + 4) * 4      # 256 -> 4
+    assert L.attn_fwd_workspace_bytes(100, 1, 64) == 1 * 1 * 8 * 128 * (64 + 4) * 4        # capped at 8
+    assert L.attn_fwd_workspace_bytes(0, 8, 128) == 0
 
 
 def test_dq_split_accounting():

@@ -207,7 +207,7 @@ def test_q_zero_gives_prefix_means():
 def test_forward_key_tile_sizes_agree(d, causal, cu):
     """The forward takes 32-key tiles (three workgroups per CU) on grids of at least 768
     workgroups and 64-key tiles (two per CU) on smaller ones; both perform the same per-half
-    operations in the same order. 48 q heads over 2100 tokens (17 row blocks: 816 workgroups)
+    operations in the same order (the smaller grid here without its key split). 48 q heads over 2100 tokens (17 row blocks: 816 workgroups)
     run with 32-key tiles, their first 8 heads alone (136 workgroups) with 64-key tiles: O, its
     rounding residual and the LSE agree bitwise (ragged tail, documents not aligned to either
     tile), and the 8-head run matches the oracle."""
@@ -220,7 +220,7 @@ def test_forward_key_tile_sizes_agree(d, causal, cu):
     o48, l48 = U.attn_fwd(g["q"], g["k"], g["v"], scale, causal, cu_dev, o_lo=lo48)
     q8, k2, v2 = (g[n][:, :h].contiguous() for n, h in (("q", 8), ("k", 2), ("v", 2)))
     lo8 = U.new_o_lo(q8)
-    o8, l8 = U.attn_fwd(q8, k2, v2, scale, causal, cu_dev, o_lo=lo8)
+    o8, l8 = U.attn_fwd(q8, k2, v2, scale, causal, cu_dev, o_lo=lo8, split=False)
     torch.cuda.synchronize()
     bits = lambda t: t.contiguous().view(torch.int16)
     assert torch.equal(bits(o48[:, :8]), bits(o8))
@@ -287,3 +287,43 @@ def test_dq_split_matches_oracle(s, Hq, Hkv, d, causal, cu):
     wq, _, _ = OA.backward(f["q"], f["k"], f["v"], f["do"], scale, causal, cu, kv_cols=np.zeros(0, int))
     compare("dQ split", dev_to_f64(dq), wq, bf16=True)
     compare("dQ unsplit", dev_to_f64(dq1), wq, bf16=True)
+
+
+@pytest.mark.parametrize("s,Hq,Hkv,d,causal,cu", [
+    (100, 1, 1, 64, True, None),                                    # 8 splits of 2 key tiles: 6 empty
+    (1800, 4, 2, 128, True, [0, 1, 2, 333, 334, 1000, 1799, 1800]),   # 8 splits, packed, ragged tail
+    (3000, 8, 2, 64, False, None),                                  # 6 uneven splits of 47 tiles
+    (4096, 8, 2, 128, True, None),                                  # 4 splits
+    (700, 4, 4, 128, False, [0, 350, 700]),                         # 8 splits, two documents
+])
+def test_fwd_split_matches_oracle(s, Hq, Hkv, d, causal, cu):
+    """The forward with each 128-row block's key tiles split over several workgroups (grids of
+    fewer than 768 workgroups) and the partial results merged by a second kernel: O, its
+    rounding residual and the LSE, every element against the oracle, next to the unsplit run.
+    The outputs start as NaN, so a row the merge never writes fails; so does a split whose
+    partials were never stored, the workspace being NaN-filled."""
+    need = U.attn_fwd_workspace_bytes(s, Hq, d)
+    assert need > 0
+    print(f"case split forward s={s} Hq={Hq} d={d} causal={causal} docs={None if cu is None else len(cu) - 1}",
+          flush=True)
+    f, g = _inputs(s, Hq, Hkv, d, "bf16", seed=s + d + 1)
+    scale = 1.0 / np.sqrt(d)
+    cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    outs = {}
+    for split in (True, False):
+        o = torch.full_like(g["q"], float("nan"))
+        lo = torch.full_like(g["q"], float("nan"))
+        lse = torch.full((Hq, s), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda") if split else None
+        U.attn_fwd(g["q"], g["k"], g["v"], scale, causal, cu_dev, out=o, lse=lse, o_lo=lo, workspace=ws,
+                   split=split)
+        outs[split] = (o, lo, lse)
+    torch.cuda.synchronize()
+    wo, wl = OA.forward(f["q"], f["k"], f["v"], scale, causal, cu)
+    for split, (o, lo, lse) in outs.items():
+        tag = "split" if split else "unsplit"
+        compare(f"O {tag}", dev_to_f64(o), wo, bf16=True)
+        hi, rl = dev_to_f64(o), dev_to_f64(lo)
+        assert (np.abs(rl) <= half_ulp_bf16(hi) * (1 + 2.0 ** -7)).all(), f"residual {tag}"
+        assert np.linalg.norm(hi + rl - wo) <= np.linalg.norm(hi - wo), f"residual {tag}"
+        compare(f"LSE {tag}", lse.cpu().numpy(), wl, max_abs=LSE_ABS, rel_fro=1e-4)

@@ -21,7 +21,8 @@ pytestmark = pytest.mark.gpu
 def _unchunked(qs, ks, vs, rank, scale, causal, cu_dev, with_lo=False):
     q, k, v = (U.ulysses_pack(x, rank) for x in (qs, ks, vs))
     o_lo = U.new_o_lo(q) if with_lo and q.dtype == torch.bfloat16 else None
-    o, lse = U.attn_fwd(q, k, v, scale, causal, cu_dev, o_lo=o_lo)
+    # unsplit, as the chunks run: the comparisons with it are bitwise
+    o, lse = U.attn_fwd(q, k, v, scale, causal, cu_dev, o_lo=o_lo, split=False)
     o_sh = [torch.zeros_like(t) for t in qs]
     U.ulysses_unpack(o, rank, o_sh)
     return (o_sh, lse, o_lo) if with_lo else (o_sh, lse)

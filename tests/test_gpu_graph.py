@@ -5,7 +5,9 @@ graph is replayed several times on new inputs copied into its static buffers, wi
 and synchronisations between the replays, and every replay must give the bits an eager run on
 the same inputs gives (the library records no memset, which has misbehaved on replays after
 the first on these GPUs). Two graphs: attn_fwd + attn_bwd with a caller workspace, and
-attn_fwd + attn_bwd_noalloc (its static delta array), on a causal packed batch."""
+attn_fwd + attn_bwd_noalloc (its static delta array), on a causal packed batch short enough
+that the forward, given its workspace, splits its row blocks' keys and merges them in a
+second kernel, as the backward's dK/dV and dQ do with theirs."""
 import numpy as np
 import pytest
 import torch
@@ -39,9 +41,11 @@ def test_graph_replays_match_eager(noalloc):
     o, lse, o_lo = torch.empty_like(q), torch.empty((Hq, s), dtype=torch.float32, device="cuda"), U.new_o_lo(q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(U.attn_bwd_workspace_bytes(s, Hq, Hkv, d), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(U.attn_fwd_workspace_bytes(s, Hq, d), dtype=torch.uint8, device="cuda")  # split forward
+    assert fws.numel() > 0
 
     def step():
-        U.attn_fwd(q, k, v, None, True, cu, out=o, lse=lse, o_lo=o_lo)
+        U.attn_fwd(q, k, v, None, True, cu, out=o, lse=lse, o_lo=o_lo, workspace=fws)
         if noalloc:
             U.attn_bwd_noalloc(q, k, v, o, lse, do, None, True, cu, dq=dq, dk=dk, dv=dv, o_lo=o_lo)
         else:

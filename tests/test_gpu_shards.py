@@ -21,7 +21,8 @@ pytestmark = pytest.mark.gpu
 def _packed_path(dev, rank, scale, causal, cu_dev, with_lo=False):
     q, k, v = (U.ulysses_pack(dev[n], rank) for n in ("q", "k", "v"))
     o_lo = U.new_o_lo(q) if with_lo else None
-    o, lse = U.attn_fwd(q, k, v, scale, causal, cu_dev, o_lo=o_lo)
+    # unsplit, as the shard-reading forward runs: the comparisons with it are bitwise
+    o, lse = U.attn_fwd(q, k, v, scale, causal, cu_dev, o_lo=o_lo, split=False)
     o_sh = [torch.full_like(t, 3.0) for t in dev["q"]]
     U.ulysses_unpack(o, rank, o_sh)
     return (o_sh, lse, o_lo) if with_lo else (o_sh, lse)

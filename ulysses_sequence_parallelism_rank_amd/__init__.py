@@ -54,7 +54,9 @@ SIGNATURES = {
     "ulysses_recv_unpack": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp]),
     "ulysses_pack_group": (_i32, [_i32, _vpp, _i32p, _vpp, _i32, _i32, _i64, _i32, _i32, _vp]),
     "ulysses_unpack_group": (_i32, [_i32, _vpp, _i32p, _vpp, _i32, _i32, _i64, _i32, _i32, _vp]),
-    "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp]),
+    "attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz,
+                        _vp]),
+    "attn_fwd_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _f32, _i32,
                         _vp, _i32, _vp, _szp, _vp]),
     "attn_bwd_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
@@ -314,9 +316,16 @@ def _qkv(q, k, v):
     return s, Hq, Hkv, d
 
 
-def attn_fwd(q, k, v, scale=None, causal=True, cu_seqlens=None, out=None, lse=None, o_lo=None):
+def attn_fwd_workspace_bytes(s, Hq, d):
+    return int(lib().attn_fwd_workspace_bytes(s, Hq, d))
+
+
+def attn_fwd(q, k, v, scale=None, causal=True, cu_seqlens=None, out=None, lse=None, o_lo=None, workspace=None,
+             split=True):
     """q [s, Hq, d], k, v [s, Hkv, d] -> (o [s, Hq, d], lse [Hq, s] fp32). When `o_lo` (bf16
-    [s, Hq, d], e.g. new_o_lo(q)) is given, O's bf16 rounding residual is written into it."""
+    [s, Hq, d], e.g. new_o_lo(q)) is given, O's bf16 rounding residual is written into it. On
+    short sequences each row block's keys split over several workgroups when a workspace of
+    attn_fwd_workspace_bytes is given (allocated here unless split=False)."""
     s, Hq, Hkv, d = _qkv(q, k, v)
     o = torch.empty_like(q) if out is None else out
     if lse is None:
@@ -324,9 +333,15 @@ def attn_fwd(q, k, v, scale=None, causal=True, cu_seqlens=None, out=None, lse=No
     _need(o, "out", (s, Hq, d), q.dtype, q.device)
     _need(lse, "lse", (Hq, s), torch.float32, q.device)
     lo = _opt(o_lo, "o_lo", (s, Hq, d), torch.bfloat16, q.device)
+    if workspace is None and split:
+        need = attn_fwd_workspace_bytes(s, Hq, d)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws, cap = (None, 0) if workspace is None or not split else (_dev(workspace),
+                                                                 workspace.numel() * workspace.element_size())
     cu, nd = _cu(cu_seqlens, q.device)
     _call("attn_fwd", _dev(q), _dev(k), _dev(v), _dev(o), lo, _dev(lse), s, Hq, Hkv, d, _dtype(q),
-          _default_scale(d, scale), int(causal), cu, nd, _stream())
+          _default_scale(d, scale), int(causal), cu, nd, ws, cap, _stream())
     return o, lse
 
 

@@ -14,7 +14,7 @@ using namespace uly;
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline int esize(int dtype) { return dtype == ULY_BF16 ? 2 : 4; }
@@ -83,6 +83,7 @@ AttnArgs make_args(int64_t s, int Hq, int Hkv, int d, float scale, int causal, c
   a.acc_final = -1;
   a.nsplit = 1;
   a.nsplit_q = 1;
+  a.nsplit_o = 1;
   return a;
 }
 
@@ -273,15 +274,28 @@ int ulysses_unpack_group(int n, const void* const* in, const int* H, void* const
   return hip_status(launch_unpack_group(segs, n, s_l, as_stream(stream)));
 }
 
+size_t attn_fwd_workspace_bytes(int64_t s, int Hq, int d) {
+  if (s < 1 || Hq < 1 || d < 1) return 0;
+  return fwd_part_bytes(s, Hq, d);
+}
+
 int attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse, int64_t s, int Hq,
              int Hkv, int d, int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,
-             void* stream) {
+             void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_attn(q, k, v, s, Hq, Hkv, d, dtype, cu_seqlens, n_docs);
   if (st != ULY_OK) return st;
   if (!o || !lse) return ULY_ERR_NULL;
   if (!aligned16(o) || !aligned16(lse)) return ULY_ERR_ALIGN;
+  if (workspace != nullptr && !aligned16(workspace)) return ULY_ERR_ALIGN;
   if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
   AttnArgs a = make_args(s, Hq, Hkv, d, scale, causal, cu_seqlens, n_docs);
+  const size_t part = attn_fwd_workspace_bytes(s, Hq, d);
+  if (dtype == ULY_BF16 && part > 0 && workspace != nullptr && workspace_bytes >= part) {
+    // small grid: each row block's key tiles over several workgroups, merged in split order
+    a.nsplit_o = fwd_split_count(s, Hq);
+    a.o_part = static_cast<float*>(workspace);
+    a.o_stat = a.o_part + fwd_part_floats(s, Hq, d);
+  }
   a.q = q;
   a.k = k;
   a.v = v;

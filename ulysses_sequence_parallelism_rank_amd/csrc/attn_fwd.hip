@@ -62,7 +62,11 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void attn_fwd_kernel(AttnArg
   const int64_t s = a.s;
   const int nmb = (int)((s + BM - 1) / BM);
   const int h = blockIdx.x % a.n_heads;
-  const int mb = nmb - 1 - (int)(blockIdx.x / a.n_heads);
+  // workgroups per row block: splits run only on small grids, which take 64-key tiles (the
+  // 32-key instance carries no split code)
+  const int nso = BN == 64 && a.nsplit_o > 1 ? a.nsplit_o : 1;
+  const int sp = (int)((blockIdx.x / a.n_heads) % nso);
+  const int mb = nmb - 1 - (int)(blockIdx.x / a.n_heads / nso);
   const int64_t m0 = (int64_t)mb * BM;
   const int kvh = (h + a.q_off) / a.G - a.kv_off;
   // shard of the workgroup's rows (all in one) and the row offset of that shard
@@ -113,7 +117,12 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void attn_fwd_kernel(AttnArg
   if (a.causal) full_hi = full_hi < wr0 - 31 ? full_hi : wr0 - 31;
   const bool any_full = wr0 < s && full_hi >= full_lo;
   const uint32_t full_w = any_full ? (uint32_t)(full_hi - full_lo) : 0u;
-  const int ntiles = kbeg < kend ? (int)((kend - kbeg + BN - 1) / BN) : 0;
+  int ntiles = kbeg < kend ? (int)((kend - kbeg + BN - 1) / BN) : 0;
+  if (nso > 1) {  // this split's share of the block's key tiles
+    const int t0 = (int)((int64_t)ntiles * sp / nso), t1 = (int)((int64_t)ntiles * (sp + 1) / nso);
+    kbeg += (int64_t)t0 * BN;
+    ntiles = t1 - t0;
+  }
 
   // tile k0 of K and V from its shard (rows past the sequence end read the shard's last row);
   // K and V share the row stride, so one set of lane offsets serves both
@@ -267,6 +276,22 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void attn_fwd_kernel(AttnArg
   }
 
   const float lt = half_swap_sum(l), lrt = half_swap_sum(lr);
+  if (nso > 1) {
+    // this split's unnormalised fp32 sums and its row statistics; the combine kernel merges them
+    if (row < s) {
+      const int64_t slot = ((int64_t)h * nmb + mb) * nso + sp;
+      const int64_t r = wave * 32 + l32;
+      float* op = a.o_part + slot * (BM * D) + r * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<f32x4*>(op + db * 32 + 8 * jj + 4 * hf) =
+              f32x4{oacc[db][4 * jj + 0], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
+      if (hf == 0) *reinterpret_cast<f32x4*>(a.o_stat + (slot * BM + r) * 4) = f32x4{m, lt, lrt, 0.f};
+    }
+    return;
+  }
   if (row < s) {
     uint16_t* O = static_cast<uint16_t*>(src.o[ps]) + (int64_t)h * D - r_sh * a.q_row;
     // O's bf16 rounding residual, when asked for: O_fp32 - bf16(O_fp32), rounded to bf16
@@ -294,9 +319,63 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void attn_fwd_kernel(AttnArg
   }
 }
 
+// Rows of split row blocks: for 8 consecutive elements of one row and q head, the nsplit_o
+// partial results merged in split order. With M the largest running max over the splits and
+// w = 2^(m_sp - M): O = sum w O_sp / sum w l'_sp (the rounded-weight sums, as the unsplit
+// kernel normalises) and LSE = (M + log2 sum w l_sp) ln 2. Writes O, its residual if asked
+// for, and (one thread per row) the LSE. One thread each.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(AttnArgs a, ShardSrc src) {
+  constexpr int BM = 128, PER = D / 8;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t s = a.s, nmb = (s + BM - 1) / BM;
+  if (c >= (int64_t)a.n_heads * s * PER) return;
+  const int part8 = (int)(c % PER);
+  const int64_t row = (c / PER) % s;
+  const int h = (int)(c / PER / s);
+  const int ns = a.nsplit_o;
+  const int64_t mb = row / BM, r = row - mb * BM;
+  const int64_t slot0 = ((int64_t)h * nmb + mb) * ns;
+  float M = -INFINITY;
+  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, a.o_stat[((slot0 + sp) * BM + r) * 4]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float lt = 0.f, lrt = 0.f;
+  for (int sp = 0; sp < ns; ++sp) {
+    const f32x4 st = *reinterpret_cast<const f32x4*>(a.o_stat + ((slot0 + sp) * BM + r) * 4);
+    const float w = st[0] == -INFINITY ? 0.f : fast_exp2(st[0] - M);  // a split that saw no key: 0
+    lt = __builtin_fmaf(w, st[1], lt);
+    lrt = __builtin_fmaf(w, st[2], lrt);
+    const float* op = a.o_part + (slot0 + sp) * (BM * D) + r * D + part8 * 8;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(op);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(op + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] = __builtin_fmaf(w, x0[e], acc[e]);
+      acc[4 + e] = __builtin_fmaf(w, x1[e], acc[4 + e]);
+    }
+  }
+  const float inv = 1.f / lrt;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  const int p = (int)((uint32_t)row / (uint32_t)src.s_l);
+  uint16_t* O = static_cast<uint16_t*>(src.o[p]) + (row - (int64_t)p * src.s_l) * a.q_row + (int64_t)h * D + part8 * 8;
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+  *reinterpret_cast<u32x4*>(O) = w;
+  if (a.o_lo != nullptr) {
+    // O's bf16 rounding residual O_fp32 - bf16(O_fp32), rounded to bf16
+    u32x4 rl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rl[e] = pack_bf16x2(acc[2 * e] - bf16_lo(w[e]), acc[2 * e + 1] - bf16_hi(w[e]));
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o_lo) + (int64_t)h * D + row * a.lo_row + part8 * 8) = rl;
+  }
+  if (part8 == 0) a.lse_out[(int64_t)h * a.lse_row + row] = (M + log2f(lt)) * kLn2;
+}
+
 // Grids of at least three workgroups per CU (256 CUs) take 32-key tiles and three workgroups
 // per CU; smaller grids, which would leave that third slot empty, take 64-key tiles (fewer
-// barriers and tile requests per key) at two per CU.
+// barriers and tile requests per key) at two per CU, also when their row blocks split.
 constexpr int64_t kFwdSmallGrid = 3 * 256;
 
 template <int D>
@@ -304,14 +383,31 @@ hipError_t launch_fwd_t(const AttnArgs& a, const ShardSrc& src, hipStream_t stre
   const int64_t nmb = (a.s + 127) / 128;
   const int64_t blocks = nmb * a.n_heads;
   if (blocks == 0) return hipSuccess;
+  const int nso = a.nsplit_o > 1 ? a.nsplit_o : 1;
   if (blocks >= kFwdSmallGrid)
     hipLaunchKernelGGL((attn_fwd_kernel<D, 32>), dim3((unsigned)blocks), dim3(256), 0, stream, a, src);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, 64>), dim3((unsigned)blocks), dim3(256), 0, stream, a, src);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, 64>), dim3((unsigned)(blocks * nso)), dim3(256), 0, stream, a, src);
+  if (nso > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t items = a.n_heads * a.s * (D / 8);
+    hipLaunchKernelGGL((fwd_combine_kernel<D>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a, src);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
+
+int fwd_split_count(int64_t s, int n_heads) {
+  // below three workgroups per CU the grid is one round of 64-key tiles at two per CU (512
+  // slots), in which the last row block (it sees every key) takes about twice the mean: split
+  // every block's key tiles, aiming at 1024 workgroups, at most 8 per block
+  const int64_t wg = (s + 127) / 128 * n_heads;
+  if (wg >= kFwdSmallGrid || wg < 1) return 1;
+  const int64_t ns = (1024 + wg - 1) / wg;
+  return (int)(ns < 8 ? ns : 8);
+}
 
 hipError_t launch_attn_fwd_bf16_shards(const AttnArgs& a, const ShardSrc& src, int d, hipStream_t stream) {
   if (d == 128) return launch_fwd_t<128>(a, src, stream);

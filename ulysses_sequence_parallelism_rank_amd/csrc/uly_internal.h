@@ -76,6 +76,14 @@ struct AttnArgs {
   // launches is combined with a split).
   int nsplit_q;
   float* dq_part;
+  // forward of one 128-row block split over nsplit_o workgroups (small grids): workgroup sp
+  // walks its share of the block's key tiles and stores, in slot ((q head * row blocks + block)
+  // * nsplit_o + sp), its unnormalised fp32 O sums ([128 rows][D], of o_part) and per row its
+  // running max (log2 units), fp32 weight sum and rounded-weight sum ([128 rows][4], of
+  // o_stat); a combine kernel merges the slots in split order. Values below 2: no split.
+  int nsplit_o;
+  float* o_part;
+  float* o_stat;
 };
 // dK/dV workgroups split per key block for a grid of n_kv * ceil(s/128) blocks (1 = no split)
 int dkdv_split_count(int64_t s, int n_kv);
@@ -84,6 +92,17 @@ int dq_split_count(int64_t s, int n_heads);
 inline size_t dq_part_bytes(int64_t s, int n_heads, int d) {
   const int ns = dq_split_count(s, n_heads);
   return ns <= 1 ? 0 : (size_t)n_heads * (size_t)((s + 127) / 128) * (size_t)ns * 128 * (size_t)d * sizeof(float);
+}
+// forward workgroups split per row block for a grid of n_heads * ceil(s/128) blocks (1 = no split)
+int fwd_split_count(int64_t s, int n_heads);
+// o_part then o_stat, both in floats
+inline size_t fwd_part_floats(int64_t s, int n_heads, int d) {
+  const int ns = fwd_split_count(s, n_heads);
+  return ns <= 1 ? 0 : (size_t)n_heads * (size_t)((s + 127) / 128) * (size_t)ns * 128 * (size_t)d;
+}
+inline size_t fwd_part_bytes(int64_t s, int n_heads, int d) {
+  const size_t nf = fwd_part_floats(s, n_heads, d);
+  return nf == 0 ? 0 : (nf + nf / (size_t)d * 4) * sizeof(float);
 }
 inline size_t dkdv_part_bytes(int64_t s, int n_kv, int d) {
   const int ns = dkdv_split_count(s, n_kv);
