@@ -207,8 +207,8 @@ size_t attn_bwd_workspace_bytes(int64_t s, int Hq, int Hkv, int d);
  * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * arguments without the workspace, and the same kernels (dK/dV and dQ unsplit), so the
- * results are bitwise those of attn_bwd wherever attn_bwd runs both unsplit (at least 256 key
- * blocks x kv heads, i.e. s * Hkv >= 32768, and more than 512 row blocks x q heads, i.e.
+ * results are bitwise those of attn_bwd wherever attn_bwd runs both unsplit (at least 512 key
+ * blocks x kv heads, i.e. s * Hkv >= 65536, and more than 512 row blocks x q heads, i.e.
  * ceil(s / 128) * Hq > 512). delta lives in a static device array of ULY_NOALLOC_MAX_DELTA floats
  * (16 MiB) that each GPU the library runs on holds until the process ends; the call
  * allocates nothing. s * Hq above ULY_NOALLOC_MAX_DELTA -> ULY_ERR_WORKSPACE; the array's
@@ -229,8 +229,9 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
 int attn_bwd_preprocess(const void* o, const void* o_lo, const void* dout, float* delta,
                         int64_t s, int Hq, int d, int dtype, void* stream);
 /* dk, dv for every key: per kv head, loops over the rows of its G q heads. A workgroup
- * holds 128 keys of one kv head and fills a CU; when fewer than 256 such workgroups would run
- * (short sequences) and a workspace of attn_bwd_dkdv_workspace_bytes(s, Hkv, d) bytes is
+ * holds 128 keys of one kv head and fills a CU; when fewer than 512 such workgroups would run
+ * (short sequences: under two rounds of them, so the first key block, which sees every row,
+ * sets the time) and a workspace of attn_bwd_dkdv_workspace_bytes(s, Hkv, d) bytes is
  * given (bf16), each key block's rows are split over up to 8 workgroups (aiming at 512) that
  * store fp32 partial sums, and a second kernel adds them in split order and rounds once:
  * still deterministic; the sums' order, and so the last bits, differ from the unsplit run.

@@ -347,13 +347,16 @@ def test_ring_rejects_on_the_host():
 
 
 def test_dkdv_split_accounting():
-    """Key blocks split over workgroups only while the grid is under the CUs: 8K share (2 kv
-    heads) -> 4 splits and 64 MiB of fp32 partials; 64K share -> none."""
+    """Key blocks split over workgroups while the grid is under two rounds (512 workgroups of
+    one per CU): 8K share (2 kv heads) -> 4 splits and 64 MiB of fp32 partials; 16K share -> 2;
+    64K share -> none."""
     L = U.lib()
     MiB = 2 ** 20
     assert L.attn_bwd_dkdv_workspace_bytes(8192, 2, 128) == 2 * 64 * 4 * 2 * 128 * 128 * 4 == 64 * MiB
     assert L.attn_bwd_dkdv_workspace_bytes(65536, 2, 128) == 0
-    assert L.attn_bwd_dkdv_workspace_bytes(32768, 1, 128) == 0      # 256 blocks: full
+    assert L.attn_bwd_dkdv_workspace_bytes(16384, 2, 128) == 2 * 128 * 2 * 2 * 128 * 128 * 4 == 64 * MiB
+    assert L.attn_bwd_dkdv_workspace_bytes(32768, 1, 128) == 1 * 256 * 2 * 2 * 128 * 128 * 4   # 256 -> 2
+    assert L.attn_bwd_dkdv_workspace_bytes(65536, 1, 128) == 0      # 512 blocks: two full rounds
     assert L.attn_bwd_dkdv_workspace_bytes(128, 1, 64) == 1 * 1 * 8 * 2 * 128 * 64 * 4   # capped at 8
     delta = U.delta_bytes(8192, 8)
     assert L.attn_bwd_workspace_bytes(8192, 8, 2, 128) == delta + 64 * MiB

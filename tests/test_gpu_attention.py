@@ -327,3 +327,36 @@ def test_fwd_split_matches_oracle(s, Hq, Hkv, d, causal, cu):
         assert (np.abs(rl) <= half_ulp_bf16(hi) * (1 + 2.0 ** -7)).all(), f"residual {tag}"
         assert np.linalg.norm(hi + rl - wo) <= np.linalg.norm(hi - wo), f"residual {tag}"
         compare(f"LSE {tag}", lse.cpu().numpy(), wl, max_abs=LSE_ABS, rel_fro=1e-4)
+
+
+def test_dkdv_split_at_two_rounds_matches_oracle():
+    """A 16K share with 2 kv heads has 256 dK/dV key-block workgroups, one round at one per
+    CU: the key blocks split in two. dK and dV against the oracle on every key of the first
+    block (it sees every row, and its two halves of the rows meet in the reduce), both sides of
+    block boundaries at a stride, and the last keys; every element against the unsplit run.
+    The outputs start as NaN."""
+    s, Hq, Hkv, d = 16384, 4, 2, 128
+    assert U.attn_bwd_dkdv_workspace_bytes(s, Hkv, d) > 0
+    print(f"case dK/dV split at two rounds s={s}", flush=True)
+    f, g = _inputs(s, Hq, Hkv, d, "bf16", seed=21)
+    scale = 1.0 / np.sqrt(d)
+    o_lo = U.new_o_lo(g["q"])
+    o, lse = U.attn_fwd(g["q"], g["k"], g["v"], scale, True, o_lo=o_lo)
+    delta = U.attn_bwd_preprocess(o, g["do"], o_lo=o_lo)
+    out = {}
+    for split in (True, False):
+        dk = torch.full_like(g["k"], float("nan"))
+        dv = torch.full_like(g["v"], float("nan"))
+        U.attn_bwd_dkdv(g["q"], g["k"], g["v"], lse, g["do"], delta, scale, True, dk=dk, dv=dv, split=split)
+        out[split] = (dk, dv)
+    torch.cuda.synchronize()
+    keys = np.unique(np.concatenate([np.arange(128), [b + e for b in range(1024, s, 2048) for e in (-1, 0, 1)],
+                                     np.arange(s - 64, s)]))
+    _, wk, wv = OA.backward(f["q"], f["k"], f["v"], f["do"], scale, True, q_rows=np.zeros(0, int), kv_cols=keys)
+    idx = torch.as_tensor(keys, device="cuda")
+    compare("dK split keys", dev_to_f64(out[True][0][idx]), wk, bf16=True)
+    compare("dV split keys", dev_to_f64(out[True][1][idx]), wv, bf16=True)
+    for i, n in enumerate(("dK", "dV")):
+        a, b = dev_to_f64(out[True][i]), dev_to_f64(out[False][i])
+        assert np.isfinite(a).all() and np.isfinite(b).all(), n
+        assert np.linalg.norm(a - b) <= 1e-3 * np.linalg.norm(b), f"{n}: split against unsplit"

@@ -872,10 +872,12 @@ int dq_split_count(int64_t s, int n_heads) {
 }
 
 int dkdv_split_count(int64_t s, int n_kv) {
-  // one eight-wave workgroup per CU: split the key blocks' rows while the grid is under the
-  // 256 CUs, aiming at 512 workgroups, at most 8 per block
+  // one eight-wave workgroup per CU, blocks launched longest first: a causal grid balances
+  // over the 256 CUs only from about two rounds (the first block walks twice the mean), so
+  // split the key blocks' rows while the grid is under 512, aiming at 512 workgroups, at
+  // most 8 per block
   const int64_t wg = (s + 127) / 128 * n_kv;
-  if (wg >= 256 || wg < 1) return 1;
+  if (wg >= 512 || wg < 1) return 1;
   const int64_t ns = (512 + wg - 1) / wg;
   return (int)(ns < 8 ? ns : 8);
 }
