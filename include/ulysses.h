@@ -163,11 +163,12 @@ int ulysses_recv_unpack(const void* in, int P, int64_t s_l, int H, int d, int dt
  *   cu_seqlens : NULL, or device int32 [n_docs + 1], 0 = cu[0] < ... < cu[n_docs] = s;
  *                keys are then further restricted to the row's own document
  *   workspace : NULL, or device scratch (16-byte aligned, else ULY_ERR_ALIGN) of
- *               workspace_bytes bytes. A workgroup holds 128 rows of one q head; below 768
- *               of them (short sequences: one round in which the last row block, which sees
- *               every key, sets the time) and given attn_fwd_workspace_bytes(s, Hq, d) bytes
- *               (bf16), each row block's key tiles are split over up to 8 workgroups (aiming
- *               at 1024) that store fp32 partial results (O sums, running max, weight sums),
+ *               workspace_bytes bytes. A workgroup holds 128 rows of one q head; below 1152
+ *               of them (short and mid-size sequences: one or one and a half rounds, in which
+ *               the last row blocks, which see the most keys, set the time) and given
+ *               attn_fwd_workspace_bytes(s, Hq, d) bytes (bf16), each row block's key tiles are
+ *               split over up to 8 workgroups (aiming at 1024 below 768 of them, else 2) that
+ *               store fp32 partial results (O sums, running max, weight sums),
  *               and a second kernel merges them in split order: deterministic; the last bits
  *               differ from the unsplit run. A smaller or NULL workspace runs unsplit. The
  *               size is 0 where no split applies.
@@ -208,8 +209,8 @@ size_t attn_bwd_workspace_bytes(int64_t s, int Hq, int Hkv, int d);
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * arguments without the workspace, and the same kernels (dK/dV and dQ unsplit), so the
  * results are bitwise those of attn_bwd wherever attn_bwd runs both unsplit (at least 512 key
- * blocks x kv heads, i.e. s * Hkv >= 65536, and more than 512 row blocks x q heads, i.e.
- * ceil(s / 128) * Hq > 512). delta lives in a static device array of ULY_NOALLOC_MAX_DELTA floats
+ * blocks x kv heads, i.e. s * Hkv >= 65536, and at least 1024 row blocks x q heads, i.e.
+ * ceil(s / 128) * Hq >= 1024). delta lives in a static device array of ULY_NOALLOC_MAX_DELTA floats
  * (16 MiB) that each GPU the library runs on holds until the process ends; the call
  * allocates nothing. s * Hq above ULY_NOALLOC_MAX_DELTA -> ULY_ERR_WORKSPACE; the array's
  * address not obtainable -> ULY_ERR_HIP. Every call on one GPU uses that GPU's one array:
@@ -243,8 +244,9 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                   const int32_t* cu_seqlens, int n_docs, void* workspace, size_t workspace_bytes,
                   void* stream);
 /* dq for every row: loops over the visible keys. A workgroup holds 128 rows of one q head,
- * two share a CU; when at most 512 such workgroups would run (short sequences: the longest row
- * block, which sees every key, then sets the time) and a workspace of
+ * two share a CU; when fewer than 1024 such workgroups would run (short and mid-size
+ * sequences: under two rounds, so the longest row blocks, which see the most keys, set the
+ * time) and a workspace of
  * attn_bwd_dq_workspace_bytes(s, Hq, d) bytes is given (bf16), each row block's key tiles are
  * split over up to 8 workgroups (aiming at 1024) that store fp32 partial sums, and a second
  * kernel adds them in split order, scales and rounds once: deterministic; the sums' order,

@@ -364,13 +364,17 @@ def test_dkdv_split_accounting():
 
 
 def test_fwd_split_accounting():
-    """Forward row blocks split below 768 workgroups (128 rows x q head), aiming at 1024, at most
-    8 per block; each split keeps fp32 O sums (128 x d) and 4 floats of row statistics per row:
-    8K share (8 q heads, 512 workgroups) -> 2 splits; 64K share and 768 workgroups -> none."""
+    """Forward row blocks split below 768 workgroups (128 rows x q head) aiming at 1024, at most
+    8 per block, and in two from 768 to 1151; each split keeps fp32 O sums (128 x d) and 4
+    floats of row statistics per row: 8K share (8 q heads, 512 workgroups) -> 2 splits; 12K and
+    16K -> 2; 20K (1280) and the 64K share -> none."""
     L = U.lib()
     assert L.attn_fwd_workspace_bytes(8192, 8, 128) == 8 * 64 * 2 * 128 * (128 + 4) * 4
     assert L.attn_fwd_workspace_bytes(65536, 8, 128) == 0
-    assert L.attn_fwd_workspace_bytes(8192, 12, 128) == 0            # 768 workgroups: no split
+    assert L.attn_fwd_workspace_bytes(12288, 8, 128) == 8 * 96 * 2 * 128 * (128 + 4) * 4    # 768 -> 2
+    assert L.attn_fwd_workspace_bytes(16384, 8, 128) == 8 * 128 * 2 * 128 * (128 + 4) * 4   # 1024 -> 2
+    assert L.attn_fwd_workspace_bytes(18432, 8, 128) == 0            # 1152 workgroups: no split
+    assert L.attn_fwd_workspace_bytes(20480, 8, 128) == 0
     assert L.attn_fwd_workspace_bytes(8192, 11, 128) == 11 * 64 * 2 * 128 * (128 + 4) * 4   # 704 -> 2
     assert L.attn_fwd_workspace_bytes(4096, 8, 64) == 8 * 32 * 4 * 128 * (64 + 4) * 4      # 256 -> 4
     assert L.attn_fwd_workspace_bytes(100, 1, 64) == 1 * 1 * 8 * 128 * (64 + 4) * 4        # capped at 8
@@ -378,15 +382,17 @@ def test_fwd_split_accounting():
 
 
 def test_dq_split_accounting():
-    """dQ row blocks split while at most 512 workgroups (128 rows x q head) would run, aiming at
-    1024, at most 8 per block: 8K share (8 q heads) -> 2 splits, 64 MiB of fp32 partials, the
-    same bytes the dK/dV split needs, so attn_bwd's workspace is delta + their maximum; 64K
-    share -> none."""
+    """dQ row blocks split while fewer than 1024 workgroups (128 rows x q head) would run, aiming
+    at 1024, at most 8 per block: 8K share (8 q heads) -> 2 splits, 64 MiB of fp32 partials,
+    the same bytes the dK/dV split needs, so attn_bwd's workspace is delta + their maximum;
+    12K -> 2; 16K and the 64K share -> none."""
     L = U.lib()
     MiB = 2 ** 20
     assert L.attn_bwd_dq_workspace_bytes(8192, 8, 128) == 8 * 64 * 2 * 128 * 128 * 4 == 64 * MiB
     assert L.attn_bwd_dq_workspace_bytes(65536, 8, 128) == 0
     assert L.attn_bwd_dq_workspace_bytes(8192, 16, 128) == 0         # 1024 workgroups: full
+    assert L.attn_bwd_dq_workspace_bytes(16384, 8, 128) == 0
+    assert L.attn_bwd_dq_workspace_bytes(12288, 8, 128) == 8 * 96 * 2 * 128 * 128 * 4   # 768 -> 2
     assert L.attn_bwd_dq_workspace_bytes(4096, 8, 64) == 8 * 32 * 4 * 128 * 64 * 4   # 256 -> 4 splits
     assert L.attn_bwd_dq_workspace_bytes(128, 1, 64) == 1 * 1 * 8 * 128 * 64 * 4     # capped at 8
     assert L.attn_bwd_dq_workspace_bytes(0, 8, 128) == 0

@@ -207,7 +207,7 @@ def test_q_zero_gives_prefix_means():
 def test_forward_key_tile_sizes_agree(d, causal, cu):
     """The forward takes 32-key tiles (three workgroups per CU) on grids of at least 768
     workgroups and 64-key tiles (two per CU) on smaller ones; both perform the same per-half
-    operations in the same order (the smaller grid here without its key split). 48 q heads over 2100 tokens (17 row blocks: 816 workgroups)
+    operations in the same order (both grids here without their key split). 48 q heads over 2100 tokens (17 row blocks: 816 workgroups)
     run with 32-key tiles, their first 8 heads alone (136 workgroups) with 64-key tiles: O, its
     rounding residual and the LSE agree bitwise (ragged tail, documents not aligned to either
     tile), and the 8-head run matches the oracle."""
@@ -217,7 +217,7 @@ def test_forward_key_tile_sizes_agree(d, causal, cu):
     scale = 1.0 / np.sqrt(d)
     cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
     lo48 = U.new_o_lo(g["q"])
-    o48, l48 = U.attn_fwd(g["q"], g["k"], g["v"], scale, causal, cu_dev, o_lo=lo48)
+    o48, l48 = U.attn_fwd(g["q"], g["k"], g["v"], scale, causal, cu_dev, o_lo=lo48, split=False)
     q8, k2, v2 = (g[n][:, :h].contiguous() for n, h in (("q", 8), ("k", 2), ("v", 2)))
     lo8 = U.new_o_lo(q8)
     o8, l8 = U.attn_fwd(q8, k2, v2, scale, causal, cu_dev, o_lo=lo8, split=False)
@@ -262,10 +262,11 @@ def test_packed_dkdv_unsplit_matches_oracle(cu):
     (1800, 4, 2, 128, True, [0, 1, 2, 333, 334, 1000, 1799, 1800]),  # 8 splits, packed, ragged tail
     (3000, 8, 2, 64, False, None),                                 # 6 uneven splits of 47 tiles
     (4096, 8, 2, 128, True, None),                                 # 4 splits
+    (4500, 24, 6, 128, True, [0, 1, 1000, 1001, 4500]),            # 2 splits of 864 workgroups
 ])
 def test_dq_split_matches_oracle(s, Hq, Hkv, d, causal, cu):
-    """dQ with each 128-row block's key tiles split over several workgroups (grids of at most
-    512 workgroups) and the fp32 partials summed in split order by a second kernel: every
+    """dQ with each 128-row block's key tiles split over several workgroups (grids of fewer
+    than 1024 workgroups) and the fp32 partials summed in split order by a second kernel: every
     element against the oracle, next to the unsplit run. dQ starts as NaN, so a row the reduce
     never writes fails."""
     ns_bytes = U.attn_bwd_dq_workspace_bytes(s, Hq, d)
@@ -295,10 +296,12 @@ def test_dq_split_matches_oracle(s, Hq, Hkv, d, causal, cu):
     (3000, 8, 2, 64, False, None),                                  # 6 uneven splits of 47 tiles
     (4096, 8, 2, 128, True, None),                                  # 4 splits
     (700, 4, 4, 128, False, [0, 350, 700]),                         # 8 splits, two documents
+    (4500, 24, 6, 128, True, [0, 1, 1000, 1001, 4500]),             # 32-key tiles, 2 splits (864 workgroups)
 ])
 def test_fwd_split_matches_oracle(s, Hq, Hkv, d, causal, cu):
     """The forward with each 128-row block's key tiles split over several workgroups (grids of
-    fewer than 768 workgroups) and the partial results merged by a second kernel: O, its
+    fewer than 1152 workgroups; 64-key tiles below 768, 32-key tiles above) and the partial
+    results merged by a second kernel: O, its
     rounding residual and the LSE, every element against the oracle, next to the unsplit run.
     The outputs start as NaN, so a row the merge never writes fails; so does a split whose
     partials were never stored, the workspace being NaN-filled."""

@@ -862,11 +862,12 @@ hipError_t launch_dkdv_split_t(const AttnArgs& a, const BwdSrc& src, hipStream_t
 }  // namespace
 
 int dq_split_count(int64_t s, int n_heads) {
-  // two four-wave workgroups per CU: while the grid is at most one round of them (512), its
-  // longest row block sets the time (twice the mean for one causal sequence); split every
-  // block's key tiles, aiming at 1024 workgroups, at most 8 per block
+  // two four-wave workgroups per CU (512 slots), row blocks launched longest first: the last
+  // row block sees every key (twice the mean for one causal sequence), so the grid balances
+  // only from about two rounds; below that, split every block's key tiles, aiming at 1024
+  // workgroups, at most 8 per block
   const int64_t wg = (s + 127) / 128 * n_heads;
-  if (wg > 512 || wg < 1) return 1;
+  if (wg >= 1024 || wg < 1) return 1;
   const int64_t ns = (1024 + wg - 1) / wg;
   return (int)(ns < 8 ? ns : 8);
 }

@@ -50,7 +50,7 @@ constexpr int kPfS = 2, kPfV = 2;
 // Key tiles of BN = 32 (three workgroups per CU) or 64 keys (two): a tile is processed as
 // BN / 32 halves of 32 keys, each S, its softmax and PV in turn, so both tile sizes perform the
 // same operations in the same order and give bitwise-identical results.
-template <int D, int BN>
+template <int D, int BN, bool SPLIT>
 __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void attn_fwd_kernel(AttnArgs a, ShardSrc src) {
   constexpr int BM = 128, DT = D / 16, DB = D / 32;
   static_assert(BN == 32 || BN == 64, "key tile");
@@ -62,9 +62,9 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void attn_fwd_kernel(AttnArg
   const int64_t s = a.s;
   const int nmb = (int)((s + BM - 1) / BM);
   const int h = blockIdx.x % a.n_heads;
-  // workgroups per row block: splits run only on small grids, which take 64-key tiles (the
-  // 32-key instance carries no split code)
-  const int nso = BN == 64 && a.nsplit_o > 1 ? a.nsplit_o : 1;
+  // workgroups per row block (short and mid-size grids; the instance for large grids carries
+  // no split code)
+  const int nso = SPLIT && a.nsplit_o > 1 ? a.nsplit_o : 1;
   const int sp = (int)((blockIdx.x / a.n_heads) % nso);
   const int mb = nmb - 1 - (int)(blockIdx.x / a.n_heads / nso);
   const int64_t m0 = (int64_t)mb * BM;
@@ -384,10 +384,13 @@ hipError_t launch_fwd_t(const AttnArgs& a, const ShardSrc& src, hipStream_t stre
   const int64_t blocks = nmb * a.n_heads;
   if (blocks == 0) return hipSuccess;
   const int nso = a.nsplit_o > 1 ? a.nsplit_o : 1;
-  if (blocks >= kFwdSmallGrid)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, 32>), dim3((unsigned)blocks), dim3(256), 0, stream, a, src);
+  const dim3 grid((unsigned)(blocks * nso));
+  if (blocks >= kFwdSmallGrid && nso == 1)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, 32, false>), grid, dim3(256), 0, stream, a, src);
+  else if (blocks >= kFwdSmallGrid)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, 32, true>), grid, dim3(256), 0, stream, a, src);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, 64>), dim3((unsigned)(blocks * nso)), dim3(256), 0, stream, a, src);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, 64, true>), grid, dim3(256), 0, stream, a, src);
   if (nso > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -400,12 +403,15 @@ hipError_t launch_fwd_t(const AttnArgs& a, const ShardSrc& src, hipStream_t stre
 }  // namespace
 
 int fwd_split_count(int64_t s, int n_heads) {
-  // below three workgroups per CU the grid is one round of 64-key tiles at two per CU (512
-  // slots), in which the last row block (it sees every key) takes about twice the mean: split
-  // every block's key tiles, aiming at 1024 workgroups, at most 8 per block
+  // Row blocks launch longest first, and the last one sees every key (about twice the mean),
+  // so a grid of one or two rounds is set by its longest blocks. Below three per CU it is one
+  // round of 64-key tiles at two per CU (512 slots): split every block's key tiles aiming at
+  // 1024 workgroups, at most 8 per block; from there to one and a half rounds of 32-key tiles
+  // at three per CU (1152 workgroups), split in two (measured: 768 and 1024 workgroups gain,
+  // 1280 loses).
   const int64_t wg = (s + 127) / 128 * n_heads;
-  if (wg >= kFwdSmallGrid || wg < 1) return 1;
-  const int64_t ns = (1024 + wg - 1) / wg;
+  if (wg < 1 || wg >= 3 * kFwdSmallGrid / 2) return 1;
+  const int64_t ns = wg < kFwdSmallGrid ? (1024 + wg - 1) / wg : 2;
   return (int)(ns < 8 ? ns : 8);
 }
 
