@@ -363,3 +363,38 @@ def test_dkdv_split_at_two_rounds_matches_oracle():
         a, b = dev_to_f64(out[True][i]), dev_to_f64(out[False][i])
         assert np.isfinite(a).all() and np.isfinite(b).all(), n
         assert np.linalg.norm(a - b) <= 1e-3 * np.linalg.norm(b), f"{n}: split against unsplit"
+
+
+def test_short_workspace_runs_unsplit():
+    """A workspace one byte short of the queried size is not used: attn_fwd, attn_bwd_dkdv and
+    attn_bwd_dq then run unsplit, bitwise equal to split=False, and the queried size splits
+    (its results differ from the unsplit ones only in the last bits)."""
+    s, Hq, Hkv, d = 1000, 4, 2, 128
+    f, g = _inputs(s, Hq, Hkv, d, "bf16", seed=31)
+    scale = 1.0 / np.sqrt(d)
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    sizes = {"fwd": U.attn_fwd_workspace_bytes(s, Hq, d), "dkdv": U.attn_bwd_dkdv_workspace_bytes(s, Hkv, d),
+             "dq": U.attn_bwd_dq_workspace_bytes(s, Hq, d)}
+    assert all(v > 0 for v in sizes.values()), sizes
+    o_lo = U.new_o_lo(g["q"])
+    o, lse = U.attn_fwd(g["q"], g["k"], g["v"], scale, True, o_lo=o_lo, split=False)
+    delta = U.attn_bwd_preprocess(o, g["do"], o_lo=o_lo)
+
+    def run(kind, ws, split):
+        if kind == "fwd":
+            lo = U.new_o_lo(g["q"])
+            return U.attn_fwd(g["q"], g["k"], g["v"], scale, True, o_lo=lo, workspace=ws, split=split) + (lo,)
+        if kind == "dkdv":
+            return U.attn_bwd_dkdv(g["q"], g["k"], g["v"], lse, g["do"], delta, scale, True, workspace=ws,
+                                   split=split)
+        return (U.attn_bwd_dq(g["q"], g["k"], g["v"], lse, g["do"], delta, scale, True, workspace=ws, split=split),)
+
+    for kind, need in sizes.items():
+        print(f"case short workspace {kind} need={need}", flush=True)
+        ref = run(kind, None, False)
+        short = run(kind, torch.empty(need - 1, dtype=torch.uint8, device="cuda"), True)
+        full = run(kind, torch.empty(need, dtype=torch.uint8, device="cuda"), True)
+        torch.cuda.synchronize()
+        for a, b, c in zip(ref, short, full):
+            assert torch.equal(bits(a), bits(b)), f"{kind}: short workspace did not run unsplit"
+            assert not torch.equal(bits(a), bits(c)), f"{kind}: queried workspace did not split"
