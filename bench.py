@@ -192,9 +192,13 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
     lse = torch.empty((Hq_l, s), dtype=torch.float32, device=dev)
 
     def heads():  # the head-shard intermediates and the backward's delta, allocated once
+        if fused:  # the shard-reading kernels need no head shards
+            # the backward's delta with room for its split runs' partials (short sequences), and
+            # the forward's partials
+            ws = torch.empty(U.attn_bwd_workspace_bytes(s, Hq_l, Hkv_l, d), dtype=torch.uint8, device=dev)
+            need = U.attn_fwd_workspace_bytes(s, Hq_l, d)
+            return (None,) * 8 + (ws, torch.empty(need, dtype=torch.uint8, device=dev) if need else None)
         ws = torch.empty(U.delta_bytes(s, Hq_l), dtype=torch.uint8, device=dev)
-        if fused:  # the shard-reading kernels need no head shards (and run unsplit)
-            return (None,) * 8 + (ws, None)
         q = torch.empty((s, Hq_l, d), dtype=dt, device=dev)
         k = torch.empty((s, Hkv_l, d), dtype=dt, device=dev)
         # room for the partial results of the split runs on short sequences (none at 64K): the
@@ -215,7 +219,8 @@ def run_training_share(cfg, steps, warmup, cu_dev, fused=False):
 
     def step_fused(rec):
         ph.run("attn_fwd_shards", lambda: U.attn_fwd_shards(sh["q"], sh["k"], sh["v"], o_sh, rank, cfg.scale,
-                                                            cfg.causal, cu_dev, lse=lse, o_lo=o_lo), rec)
+                                                            cfg.causal, cu_dev, lse=lse, o_lo=o_lo,
+                                                            workspace=part_ws), rec)
         ph.run("attn_bwd_shards", lambda: U.attn_bwd_shards(sh["q"], sh["k"], sh["v"], o_sh, lse, sh["do"], dq_sh,
                                                             dk_sh, dv_sh, rank, cfg.scale, cfg.causal, cu_dev,
                                                             workspace=ws, o_lo=o_lo), rec)
@@ -290,12 +295,12 @@ def run_forward_share(cfg, steps, warmup, cu_dev, fused):
     lse = torch.empty((Hq_l, s), dtype=torch.float32, device="cuda")
 
     def heads():  # the head-shard intermediates of the unchunked forward (not needed fused)
-        if fused:
-            return None, None, None, None, None
-        q = torch.empty((s, Hq_l, d), dtype=dt, device="cuda")
-        k = torch.empty((s, Hkv_l, d), dtype=dt, device="cuda")
         need = U.attn_fwd_workspace_bytes(s, Hq_l, d)  # the split forward's partials (short sequences)
         part = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+        if fused:
+            return None, None, None, None, part
+        q = torch.empty((s, Hq_l, d), dtype=dt, device="cuda")
+        k = torch.empty((s, Hkv_l, d), dtype=dt, device="cuda")
         return q, k, torch.empty_like(k), torch.empty_like(q), part
     (q, k, v, o, part_ws), inter, _ = alloc_bytes(heads)
     ph = Phases()
@@ -305,7 +310,8 @@ def run_forward_share(cfg, steps, warmup, cu_dev, fused):
     def step(rec):
         if fused:
             ph.run("attn_fwd_shards", lambda: U.attn_fwd_shards(sh["q"], sh["k"], sh["v"], o_sh, rank, cfg.scale,
-                                                                cfg.causal, cu_dev, lse=lse, o_lo=o_lo), rec)
+                                                                cfg.causal, cu_dev, lse=lse, o_lo=o_lo,
+                                                                workspace=part_ws), rec)
             return
         ph.run("pack_qkv", lambda: U.ulysses_pack_group([sh["q"], sh["k"], sh["v"]], rank, [q, k, v]), rec)
         ph.run("attn_fwd", lambda: U.attn_fwd(q, k, v, cfg.scale, cfg.causal, cu_dev, out=o, lse=lse, o_lo=o_lo,

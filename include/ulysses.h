@@ -297,12 +297,15 @@ size_t attn_fwd_chunked_workspace_bytes(int P, int64_t s_l, int Hq, int Hkv, int
  * sequence shards). Instead of materialising the head shard, the kernel reads the rank's
  * Q heads and kv heads straight from the P sequence shards and writes O straight into
  * the rank's head slice of the o shards: no intermediate buffer. Results are bitwise
- * those of ulysses_pack + attn_fwd + ulysses_unpack.
+ * those of ulysses_pack + attn_fwd + ulysses_unpack given the same workspace size.
  *   q_shards / o_shards : host arrays of P device pointers [s_l, Hq, d] (global Hq);
  *                        only head slice `rank` of the o shards is written
  *   k_shards / v_shards : host arrays of P device pointers [s_l, Hkv, d]
  *   o_lo : device bf16 [s, Hq/P, d] or NULL: O's rounding residual of this rank's heads
  *   lse : device fp32 [Hq/P, s] for this rank's heads
+ *   workspace : NULL, or workspace_bytes of device scratch (16-byte aligned) for the split
+ *               run of short and mid-size grids, as for attn_fwd with s = P * s_l and Hq/P
+ *               heads: attn_fwd_workspace_bytes(P * s_l, Hq / P, d) bytes split.
  * bf16 only (ULY_ERR_UNSUPPORTED for fp32), and every workgroup's rows must lie in one
  * shard: s_l a multiple of 128 (ULY_ERR_UNSUPPORTED otherwise). Other errors as for
  * attn_fwd_chunked.
@@ -311,7 +314,7 @@ int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards,
                     const void* const* v_shards, void* const* o_shards, void* o_lo, float* lse,
                     int P, int rank, int64_t s_l, int Hq, int Hkv, int d, int dtype,
                     float scale, int causal, const int32_t* cu_seqlens, int n_docs,
-                    void* stream);
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * attn_bwd_shards -- the backward of rank `rank` with the exchange folded in, as
@@ -319,15 +322,20 @@ int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards,
  * two all-to-alls for the gradients). The kernels read Q, K, V, O and dO of the rank's
  * heads straight from the sequence shards and write dQ, dK and dV straight into the
  * rank's head slices of the gradient shards. Results are bitwise those of ulysses_pack +
- * attn_bwd + ulysses_unpack.
+ * attn_bwd + ulysses_unpack given the same workspace size.
  *   q_shards / o_shards / do_shards / dq_shards : host arrays of P device pointers
  *                        [s_l, Hq, d] (global Hq); o and lse as written by the forward
  *   k_shards / v_shards / dk_shards / dv_shards : host arrays of P device pointers
  *                        [s_l, Hkv, d]
  *   o_lo : the residual attn_fwd_shards wrote ([s, Hq/P, d]) or NULL
  *   lse : device fp32 [Hq/P, s]
- *   workspace : delta, 4 * P * s_l * (Hq / P) bytes rounded up to a multiple of 256; NULL ->
- *               size query into *workspace_bytes as for attn_bwd (dK/dV run unsplit).
+ *   workspace : delta, 4 * P * s_l * (Hq / P) bytes rounded up to a multiple of 256
+ *               (required), then room for the partial sums of the split dK/dV and dQ runs
+ *               of short and mid-size grids, as in attn_bwd (optional: used only where
+ *               *workspace_bytes states room for it; with workspace_bytes NULL the buffer
+ *               is taken to hold delta alone and both run unsplit). NULL -> the full size
+ *               (delta and partial region) is stored into *workspace_bytes: the size
+ *               attn_bwd_workspace_bytes(P * s_l, Hq / P, Hkv / P, d) reports.
  * bf16 only and s_l a multiple of 128 (ULY_ERR_UNSUPPORTED otherwise); other errors as
  * for attn_bwd_chunked.
  * ------------------------------------------------------------------------- */

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = U.lib()
-    assert L.uly_abi_version() == 6
+    assert L.uly_abi_version() == 7
     for code, name in U.STATUS.items():
         assert L.uly_status_string(code).decode() == name
 
@@ -238,8 +238,9 @@ def test_shards_rejects():
     pp, keep = _ptr_array([FAKE] * 2)
     mp, keep2 = _ptr_array([FAKE, MIS])
 
-    def fwd(q=pp, s_l=128, Hq=8, Hkv=4, d=128, dt=0, rank=0, lse=FAKE, o_lo=None):
-        return L.attn_fwd_shards(q, pp, pp, pp, o_lo, lse, 2, rank, s_l, Hq, Hkv, d, dt, 0.1, 1, None, 0, None)
+    def fwd(q=pp, s_l=128, Hq=8, Hkv=4, d=128, dt=0, rank=0, lse=FAKE, o_lo=None, ws=None, cap=0):
+        return L.attn_fwd_shards(q, pp, pp, pp, o_lo, lse, 2, rank, s_l, Hq, Hkv, d, dt, 0.1, 1, None, 0, ws, cap,
+                                 None)
     assert fwd(s_l=96) == 3          # a workgroup's rows must lie in one shard
     assert fwd(dt=1, d=64) == 3      # bf16 only
     assert fwd(d=96) == 3
@@ -248,15 +249,19 @@ def test_shards_rejects():
     assert fwd(lse=None) == 1
     assert fwd(q=mp) == 4
     assert fwd(o_lo=MIS) == 4
+    assert fwd(ws=MIS, cap=1 << 20) == 4
     need = ctypes.c_size_t(0)
 
     def bwd(ws=None, cap=None, s_l=128, dt=0, d=128):
         return L.attn_bwd_shards(pp, pp, pp, pp, None, FAKE, pp, pp, pp, pp, 2, 0, s_l, 8, 4, d, dt, 0.1, 1, None, 0,
                                  ws, cap, None)
-    assert bwd(cap=ctypes.byref(need)) == 0 and need.value == U.delta_bytes(256, 4)
+    # the query: delta, then room for the split runs' partial sums (256 tokens: both split)
+    part = max(L.attn_bwd_dkdv_workspace_bytes(256, 2, 128), L.attn_bwd_dq_workspace_bytes(256, 4, 128))
+    assert part > 0
+    assert bwd(cap=ctypes.byref(need)) == 0 and need.value == U.delta_bytes(256, 4) + part
     assert bwd(cap=ctypes.byref(need), s_l=64) == 3
     assert bwd(cap=ctypes.byref(need), dt=1, d=64) == 3
-    small = ctypes.c_size_t(need.value - 1)
+    small = ctypes.c_size_t(U.delta_bytes(256, 4) - 1)   # delta is required, the partials are not
     assert bwd(ws=FAKE, cap=ctypes.byref(small)) == 5
     assert bwd(ws=None, cap=None) == 1
 

@@ -18,11 +18,11 @@ from tests.helpers import LSE_ABS, compare, dev_to_f64, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _packed_path(dev, rank, scale, causal, cu_dev, with_lo=False):
+def _packed_path(dev, rank, scale, causal, cu_dev, with_lo=False, split=False):
     q, k, v = (U.ulysses_pack(dev[n], rank) for n in ("q", "k", "v"))
     o_lo = U.new_o_lo(q) if with_lo else None
-    # unsplit, as the shard-reading forward runs: the comparisons with it are bitwise
-    o, lse = U.attn_fwd(q, k, v, scale, causal, cu_dev, o_lo=o_lo, split=False)
+    # split or not as the shard-reading forward it is compared with, bitwise
+    o, lse = U.attn_fwd(q, k, v, scale, causal, cu_dev, o_lo=o_lo, split=split)
     o_sh = [torch.full_like(t, 3.0) for t in dev["q"]]
     U.ulysses_unpack(o, rank, o_sh)
     return (o_sh, lse, o_lo) if with_lo else (o_sh, lse)
@@ -39,19 +39,24 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("P,s_l,Hq,Hkv,d,rank,causal,cu", CASES)
-def test_shards_equal_packed_path(P, s_l, Hq, Hkv, d, rank, causal, cu):
-    print(f"case P={P} s_l={s_l} Hq={Hq} Hkv={Hkv} d={d} rank={rank} causal={causal} cu={cu is not None}",
-          flush=True)
+def test_shards_equal_packed_path(P, s_l, Hq, Hkv, d, rank, causal, cu, split):
+    """These grids are short: with split=True both sides split their keys over several
+    workgroups (the same counts) and must still agree bitwise."""
+    print(f"case P={P} s_l={s_l} Hq={Hq} Hkv={Hkv} d={d} rank={rank} causal={causal} cu={cu is not None} "
+          f"split={split}", flush=True)
+    assert U.attn_fwd_workspace_bytes(P * s_l, Hq // P, d) > 0
     cfg = W.Config("shards_small", P=P, s_l=s_l, Hq=Hq, Hkv=Hkv, d=d, dtype="bf16", causal=causal)
     bits = {n: W.gen_global(cfg, n, seed=21) for n in ("q", "k", "v")}
     dev = {n: [to_dev(b, "bf16") for b in W.shards_of(bits[n], P)] for n in bits}
     cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
-    want_o, want_lse, want_lo = _packed_path(dev, rank, cfg.scale, causal, cu_dev, True)
+    want_o, want_lse, want_lo = _packed_path(dev, rank, cfg.scale, causal, cu_dev, True, split)
     o_sh = [torch.full_like(t, 3.0) for t in dev["q"]]
     keep = [t.clone() for t in o_sh]
     o_lo = torch.full_like(want_lo, 5.0)
-    lse = U.attn_fwd_shards(dev["q"], dev["k"], dev["v"], o_sh, rank, cfg.scale, causal, cu_dev, o_lo=o_lo)
+    lse = U.attn_fwd_shards(dev["q"], dev["k"], dev["v"], o_sh, rank, cfg.scale, causal, cu_dev, o_lo=o_lo,
+                            split=split)
     torch.cuda.synchronize()
     assert torch.equal(o_lo.view(torch.int16), want_lo.view(torch.int16))
     Hl = Hq // P
@@ -68,9 +73,9 @@ def test_shards_equal_packed_path(P, s_l, Hq, Hkv, d, rank, causal, cu):
     compare("shards LSE", lse.cpu().numpy(), wl, max_abs=LSE_ABS, rel_fro=1e-4)
 
 
-def _packed_bwd(dev, o_sh, lse, rank, scale, causal, cu_dev, o_lo=None):
+def _packed_bwd(dev, o_sh, lse, rank, scale, causal, cu_dev, o_lo=None, split=False):
     q, k, v, o, g = (U.ulysses_pack(x, rank) for x in (dev["q"], dev["k"], dev["v"], o_sh, dev["do"]))
-    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, g, scale, causal, cu_dev, o_lo=o_lo, split=False)
+    dq, dk, dv = U.attn_bwd(q, k, v, o, lse, g, scale, causal, cu_dev, o_lo=o_lo, split=split)
     out = {}
     for n, y, like in (("dq", dq, dev["q"]), ("dk", dk, dev["k"]), ("dv", dv, dev["v"])):
         out[n] = [torch.full_like(t, 3.0) for t in like]
@@ -78,19 +83,21 @@ def _packed_bwd(dev, o_sh, lse, rank, scale, causal, cu_dev, o_lo=None):
     return out
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("P,s_l,Hq,Hkv,d,rank,causal,cu", CASES)
-def test_bwd_shards_equal_packed_path(P, s_l, Hq, Hkv, d, rank, causal, cu):
-    print(f"case P={P} s_l={s_l} Hq={Hq} Hkv={Hkv} d={d} rank={rank} causal={causal} cu={cu is not None}",
-          flush=True)
+def test_bwd_shards_equal_packed_path(P, s_l, Hq, Hkv, d, rank, causal, cu, split):
+    """As the forward: unsplit, and with dK/dV and dQ split on both sides."""
+    print(f"case P={P} s_l={s_l} Hq={Hq} Hkv={Hkv} d={d} rank={rank} causal={causal} cu={cu is not None} "
+          f"split={split}", flush=True)
     cfg = W.Config("shards_bwd", P=P, s_l=s_l, Hq=Hq, Hkv=Hkv, d=d, dtype="bf16", causal=causal)
     bits = {n: W.gen_global(cfg, n, seed=23) for n in ("q", "k", "v", "do")}
     dev = {n: [to_dev(b, "bf16") for b in W.shards_of(bits[n], P)] for n in bits}
     cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
     o_sh, lse, o_lo = _packed_path(dev, rank, cfg.scale, causal, cu_dev, True)
-    want = _packed_bwd(dev, o_sh, lse, rank, cfg.scale, causal, cu_dev, o_lo)
+    want = _packed_bwd(dev, o_sh, lse, rank, cfg.scale, causal, cu_dev, o_lo, split)
     got = {n: [torch.full_like(t, 3.0) for t in want[n]] for n in want}
     U.attn_bwd_shards(dev["q"], dev["k"], dev["v"], o_sh, lse, dev["do"], got["dq"], got["dk"], got["dv"], rank,
-                      cfg.scale, causal, cu_dev, o_lo=o_lo)
+                      cfg.scale, causal, cu_dev, o_lo=o_lo, split=split)
     torch.cuda.synchronize()
     for n in ("dq", "dk", "dv"):
         for a, b in zip(got[n], want[n]):

@@ -76,7 +76,7 @@ SIGNATURES = {
                                 _i32, _i32, _i32, _f32, _i32, _vp, _i32, _i32, _vp, _szp, _vp]),
     "attn_bwd_chunked_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
     "attn_fwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
-                               _i32, _vp, _i32, _vp]),
+                               _i32, _vp, _i32, _vp, _sz, _vp]),
     "attn_bwd_shards": (_i32, [_vpp, _vpp, _vpp, _vpp, _vp, _vp, _vpp, _vpp, _vpp, _vpp, _i32, _i32, _i64, _i32,
                                _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _szp, _vp]),
     "ring_attn_fwd_workspace_bytes": (_sz, [_i64, _i32, _i32]),
@@ -551,9 +551,10 @@ def attn_bwd_chunked(q_shards, k_shards, v_shards, o_shards, lse, do_shards, dq_
 
 
 def attn_fwd_shards(q_shards, k_shards, v_shards, o_shards, rank, scale=None, causal=True, cu_seqlens=None,
-                    lse=None, o_lo=None):
+                    lse=None, o_lo=None, workspace=None, split=True):
     """Forward of rank `rank` straight from the sequence shards into head slice `rank` of
-    o_shards (no head-shard buffers); returns the LSE [Hq/P, s]."""
+    o_shards (no head-shard buffers); returns the LSE [Hq/P, s]. Short and mid-size grids split
+    their keys as attn_fwd does, given a workspace (allocated here unless split=False)."""
     P, s_l, Hq, Hkv, d, q0 = _shard_sets(q_shards, k_shards, v_shards, o_shards)
     if lse is None:
         lse = torch.empty((Hq // P, P * s_l), dtype=torch.float32, device=q0.device)
@@ -561,27 +562,39 @@ def attn_fwd_shards(q_shards, k_shards, v_shards, o_shards, rank, scale=None, ca
     lo = _opt(o_lo, "o_lo", (P * s_l, Hq // P, d), torch.bfloat16, q0.device)
     keep = [_ptrs(x) for x in (q_shards, k_shards, v_shards, o_shards)]
     qp, kp, vp, op = (k[0] for k in keep)
+    if workspace is None and split:
+        need = attn_fwd_workspace_bytes(P * s_l, Hq // P, d)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q0.device)
+    ws, cap = (None, 0) if workspace is None or not split else (_dev(workspace),
+                                                                 workspace.numel() * workspace.element_size())
     cu, nd = _cu(cu_seqlens, q0.device)
     _call("attn_fwd_shards", qp, kp, vp, op, lo, _dev(lse), P, rank, s_l, Hq, Hkv, d, _dtype(q0),
-          _default_scale(d, scale), int(causal), cu, nd, _stream())
+          _default_scale(d, scale), int(causal), cu, nd, ws, cap, _stream())
     return lse
 
 
 def attn_bwd_shards(q_shards, k_shards, v_shards, o_shards, lse, do_shards, dq_shards, dk_shards, dv_shards,
-                    rank, scale=None, causal=True, cu_seqlens=None, workspace=None, o_lo=None):
+                    rank, scale=None, causal=True, cu_seqlens=None, workspace=None, o_lo=None, split=True):
     """Backward of rank `rank` straight from the sequence shards into head slice `rank` of
-    the dq / dk / dv shards."""
+    the dq / dk / dv shards. The workspace holds delta and, if it has room (the queried size,
+    which is allocated here unless split=False), the partial sums of the split dK/dV and dQ
+    runs of short and mid-size grids."""
     P, s_l, Hq, Hkv, d, q0 = _shard_sets(q_shards, k_shards, v_shards, o_shards, do_shards, dq_shards,
                                          more_kv=(dk_shards, dv_shards))
     _need(lse, "lse", (Hq // P, P * s_l), torch.float32, q0.device)
     lo = _opt(o_lo, "o_lo", (P * s_l, Hq // P, d), torch.bfloat16, q0.device)
-    need = delta_bytes(P * s_l, Hq // P)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q0.device)
-    cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     keep = [_ptrs(x) for x in (q_shards, k_shards, v_shards, o_shards, do_shards, dq_shards, dk_shards, dv_shards)]
     qp, kp, vp, op, gp, dqp, dkp, dvp = (k[0] for k in keep)
     cu, nd = _cu(cu_seqlens, q0.device)
+    if workspace is None:
+        need = ctypes.c_size_t(0)
+        if split:
+            _call("attn_bwd_shards", qp, kp, vp, op, lo, _dev(lse), gp, dqp, dkp, dvp, P, rank, s_l, Hq, Hkv, d,
+                  _dtype(q0), _default_scale(d, scale), int(causal), cu, nd, None, ctypes.byref(need), _stream())
+        workspace = torch.empty(need.value if split else delta_bytes(P * s_l, Hq // P), dtype=torch.uint8,
+                                device=q0.device)
+    cap = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     _call("attn_bwd_shards", qp, kp, vp, op, lo, _dev(lse), gp, dqp, dkp, dvp, P, rank, s_l, Hq, Hkv, d,
           _dtype(q0), _default_scale(d, scale), int(causal), cu, nd, _dev(workspace), ctypes.byref(cap),
           _stream())

@@ -14,7 +14,7 @@ using namespace uly;
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline int esize(int dtype) { return dtype == ULY_BF16 ? 2 : 4; }
@@ -623,7 +623,7 @@ int attn_fwd_chunked(const void* const* q_shards, const void* const* k_shards, c
 int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards, const void* const* v_shards,
                     void* const* o_shards, void* o_lo, float* lse, int P, int rank, int64_t s_l, int Hq, int Hkv,
                     int d, int dtype, float scale, int causal, const int32_t* cu_seqlens, int n_docs,
-                    void* stream) {
+                    void* workspace, size_t workspace_bytes, void* stream) {
   if (!q_shards || !k_shards || !v_shards || !o_shards || !lse) return ULY_ERR_NULL;
   int st = check_ranks(P, rank, s_l, Hq);
   if (st != ULY_OK) return st;
@@ -635,6 +635,7 @@ int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards, co
   if (s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
   if (cu_seqlens != nullptr && n_docs < 1) return ULY_ERR_SHAPE;
   if (!aligned16(lse)) return ULY_ERR_ALIGN;
+  if (workspace != nullptr && !aligned16(workspace)) return ULY_ERR_ALIGN;
   if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
   const int Hq_l = Hq / P, Hkv_l = Hkv / P;
   ShardSrc src{};
@@ -657,6 +658,12 @@ int attn_fwd_shards(const void* const* q_shards, const void* const* k_shards, co
   a.o_lo = o_lo;  // the rank's [s, Hq/P, d] layout
   a.lo_row = (int64_t)Hq_l * d;
   a.lse_out = lse;
+  const size_t part = attn_fwd_workspace_bytes(s, Hq_l, d);
+  if (part > 0 && workspace != nullptr && workspace_bytes >= part) {  // as attn_fwd: short grids split
+    a.nsplit_o = fwd_split_count(s, Hq_l);
+    a.o_part = static_cast<float*>(workspace);
+    a.o_stat = a.o_part + fwd_part_floats(s, Hq_l, d);
+  }
   return hip_status(launch_attn_fwd_bf16_shards(a, src, d, as_stream(stream)));
 }
 
@@ -678,13 +685,17 @@ int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards, co
   if (s > (int64_t)INT32_MAX) return ULY_ERR_SHAPE;
   if (cu_seqlens != nullptr && n_docs < 1) return ULY_ERR_SHAPE;
   const int Hq_l = Hq / P, Hkv_l = Hkv / P;
-  const size_t need = delta_bytes(s, Hq_l);
+  // delta, then (optional) the partial sums of the split dK/dV and dQ runs in one region
+  const size_t dpart = delta_bytes(s, Hq_l);
+  const size_t kvp = attn_bwd_dkdv_workspace_bytes(s, Hkv_l, d), qp = attn_bwd_dq_workspace_bytes(s, Hq_l, d);
   if (workspace == nullptr) {
     if (!workspace_bytes) return ULY_ERR_NULL;
-    *workspace_bytes = need;
+    *workspace_bytes = dpart + round256(std::max(kvp, qp));
     return ULY_OK;
   }
-  if (workspace_bytes && *workspace_bytes < need) return ULY_ERR_WORKSPACE;
+  // without a stated capacity only delta is assumed (the partial region is used when stated)
+  const size_t cap = workspace_bytes ? *workspace_bytes : dpart;
+  if (cap < dpart) return ULY_ERR_WORKSPACE;
   if (!lse) return ULY_ERR_NULL;
   if (!aligned16(lse) || !aligned16(workspace)) return ULY_ERR_ALIGN;
   if ((st = check_o_lo(o_lo, dtype)) != ULY_OK) return st;
@@ -720,9 +731,20 @@ int attn_bwd_shards(const void* const* q_shards, const void* const* k_shards, co
   pre.lo_row = (int64_t)Hq_l * d;
   hipStream_t strm = as_stream(stream);
   hipError_t err;
+  // as attn_bwd: short grids split dK/dV and dQ when the partial region is there
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + dpart);
+  AttnArgs akv = a, aq = a;
+  if (kvp > 0 && cap - dpart >= kvp) {
+    akv.nsplit = dkdv_split_count(s, Hkv_l);
+    akv.dkv_part = part;
+  }
+  if (qp > 0 && cap - dpart >= qp) {
+    aq.nsplit_q = dq_split_count(s, Hq_l);
+    aq.dq_part = part;
+  }
   if ((err = launch_bwd_preprocess_bf16_shards(pre, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
-  if ((err = launch_attn_dkdv_bf16_shards(a, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
-  if ((err = launch_attn_dq_bf16_shards(a, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
+  if ((err = launch_attn_dkdv_bf16_shards(akv, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
+  if ((err = launch_attn_dq_bf16_shards(aq, src, d, strm)) != hipSuccess) return ULY_ERR_HIP;
   return ULY_OK;
 }
 
