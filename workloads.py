@@ -80,6 +80,9 @@ WORKLOADS = {
     "tiny_f32": Config("tiny_f32", P=2, s_l=256, Hq=4, Hkv=4, d=64, dtype="f32", amp=0.5),
     # Qwen3-4B-shaped SP=4 share at 8K tokens
     "qwen_8k": Config("qwen_8k", P=4, s_l=2048, Hq=32, Hkv=8, d=128, dtype="bf16"),
+    # mid-size shares of the same model at 16K and 32K tokens (grids of one to two rounds)
+    "qwen_16k": Config("qwen_16k", P=4, s_l=4096, Hq=32, Hkv=8, d=128, dtype="bf16"),
+    "qwen_32k": Config("qwen_32k", P=4, s_l=8192, Hq=32, Hkv=8, d=128, dtype="bf16"),
     # the 64K headline share: 8 q / 2 kv heads after the all-to-all
     "qwen_64k": Config("qwen_64k", P=4, s_l=16384, Hq=32, Hkv=8, d=128, dtype="bf16"),
     # packed SFT batch at 98304 tokens, documents of mean length 6000
