@@ -49,7 +49,9 @@ constexpr int kPfS = 2, kPfV = 2;
 
 // Key tiles of BN = 32 (three workgroups per CU) or 64 keys (two): a tile is processed as
 // BN / 32 halves of 32 keys, each S, its softmax and PV in turn, so both tile sizes perform the
-// same operations in the same order and give bitwise-identical results.
+// same operations in the same order and give bitwise-identical results. SPLIT instances can
+// run a row block as nsplit_o workgroups over contiguous ranges of its key tiles, each storing
+// partial results for the combine kernel below.
 template <int D, int BN, bool SPLIT>
 __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void attn_fwd_kernel(AttnArgs a, ShardSrc src) {
   constexpr int BM = 128, DT = D / 16, DB = D / 32;
