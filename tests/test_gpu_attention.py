@@ -263,6 +263,7 @@ def test_packed_dkdv_unsplit_matches_oracle(cu):
     (3000, 8, 2, 64, False, None),                                 # 6 uneven splits of 47 tiles
     (4096, 8, 2, 128, True, None),                                 # 4 splits
     (4500, 24, 6, 128, True, [0, 1, 1000, 1001, 4500]),            # 2 splits of 864 workgroups
+    (3000, 32, 8, 64, False, [0, 1500, 3000]),                     # 2 splits of 768, d 64, non-causal
 ])
 def test_dq_split_matches_oracle(s, Hq, Hkv, d, causal, cu):
     """dQ with each 128-row block's key tiles split over several workgroups (grids of fewer
@@ -297,6 +298,7 @@ def test_dq_split_matches_oracle(s, Hq, Hkv, d, causal, cu):
     (4096, 8, 2, 128, True, None),                                  # 4 splits
     (700, 4, 4, 128, False, [0, 350, 700]),                         # 8 splits, two documents
     (4500, 24, 6, 128, True, [0, 1, 1000, 1001, 4500]),             # 32-key tiles, 2 splits (864 workgroups)
+    (3000, 32, 8, 64, False, [0, 1500, 3000]),                      # 32-key tiles, d 64, non-causal (768)
 ])
 def test_fwd_split_matches_oracle(s, Hq, Hkv, d, causal, cu):
     """The forward with each 128-row block's key tiles split over several workgroups (grids of
@@ -332,16 +334,17 @@ def test_fwd_split_matches_oracle(s, Hq, Hkv, d, causal, cu):
         compare(f"LSE {tag}", lse.cpu().numpy(), wl, max_abs=LSE_ABS, rel_fro=1e-4)
 
 
-def test_dkdv_split_at_two_rounds_matches_oracle():
+@pytest.mark.parametrize("d", [128, 64])
+def test_dkdv_split_at_two_rounds_matches_oracle(d):
     """A 16K share with 2 kv heads has 256 dK/dV key-block workgroups, one round at one per
     CU: the key blocks split in two. dK and dV against the oracle on every key of the first
     block (it sees every row, and its two halves of the rows meet in the reduce), both sides of
     block boundaries at a stride, and the last keys; every element against the unsplit run.
     The outputs start as NaN."""
-    s, Hq, Hkv, d = 16384, 4, 2, 128
+    s, Hq, Hkv = 16384, 4, 2
     assert U.attn_bwd_dkdv_workspace_bytes(s, Hkv, d) > 0
-    print(f"case dK/dV split at two rounds s={s}", flush=True)
-    f, g = _inputs(s, Hq, Hkv, d, "bf16", seed=21)
+    print(f"case dK/dV split at two rounds s={s} d={d}", flush=True)
+    f, g = _inputs(s, Hq, Hkv, d, "bf16", seed=21 + d)
     scale = 1.0 / np.sqrt(d)
     o_lo = U.new_o_lo(g["q"])
     o, lse = U.attn_fwd(g["q"], g["k"], g["v"], scale, True, o_lo=o_lo)
