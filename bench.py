@@ -30,8 +30,15 @@ Besides the step, the permutes are timed cold: each permute of the step is run a
 512 MiB write that evicts the 256 MB Infinity Cache and the L2s, several times, and reported
 with median, min and max; their rate against the 8 TB/s HBM peak is `permute_roofline`.
 
+--ring times Ring Attention, the pages' comparison workload, over the whole layer on one GPU
+(every rank's ring forward, then every rank's ring backward in rank order), with P times the
+Ulysses rank share of the same layer beside it. --exchange times one rank's send-side and
+receive-side permutes of a training step (what a real all-to-all needs around it), cold, on
+the workload and with its kv heads replicated to two ranks each; it prints its own line.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                       [--heads-per-chunk U] [--unchunked] [--forward-only [--fused]]
+                       [--heads-per-chunk U] [--unchunked] [--forward-only [--fused]] [--ring]
+                       [--exchange]
 """
 import argparse
 import contextlib
@@ -93,6 +100,45 @@ def training_work(cfg, pairs):
         "attn_fwd_shards": ("mfma", 4.0 * d * pairs * Hq_l),
         "attn_bwd_shards": ("mfma", 10.0 * d * pairs * Hq_l),
     }
+
+
+def ring_work(cfg):
+    """Ring Attention on the whole layer (every rank's token block of all Hq heads): per rank
+    call, (bound, counted FLOPs). Rank r's rows see r earlier blocks whole and its own block
+    causally (s_l^2 (r + 1/2) pairs per head; every block whole without the causal mask); the
+    forward counts 4 d N and the backward 10 d N per head, as the training step does."""
+    s_l, P, d, Hq = float(cfg.s_l), cfg.P, cfg.d, cfg.Hq
+    out = {}
+    for r in range(P):
+        pairs = s_l * s_l * (r + 0.5) if cfg.causal else s_l * s_l * P
+        out[f"ring_fwd_r{r}"] = ("mfma", 4.0 * d * pairs * Hq)
+        out[f"ring_bwd_r{r}"] = ("mfma", 10.0 * d * pairs * Hq)
+    return out
+
+
+def exchange_shapes(cfg):
+    """The send-side and receive-side permutes of one rank per training step, as (name, H, kind):
+    send_pack of Q, K, V (forward) and dO (backward) from its sequence shards, recv_unpack of O
+    (forward) and dQ, dK, dV (backward) into them."""
+    return [("send_q", cfg.Hq, "send"), ("send_k", cfg.Hkv, "send"), ("send_v", cfg.Hkv, "send"),
+            ("send_do", cfg.Hq, "send"), ("recv_o", cfg.Hq, "recv"), ("recv_dq", cfg.Hq, "recv"),
+            ("recv_dk", cfg.Hkv, "recv"), ("recv_dv", cfg.Hkv, "recv")]
+
+
+def exchange_bytes(cfg, H):
+    """Bytes one send_pack or recv_unpack moves (read + write) for H heads: the shard
+    [s_l, H, d] and the P blocks [P, s_l, H_l, d], H_l = H/P, or one replicated head each
+    when H < P (a send then writes, and a receive reads, P/H copies of each head)."""
+    e = cfg.esize
+    hl = H // cfg.P if H % cfg.P == 0 else 1
+    return float(cfg.s_l * H * cfg.d * e + cfg.P * cfg.s_l * hl * cfg.d * e)
+
+
+def replicated_variant(cfg):
+    """The same model and sequence over twice as many ranks as kv heads: each kv head then goes
+    to two ranks (send_pack writes it twice, recv_unpack sums its two gradient partials)."""
+    P = 2 * cfg.Hkv
+    return W.Config(f"{cfg.name}_sp{P}", P=P, s_l=cfg.s // P, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, dtype=cfg.dtype)
 
 
 def source_hash(kernel=None):
@@ -368,6 +414,94 @@ def run_upipe(cfg, steps, warmup, u, forward_only):
     return (wall,) + ph.summary(steps) + (need,)
 
 
+def run_ring(cfg, steps, warmup):
+    """Ring Attention over the whole layer on one GPU (the pages' comparison workload): every
+    rank's ring forward, then every rank's ring backward in rank order (the order in which the
+    dK/dV sums travel round the ring), each call timed; the ranks' buffers are separate
+    allocations, as in the tests."""
+    _, sh = make_inputs(cfg)
+    P, s_l, Hq, Hkv, d = cfg.P, cfg.s_l, cfg.Hq, cfg.Hkv, cfg.d
+    L = U.lib()
+
+    def bufs():
+        o = [torch.empty_like(x) for x in sh["q"]]
+        lo = [torch.empty(x.shape, dtype=torch.bfloat16, device="cuda") for x in sh["q"]]
+        lse = [torch.empty((Hq, s_l), dtype=torch.float32, device="cuda") for _ in range(P)]
+        dq = [torch.empty_like(x) for x in sh["q"]]
+        dk = [torch.empty_like(x) for x in sh["k"]]
+        dv = [torch.empty_like(x) for x in sh["v"]]
+        acc = [torch.empty((P, s_l, Hkv, d), dtype=torch.float32, device="cuda") for _ in range(2)]
+        ws = [torch.empty(int(L.ring_attn_fwd_workspace_bytes(s_l, Hq, d)), dtype=torch.uint8, device="cuda"),
+              torch.empty(int(L.ring_attn_bwd_workspace_bytes(s_l, Hq, d)), dtype=torch.uint8, device="cuda")]
+        return o, lo, lse, dq, dk, dv, acc, ws
+    (o, lo, lse, dq, dk, dv, acc, ws), inter, _ = alloc_bytes(bufs)
+    ph = Phases()
+
+    def step(rec):
+        for r in range(P):
+            ph.run(f"ring_fwd_r{r}", lambda: U.ring_attn_fwd(sh["q"], sh["k"], sh["v"], r, cfg.scale, cfg.causal,
+                                                             out=o[r], lse=lse[r], o_lo=lo[r], workspace=ws[0]), rec)
+        for r in range(P):
+            ph.run(f"ring_bwd_r{r}", lambda: U.ring_attn_bwd(sh["q"], sh["k"], sh["v"], o[r], lse[r], sh["do"][r], r,
+                                                             acc[0], acc[1], dk, dv, cfg.scale, cfg.causal, dq=dq[r],
+                                                             o_lo=lo[r], workspace=ws[1]), rec)
+
+    for _ in range(warmup):
+        step(False)
+    with no_gc():
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(True)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        call_peak = torch.cuda.max_memory_allocated() - base
+    return (wall,) + ph.summary(steps) + ({"intermediate_bytes": int(inter), "calls_peak_alloc_bytes": int(call_peak)},)
+
+
+def run_exchange(cfg, reps=7):
+    """One rank's send-side and receive-side permutes of a training step, each alone on a cold
+    cache (after a 512 MiB cache-evicting write, as the step's permutes are timed cold):
+    ulysses_send_pack of its Q, K, V and dO sequence shards into P per-destination blocks and
+    ulysses_recv_unpack of P received blocks of O, dQ, dK and dV into its sequence shards
+    (replicated kv heads summed). Returns per-phase median / min / max ms and bytes."""
+    P, s_l, d = cfg.P, cfg.s_l, cfg.d
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    src = {n: W.torch_from_bits(W.gen_rows(cfg, n, 0, s_l), cfg.dtype, "cuda") for n in ("q", "k", "v", "do")}
+    calls, nbytes = {}, {}
+    for name, H, kind in exchange_shapes(cfg):
+        hl = U.rank_heads(0, P, H)[1]
+        blocks = torch.zeros((P, s_l, hl, d), dtype=dt, device="cuda")
+        if kind == "send":
+            shard = src[name.split("_", 1)[1]]
+            calls[name] = (lambda x=shard, b=blocks: U.ulysses_send_pack(x, P, b))
+        else:
+            shard = torch.empty((s_l, H, d), dtype=dt, device="cuda")
+            calls[name] = (lambda b=blocks, x=shard, h=H: U.ulysses_recv_unpack(b, h, x))
+        nbytes[name] = exchange_bytes(cfg, H)
+    for fn in calls.values():
+        fn()
+    torch.cuda.synchronize()
+    return cold_permutes(calls, reps), nbytes
+
+
+def exchange_line(cfg, spread, nbytes):
+    ms = sum(v["median"] for v in spread.values())
+    total = sum(nbytes.values())
+    gbs = total / (ms * 1e-3) / 1e9
+    return {"config": {"P": cfg.P, "s_l": cfg.s_l, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.d,
+                       "kv_replicated_to": cfg.P // cfg.Hkv if cfg.Hkv < cfg.P else 1},
+            "ms_per_step": round(ms, 4), "bytes_per_step": int(total),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)},
+            "phase_ms_median": {k: round(v["median"], 4) for k, v in spread.items()},
+            "phase_ms_min": {k: round(v["min"], 4) for k, v in spread.items()},
+            "phase_ms_max": {k: round(v["max"], 4) for k, v in spread.items()},
+            "phase_bytes": {k: int(v) for k, v in nbytes.items()}}
+
+
 def measured_ceilings():
     """Practical ceilings on this GPU, beside the published peaks: back-to-back bf16 MFMAs on
     every SIMD (uly_mfma_probe, with the sustained shader clock), the attention kernels'
@@ -440,6 +574,33 @@ def cpu_baseline(cfg):
                                   f"shards ({moved / 2**20:.1f} MiB read + written, one thread); {dtp:.2f} s"}}
 
 
+def main_exchange(args, cfg):
+    """--exchange: one JSON line for one rank's send/recv permutes of a training step on the
+    workload, with the kv-replicated variant beside it."""
+    spread, nbytes = run_exchange(cfg)
+    line = exchange_line(cfg, spread, nbytes)
+    rcfg = replicated_variant(cfg)
+    rep_line = None
+    if rcfg.Hq % rcfg.P == 0 and cfg.dtype == "bf16":
+        rs, rb = run_exchange(rcfg)
+        rep_line = exchange_line(rcfg, rs, rb)
+    ceil = measured_ceilings()
+    roof = dict(line["roofline"], kernel="ulysses_send_pack + ulysses_recv_unpack", avg_ms=line["ms_per_step"],
+                traffic=None)
+    roof["frac_of_measured"] = round(roof["achieved"] / ceil["copy_gbs"], 4)
+    out = {"metric": f"send/recv exchange permutes GB/s [workload {args.workload}: one rank's per-step send_pack "
+                     "of Q, K, V, dO and recv_unpack of O, dQ, dK, dV, each alone on a cold cache]",
+           "value": roof["achieved"], "unit": "GB/s", "n_gpus": 1, "steps": 7, "warmup": 1,
+           "ms_per_step": line["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": cfg.dtype, "data": "synthetic",
+           "config": dict(line["config"], workload=f"{args.workload}: one rank's all-to-all buffers"),
+           "roofline": roof, "bytes_per_step": line["bytes_per_step"],
+           "phase_ms_median": line["phase_ms_median"], "phase_ms_min": line["phase_ms_min"],
+           "phase_ms_max": line["phase_ms_max"], "phase_bytes": line["phase_bytes"],
+           "replicated_kv": rep_line, "measured_ceilings": ceil}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -455,6 +616,13 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="attn_fwd_shards / attn_bwd_shards, reading and writing the sequence shards directly "
                          "(no head-shard buffers, no separate permutes)")
+    ap.add_argument("--ring", action="store_true",
+                    help="Ring Attention over the whole layer (every rank's token block of all heads, forward then "
+                         "backward in rank order), beside the Ulysses ranks' shares of the same layer")
+    ap.add_argument("--exchange", action="store_true",
+                    help="one rank's send-side and receive-side permutes of a training step (send_pack of Q, K, V, "
+                         "dO; recv_unpack of O, dQ, dK, dV), cold cache, and the same with each kv head "
+                         "replicated to two ranks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy (ulysses_pack with one rank) and exit; "
@@ -477,14 +645,37 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
         return
     cfg = W.WORKLOADS[args.workload]
+    if args.exchange:
+        return main_exchange(args, cfg)
     cu = W.cu_seqlens_for(cfg)
     cu_dev = None if cu is None else torch.from_numpy(cu).to("cuda")
     pairs = counted_pairs(cfg, cu)
     d, Hq_l, Hkv_l, e = cfg.d, cfg.Hq_l, cfg.Hkv_l, cfg.esize
 
-    chunked = bool(cfg.chunk_heads) and not args.unchunked
-    cold = mem = None
-    if not chunked and args.forward_only:
+    chunked = bool(cfg.chunk_heads) and not args.unchunked and not args.ring
+    cold = mem = ring_cmp = None
+    if args.ring:
+        if cu is not None or cfg.dtype != "bf16":
+            print("--ring runs bf16 workloads without packed documents", file=sys.stderr)
+            sys.exit(2)
+        wall, ph, spread, mem = run_ring(cfg, args.steps, args.warmup)
+        kern = ring_work(cfg)
+        flops = sum(w for _, w in kern.values())
+        # the same layer as the Ulysses ranks split it, on this machine: the ranks' shares are equal
+        # (every position of H/P heads each), so P times rank 0's training step
+        u_steps = max(2, args.steps // 2)
+        u_wall = run_training_share(cfg, u_steps, 1, cu_dev)[0]
+        # per rank: a P-GPU job waits for its slowest rank, and the causal ring's ranks do unequal
+        # work (rank r attends r + 1 blocks); the Ulysses ranks' shares are equal
+        rank_ms = [ph[f"ring_fwd_r{r}"] + ph[f"ring_bwd_r{r}"] for r in range(cfg.P)]
+        ring_cmp = {"ring_layer_ms": round(wall * 1e3, 3), "ulysses_layer_ms": round(cfg.P * u_wall * 1e3, 3),
+                    "ring_over_ulysses": round(wall / (cfg.P * u_wall), 4),
+                    "ring_rank_ms": [round(x, 3) for x in rank_ms], "ulysses_rank_ms": round(u_wall * 1e3, 3),
+                    "slowest_ring_rank_over_ulysses_rank": round(max(rank_ms) / (u_wall * 1e3), 4),
+                    "how": f"Ulysses: {cfg.P} x rank 0's training step (permutes, forward, backward), "
+                           f"{u_steps} steps; ring: every rank's ring_attn_fwd then ring_attn_bwd; attention work "
+                           "only, one GPU, no collective"}
+    elif not chunked and args.forward_only:
         wall, ph, spread, mem = run_forward_share(cfg, args.steps, args.warmup, cu_dev, args.fused)
         fw = 4.0 * d * pairs * Hq_l
         kern = {"attn_fwd": ("mfma", fw), "attn_fwd_shards": ("mfma", fw),
@@ -519,8 +710,9 @@ def main():
     roof["avg_ms"] = round(ms, 4)
     roof["traffic"] = read_traffic(dom, args.workload)
 
-    attn_ms = sum(ph.get(k, 0.0) for k in ("attn_fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "attn_fwd_chunked",
-                                           "attn_bwd_chunked", "attn_fwd_shards", "attn_bwd_shards"))
+    attn_ms = sum(v for k, v in ph.items() if k.startswith("ring_") or k in (
+        "attn_fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "attn_fwd_chunked", "attn_bwd_chunked", "attn_fwd_shards",
+        "attn_bwd_shards"))
     # the permutes' rate inside the step from the per-phase medians (see Phases.summary: the first
     # phase of the first timed step also holds a host launch latency)
     perm_names = ("pack_qkv", "unpack_o", "pack_do", "unpack_grads")
@@ -528,9 +720,10 @@ def main():
     perm_bytes = sum(kern[k][1] for k in perm_names if k in ph)
     value = flops / wall / 1e12
     out = {
-        "metric": METRIC if args.workload == "qwen_64k" and not (args.forward_only or args.fused) else
+        "metric": METRIC if args.workload == "qwen_64k" and not (args.forward_only or args.fused or args.ring) else
         f"{METRIC} [workload {args.workload}{', unchunked' if args.unchunked else ''}"
-        f"{', forward only' if args.forward_only else ''}{', fused exchange' if args.fused else ''}]",
+        f"{', forward only' if args.forward_only else ''}{', fused exchange' if args.fused else ''}"
+        f"{f', Ring Attention over all {cfg.P} ranks and {cfg.Hq} heads' if args.ring else ''}]",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -554,7 +747,8 @@ def main():
                          (f"unchunked {'forward' if args.forward_only else 'forward+backward'} of the 32B-shaped "
                           "SP=8 share at 262144 tokens (every local head at once)"),
                          "tiny_f32": "tiny fp32 case"}[args.workload],
-            "seq_len": cfg.s, "ranks_simulated": cfg.P, "rank": 0, "q_heads": Hq_l, "kv_heads": Hkv_l,
+            "seq_len": cfg.s, "ranks_simulated": cfg.P, "rank": "all" if args.ring else 0,
+            "q_heads": cfg.Hq if args.ring else Hq_l, "kv_heads": cfg.Hkv if args.ring else Hkv_l,
             "head_dim": d, "causal": cfg.causal, "packed_docs": None if cu is None else int(len(cu) - 1),
             "global_batch": 1, "parallelism": f"sp{cfg.P} (one rank's share, ranks as buffers)",
         },
@@ -578,6 +772,8 @@ def main():
             "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": cold_bytes, "ms": round(cold_ms, 4),
             "how": "each permute of the step alone after a 512 MiB cache-evicting write, 7 runs, medians",
             "phases": {k: {m: round(x, 4) for m, x in v.items()} for k, v in cold.items()}}
+    if ring_cmp:
+        out["ring_vs_ulysses"] = ring_cmp
     if mem is not None:
         # device memory of the share's intermediates (head shards, delta), measured with torch's
         # allocator, and the peak the library's calls added (they allocate nothing)

@@ -58,3 +58,34 @@ def test_counter_readings_are_keyed_to_their_own_kernel(bench):
     assert "attn_fwd.hip" not in bench.KERNEL_SOURCES["bwd_dkdv"]
     assert bench.source_hash("bwd_dkdv") == bench.source_hash("bwd_dq")
     assert bench.source_hash("bwd_dkdv") != bench.source_hash("attn_fwd")
+
+
+def test_ring_work_sums_to_the_layer(bench):
+    """Ring Attention's per-rank calls cover the whole causal layer once: rank r's rows see r
+    earlier blocks whole and their own block causally, s_l^2 (r + 1/2) pairs per head, summing to
+    s^2/2; 14 d N FLOPs per head over all 32 heads at 64K."""
+    cfg = W.WORKLOADS["qwen_64k"]
+    k = bench.ring_work(cfg)
+    s_l = float(cfg.s_l)
+    assert sorted(k) == sorted([f"ring_fwd_r{r}" for r in range(4)] + [f"ring_bwd_r{r}" for r in range(4)])
+    for r in range(4):
+        assert k[f"ring_fwd_r{r}"][1] == 4.0 * cfg.d * s_l * s_l * (r + 0.5) * cfg.Hq
+        assert k[f"ring_bwd_r{r}"][1] == 2.5 * k[f"ring_fwd_r{r}"][1]
+    total = sum(w for _, w in k.values())
+    assert total == pytest.approx(14.0 * cfg.d * cfg.s ** 2 / 2 * cfg.Hq, rel=1e-12)
+    assert total == pytest.approx(4 * 3.079e13, rel=1e-3)   # the 4 Ulysses ranks' shares together
+
+
+def test_exchange_bytes(bench):
+    """send_pack / recv_unpack move the shard [s_l, H, d] and the P blocks [P, s_l, H/P, d]; with
+    a kv head replicated to two ranks the blocks hold one head each, twice the shard's kv bytes."""
+    cfg = W.WORKLOADS["qwen_64k"]
+    mib = 1 << 20
+    names = [n for n, _, _ in bench.exchange_shapes(cfg)]
+    assert names == ["send_q", "send_k", "send_v", "send_do", "recv_o", "recv_dq", "recv_dk", "recv_dv"]
+    assert bench.exchange_bytes(cfg, cfg.Hq) == 256 * mib      # 128 MiB shard + 128 MiB of blocks
+    assert bench.exchange_bytes(cfg, cfg.Hkv) == 64 * mib
+    rcfg = bench.replicated_variant(cfg)
+    assert (rcfg.P, rcfg.s_l, rcfg.s) == (16, 4096, cfg.s)
+    assert bench.exchange_bytes(rcfg, rcfg.Hkv) == 8 * mib + 16 * mib    # shard 8 MiB, 16 blocks of one head
+    assert bench.exchange_bytes(rcfg, rcfg.Hq) == 64 * mib     # 32 MiB shard + 32 MiB of blocks
