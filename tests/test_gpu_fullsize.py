@@ -1,5 +1,6 @@
 """Parity at the full size of the 64K headline share and of the packed 96K share (rank 0),
-through the same calls and launch configuration the bench times.
+and of a one-rank share of a million-token sequence, through the same calls and launch
+configuration the bench times.
 
 The oracle cannot afford every element at these sizes, so it checks what it can compute
 exactly one by one:
@@ -109,6 +110,21 @@ def test_qwen_64k_share():
     s = cfg.s
     keys = set(range(s - 64, s))
     for b in range(s - 1024, s, 128):
+        keys |= {b - 1, b}
+    _run(cfg, 0, (), np.array(sorted(keys)), [(0, s)])
+
+
+@pytest.mark.timeout(900)
+def test_million_token_share():
+    """One rank's share of a 1,048,576-token sequence, the context length in the title of the
+    first page: 8 ranks of 131072 tokens, 16 q / 8 kv heads, so 2 q / 1 kv heads per rank after
+    the exchange. The checks of the 64K share at sixteen times its length: sampled rows of O,
+    LSE and dQ, the last keys' dK and dV, and the column sums of dV and dK over all 2^20
+    keys."""
+    cfg = W.Config("million", P=8, s_l=131072, Hq=16, Hkv=8, d=128, dtype="bf16")
+    s = cfg.s
+    keys = set(range(s - 64, s))
+    for b in range(s - 512, s, 128):
         keys |= {b - 1, b}
     _run(cfg, 0, (), np.array(sorted(keys)), [(0, s)])
 
