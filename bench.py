@@ -741,6 +741,7 @@ def main():
                          "qwen_16k": "Qwen3-4B-shaped SP=4 rank share at 16384 tokens",
                          "qwen_32k": "Qwen3-4B-shaped SP=4 rank share at 32768 tokens",
                          "packed_96k": "packed SFT batch at 98304 tokens (documents ~ geometric, mean 6000)",
+                         "million": "one rank's share of a 1048576-token sequence (SP=8, 16 q / 8 kv heads)",
                          "upipe_256k": (f"UPipe headwise-chunked {'forward' if args.forward_only else 'forward+backward'}, "
                                         f"32B-shaped SP=8 share at 262144 tokens, {args.heads_per_chunk} q heads per "
                                         "chunk") if chunked else

@@ -121,7 +121,7 @@ def test_million_token_share():
     the exchange. The checks of the 64K share at sixteen times its length: sampled rows of O,
     LSE and dQ, the last keys' dK and dV, and the column sums of dV and dK over all 2^20
     keys."""
-    cfg = W.Config("million", P=8, s_l=131072, Hq=16, Hkv=8, d=128, dtype="bf16")
+    cfg = W.WORKLOADS["million"]
     s = cfg.s
     keys = set(range(s - 64, s))
     for b in range(s - 512, s, 128):

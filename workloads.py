@@ -88,6 +88,8 @@ WORKLOADS = {
     # packed SFT batch at 98304 tokens, documents of mean length 6000
     "packed_96k": Config("packed_96k", P=4, s_l=24576, Hq=32, Hkv=8, d=128, dtype="bf16",
                          packed_mean=6000.0),
+    # one rank's share of a million-token sequence: 8 ranks of 131072 tokens, 16 q / 8 kv heads
+    "million": Config("million", P=8, s_l=131072, Hq=16, Hkv=8, d=128, dtype="bf16"),
     # UPipe headwise-chunked share, 32B-shaped SP=8 at 262144 tokens
     "upipe_256k": Config("upipe_256k", P=8, s_l=32768, Hq=64, Hkv=8, d=128, dtype="bf16",
                          chunk_heads=(1, 2)),
