@@ -236,7 +236,8 @@ int attn_bwd_preprocess(const void* o, const void* o_lo, const void* dout, float
  * given (bf16), each key block's rows are split over up to 8 workgroups (aiming at 512) that
  * store fp32 partial sums, and a second kernel adds them in split order and rounds once:
  * still deterministic; the sums' order, and so the last bits, differ from the unsplit run.
- * The size is 0 when no split applies; workspace NULL runs unsplit.                     */
+ * The size is 0 when no split applies; a NULL or smaller workspace runs unsplit; a workspace
+ * must be 16-byte aligned (ULY_ERR_ALIGN).                                                 */
 size_t attn_bwd_dkdv_workspace_bytes(int64_t s, int Hkv, int d);
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                   const void* dout, const float* delta, void* dk, void* dv,
@@ -251,7 +252,8 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
  * split over up to 8 workgroups (aiming at 1024) that store fp32 partial sums, and a second
  * kernel adds them in split order, scales and rounds once: deterministic; the sums' order,
  * and so the last bits, differ from the unsplit run. The size is 0 when no split applies;
- * workspace NULL runs unsplit.                                                        */
+ * a NULL or smaller workspace runs unsplit; a workspace must be 16-byte aligned
+ * (ULY_ERR_ALIGN).                                                                    */
 size_t attn_bwd_dq_workspace_bytes(int64_t s, int Hq, int d);
 int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                 const void* dout, const float* delta, void* dq,
