@@ -2,7 +2,9 @@
 head counts and GQA group sizes, head dims 64 and 128, causal and not, and packed batches of
 1 to 80 documents (some of length 1 or 0), against the fp64 oracle with the tolerances of
 tests/helpers.py. Each case also runs dK/dV with one workgroup per key block (no split), the
-launch configuration of long sequences, and checks it against the same oracle values."""
+launch configuration of long sequences, and checks it against the same oracle values. A
+second batch puts 32 q heads over 2945-4480 tokens, the mid-size grids where the forward's
+32-key tiles, dQ and dK/dV all split, with the unsplit forward beside it."""
 import numpy as np
 import pytest
 import torch
@@ -55,3 +57,44 @@ def test_random_shape_matches_oracle(seed):
     compare("dV", dev_to_f64(dv), wv, bf16=True)
     compare("dK unsplit", dev_to_f64(dk1), wk, bf16=True)
     compare("dV unsplit", dev_to_f64(dv1), wv, bf16=True)
+
+
+def _mid_case(seed):
+    """32 q heads over 2945-4480 tokens: 768-1120 forward workgroups (the 32-key tiles split in
+    two), dQ split below 1024 workgroups, dK/dV split below 512."""
+    rng = np.random.default_rng(2000 + seed)
+    s = int(rng.integers(2945, 4481))
+    G = int(rng.choice([4, 8]))
+    d = 128 if seed % 2 == 0 else 64
+    causal = bool(rng.random() < 0.7)
+    n = int(rng.choice([1, 3, 30]))
+    cu = None
+    if n > 1:
+        cuts = np.sort(rng.integers(0, s + 1, n - 1))
+        cu = [0] + [int(c) for c in cuts] + [s]
+    return s, 32, 32 // G, d, causal, cu
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_mid_grid_matches_oracle(seed):
+    s, Hq, Hkv, d, causal, cu = _mid_case(seed)
+    assert 768 <= (s + 127) // 128 * Hq < 1152 and U.attn_fwd_workspace_bytes(s, Hq, d) > 0
+    print(f"case random mid seed={seed} s={s} Hq={Hq} Hkv={Hkv} d={d} causal={causal} "
+          f"docs={None if cu is None else len(cu) - 1}", flush=True)
+    f, g = _inputs(s, Hq, Hkv, d, "bf16", seed=100 + seed)
+    scale = 1.0 / np.sqrt(d)
+    cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    o_lo = U.new_o_lo(g["q"])
+    o, lse = U.attn_fwd(g["q"], g["k"], g["v"], scale, causal, cu_dev, o_lo=o_lo)
+    o1, lse1 = U.attn_fwd(g["q"], g["k"], g["v"], scale, causal, cu_dev, split=False)
+    dq, dk, dv = U.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale, causal, cu_dev, o_lo=o_lo)
+    torch.cuda.synchronize()
+    wo, wl = OA.forward(f["q"], f["k"], f["v"], scale, causal, cu)
+    wq, wk, wv = OA.backward(f["q"], f["k"], f["v"], f["do"], scale, causal, cu)
+    compare("O", dev_to_f64(o), wo, bf16=True)
+    compare("LSE", lse.cpu().numpy(), wl, max_abs=LSE_ABS, rel_fro=1e-4)
+    compare("O unsplit", dev_to_f64(o1), wo, bf16=True)
+    compare("LSE unsplit", lse1.cpu().numpy(), wl, max_abs=LSE_ABS, rel_fro=1e-4)
+    compare("dQ", dev_to_f64(dq), wq, bf16=True)
+    compare("dK", dev_to_f64(dk), wk, bf16=True)
+    compare("dV", dev_to_f64(dv), wv, bf16=True)
